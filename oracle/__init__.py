@@ -1,0 +1,252 @@
+"""CPU oracle for the weight-quantized decode GEMV (TEST INFRASTRUCTURE).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path never does.
+
+The arithmetic lives in ``qlin_oracle.c`` (plain loops, fp64/int64
+accumulation, one final round to bf16); this module only marshals numpy
+arrays through ctypes.  bf16 arrays are carried as ``uint16`` bit patterns.
+Each wrapper names the page section its C function follows (see the header of
+``qlin_oracle.c`` for the page titles).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qlin_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+BLK = 128  # weight block edge and activation group width of the block-scaled path
+
+
+def build(verbose: bool = False) -> str:
+    """Compile ``qlin_oracle.c`` into ``liboracle.so`` (gcc -O2, OpenMP, no fast-math)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+           "-ffp-contract=off", "-fno-fast-math", _SRC, "-o", _LIB_PATH + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    I = ctypes.c_int
+    lib.orc_set_threads.argtypes = [I]
+    lib.orc_max_threads.restype = I
+    lib.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.orc_bf16_to_f32.restype = ctypes.c_float
+    lib.orc_f32_to_bf16.argtypes = [ctypes.c_float]
+    lib.orc_f32_to_bf16.restype = ctypes.c_uint16
+    lib.orc_f64_to_bf16.argtypes = [ctypes.c_double]
+    lib.orc_f64_to_bf16.restype = ctypes.c_uint16
+    lib.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.orc_e4m3_decode.restype = ctypes.c_double
+    lib.orc_e4m3_encode.argtypes = [ctypes.c_double]
+    lib.orc_e4m3_encode.restype = ctypes.c_uint8
+    lib.orc_e2m1_decode.argtypes = [ctypes.c_uint8]
+    lib.orc_e2m1_decode.restype = ctypes.c_double
+    lib.orc_ue8m0_decode.argtypes = [ctypes.c_uint8]
+    lib.orc_ue8m0_decode.restype = ctypes.c_double
+    lib.orc_act_quant_i8.argtypes = [P, I64, I64, I64, P, I64, P]
+    lib.orc_gemv_i8.argtypes = [P, I64, P, I, I64, I64, P, I64, I64, P, I, P, P, P, I64]
+    lib.orc_gemv_fp8.argtypes = [P, I64, I64, I64, P, I64, I64, P, I, P, I64, P, P]
+    lib.orc_blk_act_quant.argtypes = [P, I64, I64, I64, P, P]
+    lib.orc_gemv_fp8_blk.argtypes = [P, P, I64, I64, P, I64, I64, P, P, I64, P, P]
+    lib.orc_moe_mxfp4.argtypes = [P, I64, I64, I64, P, P, I64, I64, P, P, I64, P, I64, P, P]
+    _lib = lib
+    return lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a)
+    if a.dtype != dtype:
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    return a
+
+
+def set_threads(n: int) -> None:
+    _load().orc_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(_load().orc_max_threads())
+
+
+# --------------------------------------------------------------------------- formats
+
+def bf16_to_f32(h: np.ndarray) -> np.ndarray:
+    lib = _load()
+    h = np.asarray(h, dtype=np.uint16)
+    return np.array([lib.orc_bf16_to_f32(int(v)) for v in h.ravel()], dtype=np.float32).reshape(h.shape)
+
+
+def f32_to_bf16(f: np.ndarray) -> np.ndarray:
+    lib = _load()
+    f = np.asarray(f, dtype=np.float32)
+    return np.array([lib.orc_f32_to_bf16(float(v)) for v in f.ravel()], dtype=np.uint16).reshape(f.shape)
+
+
+def f64_to_bf16(d: np.ndarray) -> np.ndarray:
+    lib = _load()
+    d = np.asarray(d, dtype=np.float64)
+    return np.array([lib.orc_f64_to_bf16(float(v)) for v in d.ravel()], dtype=np.uint16).reshape(d.shape)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    lib = _load()
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.array([lib.orc_e4m3_decode(int(v)) for v in c.ravel()], dtype=np.float64).reshape(c.shape)
+
+
+def e4m3_encode(values) -> np.ndarray:
+    lib = _load()
+    v = np.asarray(values, dtype=np.float64)
+    return np.array([lib.orc_e4m3_encode(float(t)) for t in v.ravel()], dtype=np.uint8).reshape(v.shape)
+
+
+def e2m1_decode(nibbles) -> np.ndarray:
+    lib = _load()
+    c = np.asarray(nibbles, dtype=np.uint8)
+    return np.array([lib.orc_e2m1_decode(int(v)) for v in c.ravel()], dtype=np.float64).reshape(c.shape)
+
+
+def ue8m0_decode(b) -> np.ndarray:
+    lib = _load()
+    c = np.asarray(b, dtype=np.uint8)
+    return np.array([lib.orc_ue8m0_decode(int(v)) for v in c.ravel()], dtype=np.float64).reshape(c.shape)
+
+
+# --------------------------------------------------------------------------- (a) INT8
+
+def act_quant_i8(x_bf16: np.ndarray):
+    """Per-token dynamic symmetric INT8 quantisation ([Z100] section 2.1).
+
+    x_bf16: uint16 [M, K].  Returns (xq int8 [M, K], xs float32 [M])."""
+    x = _c(x_bf16, np.uint16)
+    M, K = x.shape
+    xq = np.zeros((M, K), dtype=np.int8)
+    xs = np.zeros((M,), dtype=np.float32)
+    _load().orc_act_quant_i8(_p(x), K, M, K, _p(xq), K, _p(xs))
+    return xq, xs
+
+
+def gemv_i8(xq, xs, w, ws, bias=None):
+    """W8A8 GEMV with int32 accumulation and the (acc*x_s)*w_s -> bf16 -> +bias
+    epilogue ([Z100] section 2 table, INT8 row).
+
+    xs is [M] or [1]; ws is [N] or [1].  Returns (acc int32 [M, N], y uint16 [M, N])."""
+    xq = _c(xq, np.int8)
+    w = _c(w, np.int8)
+    xs = _c(np.atleast_1d(xs), np.float32)
+    ws = _c(np.atleast_1d(ws), np.float32)
+    M, K = xq.shape
+    N, Kw = w.shape
+    assert Kw == K
+    b = None if bias is None else _c(bias, np.uint16)
+    acc = np.zeros((M, N), dtype=np.int32)
+    y = np.zeros((M, N), dtype=np.uint16)
+    _load().orc_gemv_i8(_p(xq), K, _p(xs), int(xs.size > 1), M, K, _p(w), K, N,
+                        _p(ws), int(ws.size > 1), _p(b), _p(acc), _p(y), N)
+    return acc, y
+
+
+# --------------------------------------------------------------------------- (b) FP8 weight-only
+
+def gemv_fp8(x_bf16, w_e4m3, ws):
+    """FP8-E4M3 weight-only GEMV, scale applied once ([Z100] section 2.2).
+
+    Returns (y uint16 [M, N], y_exact float64 [M, N], S float64 [M, N])."""
+    x = _c(x_bf16, np.uint16)
+    w = _c(w_e4m3, np.uint8)
+    ws = _c(np.atleast_1d(ws), np.float32)
+    M, K = x.shape
+    N = w.shape[0]
+    y = np.zeros((M, N), dtype=np.uint16)
+    ye = np.zeros((M, N), dtype=np.float64)
+    S = np.zeros((M, N), dtype=np.float64)
+    _load().orc_gemv_fp8(_p(x), K, M, K, _p(w), K, N, _p(ws), int(ws.size > 1), _p(y), N, _p(ye), _p(S))
+    return y, ye, S
+
+
+# --------------------------------------------------------------------------- (c) block-scaled FP8
+
+def blk_act_quant(x_bf16):
+    """Per-token, per-128-group E4M3 quantisation with a UE8M0 scale
+    ([DSV4] section 3.3).  Returns (xq uint8 [M, K], xs uint8 [M, K/128])."""
+    x = _c(x_bf16, np.uint16)
+    M, K = x.shape
+    assert K % BLK == 0
+    xq = np.zeros((M, K), dtype=np.uint8)
+    xs = np.zeros((M, K // BLK), dtype=np.uint8)
+    _load().orc_blk_act_quant(_p(x), K, M, K, _p(xq), _p(xs))
+    return xq, xs
+
+
+def gemv_fp8_blk(xq, xs, w_e4m3, ws_blk):
+    """Block-scaled GEMV core ([Z100] section 2.4).  ws_blk is [ceil(N/128), K/128].
+
+    Returns (y uint16 [M, N], y_exact float64, S float64)."""
+    xq = _c(xq, np.uint8)
+    xs = _c(xs, np.uint8)
+    w = _c(w_e4m3, np.uint8)
+    wsb = _c(ws_blk, np.uint8)
+    M, K = xq.shape
+    N = w.shape[0]
+    assert wsb.shape == ((N + BLK - 1) // BLK, K // BLK)
+    y = np.zeros((M, N), dtype=np.uint16)
+    ye = np.zeros((M, N), dtype=np.float64)
+    S = np.zeros((M, N), dtype=np.float64)
+    _load().orc_gemv_fp8_blk(_p(xq), _p(xs), M, K, _p(w), K, N, _p(wsb), _p(y), N, _p(ye), _p(S))
+    return y, ye, S
+
+
+def fp8_blk(x_bf16, w_e4m3, ws_blk):
+    """Whole block-scaled path: activation quantisation then GEMV.
+
+    Returns (xq, xs, y, y_exact, S)."""
+    xq, xs = blk_act_quant(x_bf16)
+    y, ye, S = gemv_fp8_blk(xq, xs, w_e4m3, ws_blk)
+    return xq, xs, y, ye, S
+
+
+# --------------------------------------------------------------------------- (d) MXFP4 MoE
+
+def moe_mxfp4(x_bf16, w_fp4, s_ue8m0, topk_ids, topk_w):
+    """Top-k routed MXFP4 expert GEMV with weighted sum ([DSV4] section 9.3).
+
+    w_fp4: uint8 [E, N, K/2] (element 2i in the low nibble); s_ue8m0: uint8
+    [E, N, K/32]; topk_ids int32 [M, topk]; topk_w float32 [M, topk].
+    Returns (y uint16 [M, N], y_exact float64, S float64)."""
+    x = _c(x_bf16, np.uint16)
+    w = _c(w_fp4, np.uint8)
+    s = _c(s_ue8m0, np.uint8)
+    ids = _c(topk_ids, np.int32)
+    gw = _c(topk_w, np.float32)
+    M, K = x.shape
+    E, N, Kh = w.shape
+    assert Kh * 2 == K and s.shape == (E, N, K // 32)
+    topk = ids.shape[1]
+    y = np.zeros((M, N), dtype=np.uint16)
+    ye = np.zeros((M, N), dtype=np.float64)
+    S = np.zeros((M, N), dtype=np.float64)
+    _load().orc_moe_mxfp4(_p(x), K, M, K, _p(w), _p(s), E, N, _p(ids), _p(gw), topk, _p(y), N, _p(ye), _p(S))
+    return y, ye, S

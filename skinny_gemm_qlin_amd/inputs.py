@@ -1,0 +1,104 @@
+"""Seeded synthetic inputs for the quantized decode GEMV workloads.
+
+This module is shared by the tests, the benchmark and the smoke check, and is
+the ONLY code the HIP path and the CPU oracle have in common.  It holds none
+of the method's arithmetic: values are drawn with ``numpy.random.default_rng``
+(PCG64) and rounded to bf16 / E4M3 storage with torch's own CPU casts (library
+rounding, nearest-even).  Draw order inside one generator is always:
+weights, then weight scales, then activations, then routing.
+
+Workload shapes and distributions (all "seed 0" unless a test says otherwise):
+
+* ``int8_small``  W8A8 GEMV, M=1, N=K=1024.
+* ``int8_decode`` W8A8 GEMV, N=17408, K=5120, M in {1,2,4,8,16}.
+  W int8 uniform in [-127, 127]; per-row fp32 scale uniform in [1e-3, 1e-2];
+  x bf16 ~ N(0, 1).
+* ``fp8_decode``  E4M3 weight-only GEMV, N=17408, K=5120, M in {1,4,8}.
+  Weights drawn bf16 ~ N(0, 0.02) and stored as E4M3 codes with a per-row
+  (or per-tensor) fp32 scale absmax/448; x bf16 ~ N(0, 1).
+* ``fp8_blk``     block-scaled FP8, N=4096, K=7168, M in {1,8,16}.  Weight
+  codes uniform over the 254 finite E4M3 codes; one UE8M0 byte uniform in
+  [115, 125] per 128x128 block; x bf16 ~ N(0, 1).
+* ``moe_mxfp4``   64 experts of [N=2048, K=7168] E2M1 nibbles uniform over
+  all 16 codes, one UE8M0 byte uniform in [118, 126] per (expert, row,
+  32-wide K group); M=8 tokens, x bf16 ~ N(0, 1); per token 6 distinct
+  experts drawn uniformly, weights = softmax of 6 iid N(0, 1) logits.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+# 254 finite OCP E4M3 codes (every byte except S.1111.111)
+_E4M3_FINITE = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+
+
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), torch's round-to-nearest-even cast."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def bf16_values(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float32 values (exact widening)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _e4m3_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> OCP E4M3 codes via torch's float8_e4m3fn cast (inputs are in range)."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+
+
+def gen_int8(M: int, N: int, K: int, seed: int = 0) -> dict:
+    rng = np.random.default_rng(seed)
+    w = rng.integers(-127, 128, size=(N, K), dtype=np.int8)
+    ws = rng.uniform(1e-3, 1e-2, size=(N,)).astype(np.float32)
+    x = bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    return {"w": w, "ws": ws, "x": x}
+
+
+def gen_fp8(M: int, N: int, K: int, seed: int = 0, per_tensor: bool = False) -> dict:
+    rng = np.random.default_rng(seed)
+    wf = bf16_values(bf16_bits(rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)))
+    if per_tensor:
+        ws = np.array([np.abs(wf).max() / np.float32(448.0)], dtype=np.float32)
+        codes = _e4m3_bits(wf / ws[0])
+    else:
+        ws = (np.abs(wf).max(axis=1) / np.float32(448.0)).astype(np.float32)
+        ws = np.where(ws == 0, np.float32(1.0), ws).astype(np.float32)
+        codes = _e4m3_bits(wf / ws[:, None])
+    x = bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    return {"w": codes, "ws": ws, "x": x}
+
+
+def gen_fp8_blk(M: int, N: int, K: int, seed: int = 0, scale_lo: int = 115, scale_hi: int = 125) -> dict:
+    rng = np.random.default_rng(seed)
+    w = _E4M3_FINITE[rng.integers(0, _E4M3_FINITE.size, size=(N, K))]
+    nb = (N + 127) // 128
+    ws = rng.integers(scale_lo, scale_hi + 1, size=(nb, K // 128)).astype(np.uint8)
+    x = bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    return {"w": w, "ws": ws, "x": x}
+
+
+def gen_moe(M: int, E: int, N: int, K: int, topk: int, seed: int = 0,
+            scale_lo: int = 118, scale_hi: int = 126) -> dict:
+    rng = np.random.default_rng(seed)
+    w = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)  # two uniform nibbles per byte
+    s = rng.integers(scale_lo, scale_hi + 1, size=(E, N, K // 32)).astype(np.uint8)
+    x = bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    ids = np.stack([rng.choice(E, size=topk, replace=False) for _ in range(M)]).astype(np.int32)
+    logits = rng.standard_normal((M, topk))
+    e = np.exp(logits - logits.max(axis=1, keepdims=True))
+    gw = (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
+    return {"x": x, "w": w, "s": s, "ids": ids, "gw": gw}
+
+
+# Named workloads (shapes fixed by the published decode configurations).
+WORKLOADS = {
+    "int8_small": {"kind": "int8", "N": 1024, "K": 1024, "Ms": [1]},
+    "int8_decode": {"kind": "int8", "N": 17408, "K": 5120, "Ms": [1, 2, 4, 8, 16]},
+    "fp8_decode": {"kind": "fp8", "N": 17408, "K": 5120, "Ms": [1, 4, 8]},
+    "fp8_blk": {"kind": "fp8_blk", "N": 4096, "K": 7168, "Ms": [1, 8, 16]},
+    "moe_mxfp4": {"kind": "moe", "E": 64, "N": 2048, "K": 7168, "Ms": [8], "topk": 6},
+}

@@ -1,0 +1,83 @@
+"""Pins of the oracle's MXFP4 top-k expert GEMV.
+
+References: a plain dense MXFP4 GEMV written with numpy over the OCP E2M1
+value table (one expert, weight 1), the weighted sum over experts done with
+numpy per expert, slot-order invariance, linearity in the routing weights,
+and the rule that out-of-range expert ids contribute nothing."""
+import numpy as np
+
+from skinny_gemm_qlin_amd.inputs import bf16_values, gen_moe
+
+OCP_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+                     -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0])
+
+
+def _dense_expert(w_e, s_e):
+    """[N, K/2] packed nibbles (element 2i in the low nibble) + [N, K/32] scales -> float64 [N, K]."""
+    N, Kh = w_e.shape
+    vals = np.empty((N, Kh * 2))
+    vals[:, 0::2] = OCP_E2M1[w_e & 0xF]
+    vals[:, 1::2] = OCP_E2M1[w_e >> 4]
+    return vals * np.repeat(2.0 ** (s_e.astype(np.float64) - 127), 32, axis=1)
+
+
+def test_single_expert_is_plain_mxfp4_gemv(orc):
+    d = gen_moe(1, 1, 24, 256, 1, seed=30)
+    ids = np.zeros((1, 1), np.int32)
+    gw = np.ones((1, 1), np.float32)
+    y, ye, S = orc.moe_mxfp4(d["x"], d["w"], d["s"], ids, gw)
+    ref = bf16_values(d["x"]).astype(np.float64) @ _dense_expert(d["w"][0], d["s"][0]).T
+    assert np.all(np.abs(ye - ref) <= 1e-12 * S)
+
+
+def test_nibble_order_one_hot(orc):
+    # byte 0x5A holds element 0 = 0xA (-1.0) in the low nibble and element 1 = 0x5 (3.0)
+    K = 64
+    w = np.zeros((1, 1, K // 2), np.uint8)
+    w[0, 0, 0] = 0x5A
+    s = np.full((1, 1, K // 32), 127, np.uint8)
+    ids = np.zeros((1, 1), np.int32)
+    gw = np.ones((1, 1), np.float32)
+    for k, expect in [(0, -1.0), (1, 3.0)]:
+        x = np.zeros((1, K), np.uint16)
+        x[0, k] = 0x3F80  # 1.0
+        _, ye, _ = orc.moe_mxfp4(x, w, s, ids, gw)
+        assert ye[0, 0] == expect
+
+
+def test_weighted_sum_matches_numpy(orc):
+    d = gen_moe(3, 5, 40, 128, 2, seed=31)
+    y, ye, S = orc.moe_mxfp4(d["x"], d["w"], d["s"], d["ids"], d["gw"])
+    xf = bf16_values(d["x"]).astype(np.float64)
+    ref = np.zeros((3, 40))
+    for t in range(3):
+        for j in range(2):
+            e = d["ids"][t, j]
+            ref[t] += float(d["gw"][t, j]) * (_dense_expert(d["w"][e], d["s"][e]) @ xf[t])
+    assert np.all(np.abs(ye - ref) <= 1e-12 * S)
+
+
+def test_slot_order_and_linearity(orc):
+    d = gen_moe(2, 6, 16, 96, 3, seed=32)
+    _, ye, S = orc.moe_mxfp4(d["x"], d["w"], d["s"], d["ids"], d["gw"])
+    perm = [2, 0, 1]
+    _, ye2, _ = orc.moe_mxfp4(d["x"], d["w"], d["s"], d["ids"][:, perm].copy(), d["gw"][:, perm].copy())
+    assert np.all(np.abs(ye - ye2) <= 1e-12 * S)
+    _, ye3, _ = orc.moe_mxfp4(d["x"], d["w"], d["s"], d["ids"], (d["gw"] * 2).astype(np.float32))
+    assert np.array_equal(ye3, 2 * ye)
+
+
+def test_out_of_range_ids_contribute_nothing(orc):
+    d = gen_moe(2, 4, 8, 64, 3, seed=33)
+    ids = d["ids"].copy()
+    ids[0, 1] = -1
+    ids[1, 2] = 4
+    _, ye, _ = orc.moe_mxfp4(d["x"], d["w"], d["s"], ids, d["gw"])
+    gw = d["gw"].copy()
+    gw[0, 1] = 0.0
+    gw[1, 2] = 0.0
+    ids2 = d["ids"].copy()
+    ids2[0, 1] = 0
+    ids2[1, 2] = 0
+    _, ye2, _ = orc.moe_mxfp4(d["x"], d["w"], d["s"], ids2, gw)
+    assert np.array_equal(ye, ye2)
