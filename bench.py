@@ -1,0 +1,338 @@
+#!/usr/bin/env python3
+"""Benchmark of the weight-quantized decode GEMV on one MI355X.
+
+Default workload (the decode configuration the metric is quoted on):
+W8A8 INT8, N=17408, K=5120.  One step = the whole INT8 decode linear layer
+(qlin_act_quant_i8 + qlin_gemv_i8 with its bf16 epilogue) once at every
+M in {1, 2, 4, 8, 16}.  Weights are cold: each call reads the next of B
+rotating weight copies (B * |W| >= 2 x the 256 MB Infinity Cache).
+
+Prints ONE JSON line.  `value` = algorithmic bytes moved by the timed steps /
+their wall time on the GPU (GB/s, inputs already in HBM).  `roofline`
+describes the dominant kernel (the GEMV): algorithmic bytes per launch /
+mean launch duration from HIP events recorded around every launch on the
+stream it runs on.  `cpu_baseline` times the CPU oracle (oracle/, plain C,
+OpenMP over rows) on the host on the same workload.
+
+Other workloads (--workload fp8_decode | fp8_blk | moe_mxfp4) time the other
+entry points the same way; they are used for profiling, the default run is
+the int8 one.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+MALL_BYTES = 256 << 20  # Infinity Cache
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- byte counts
+
+def bytes_gemv_i8(M, N, K):
+    return N * K + 4 * N + M * K + 4 * M + 2 * M * N          # W, ws, xq, xs, y
+
+
+def bytes_act_quant_i8(M, K):
+    return 2 * M * K + M * K + 4 * M                           # x, xq, xs
+
+
+def bytes_gemv_fp8(M, N, K):
+    return N * K + 4 * N + 2 * M * K + 2 * M * N               # W, ws (per row), x, y
+
+
+def bytes_blk_call(M, N, K):
+    return N * K + ((N + 127) // 128) * (K // 128) + 2 * M * K + 2 * M * N   # W, ws, x, y
+
+
+def bytes_blk_gemv(M, N, K):
+    return N * K + ((N + 127) // 128) * (K // 128) + M * K + M * (K // 128) + 2 * M * N
+
+
+def bytes_moe_call(M, N, K, topk, live):
+    return live * (N * K // 2 + N * K // 32) + 2 * M * K + 2 * M * N + 8 * M * topk
+
+
+# ----------------------------------------------------------------------------- workloads
+
+class Workload:
+    name = ""
+    dtype = ""
+    desc = ""
+
+    def calls(self):
+        """list of (label, fn(copy_index) -> list of (kernel_name, launch_fn))"""
+        raise NotImplementedError
+
+
+def src_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "skinny_gemm_qlin_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload):
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        t = json.load(open(p)).get(workload)
+    except Exception:
+        return None
+    if not t or t.get("src_hash") != src_hash():
+        return None  # counters were taken on other kernel code
+    return t.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="int8_decode",
+                    choices=["int8_decode", "fp8_decode", "fp8_blk", "moe_mxfp4"])
+    ap.add_argument("--ms", default=None, help="comma list of M values (default: the workload's)")
+    ap.add_argument("--rotate", type=int, default=0, help="weight copies (0 = enough to defeat the MALL)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    ap.add_argument("--per-tensor", action="store_true", help="fp8_decode: per-tensor weight scale")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(the per-GPU kernel at a shard's shape is what one GPU measures).", file=sys.stderr)
+        sys.exit(1)
+
+    import numpy as np
+    import torch
+
+    import skinny_gemm_qlin_amd as ql
+    from skinny_gemm_qlin_amd import inputs
+
+    ql.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def tb(b):
+        return t(b.view(np.int16)).view(torch.bfloat16)
+
+    wl = args.workload
+    spec = inputs.WORKLOADS[wl]
+    Ms = [int(m) for m in args.ms.split(",")] if args.ms else list(spec["Ms"])
+    Mmax = max(Ms)
+    N, K = spec["N"], spec["K"]
+
+    # ---------------------------------------------------------------- inputs (seed 0)
+    log(f"bench: generating {wl} inputs N={N} K={K} Ms={Ms}")
+    if wl == "int8_decode":
+        d = inputs.gen_int8(Mmax, N, K, seed=0)
+        wbytes = N * K
+    elif wl == "fp8_decode":
+        d = inputs.gen_fp8(Mmax, N, K, seed=0, per_tensor=args.per_tensor)
+        wbytes = N * K
+    elif wl == "fp8_blk":
+        d = inputs.gen_fp8_blk(Mmax, N, K, seed=0)
+        wbytes = N * K
+    else:
+        E, topk = spec["E"], spec["topk"]
+        d = inputs.gen_moe(Mmax, E, N, K, topk, seed=0)
+        wbytes = E * N * K // 2
+    B = args.rotate or max(1, -(-2 * MALL_BYTES // wbytes))
+    log(f"bench: {B} rotating weight copies ({B * wbytes / 1e6:.0f} MB)")
+
+    x = tb(d["x"])
+    if wl == "moe_mxfp4":
+        ws_copies = [t(d["w"])] + [None] * (B - 1)
+        s_copies = [t(d["s"])] + [None] * (B - 1)
+        for i in range(1, B):
+            ws_copies[i] = ws_copies[0].clone()
+            s_copies[i] = s_copies[0].clone()
+    else:
+        w0 = t(d["w"])
+        ws_copies = [w0] + [w0.clone() for _ in range(B - 1)]
+    sc = t(d["ws"])
+
+    # ---------------------------------------------------------------- per-call launch lists
+    xq_buf = torch.empty((Mmax, K), dtype=torch.int8 if wl == "int8_decode" else torch.uint8, device=dev)
+    xs_buf = torch.empty((Mmax,), dtype=torch.float32, device=dev)
+    xsb_buf = torch.empty((Mmax, K // 128), dtype=torch.uint8, device=dev)
+    y_buf = torch.empty((Mmax, N), dtype=torch.bfloat16, device=dev)
+    if wl == "moe_mxfp4":
+        ids, gw = t(d["ids"]), t(d["gw"])
+        ws_moe = torch.empty((ql.qlin_moe_mxfp4_workspace_bytes(Mmax, N, spec["topk"], spec["E"]),),
+                             dtype=torch.uint8, device=dev)
+        live = len(np.unique(d["ids"]))
+
+    def launches(M, ci):
+        """[(kernel, bytes, fn)] for one call of the workload's entry point."""
+        w = ws_copies[ci]
+        xm = x[:M]
+        if wl == "int8_decode":
+            return [("act_quant_i8", bytes_act_quant_i8(M, K),
+                     lambda: ql.qlin_act_quant_i8(xm, xq_buf[:M], xs_buf[:M])),
+                    ("gemv_i8", bytes_gemv_i8(M, N, K),
+                     lambda: ql.qlin_gemv_i8(xq_buf[:M], xs_buf[:M], w, sc, y=y_buf[:M]))]
+        if wl == "fp8_decode":
+            return [("gemv_fp8", bytes_gemv_fp8(M, N, K), lambda: ql.qlin_gemv_fp8(xm, w, sc, y=y_buf[:M]))]
+        if wl == "fp8_blk":
+            return [("act_quant_blk+gemv_fp8_blk", bytes_blk_call(M, N, K),
+                     lambda: ql.qlin_gemv_fp8_blk(xm, w, sc, xq=xq_buf[:M], xs=xsb_buf[:M], y=y_buf[:M]))]
+        return [("moe_mxfp4", bytes_moe_call(M, N, K, spec["topk"], live),
+                 lambda: ql.qlin_moe_mxfp4(xm, w, s_copies[ci], ids, gw, y=y_buf[:M], workspace=ws_moe))]
+
+    dominant = {"int8_decode": "gemv_i8", "fp8_decode": "gemv_fp8",
+                "fp8_blk": "act_quant_blk+gemv_fp8_blk", "moe_mxfp4": "moe_mxfp4"}[wl]
+
+    def run_step(step, record):
+        for i, M in enumerate(Ms):
+            ci = (step * len(Ms) + i) % B
+            for kname, nbytes, fn in launches(M, ci):
+                if record is not None:
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    fn()
+                    e1.record(stream)
+                    record.append((kname, M, nbytes, e0, e1))
+                else:
+                    fn()
+
+    log(f"bench: warmup {args.warmup} steps")
+    for s in range(args.warmup):
+        run_step(s, None)
+    torch.cuda.synchronize()
+
+    # timed region A: plain steps (wall time of the whole job)
+    log(f"bench: timing {args.steps} steps")
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(args.steps):
+        run_step(args.warmup + s, None)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(end)
+    ms_per_step = ms_total / args.steps
+
+    # timed region B: same steps with an event pair around every launch
+    rec = []
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        run_step(args.warmup + args.steps + s, rec)
+    torch.cuda.synchronize()
+
+    step_bytes = 0
+    for M in Ms:
+        step_bytes += sum(nb for _, nb, _ in launches(M, 0))
+    value = step_bytes * args.steps / (ms_total * 1e-3) / 1e9
+
+    per_m = {}
+    dom_bytes, dom_ms, dom_n = 0, 0.0, 0
+    for kname, M, nb, e0, e1 in rec:
+        ms = e0.elapsed_time(e1)
+        ent = per_m.setdefault(str(M), {})
+        k = ent.setdefault(kname, {"us": [], "bytes": nb})
+        k["us"].append(ms * 1e3)
+        if kname == dominant:
+            dom_bytes += nb
+            dom_ms += ms
+            dom_n += 1
+    for M, ent in per_m.items():
+        tot = 0.0
+        for kname, k in ent.items():
+            us = statistics.mean(k["us"])
+            tot += us
+            ent[kname] = {"us": round(us, 3), "GBps": round(k["bytes"] / (us * 1e-6) / 1e9, 1),
+                          "frac": round(k["bytes"] / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        ent["call_us"] = round(tot, 3)
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = load_traffic(wl)
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+        oracle.set_threads(threads)
+        used = oracle.max_threads()
+        log(f"bench: cpu_baseline with {used} threads")
+
+        def oracle_step():
+            for M in Ms:
+                xm = d["x"][:M]
+                if wl == "int8_decode":
+                    xq, xs = oracle.act_quant_i8(xm)
+                    oracle.gemv_i8(xq, xs, d["w"], d["ws"])
+                elif wl == "fp8_decode":
+                    oracle.gemv_fp8(xm, d["w"], d["ws"])
+                elif wl == "fp8_blk":
+                    oracle.fp8_blk(xm, d["w"], d["ws"])
+                else:
+                    oracle.moe_mxfp4(xm, d["w"], d["s"], d["ids"][:M], d["gw"][:M])
+
+        times = []
+        t_begin = time.perf_counter()
+        while len(times) < 3 and (time.perf_counter() - t_begin) < 30.0:
+            t0 = time.perf_counter()
+            oracle_step()
+            times.append(time.perf_counter() - t0)
+        med = statistics.median(times)
+        cpu = {"value": round(step_bytes / med / 1e9, 3), "unit": "GB/s", "cores": used, "kind": "oracle",
+               "sample": f"{len(times)} full step(s) of the same workload (Ms={Ms}, N={N}, K={K}), "
+                         f"median {med:.3f} s per step"}
+
+    cfg = {"workload": {
+        "int8_decode": f"W8A8 INT8 decode linear (act quant + GEMV, bf16 out) N={N} K={K}, one call per M",
+        "fp8_decode": f"E4M3 weight-only GEMV ({'per-tensor' if args.per_tensor else 'per-channel'}) N={N} K={K}",
+        "fp8_blk": f"128x128 block-scaled FP8 (act quant + GEMV) N={N} K={K}",
+        "moe_mxfp4": f"MXFP4 top-{spec.get('topk')} expert GEMV E={spec.get('E')} N={N} K={K}",
+    }[wl], "N": N, "K": K, "Ms": Ms, "weight_copies": B, "cold_weights": B * wbytes >= 2 * MALL_BYTES}
+    if wl == "moe_mxfp4":
+        cfg["live_experts"] = int(live)
+
+    out = {
+        "metric": "us/call + achieved HBM GB/s (% of peak) for quantized decode GEMV, M=1..16",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"int8_decode": "int8", "fp8_decode": "fp8e4m3*bf16->f32",
+                  "fp8_blk": "fp8e4m3->f32", "moe_mxfp4": "fp4e2m1*bf16->f32"}[wl],
+        "data": "synthetic",
+        "config": cfg,
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "launches": dom_n},
+        "cpu_baseline": cpu,
+        "per_m": per_m,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,179 @@
+/*
+ * qlin.h -- C ABI of the MI355X (gfx950) weight-quantized decode linear layer
+ *
+ *     y[M,N] = dequant(W[N,K]) . x[M,K],   M = 1..16 tokens
+ *
+ * in four variants: W8A8 INT8, FP8-E4M3 weight-only, 128x128 block-scaled
+ * FP8 with UE8M0 scales, and the MXFP4 expert GEMV behind top-k routing.
+ *
+ * Sources (web pages, by title and section):
+ *   [Z100] "Hygon Z100 (gfx906) vLLM adaptation: optimisation and operator
+ *          development record (condensed)", chapter 2 (hand-written HIP
+ *          operators): operator-family table; 2.1 INT8 W8A8 sdot4; 2.2 FP8
+ *          emulation; 2.4 block-scaled (128x128) FP8 extension; pitfall 6 of
+ *          section 3 (padded weight row stride).
+ *   [DSV4] "vLLM 0.27.x port: DeepSeek V4 Flash FP4 on Hygon DCU gfx936,
+ *          full report": 3.3 quantisation config; 7.4 UE8M0 decode;
+ *          9.3 MXFP4 MoE emulation.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every data pointer is a DEVICE pointer owned by the caller.  The library
+ *   never allocates, frees or synchronises: each call only enqueues kernels
+ *   on `stream` (a hipStream_t passed as void*; NULL = the null stream) and
+ *   returns.  Calls are stateless and thread-safe; two calls that write the
+ *   same output buffer race like any two kernels would.
+ * - Matrices are row-major.  A row pitch `ld*` is counted in ELEMENTS of the
+ *   stored type (bytes for int8 / E4M3 / UE8M0 codes, 2-byte units for bf16).
+ *   Weights are [N, K] with K contiguous, used exactly as stored; a padded
+ *   row pitch ldw > K is accepted (the padded view reads the same values as
+ *   the contiguous one), an unsupported stride is an error, never a copy.
+ * - bf16 values are IEEE binary32 with the low 16 bits dropped; outputs are
+ *   rounded to nearest, ties to even.
+ * - Return value: QLIN_OK (0) or a negative QLIN_ERR_* code.  Every argument
+ *   error is detected on the host BEFORE anything is enqueued, and then no
+ *   output is touched.  QLIN_ERR_LAUNCH reports a HIP launch failure.
+ * - Device-resident data is not validated (that would need a host sync):
+ *   NaN/Inf inputs give unspecified outputs; see each call for the rest.
+ * - M (tokens) must be in [1, 16].  Base pointers and row pitches of
+ *   weights, codes and bf16 activations must be 16-byte aligned (128-bit
+ *   loads); scale arrays must be naturally aligned.
+ */
+#ifndef QLIN_H
+#define QLIN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    QLIN_OK = 0,
+    QLIN_ERR_NULL = -1,      /* a required pointer is NULL */
+    QLIN_ERR_SHAPE = -2,     /* M, N, K or topk outside the supported range / multiple */
+    QLIN_ERR_STRIDE = -3,    /* a row pitch is smaller than the row it must hold */
+    QLIN_ERR_ALIGN = -4,     /* a base pointer or row pitch breaks the alignment rule */
+    QLIN_ERR_WORKSPACE = -5, /* workspace missing or smaller than required */
+    QLIN_ERR_ARG = -6,       /* an enum/flag argument has an unknown value */
+    QLIN_ERR_LAUNCH = -7     /* HIP reported an error when enqueuing a kernel */
+};
+
+#define QLIN_MAX_M 16
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* qlin_status_str(int status);
+
+/* Library version as an integer (major*10000 + minor*100 + patch). */
+int qlin_version(void);
+
+/* ------------------------------------------------------------------------
+ * (a) W8A8 INT8 -- [Z100] operator-family table (INT8 row) and section 2.1
+ * ------------------------------------------------------------------------ */
+
+/* Dynamic per-token symmetric INT8 activation quantisation.
+ *   x   bf16 [M, ldx]   input activations (row pitch ldx >= K)
+ *   xq  int8 [M, ldxq]  output codes:  q = clamp(rne(x / s), -127, 127)
+ *   xs  fp32 [M]        output scales: s = max_k |x[m,k]| / 127
+ * Both divisions are IEEE fp32 with round-to-nearest-even; rne rounds half
+ * to even.  A token whose row is all zero gets s = 0 and codes 0.
+ * Requires K % 16 == 0, 16 <= K <= 131072, ldx % 8 == 0, ldxq % 16 == 0. */
+int qlin_act_quant_i8(const void* x, int64_t ldx, int64_t M, int64_t K,
+                      int8_t* xq, int64_t ldxq, float* xs, void* stream);
+
+/* INT8 x INT8 GEMV with exact int32 accumulation and the epilogue
+ *   acc[m,n] = sum_k xq[m,k] * w[n,k]                      (exact, int32)
+ *   y[m,n]   = bf16( (fp32(acc) * xs[m]) * ws[n] )          (two fp32 products)
+ *   y[m,n]   = bf16( fp32(y[m,n]) + fp32(bias[n]) )         (only if bias != NULL)
+ *   xq   int8 [M, ldxq]; xs fp32 [M] (xs_per_token = 1) or [1] (= 0, broadcast)
+ *   w    int8 [N, ldw];  ws fp32 [N] (ws_per_row = 1) or [1] (= 0, broadcast)
+ *   bias bf16 [N] or NULL
+ *   out_kind 0: y is bf16 [M, ldy] holding the epilogue result;
+ *   out_kind 1: y is int32 [M, ldy] holding acc (scales and bias unused).
+ * Requires K % 16 == 0, 16 <= K <= 131072 (int32 cannot overflow),
+ * ldxq % 16 == 0, ldw % 16 == 0, N >= 1, ldy >= N. */
+int qlin_gemv_i8(const int8_t* xq, int64_t ldxq, const float* xs, int xs_per_token,
+                 int64_t M, int64_t K,
+                 const int8_t* w, int64_t ldw, int64_t N,
+                 const float* ws, int ws_per_row, const void* bias,
+                 void* y, int64_t ldy, int out_kind, void* stream);
+
+/* ------------------------------------------------------------------------
+ * (b) FP8-E4M3 weight-only -- [Z100] operator-family table (FP8 row), 2.2
+ * ------------------------------------------------------------------------ */
+
+/* y[m,n] = bf16( ws[n] * sum_k e4m3(w[n,k]) * x[m,k] )
+ * The weights stay E4M3 in memory and are converted as they are read; the
+ * scale is applied once to the fp32 sum.  Accumulation is fp32.
+ *   x  bf16 [M, ldx];  w OCP E4M3 codes [N, ldw];
+ *   ws fp32 [N] (ws_per_row = 1, per-channel) or [1] (= 0, per-tensor)
+ *   y  bf16 [M, ldy]
+ * Requires K % 16 == 0, K >= 16, ldx % 8 == 0, ldw % 16 == 0, ldy >= N. */
+int qlin_gemv_fp8(const void* x, int64_t ldx, int64_t M, int64_t K,
+                  const uint8_t* w, int64_t ldw, int64_t N,
+                  const float* ws, int ws_per_row,
+                  void* y, int64_t ldy, void* stream);
+
+/* ------------------------------------------------------------------------
+ * (c) Block-scaled FP8 -- [Z100] 2.4 (block formula, scale folding, padded
+ *     row stride); [DSV4] 3.3 (dynamic E4M3 activations, UE8M0 scales,
+ *     128x128 weight blocks) and 7.4 (UE8M0: scale = 2^(byte - 127))
+ * ------------------------------------------------------------------------ */
+
+/* Two steps, one call:
+ * 1. Activation quantisation per token m and 128-wide K group kb:
+ *      E = 127 + p, p the smallest integer with max|x| <= 448 * 2^p,
+ *      clamped to [1, 254] (E = 127 for an all-zero group);
+ *      xq[m,k] = e4m3_rne(x[m,k] / 2^(E-127)),  xs[m,kb] = E.
+ *    xq / xs are written to the caller's buffers (they are also the exported
+ *    quantised activations).
+ * 2. out[m,n] = sum_kb ( sum_{k in kb} xq[m,k] * w[n,k] )
+ *                     * 2^(xs[m,kb]-127) * 2^(ws[n/128, kb]-127)
+ *    The block scales multiply each lane's partial sum of the current block
+ *    before any reduction (scale folding); fp32 accumulation; y = bf16(out).
+ *   x  bf16 [M, ldx]; w E4M3 [N, ldw]; ws UE8M0 [ceil(N/128), K/128]
+ *   (row-major, byte 255 decodes to NaN); xq uint8 [M, K]; xs uint8
+ *   [M, K/128]; y bf16 [M, ldy].
+ * Requires K % 128 == 0, K >= 128, ldx % 8 == 0, ldw % 16 == 0, ldy >= N. */
+int qlin_gemv_fp8_blk(const void* x, int64_t ldx, int64_t M, int64_t K,
+                      const uint8_t* w, int64_t ldw, int64_t N,
+                      const uint8_t* ws,
+                      uint8_t* xq, uint8_t* xs,
+                      void* y, int64_t ldy, void* stream);
+
+/* ------------------------------------------------------------------------
+ * (d) MXFP4 expert GEMV behind top-k routing -- [DSV4] 9.3; element and
+ *     scale formats of the OCP MX spec (E2M1, one UE8M0 per 32 elements)
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of device workspace qlin_moe_mxfp4 needs for these sizes
+ * (per-(token, slot) fp32 partial rows, M * topk * N * 4, rounded up). */
+size_t qlin_moe_mxfp4_workspace_bytes(int64_t M, int64_t N, int64_t topk, int64_t E);
+
+/* y[t,n] = bf16( sum_{j < topk} g[t,j] * sum_k e2m1(W[e,n,k]) * 2^(S[e,n,k/32]-127) * x[t,k] ),
+ *          e = topk_ids[t,j]
+ * Steps: every (token, slot) pair is bucketed by its expert on the device;
+ * each live expert's weights are streamed once for all its tokens (fp32
+ * partial per pair into the workspace); then the partials are combined in
+ * slot order j = 0..topk-1.  No host synchronisation.
+ *   x         bf16 [M, ldx]
+ *   w_fp4     uint8 [E, N, K/2]: element 2i of a row in the LOW nibble of byte i
+ *   s_ue8m0   uint8 [E, N, K/32]
+ *   topk_ids  int32 [M, topk]: an id outside [0, E) contributes nothing
+ *   topk_w    fp32  [M, topk]
+ *   y         bf16 [M, ldy]
+ *   workspace device buffer of at least qlin_moe_mxfp4_workspace_bytes(),
+ *             16-byte aligned; its contents on entry do not matter.
+ * Requires K % 32 == 0, K >= 32, 1 <= topk <= 16, E >= 1, ldx % 8 == 0. */
+int qlin_moe_mxfp4(const void* x, int64_t ldx, int64_t M, int64_t K,
+                   const uint8_t* w_fp4, const uint8_t* s_ue8m0, int64_t E, int64_t N,
+                   const int32_t* topk_ids, const float* topk_w, int64_t topk,
+                   void* y, int64_t ldy,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLIN_H */

@@ -62,6 +62,10 @@ def _load():
     lib.orc_e2m1_decode.restype = ctypes.c_double
     lib.orc_ue8m0_decode.argtypes = [ctypes.c_uint8]
     lib.orc_ue8m0_decode.restype = ctypes.c_double
+    lib.orc_f64_to_bf16_n.argtypes = [P, I64, P]
+    lib.orc_f32_to_bf16_n.argtypes = [P, I64, P]
+    lib.orc_e4m3_decode_n.argtypes = [P, I64, P]
+    lib.orc_e4m3_encode_n.argtypes = [P, I64, P]
     lib.orc_act_quant_i8.argtypes = [P, I64, I64, I64, P, I64, P]
     lib.orc_gemv_i8.argtypes = [P, I64, P, I, I64, I64, P, I64, I64, P, I, P, P, P, I64]
     lib.orc_gemv_fp8.argtypes = [P, I64, I64, I64, P, I64, I64, P, I, P, I64, P, P]
@@ -99,28 +103,27 @@ def bf16_to_f32(h: np.ndarray) -> np.ndarray:
     return np.array([lib.orc_bf16_to_f32(int(v)) for v in h.ravel()], dtype=np.float32).reshape(h.shape)
 
 
+def _map(fn, a, in_dtype, out_dtype):
+    a = np.ascontiguousarray(a, dtype=in_dtype)
+    out = np.empty(a.shape, dtype=out_dtype)
+    getattr(_load(), fn)(a.ctypes.data, a.size, out.ctypes.data)
+    return out
+
+
 def f32_to_bf16(f: np.ndarray) -> np.ndarray:
-    lib = _load()
-    f = np.asarray(f, dtype=np.float32)
-    return np.array([lib.orc_f32_to_bf16(float(v)) for v in f.ravel()], dtype=np.uint16).reshape(f.shape)
+    return _map("orc_f32_to_bf16_n", f, np.float32, np.uint16)
 
 
 def f64_to_bf16(d: np.ndarray) -> np.ndarray:
-    lib = _load()
-    d = np.asarray(d, dtype=np.float64)
-    return np.array([lib.orc_f64_to_bf16(float(v)) for v in d.ravel()], dtype=np.uint16).reshape(d.shape)
+    return _map("orc_f64_to_bf16_n", d, np.float64, np.uint16)
 
 
 def e4m3_decode(codes) -> np.ndarray:
-    lib = _load()
-    c = np.asarray(codes, dtype=np.uint8)
-    return np.array([lib.orc_e4m3_decode(int(v)) for v in c.ravel()], dtype=np.float64).reshape(c.shape)
+    return _map("orc_e4m3_decode_n", codes, np.uint8, np.float64)
 
 
 def e4m3_encode(values) -> np.ndarray:
-    lib = _load()
-    v = np.asarray(values, dtype=np.float64)
-    return np.array([lib.orc_e4m3_encode(float(t)) for t in v.ravel()], dtype=np.uint8).reshape(v.shape)
+    return _map("orc_e4m3_encode_n", values, np.float64, np.uint8)
 
 
 def e2m1_decode(nibbles) -> np.ndarray:

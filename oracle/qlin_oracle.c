@@ -360,3 +360,23 @@ void orc_moe_mxfp4(const uint16_t* x, int64_t ldx, int64_t M, int64_t K,
         }
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Array forms of the format helpers (loops over the scalar routines).      */
+/* ------------------------------------------------------------------------ */
+
+void orc_f64_to_bf16_n(const double* v, int64_t n, uint16_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_f64_to_bf16(v[i]);
+}
+
+void orc_f32_to_bf16_n(const float* v, int64_t n, uint16_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_f32_to_bf16(v[i]);
+}
+
+void orc_e4m3_decode_n(const uint8_t* c, int64_t n, double* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_decode(c[i]);
+}
+
+void orc_e4m3_encode_n(const double* v, int64_t n, uint8_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_encode(v[i]);
+}

@@ -1,0 +1,165 @@
+"""skinny_gemm_qlin_amd -- weight-quantized decode GEMV for MI355X (gfx950).
+
+Thin torch-facing binding of the C ABI in include/qlin.h (libqlin.so).  The
+functions carry the C names and only marshal arguments: they check dtype,
+device and that the innermost dimension is contiguous, pass data pointers,
+row pitches and torch's current HIP stream, and raise QlinError on a non-zero
+status.  Outputs that are not supplied are allocated with torch (device
+memory plumbing only).  Every arithmetic step runs in the HIP kernels.
+
+Storage conventions: bf16 tensors are torch.bfloat16; int8 codes are
+torch.int8; E4M3 codes, UE8M0 scale bytes and packed E2M1 nibbles are
+torch.uint8 (a torch.float8_e4m3fn tensor may be passed for E4M3 codes).
+"""
+from __future__ import annotations
+
+import torch
+
+from ._lib import QlinError, check, load, status_str  # noqa: F401
+
+__all__ = [
+    "QlinError", "qlin_act_quant_i8", "qlin_gemv_i8", "qlin_gemv_fp8", "qlin_gemv_fp8_blk",
+    "qlin_moe_mxfp4", "qlin_moe_mxfp4_workspace_bytes", "status_str",
+]
+
+
+def _stream(t: torch.Tensor, stream):
+    if stream is None:
+        return torch.cuda.current_stream(t.device).cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _need(t: torch.Tensor, name: str, dtypes, dims: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a device tensor, got {t.device}")
+    if t.dim() != dims:
+        raise ValueError(f"{name}: expected {dims} dims, got shape {tuple(t.shape)}")
+    if dims >= 1 and t.numel() > 0 and t.stride(-1) != 1:
+        raise ValueError(f"{name}: innermost dimension must be contiguous (stride {t.stride(-1)})")
+    return t
+
+
+_U8 = (torch.uint8, torch.float8_e4m3fn)
+
+
+def qlin_act_quant_i8(x, xq=None, xs=None, stream=None):
+    """Per-token INT8 quantisation of bf16 x [M, K] -> (xq int8 [M, K], xs fp32 [M])."""
+    _need(x, "x", (torch.bfloat16,), 2)
+    M, K = x.shape
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if xs is None:
+        xs = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _need(xq, "xq", (torch.int8,), 2)
+    _need(xs, "xs", (torch.float32,), 1)
+    check(load().qlin_act_quant_i8(x.data_ptr(), x.stride(0), M, K, xq.data_ptr(), xq.stride(0),
+                                   xs.data_ptr(), _stream(x, stream)), "qlin_act_quant_i8")
+    return xq, xs
+
+
+def qlin_gemv_i8(xq, xs, w, ws, bias=None, y=None, out_kind=0, stream=None):
+    """W8A8 GEMV: xq int8 [M, K], xs fp32 [M] or [1], w int8 [N, K] (row pitch
+    w.stride(0)), ws fp32 [N] or [1], bias bf16 [N] or None.  out_kind 0 ->
+    y bf16 [M, N]; out_kind 1 -> y int32 [M, N] holding the raw accumulators."""
+    _need(xq, "xq", (torch.int8,), 2)
+    _need(w, "w", (torch.int8,), 2)
+    M, K = xq.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError(f"w has K={w.shape[1]}, xq has K={K}")
+    _need(xs, "xs", (torch.float32,), 1)
+    _need(ws, "ws", (torch.float32,), 1)
+    if bias is not None:
+        _need(bias, "bias", (torch.bfloat16,), 1)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.int32 if out_kind == 1 else torch.bfloat16, device=xq.device)
+    _need(y, "y", (torch.int32,) if out_kind == 1 else (torch.bfloat16,), 2)
+    check(load().qlin_gemv_i8(xq.data_ptr(), xq.stride(0), xs.data_ptr(), int(xs.numel() > 1), M, K,
+                              w.data_ptr(), w.stride(0), N, ws.data_ptr(), int(ws.numel() > 1),
+                              None if bias is None else bias.data_ptr(), y.data_ptr(), y.stride(0),
+                              int(out_kind), _stream(xq, stream)), "qlin_gemv_i8")
+    return y
+
+
+def qlin_gemv_fp8(x, w, ws, y=None, stream=None):
+    """E4M3 weight-only GEMV: x bf16 [M, K], w E4M3 codes [N, K], ws fp32 [N] or [1]."""
+    _need(x, "x", (torch.bfloat16,), 2)
+    _need(w, "w", _U8, 2)
+    _need(ws, "ws", (torch.float32,), 1)
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError(f"w has K={w.shape[1]}, x has K={K}")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(y, "y", (torch.bfloat16,), 2)
+    check(load().qlin_gemv_fp8(x.data_ptr(), x.stride(0), M, K, w.data_ptr(), w.stride(0), N,
+                               ws.data_ptr(), int(ws.numel() > 1), y.data_ptr(), y.stride(0),
+                               _stream(x, stream)), "qlin_gemv_fp8")
+    return y
+
+
+def qlin_gemv_fp8_blk(x, w, ws, xq=None, xs=None, y=None, stream=None):
+    """Block-scaled FP8: x bf16 [M, K], w E4M3 [N, K], ws UE8M0 [ceil(N/128), K/128].
+    Returns (y bf16 [M, N], xq E4M3 [M, K], xs UE8M0 [M, K/128])."""
+    _need(x, "x", (torch.bfloat16,), 2)
+    _need(w, "w", _U8, 2)
+    _need(ws, "ws", (torch.uint8,), 2)
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError(f"w has K={w.shape[1]}, x has K={K}")
+    if tuple(ws.shape) != ((N + 127) // 128, K // 128) or not ws.is_contiguous():
+        raise ValueError(f"ws must be contiguous [{(N + 127) // 128}, {K // 128}], got {tuple(ws.shape)}")
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if xs is None:
+        xs = torch.empty((M, K // 128), dtype=torch.uint8, device=x.device)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    if not xq.is_contiguous() or not xs.is_contiguous():
+        raise ValueError("xq / xs must be contiguous")
+    _need(y, "y", (torch.bfloat16,), 2)
+    check(load().qlin_gemv_fp8_blk(x.data_ptr(), x.stride(0), M, K, w.data_ptr(), w.stride(0), N,
+                                   ws.data_ptr(), xq.data_ptr(), xs.data_ptr(), y.data_ptr(),
+                                   y.stride(0), _stream(x, stream)), "qlin_gemv_fp8_blk")
+    return y, xq, xs
+
+
+def qlin_moe_mxfp4_workspace_bytes(M: int, N: int, topk: int, E: int) -> int:
+    return int(load().qlin_moe_mxfp4_workspace_bytes(M, N, topk, E))
+
+
+def qlin_moe_mxfp4(x, w, s, topk_ids, topk_w, y=None, workspace=None, stream=None):
+    """Top-k MXFP4 expert GEMV: x bf16 [M, K]; w uint8 [E, N, K/2] (element 2i in
+    the low nibble); s UE8M0 [E, N, K/32]; topk_ids int32 [M, topk]; topk_w fp32
+    [M, topk].  Returns y bf16 [M, N]."""
+    _need(x, "x", (torch.bfloat16,), 2)
+    _need(w, "w", (torch.uint8,), 3)
+    _need(s, "s", (torch.uint8,), 3)
+    _need(topk_ids, "topk_ids", (torch.int32,), 2)
+    _need(topk_w, "topk_w", (torch.float32,), 2)
+    M, K = x.shape
+    E, N, Kh = w.shape
+    topk = topk_ids.shape[1]
+    if Kh * 2 != K or tuple(s.shape) != (E, N, K // 32):
+        raise ValueError(f"w {tuple(w.shape)} / s {tuple(s.shape)} do not match K={K}")
+    if not (w.is_contiguous() and s.is_contiguous() and topk_ids.is_contiguous() and topk_w.is_contiguous()):
+        raise ValueError("w, s, topk_ids, topk_w must be contiguous")
+    if tuple(topk_ids.shape) != (M, topk) or tuple(topk_w.shape) != (M, topk):
+        raise ValueError("topk_ids / topk_w must be [M, topk]")
+    need = qlin_moe_mxfp4_workspace_bytes(M, N, topk, E)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(y, "y", (torch.bfloat16,), 2)
+    check(load().qlin_moe_mxfp4(x.data_ptr(), x.stride(0), M, K, w.data_ptr(), s.data_ptr(), E, N,
+                                topk_ids.data_ptr(), topk_w.data_ptr(), topk, y.data_ptr(), y.stride(0),
+                                workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                _stream(x, stream)), "qlin_moe_mxfp4")
+    return y

@@ -1,0 +1,130 @@
+// act_quant.hip -- activation quantisers for gfx950.
+//
+//   act_quant_i8_kernel   per-token symmetric INT8: s = amax/127, q = rne(x/s)
+//                         [Z100 section 2.1; operator-family table, INT8 row]
+//   blk_act_quant_kernel  per (token, 128-wide K group) E4M3 codes with a
+//                         UE8M0 exponent [DSV4 section 3.3; Z100 section 2.4]
+#include "qlin_device.hpp"
+#include "qlin_launch.hpp"
+
+namespace qlin {
+
+// One workgroup (256 lanes) per token.  Pass 1: amax over the row with
+// 16-byte loads; DPP row max, then across the 4 rows of a wave, then across
+// the 4 waves through LDS.  Pass 2: IEEE fp32 division and round-half-even
+// (v_rndne_f32), clamp to +-127, 8 codes per 8-byte store.
+__global__ __launch_bounds__(256) void act_quant_i8_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, int64_t K,
+    int8_t* __restrict__ xq, int64_t ldxq, float* __restrict__ xs) {
+    __shared__ float wave_max[4];
+    const int64_t m = blockIdx.x;
+    const uint16_t* row = x + m * ldx;
+    const int tid = threadIdx.x;
+    const int64_t nvec = K >> 3;  // 8 bf16 per 16-byte vector
+
+    float a = 0.0f;
+    for (int64_t i = tid; i < nvec; i += 256) {
+        u32x4_t v = ld16(row + i * 8);
+        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            a = fmaxf(a, fabsf(bf16_to_f32(d[q] & 0xFFFFu)));
+            a = fmaxf(a, fabsf(bf16_to_f32(d[q] >> 16)));
+        }
+    }
+    a = row_max_f32(a);
+    a = fmaxf(a, __shfl_xor(a, 16));
+    a = fmaxf(a, __shfl_xor(a, 32));
+    if ((tid & 63) == 0) wave_max[tid >> 6] = a;
+    __syncthreads();
+    const float amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+    const float s = amax / 127.0f;
+    if (tid == 0) xs[m] = s;
+
+    int8_t* qrow = xq + m * ldxq;
+    for (int64_t i = tid; i < nvec; i += 256) {
+        u32x4_t v = ld16(row + i * 8);
+        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+        uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t h = (e & 1) ? (d[e >> 1] >> 16) : (d[e >> 1] & 0xFFFFu);
+            int q = 0;
+            if (amax != 0.0f) {
+                float t = rintf(bf16_to_f32(h) / s);
+                t = fminf(fmaxf(t, -127.0f), 127.0f);
+                q = (int)t;
+            }
+            packed[e >> 2] |= ((uint32_t)q & 0xFFu) << (8 * (e & 3));
+        }
+        *(uint2*)(qrow + i * 8) = make_uint2(packed[0], packed[1]);
+    }
+}
+
+hipError_t launch_act_quant_i8(const ActQuantI8Args& a, hipStream_t st) {
+    hipLaunchKernelGGL(act_quant_i8_kernel, dim3((unsigned)a.M), dim3(256), 0, st,
+                       a.x, a.ldx, a.K, a.xq, a.ldxq, a.xs);
+    return hipGetLastError();
+}
+
+// One wavefront per 4 groups of 128: a 16-lane DPP row owns one group, each
+// lane 8 consecutive values (one 16-byte load).  E follows from the bits of
+// amax = (1+f)*2^e: amax <= 448*2^p = 1.75*2^(p+8) gives p = e-8 when
+// 1+f <= 1.75 (mantissa bits <= 0x600000), else p = e-7.  Scaling by
+// 2^(127-E) is exact; v_cvt_pk_fp8_f32 rounds to nearest even.
+__global__ __launch_bounds__(64) void blk_act_quant_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, int64_t K,
+    uint8_t* __restrict__ xq, uint8_t* __restrict__ xs) {
+    const int lane = threadIdx.x;
+    const int g = lane >> 4, j = lane & 15;
+    const int64_t m = blockIdx.y;
+    const int64_t nkb = K >> 7;
+    const int64_t kb = (int64_t)blockIdx.x * 4 + g;
+    const bool ok = kb < nkb;
+    const int64_t kbc = ok ? kb : nkb - 1;
+
+    u32x4_t v = ld16(x + m * ldx + kbc * 128 + j * 8);
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+    float f[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        f[2 * q] = bf16_to_f32(d[q] & 0xFFFFu);
+        f[2 * q + 1] = bf16_to_f32(d[q] >> 16);
+    }
+    float a = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(f[e]));
+    a = row_max_f32(a);
+
+    int E = 127;
+    if (a != 0.0f) {
+        const uint32_t bits = __float_as_uint(a);
+        const int ex = (int)(bits >> 23);  // biased exponent; 0 for a subnormal amax
+        int p;
+        if (ex == 0) p = -200;             // amax < 2^-126: clamps to E = 1 below
+        else p = (ex - 127) - (((bits & 0x7FFFFFu) <= 0x600000u) ? 8 : 7);
+        E = 127 + p;
+        E = E < 1 ? 1 : (E > 254 ? 254 : E);
+    }
+    const int inv = 254 - E;  // biased exponent of 2^(127-E)
+    const float sc = inv == 0 ? __uint_as_float(0x00400000u) : __uint_as_float((uint32_t)inv << 23);
+
+    int lo = 0, hi = 0;
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0] * sc, f[1] * sc, lo, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2] * sc, f[3] * sc, lo, true);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4] * sc, f[5] * sc, hi, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6] * sc, f[7] * sc, hi, true);
+    if (ok) {
+        *(uint2*)(xq + m * K + kb * 128 + j * 8) = make_uint2((uint32_t)lo, (uint32_t)hi);
+        if (j == 0) xs[m * nkb + kb] = (uint8_t)E;
+    }
+}
+
+hipError_t launch_blk_act_quant(const BlkQuantArgs& a, hipStream_t st) {
+    const int64_t nkb = a.K >> 7;
+    dim3 grid((unsigned)((nkb + 3) / 4), (unsigned)a.M);
+    hipLaunchKernelGGL(blk_act_quant_kernel, grid, dim3(64), 0, st, a.x, a.ldx, a.K, a.xq, a.xs);
+    return hipGetLastError();
+}
+
+}  // namespace qlin

@@ -1,0 +1,126 @@
+// qlin_api.hip -- the extern "C" entry points declared in include/qlin.h.
+//
+// Each entry point validates every host-visible argument (pointers, shapes,
+// pitches, alignment, flags) and returns a QLIN_ERR_* code before anything is
+// enqueued; only then does it launch the kernels on the caller's stream.
+// No allocation, no synchronisation, no state.
+#include <hip/hip_runtime.h>
+
+#include "../../include/qlin.h"
+#include "qlin_launch.hpp"
+
+namespace {
+
+inline bool misaligned(const void* p, uintptr_t a) { return ((uintptr_t)p) % a != 0; }
+
+inline int launch_status(hipError_t e) { return e == hipSuccess ? QLIN_OK : QLIN_ERR_LAUNCH; }
+
+constexpr int64_t kMaxKInt8 = 131072;  // K * 127 * 128 < 2^31: int32 accumulation is exact
+
+}  // namespace
+
+extern "C" {
+
+const char* qlin_status_str(int status) {
+    switch (status) {
+        case QLIN_OK: return "QLIN_OK";
+        case QLIN_ERR_NULL: return "QLIN_ERR_NULL: a required pointer is NULL";
+        case QLIN_ERR_SHAPE: return "QLIN_ERR_SHAPE: M, N, K or topk outside the supported range";
+        case QLIN_ERR_STRIDE: return "QLIN_ERR_STRIDE: a row pitch is smaller than its row";
+        case QLIN_ERR_ALIGN: return "QLIN_ERR_ALIGN: a pointer or row pitch is not aligned";
+        case QLIN_ERR_WORKSPACE: return "QLIN_ERR_WORKSPACE: workspace missing or too small";
+        case QLIN_ERR_ARG: return "QLIN_ERR_ARG: unknown flag value";
+        case QLIN_ERR_LAUNCH: return "QLIN_ERR_LAUNCH: HIP kernel launch failed";
+        default: return "QLIN_ERR_UNKNOWN";
+    }
+}
+
+int qlin_version(void) { return 100; }  // 0.1.0
+
+int qlin_act_quant_i8(const void* x, int64_t ldx, int64_t M, int64_t K,
+                      int8_t* xq, int64_t ldxq, float* xs, void* stream) {
+    if (!x || !xq || !xs) return QLIN_ERR_NULL;
+    if (M < 1 || M > QLIN_MAX_M || K < 16 || K % 16 != 0 || K > kMaxKInt8) return QLIN_ERR_SHAPE;
+    if (ldx < K || ldxq < K) return QLIN_ERR_STRIDE;
+    if (misaligned(x, 16) || ldx % 8 != 0 || misaligned(xq, 16) || ldxq % 16 != 0 || misaligned(xs, 4))
+        return QLIN_ERR_ALIGN;
+    qlin::ActQuantI8Args a{(const uint16_t*)x, ldx, M, K, xq, ldxq, xs};
+    return launch_status(qlin::launch_act_quant_i8(a, (hipStream_t)stream));
+}
+
+int qlin_gemv_i8(const int8_t* xq, int64_t ldxq, const float* xs, int xs_per_token,
+                 int64_t M, int64_t K, const int8_t* w, int64_t ldw, int64_t N,
+                 const float* ws, int ws_per_row, const void* bias,
+                 void* y, int64_t ldy, int out_kind, void* stream) {
+    if (out_kind != 0 && out_kind != 1) return QLIN_ERR_ARG;
+    if ((xs_per_token != 0 && xs_per_token != 1) || (ws_per_row != 0 && ws_per_row != 1)) return QLIN_ERR_ARG;
+    if (!xq || !w || !y) return QLIN_ERR_NULL;
+    if (out_kind == 0 && (!xs || !ws)) return QLIN_ERR_NULL;
+    if (M < 1 || M > QLIN_MAX_M || N < 1 || K < 16 || K % 16 != 0 || K > kMaxKInt8) return QLIN_ERR_SHAPE;
+    if (ldxq < K || ldw < K || ldy < N) return QLIN_ERR_STRIDE;
+    if (misaligned(xq, 16) || ldxq % 16 != 0 || misaligned(w, 16) || ldw % 16 != 0) return QLIN_ERR_ALIGN;
+    if (misaligned(y, out_kind == 1 ? 4 : 2) || (xs && misaligned(xs, 4)) || (ws && misaligned(ws, 4)) ||
+        (bias && misaligned(bias, 2)))
+        return QLIN_ERR_ALIGN;
+    qlin::I8Args a{xq, ldxq, xs, xs_per_token ? 1 : 0, M, K, w, ldw, N, ws, ws_per_row ? 1 : 0,
+                   (const uint16_t*)bias, y, ldy, out_kind};
+    return launch_status(qlin::launch_gemv_i8(a, (hipStream_t)stream));
+}
+
+int qlin_gemv_fp8(const void* x, int64_t ldx, int64_t M, int64_t K,
+                  const uint8_t* w, int64_t ldw, int64_t N, const float* ws, int ws_per_row,
+                  void* y, int64_t ldy, void* stream) {
+    if (ws_per_row != 0 && ws_per_row != 1) return QLIN_ERR_ARG;
+    if (!x || !w || !ws || !y) return QLIN_ERR_NULL;
+    if (M < 1 || M > QLIN_MAX_M || N < 1 || K < 16 || K % 16 != 0) return QLIN_ERR_SHAPE;
+    if (ldx < K || ldw < K || ldy < N) return QLIN_ERR_STRIDE;
+    if (misaligned(x, 16) || ldx % 8 != 0 || misaligned(w, 16) || ldw % 16 != 0 || misaligned(ws, 4) ||
+        misaligned(y, 2))
+        return QLIN_ERR_ALIGN;
+    qlin::F8Args a{(const uint16_t*)x, ldx, M, K, w, ldw, N, ws, ws_per_row ? 1 : 0, (uint16_t*)y, ldy};
+    return launch_status(qlin::launch_gemv_fp8(a, (hipStream_t)stream));
+}
+
+int qlin_gemv_fp8_blk(const void* x, int64_t ldx, int64_t M, int64_t K,
+                      const uint8_t* w, int64_t ldw, int64_t N, const uint8_t* ws,
+                      uint8_t* xq, uint8_t* xs, void* y, int64_t ldy, void* stream) {
+    if (!x || !w || !ws || !xq || !xs || !y) return QLIN_ERR_NULL;
+    if (M < 1 || M > QLIN_MAX_M || N < 1 || K < 128 || K % 128 != 0) return QLIN_ERR_SHAPE;
+    if (ldx < K || ldw < K || ldy < N) return QLIN_ERR_STRIDE;
+    if (misaligned(x, 16) || ldx % 8 != 0 || misaligned(w, 16) || ldw % 16 != 0 || misaligned(xq, 16) ||
+        misaligned(y, 2))
+        return QLIN_ERR_ALIGN;
+    hipStream_t st = (hipStream_t)stream;
+    qlin::BlkQuantArgs qa{(const uint16_t*)x, ldx, M, K, xq, xs};
+    hipError_t e = qlin::launch_blk_act_quant(qa, st);
+    if (e != hipSuccess) return QLIN_ERR_LAUNCH;
+    qlin::BlkArgs a{xq, xs, M, K, w, ldw, N, ws, (uint16_t*)y, ldy};
+    return launch_status(qlin::launch_gemv_fp8_blk(a, st));
+}
+
+size_t qlin_moe_mxfp4_workspace_bytes(int64_t M, int64_t N, int64_t topk, int64_t E) {
+    (void)E;
+    if (M < 1 || N < 1 || topk < 1) return 0;
+    const size_t b = (size_t)M * (size_t)topk * (size_t)N * sizeof(float);
+    return (b + 255) & ~(size_t)255;
+}
+
+int qlin_moe_mxfp4(const void* x, int64_t ldx, int64_t M, int64_t K,
+                   const uint8_t* w_fp4, const uint8_t* s_ue8m0, int64_t E, int64_t N,
+                   const int32_t* topk_ids, const float* topk_w, int64_t topk,
+                   void* y, int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!x || !w_fp4 || !s_ue8m0 || !topk_ids || !topk_w || !y) return QLIN_ERR_NULL;
+    if (M < 1 || M > QLIN_MAX_M || N < 1 || E < 1 || K < 32 || K % 32 != 0 || topk < 1 || topk > 16)
+        return QLIN_ERR_SHAPE;
+    if (ldx < K || ldy < N) return QLIN_ERR_STRIDE;
+    if (misaligned(x, 16) || ldx % 8 != 0 || misaligned(w_fp4, 16) || misaligned(topk_ids, 4) ||
+        misaligned(topk_w, 4) || misaligned(y, 2))
+        return QLIN_ERR_ALIGN;
+    if (!workspace || workspace_bytes < qlin_moe_mxfp4_workspace_bytes(M, N, topk, E)) return QLIN_ERR_WORKSPACE;
+    if (misaligned(workspace, 16)) return QLIN_ERR_ALIGN;
+    qlin::MoeArgs a{(const uint16_t*)x, ldx, M, K, w_fp4, s_ue8m0, E, N, topk_ids, topk_w, topk,
+                    (uint16_t*)y, ldy, (float*)workspace};
+    return launch_status(qlin::launch_moe_mxfp4(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+// qlin_device.hpp -- device-side helpers shared by the gfx950 kernels.
+//
+// Number formats decoded here (the kernels never build lookup tables):
+//   bf16   top half of an IEEE binary32;
+//   E4M3   OCP fp8 (bias 7, no infinities, max 448), converted by the
+//          gfx950 hardware converts v_cvt_scalef32_pk_bf16_fp8 /
+//          v_cvt_pk_fp8_f32;
+//   E2M1   OCP fp4 element, converted by v_cvt_scalef32_pk_bf16_fp4;
+//   UE8M0  scale byte b meaning 2^(b-127) (byte 255 = NaN), built directly
+//          as fp32 bits.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qlin {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short short2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;   // CDNA wavefront width
+constexpr int kGroup = 16;  // lanes that share one weight row (one DPP row)
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h16) { return __uint_as_float(h16 << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN -> 0x7FC0.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7FC0;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// UE8M0 byte -> fp32 scale 2^(b-127).  b = 0 is the fp32 subnormal 2^-127.
+__device__ __forceinline__ float ue8m0_to_f32(uint32_t b) {
+    if (b == 0u) return __uint_as_float(0x00400000u);
+    if (b == 255u) return __uint_as_float(0x7FC00000u);
+    return __uint_as_float(b << 23);
+}
+
+// Four E4M3 codes (one dword) -> two bf16 pairs, exact (E4M3 embeds in bf16).
+__device__ __forceinline__ void e4m3x4_to_bf16(uint32_t d, bf16x2_t& lo, bf16x2_t& hi) {
+    lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.0f, false);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.0f, true);
+}
+
+// Eight E2M1 codes (one dword, element 2i in the low nibble of byte i) ->
+// four bf16 pairs, exact.
+__device__ __forceinline__ void e2m1x8_to_bf16(uint32_t d, bf16x2_t out[4]) {
+    out[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, 0);
+    out[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, 1);
+    out[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, 2);
+    out[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, 3);
+}
+
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2_t, u); }
+
+__device__ __forceinline__ float dot2(bf16x2_t a, bf16x2_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
+
+__device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c) {
+    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+// ---------------------------------------------------------------- DPP reductions
+// DPP row = 16 lanes.  row_ror:n (control 0x120 + n) rotates a row by n lanes;
+// v + ror(v,8) + ror(.,4) + ror(.,2) + ror(.,1) leaves the row sum in every
+// lane of the row.
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ int row_sum_i32(int v) {
+    v += dpp_mov<0x128>(v);
+    v += dpp_mov<0x124>(v);
+    v += dpp_mov<0x122>(v);
+    v += dpp_mov<0x121>(v);
+    return v;
+}
+
+__device__ __forceinline__ float row_sum_f32(float v) {
+    v += __int_as_float(dpp_mov<0x128>(__float_as_int(v)));
+    v += __int_as_float(dpp_mov<0x124>(__float_as_int(v)));
+    v += __int_as_float(dpp_mov<0x122>(__float_as_int(v)));
+    v += __int_as_float(dpp_mov<0x121>(__float_as_int(v)));
+    return v;
+}
+
+__device__ __forceinline__ float row_max_f32(float v) {
+    v = fmaxf(v, __int_as_float(dpp_mov<0x128>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_mov<0x124>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_mov<0x122>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_mov<0x121>(__float_as_int(v))));
+    return v;
+}
+
+// 16-byte global load of read-once weight data (non-temporal hint).
+__device__ __forceinline__ u32x4_t ld_stream(const void* p) {
+    return __builtin_nontemporal_load((const u32x4_t*)p);
+}
+
+__device__ __forceinline__ u32x4_t ld16(const void* p) { return *(const u32x4_t*)p; }
+
+}  // namespace qlin

@@ -1,0 +1,51 @@
+// qlin_launch.hpp -- internal interface between the C-ABI layer (qlin_api.hip)
+// and the kernel translation units.  Argument structs carry validated,
+// already-normalised arguments (broadcast scales have step 0).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qlin {
+
+struct ActQuantI8Args {
+    const uint16_t* x; int64_t ldx; int64_t M; int64_t K;
+    int8_t* xq; int64_t ldxq; float* xs;
+};
+
+struct I8Args {
+    const int8_t* xq; int64_t ldxq; const float* xs; int xs_step;
+    int64_t M; int64_t K; const int8_t* w; int64_t ldw; int64_t N;
+    const float* ws; int ws_step; const uint16_t* bias; void* y; int64_t ldy; int out_kind;
+};
+
+struct F8Args {
+    const uint16_t* x; int64_t ldx; int64_t M; int64_t K;
+    const uint8_t* w; int64_t ldw; int64_t N; const float* ws; int ws_step;
+    uint16_t* y; int64_t ldy;
+};
+
+struct BlkQuantArgs {
+    const uint16_t* x; int64_t ldx; int64_t M; int64_t K; uint8_t* xq; uint8_t* xs;
+};
+
+struct BlkArgs {
+    const uint8_t* xq; const uint8_t* xs; int64_t M; int64_t K;
+    const uint8_t* w; int64_t ldw; int64_t N; const uint8_t* ws; uint16_t* y; int64_t ldy;
+};
+
+struct MoeArgs {
+    const uint16_t* x; int64_t ldx; int64_t M; int64_t K;
+    const uint8_t* w; const uint8_t* s; int64_t E; int64_t N;
+    const int32_t* ids; const float* gw; int64_t topk;
+    uint16_t* y; int64_t ldy; float* part;
+};
+
+hipError_t launch_act_quant_i8(const ActQuantI8Args& a, hipStream_t st);
+hipError_t launch_gemv_i8(const I8Args& a, hipStream_t st);
+hipError_t launch_gemv_fp8(const F8Args& a, hipStream_t st);
+hipError_t launch_blk_act_quant(const BlkQuantArgs& a, hipStream_t st);
+hipError_t launch_gemv_fp8_blk(const BlkArgs& a, hipStream_t st);
+hipError_t launch_moe_mxfp4(const MoeArgs& a, hipStream_t st);
+
+}  // namespace qlin

@@ -1,0 +1,141 @@
+"""C-ABI contract tests that need no GPU.
+
+The library must load, export every function include/qlin.h declares, and
+reject every invalid argument with the documented status BEFORE anything is
+enqueued.  Pointer arguments here are fake, never-dereferenced addresses (a
+valid call would reach HIP and is not made on the CPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "qlin.h")
+
+A = 0x10000  # 16-byte aligned fake device address, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def q():
+    from skinny_gemm_qlin_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from skinny_gemm_qlin_amd import _build
+        _build.build()
+    return _lib.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z_0-9]*\s*\*?\s*(qlin_[a-z0-9_]+)\s*\(", text, re.M)
+    return sorted(set(names))
+
+
+def test_exports_match_header(q):
+    from skinny_gemm_qlin_amd import _lib
+    declared = _declared_functions()
+    assert set(declared) == set(_lib.EXPORTS), declared
+    for name in declared:
+        assert hasattr(q, name), f"libqlin.so does not export {name}"
+
+
+def test_status_strings(q):
+    from skinny_gemm_qlin_amd import _lib
+    for code in range(0, -8, -1):
+        s = _lib.status_str(code)
+        assert s.startswith("QLIN_")
+    assert _lib.status_str(-99) == "QLIN_ERR_UNKNOWN"
+    assert q.qlin_version() >= 100
+
+
+def test_act_quant_errors(q):
+    f = q.qlin_act_quant_i8
+    assert f(None, 1024, 1, 1024, A, 1024, A, None) == -1
+    assert f(A, 1024, 1, 1024, None, 1024, A, None) == -1
+    assert f(A, 1024, 0, 1024, A, 1024, A, None) == -2          # M = 0
+    assert f(A, 1024, 17, 1024, A, 1024, A, None) == -2         # M > 16
+    assert f(A, 1024, 1, 1000, A, 1024, A, None) == -2          # K % 16
+    assert f(A, 1 << 20, 1, 131088, A, 1 << 20, A, None) == -2  # K too large for exact int32
+    assert f(A, 512, 1, 1024, A, 1024, A, None) == -3           # ldx < K
+    assert f(A, 1024, 1, 1024, A, 1000, A, None) == -3          # ldxq < K
+    assert f(A + 2, 1024, 1, 1024, A, 1024, A, None) == -4      # x misaligned
+    assert f(A, 1028, 1, 1024, A, 1024, A, None) == -4          # ldx % 8
+    assert f(A, 1024, 1, 1024, A + 8, 1024, A, None) == -4
+    assert f(A, 1024, 1, 1024, A, 1040 + 8, A, None) == -4      # ldxq % 16
+    assert f(A, 1024, 1, 1024, A, 1024, A + 2, None) == -4      # xs misaligned
+
+
+def test_gemv_i8_errors(q):
+    def call(xq=A, ldxq=1024, xs=A, xpt=1, M=1, K=1024, w=A, ldw=1024, N=64, ws=A, wpr=1, bias=None,
+             y=A, ldy=64, ok=0):
+        return q.qlin_gemv_i8(xq, ldxq, xs, xpt, M, K, w, ldw, N, ws, wpr, bias, y, ldy, ok, None)
+    assert call(ok=2) == -6
+    assert call(xpt=2) == -6
+    assert call(wpr=-1) == -6
+    assert call(xq=None) == -1
+    assert call(w=None) == -1
+    assert call(y=None) == -1
+    assert call(xs=None) == -1
+    assert call(ws=None) == -1
+    assert call(M=0) == -2
+    assert call(M=17) == -2
+    assert call(N=0) == -2
+    assert call(K=0) == -2
+    assert call(K=1032, ldxq=1040, ldw=1040) == -2
+    assert call(ldw=1000) == -3
+    assert call(ldy=63) == -3
+    assert call(ldxq=1008) == -3
+    assert call(w=A + 8) == -4
+    assert call(ldw=1024 + 8) == -4
+    assert call(y=A + 1) == -4
+    assert call(bias=A + 1) == -4
+    assert call(ok=1, y=A + 2) == -4        # int32 output needs 4-byte alignment
+
+
+def test_gemv_fp8_errors(q):
+    def call(x=A, ldx=5120, M=1, K=5120, w=A, ldw=5120, N=128, ws=A, wpr=1, y=A, ldy=128):
+        return q.qlin_gemv_fp8(x, ldx, M, K, w, ldw, N, ws, wpr, y, ldy, None)
+    assert call(wpr=3) == -6
+    assert call(ws=None) == -1
+    assert call(M=0) == -2
+    assert call(K=5128, ldx=5136, ldw=5136) == -2
+    assert call(ldx=5000) == -3
+    assert call(ldx=5124) == -4
+    assert call(w=A + 4) == -4
+    assert call(ldw=5120 + 4) == -4
+
+
+def test_gemv_fp8_blk_errors(q):
+    def call(x=A, ldx=7168, M=1, K=7168, w=A, ldw=7168, N=256, ws=A, xq=A, xs=A, y=A, ldy=256):
+        return q.qlin_gemv_fp8_blk(x, ldx, M, K, w, ldw, N, ws, xq, xs, y, ldy, None)
+    assert call(xq=None) == -1
+    assert call(xs=None) == -1
+    assert call(ws=None) == -1
+    assert call(K=7168 + 16, ldx=7184, ldw=7184) == -2   # K % 128
+    assert call(M=17) == -2
+    assert call(ldw=7000) == -3
+    assert call(xq=A + 8) == -4
+
+
+def test_moe_errors(q):
+    assert q.qlin_moe_mxfp4_workspace_bytes(8, 2048, 6, 64) == 8 * 6 * 2048 * 4
+    assert q.qlin_moe_mxfp4_workspace_bytes(1, 3, 1, 1) == 256
+    assert q.qlin_moe_mxfp4_workspace_bytes(0, 3, 1, 1) == 0
+    need = q.qlin_moe_mxfp4_workspace_bytes(8, 2048, 6, 64)
+
+    def call(x=A, ldx=7168, M=8, K=7168, w=A, s=A, E=64, N=2048, ids=A, gw=A, topk=6, y=A, ldy=2048,
+             ws=A, wsb=need):
+        return q.qlin_moe_mxfp4(x, ldx, M, K, w, s, E, N, ids, gw, topk, y, ldy, ws, wsb, None)
+    assert call(ids=None) == -1
+    assert call(gw=None) == -1
+    assert call(topk=0) == -2
+    assert call(topk=17) == -2
+    assert call(E=0) == -2
+    assert call(K=7168 + 16, ldx=7184) == -2
+    assert call(ldy=100) == -3
+    assert call(ws=None) == -5
+    assert call(wsb=need - 1) == -5
+    assert call(ws=A + 4) == -4
+    assert call(w=A + 8) == -4

@@ -1,0 +1,109 @@
+"""GPU parity of the 128x128 block-scaled FP8 path (qlin_gemv_fp8_blk): the
+exported activation codes and UE8M0 exponents are compared bit-exactly, the
+output under the float rules of tests/parity.py."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import dev, dev_bf16, host, host_bits, lib, need_gpu, padded
+from parity import check_float
+from skinny_gemm_qlin_amd.inputs import bf16_bits, bf16_values, gen_fp8_blk
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ql():
+    need_gpu()
+    return lib()
+
+
+def _gpu(ql, d, w_dev=None):
+    y, xq, xs = ql.qlin_gemv_fp8_blk(dev_bf16(d["x"]), dev(d["w"]) if w_dev is None else w_dev, dev(d["ws"]))
+    torch.cuda.synchronize()
+    return host_bits(y), host(xq), host(xs)
+
+
+def _check(orc, d, got):
+    y, xq, xs = got
+    oxq, oxs, oy, ye, S = orc.fp8_blk(d["x"], d["w"], d["ws"])
+    assert np.array_equal(xs, oxs), "UE8M0 activation exponents differ"
+    bad = np.argwhere(xq != oxq)
+    assert bad.size == 0, f"E4M3 activation codes differ at {bad[:5].tolist()}"
+    return check_float(y, ye, S, d["w"].shape[1])
+
+
+@pytest.mark.parametrize("M", list(range(1, 17)))
+def test_blk_small_all_M(ql, orc, M):
+    d = gen_fp8_blk(M, 384, 1024, seed=M)
+    _check(orc, d, _gpu(ql, d))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (2, 130, 384), (3, 257, 896), (9, 100, 640), (16, 555, 1152)])
+def test_blk_ragged(ql, orc, M, N, K):
+    d = gen_fp8_blk(M, N, K, seed=N + K)
+    _check(orc, d, _gpu(ql, d))
+
+
+@pytest.mark.parametrize("M", [1, 8, 16])
+def test_blk_full(ql, orc, M):
+    d = gen_fp8_blk(M, 4096, 7168, seed=0)
+    stats = _check(orc, d, _gpu(ql, d))
+    assert stats["ref_bits_equal"] > 0.99
+
+
+def test_blk_act_quant_edge_values(ql, orc):
+    # every E4M3 midpoint and its neighbours, zero groups, tiny / huge groups, signed zeros
+    rng = np.random.default_rng(40)
+    K = 128 * 12
+    x = rng.standard_normal((3, K)).astype(np.float32)
+    e4 = orc.e4m3_decode(np.arange(0x7F)).astype(np.float64)
+    mids = ((e4[:-1] + e4[1:]) / 2).astype(np.float32)  # exact midpoints (bf16 may round some)
+    x[0, :126] = mids
+    x[0, 126] = 448.0
+    x[0, 128:254] = -mids
+    x[0, 254] = -448.0
+    x[1, 256:384] = 0.0
+    x[1, 384:512] = -0.0
+    x[1, 512:640] *= 1e-35
+    x[1, 640:768] *= 3e35
+    x[2, 768:896] = np.where(np.arange(128) % 2 == 0, 1e-6, -1e-6)
+    x[2, 800] = 100.0
+    d = {"x": bf16_bits(x), "w": rng.integers(0, 0x7E, (130, K)).astype(np.uint8),
+         "ws": rng.integers(110, 140, (2, K // 128)).astype(np.uint8)}
+    _check(orc, d, _gpu(ql, d))
+
+
+def test_blk_unit_scales_match_plain_fp8(ql, orc):
+    # all weight scale bytes 127 and x already on E4M3 values with group max 448:
+    # the block path must equal the weight-only path with ws = 1
+    rng = np.random.default_rng(41)
+    K, N = 1024, 200
+    fin = np.array([c for c in range(256) if (c & 0x7F) != 0x7F])
+    xc = fin[rng.integers(0, fin.size, (2, K))]
+    xc[:, ::128] = 0x7E
+    x = bf16_bits(orc.e4m3_decode(xc.astype(np.uint8)).astype(np.float32))
+    w = fin[rng.integers(0, fin.size, (N, K))].astype(np.uint8)
+    d = {"x": x, "w": w, "ws": np.full(((N + 127) // 128, K // 128), 127, np.uint8)}
+    yb, xq, xs = _gpu(ql, d)
+    assert np.all(xs == 127)
+    yp = host_bits(ql.qlin_gemv_fp8(dev_bf16(x), dev(w), dev(np.ones(1, np.float32))))
+    _, ye, S = orc.gemv_fp8(x, w, np.ones(1, np.float32))
+    check_float(yb, ye, S, K)
+    check_float(yp, ye, S, K)
+
+
+def test_blk_padded_row_stride(ql, orc):
+    d = gen_fp8_blk(2, 300, 1024, seed=42)
+    wp = padded(d["w"], 256)
+    a = _gpu(ql, d, w_dev=wp)
+    b = _gpu(ql, d)
+    assert all(np.array_equal(u, v) for u, v in zip(a, b))
+
+
+def test_blk_deterministic(ql):
+    d = gen_fp8_blk(16, 4096, 7168, seed=43)
+    x, w, ws = dev_bf16(d["x"]), dev(d["w"]), dev(d["ws"])
+    ref = ql.qlin_gemv_fp8_blk(x, w, ws)[0]
+    for _ in range(10):
+        assert torch.equal(ql.qlin_gemv_fp8_blk(x, w, ws)[0].view(torch.int16), ref.view(torch.int16))
