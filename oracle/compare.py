@@ -8,7 +8,10 @@ Float outputs y (bf16) are compared with the oracle's fp64 value y_exact and
 S = sum_k |w_k x_k| (times the |scales|, and |g| for the MoE), element by
 element, with BOTH rules:
 
-  (i)  |y - y_exact| <= 1e-3 * S + 1e-6                     (the stated tolerance)
+  (i)  |y - y_exact| <= 1e-3 * S + 1e-6 + ulp(y_exact) / 2  (the stated tolerance on
+       the fp32-accumulated value, plus the half-ulp rounding of the bf16 output:
+       when |y| is close to S -- heavy-tailed E4M3 codes -- the correctly rounded
+       bf16 value alone can sit more than 1e-3 * S from y_exact)
   (ii) bf16(y_exact - eps) <= y <= bf16(y_exact + eps)       (bf16 rounding of the
        oracle, allowing for the kernel's fp32 accumulation), with
        eps = (K/8 + 32) * 2^-24 * S, a bound on the fp32 rounding error of the
@@ -27,6 +30,14 @@ def bf16_to_f64(bits):
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def bf16_ulp(v):
+    """Spacing of bf16 values at |v| (8 significant bits; 2^-133 below 2^-126)."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(np.where(a > 0, e, -126.0), -126.0)
+    return np.exp2(e - 7)
+
+
 def f64_to_bf16_val(v):
     """fp64 -> bf16 value with ONE round-to-nearest-even (the oracle's routine;
     going through float32 first would round twice)."""
@@ -41,7 +52,7 @@ def check_float(y_bits, y_exact, S, K, what="y"):
     assert y.shape == y_exact.shape == S.shape, (y.shape, y_exact.shape, S.shape)
     assert np.all(np.isfinite(y)), f"{what}: non-finite outputs"
     err = np.abs(y - y_exact)
-    tol = 1e-3 * S + 1e-6
+    tol = 1e-3 * S + 1e-6 + bf16_ulp(y_exact) / 2
     bad = err > tol
     assert not bad.any(), (f"{what}: rule (i) fails at {np.argwhere(bad)[:5].tolist()}; "
                            f"max err/tol {np.max(err / tol):.3g}")
