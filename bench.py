@@ -10,8 +10,10 @@ rotating weight copies (B * |W| >= 2 x the 256 MB Infinity Cache).
 Prints ONE JSON line.  `value` = algorithmic bytes moved by the timed steps /
 their wall time on the GPU (GB/s, inputs already in HBM).  `roofline`
 describes the dominant kernel (the GEMV): algorithmic bytes per launch /
-mean launch duration from HIP events recorded around every launch on the
-stream it runs on.  `cpu_baseline` times the CPU oracle (oracle/, plain C,
+mean launch duration, from HIP events recorded on the stream the kernel runs
+on around a batch of back-to-back launches (rotating weight copies) per M.
+All timed launches are replayed from HIP graphs, so the host's per-call
+overhead is not in the measurement.  `cpu_baseline` times the CPU oracle (oracle/, plain C,
 OpenMP over rows) on the host on the same workload.
 
 Other workloads (--workload fp8_decode | fp8_blk | moe_mxfp4) time the other
@@ -66,16 +68,6 @@ def bytes_moe_call(M, N, K, topk, live):
 
 
 # ----------------------------------------------------------------------------- workloads
-
-class Workload:
-    name = ""
-    dtype = ""
-    desc = ""
-
-    def calls(self):
-        """list of (label, fn(copy_index) -> list of (kernel_name, launch_fn))"""
-        raise NotImplementedError
-
 
 def src_hash():
     h = hashlib.sha256()
@@ -202,69 +194,86 @@ def main():
     dominant = {"int8_decode": "gemv_i8", "fp8_decode": "gemv_fp8",
                 "fp8_blk": "act_quant_blk+gemv_fp8_blk", "moe_mxfp4": "moe_mxfp4"}[wl]
 
-    def run_step(step, record):
+    def run_step(step):
         for i, M in enumerate(Ms):
             ci = (step * len(Ms) + i) % B
-            for kname, nbytes, fn in launches(M, ci):
-                if record is not None:
-                    e0 = torch.cuda.Event(enable_timing=True)
-                    e1 = torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
-                    fn()
-                    e1.record(stream)
-                    record.append((kname, M, nbytes, e0, e1))
-                else:
-                    fn()
+            for _, _, fn in launches(M, ci):
+                fn()
 
-    log(f"bench: warmup {args.warmup} steps")
+    def capture(fns):
+        """Record the launches into one HIP graph (replayed without host overhead).
+        The kernels are enqueued on torch's current stream, which is the capture
+        stream inside the context."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for fn in fns:
+                fn()
+        return g
+
+    log(f"bench: warmup {args.warmup} steps (eager)")
     for s in range(args.warmup):
-        run_step(s, None)
+        run_step(s)
     torch.cuda.synchronize()
 
-    # timed region A: plain steps (wall time of the whole job)
+    # one graph per step offset: step s uses weight copies (s*len(Ms)+i) % B
+    step_graphs = []
+    for s in range(B):
+        fns = []
+        for i, M in enumerate(Ms):
+            fns += [fn for _, _, fn in launches(M, (s * len(Ms) + i) % B)]
+        step_graphs.append(capture(fns))
+    for s in range(args.warmup):
+        step_graphs[s % B].replay()
+    torch.cuda.synchronize()
+
+    # timed region A: the whole job, args.steps steps
     log(f"bench: timing {args.steps} steps")
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for s in range(args.steps):
-        run_step(args.warmup + s, None)
+        step_graphs[s % B].replay()
     end.record(stream)
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(end)
     ms_per_step = ms_total / args.steps
 
-    # timed region B: same steps with an event pair around every launch
-    rec = []
-    torch.cuda.synchronize()
-    for s in range(args.steps):
-        run_step(args.warmup + args.steps + s, rec)
-    torch.cuda.synchronize()
+    # timed region B: per M and kernel, `reps` back-to-back launches (rotating
+    # weight copies) in one graph, between two events on the replay stream
+    # -> mean launch duration of that kernel.
+    reps = max(20, args.steps)
+    per_m = {}
+    dom_bytes, dom_ms, dom_n = 0, 0.0, 0
+    for i, M in enumerate(Ms):
+        ent = per_m.setdefault(str(M), {})
+        for kidx in range(len(launches(M, 0))):
+            kname, nb, _ = launches(M, 0)[kidx]
+            g = capture([launches(M, (i + r) % B)[kidx][2] for r in range(reps)])
+            g.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            us = ms * 1e3
+            ent[kname] = {"us": round(us, 3), "GBps": round(nb / (us * 1e-6) / 1e9, 1),
+                          "frac": round(nb / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+            if kname == dominant:
+                dom_bytes += nb * reps
+                dom_ms += ms * reps
+                dom_n += reps
+            del g
+        ent["call_us"] = round(sum(v["us"] for v in ent.values()), 3)
 
     step_bytes = 0
     for M in Ms:
         step_bytes += sum(nb for _, nb, _ in launches(M, 0))
     value = step_bytes * args.steps / (ms_total * 1e-3) / 1e9
 
-    per_m = {}
-    dom_bytes, dom_ms, dom_n = 0, 0.0, 0
-    for kname, M, nb, e0, e1 in rec:
-        ms = e0.elapsed_time(e1)
-        ent = per_m.setdefault(str(M), {})
-        k = ent.setdefault(kname, {"us": [], "bytes": nb})
-        k["us"].append(ms * 1e3)
-        if kname == dominant:
-            dom_bytes += nb
-            dom_ms += ms
-            dom_n += 1
-    for M, ent in per_m.items():
-        tot = 0.0
-        for kname, k in ent.items():
-            us = statistics.mean(k["us"])
-            tot += us
-            ent[kname] = {"us": round(us, 3), "GBps": round(k["bytes"] / (us * 1e-6) / 1e9, 1),
-                          "frac": round(k["bytes"] / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
-        ent["call_us"] = round(tot, 3)
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = load_traffic(wl)
 

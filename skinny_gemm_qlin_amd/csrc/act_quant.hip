@@ -10,9 +10,39 @@
 namespace qlin {
 
 // One workgroup (256 lanes) per token.  Pass 1: amax over the row with
-// 16-byte loads; DPP row max, then across the 4 rows of a wave, then across
-// the 4 waves through LDS.  Pass 2: IEEE fp32 division and round-half-even
+// 16-byte loads (the first kCached vectors of each lane stay in registers);
+// DPP row max, then across the 4 rows of a wave, then across the 4 waves
+// through LDS.  Pass 2: IEEE fp32 division and round-half-even
 // (v_rndne_f32), clamp to +-127, 8 codes per 8-byte store.
+constexpr int kCached = 4;  // K <= 8192 is read from HBM exactly once
+
+__device__ __forceinline__ uint2 quant8(const u32x4_t& v, float amax, float s) {
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t h = (e & 1) ? (d[e >> 1] >> 16) : (d[e >> 1] & 0xFFFFu);
+        int q = 0;
+        if (amax != 0.0f) {
+            float t = rintf(bf16_to_f32(h) / s);
+            t = fminf(fmaxf(t, -127.0f), 127.0f);
+            q = (int)t;
+        }
+        packed[e >> 2] |= ((uint32_t)q & 0xFFu) << (8 * (e & 3));
+    }
+    return make_uint2(packed[0], packed[1]);
+}
+
+__device__ __forceinline__ float absmax8(const u32x4_t& v, float a) {
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        a = fmaxf(a, fabsf(bf16_to_f32(d[q] & 0xFFFFu)));
+        a = fmaxf(a, fabsf(bf16_to_f32(d[q] >> 16)));
+    }
+    return a;
+}
+
 __global__ __launch_bounds__(256) void act_quant_i8_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int64_t K,
     int8_t* __restrict__ xq, int64_t ldxq, float* __restrict__ xs) {
@@ -22,16 +52,15 @@ __global__ __launch_bounds__(256) void act_quant_i8_kernel(
     const int tid = threadIdx.x;
     const int64_t nvec = K >> 3;  // 8 bf16 per 16-byte vector
 
+    u32x4_t cache[kCached];
     float a = 0.0f;
-    for (int64_t i = tid; i < nvec; i += 256) {
-        u32x4_t v = ld16(row + i * 8);
-        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            a = fmaxf(a, fabsf(bf16_to_f32(d[q] & 0xFFFFu)));
-            a = fmaxf(a, fabsf(bf16_to_f32(d[q] >> 16)));
-        }
+    for (int c = 0; c < kCached; ++c) {
+        const int64_t i = tid + c * 256;
+        cache[c] = i < nvec ? ld16(row + i * 8) : u32x4_t{0, 0, 0, 0};
+        a = absmax8(cache[c], a);
     }
+    for (int64_t i = tid + kCached * 256; i < nvec; i += 256) a = absmax8(ld16(row + i * 8), a);
     a = row_max_f32(a);
     a = fmaxf(a, __shfl_xor(a, 16));
     a = fmaxf(a, __shfl_xor(a, 32));
@@ -42,23 +71,13 @@ __global__ __launch_bounds__(256) void act_quant_i8_kernel(
     if (tid == 0) xs[m] = s;
 
     int8_t* qrow = xq + m * ldxq;
-    for (int64_t i = tid; i < nvec; i += 256) {
-        u32x4_t v = ld16(row + i * 8);
-        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-        uint32_t packed[2] = {0u, 0u};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t h = (e & 1) ? (d[e >> 1] >> 16) : (d[e >> 1] & 0xFFFFu);
-            int q = 0;
-            if (amax != 0.0f) {
-                float t = rintf(bf16_to_f32(h) / s);
-                t = fminf(fmaxf(t, -127.0f), 127.0f);
-                q = (int)t;
-            }
-            packed[e >> 2] |= ((uint32_t)q & 0xFFu) << (8 * (e & 3));
-        }
-        *(uint2*)(qrow + i * 8) = make_uint2(packed[0], packed[1]);
+    for (int c = 0; c < kCached; ++c) {
+        const int64_t i = tid + c * 256;
+        if (i < nvec) *(uint2*)(qrow + i * 8) = quant8(cache[c], amax, s);
     }
+    for (int64_t i = tid + kCached * 256; i < nvec; i += 256)
+        *(uint2*)(qrow + i * 8) = quant8(ld16(row + i * 8), amax, s);
 }
 
 hipError_t launch_act_quant_i8(const ActQuantI8Args& a, hipStream_t st) {

@@ -1,0 +1,304 @@
+// gemv_kernels.hpp -- VALU skinny-GEMV kernel templates for gfx950.
+//
+// One template family serves the three dense weight formats.  Work split:
+//   * a workgroup has WPB wavefronts; a wavefront is 64/GS lane groups of GS
+//     lanes (GS = 16, 32 or 64) and each group owns R consecutive weight rows;
+//   * a group walks K in steps of GS chunks of 16 bytes: lane j of the group
+//     reads chunk c = GS*step + j of each of its rows with one 128-bit load, so
+//     one load instruction covers 64/GS rows with GS*16 contiguous bytes each
+//     (GS = 64: one whole 1 KB run of one row), every weight byte is read once;
+//   * U steps are issued before any is consumed (U*R loads in flight per
+//     lane); the ragged end of K is folded into the last batch by clamping
+//     the chunk index inside the row (an L2 hit) and zeroing the activation;
+//   * the activation chunk for a step is loaded once and reused for the R
+//     rows; after the K loop each lane holds R*M partial sums, reduced over
+//     the GS lanes of the group with DPP row_ror adds (and cross-row shuffles
+//     for GS > 16); the epilogue of value v runs in lane v % GS.
+// No atomics and no cross-workgroup reduction, so results are deterministic.
+#pragma once
+#include "qlin_device.hpp"
+
+namespace qlin {
+
+template <int GS>
+__device__ __forceinline__ int group_sum(int v) {
+    v = row_sum_i32(v);
+    if (GS >= 32) v += __shfl_xor(v, 16);
+    if (GS >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+
+template <int GS>
+__device__ __forceinline__ float group_sum(float v) {
+    v = row_sum_f32(v);
+    if (GS >= 32) v += __shfl_xor(v, 16);
+    if (GS >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+
+// Row index owned by (group, r), clamped so that loads stay inside W.
+template <int GS, int R, int WPB>
+__device__ __forceinline__ int64_t first_row() {
+    constexpr int GPW = 64 / GS;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    return (((int64_t)blockIdx.x * WPB + wv) * GPW + lane / GS) * R;
+}
+
+// 16 E4M3 codes -> 8 bf16 pairs (exact)
+__device__ __forceinline__ void e4m3x16(const u32x4_t& v, bf16x2_t o[8]) {
+    e4m3x4_to_bf16(v.x, o[0], o[1]);
+    e4m3x4_to_bf16(v.y, o[2], o[3]);
+    e4m3x4_to_bf16(v.z, o[4], o[5]);
+    e4m3x4_to_bf16(v.w, o[6], o[7]);
+}
+
+// ------------------------------------------------------------------ INT8 W8A8
+// acc = sum_k xq*w with v_dot4 (exact int32); epilogue bf16((acc*xs)*ws) then
+// + bias [Z100 operator-family table, INT8 row; section 2.1].
+template <int M, int GS, int R, int U, int WPB>
+__global__ __launch_bounds__(64 * WPB) void gemv_i8_kernel(
+    const int8_t* __restrict__ xq, int64_t ldxq, const float* __restrict__ xs, int xs_step,
+    int64_t K, const int8_t* __restrict__ w, int64_t ldw, int64_t N,
+    const float* __restrict__ ws, int ws_step, const uint16_t* __restrict__ bias,
+    void* __restrict__ y, int64_t ldy, int out_kind) {
+    const int j = (threadIdx.x & 63) % GS;
+    const int64_t n0 = first_row<GS, R, WPB>();
+    const int8_t* wr[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) wr[r] = w + (n0 + r < N ? n0 + r : N - 1) * ldw;
+
+    int acc[R][M];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = 0;
+
+    const int64_t nchunk = K >> 4;  // 16 int8 per chunk
+    const int64_t nsteps = (nchunk + GS - 1) / GS;
+    for (int64_t s = 0; s < nsteps; s += U) {
+        u32x4_t wv[U][R], xv[U][M];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = (s + u) * GS + j;
+            const int64_t cc = c < nchunk ? c : nchunk - 1;
+#pragma unroll
+            for (int r = 0; r < R; ++r) wv[u][r] = ld_stream(wr[r] + cc * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = (s + u) * GS + j;
+            const int64_t cc = c < nchunk ? c : nchunk - 1;
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const u32x4_t t = ld16(xq + m * ldxq + cc * 16);
+                xv[u][m] = c < nchunk ? t : u32x4_t{0, 0, 0, 0};
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    int a = acc[r][m];
+                    a = sdot4(wv[u][r].x, xv[u][m].x, a);
+                    a = sdot4(wv[u][r].y, xv[u][m].y, a);
+                    a = sdot4(wv[u][r].z, xv[u][m].z, a);
+                    a = sdot4(wv[u][r].w, xv[u][m].w, a);
+                    acc[r][m] = a;
+                }
+    }
+
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = group_sum<GS>(acc[r][m]);
+
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const int v = r * M + m;
+            const int64_t n = n0 + r;
+            if ((v % GS) == j && n < N) {
+                if (out_kind == 1) {
+                    ((int32_t*)y)[m * ldy + n] = acc[r][m];
+                } else {
+                    float t = (float)acc[r][m];
+                    t = t * xs[m * xs_step];
+                    t = t * ws[n * ws_step];
+                    uint16_t o = f32_to_bf16(t);
+                    if (bias) o = f32_to_bf16(bf16_to_f32(o) + bf16_to_f32(bias[n]));
+                    ((uint16_t*)y)[m * ldy + n] = o;
+                }
+            }
+        }
+}
+
+// ------------------------------------------------------------------ FP8-E4M3 weight-only
+// y = bf16(ws[n] * sum_k e4m3(w)*x): hardware E4M3 -> bf16 convert, v_dot2
+// bf16 with fp32 accumulation, the scale applied once after the reduction
+// [Z100 operator-family table, FP8 row; section 2.2].
+template <int M, int GS, int R, int U, int WPB>
+__global__ __launch_bounds__(64 * WPB) void gemv_fp8_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, int64_t K,
+    const uint8_t* __restrict__ w, int64_t ldw, int64_t N,
+    const float* __restrict__ ws, int ws_step, uint16_t* __restrict__ y, int64_t ldy) {
+    const int j = (threadIdx.x & 63) % GS;
+    const int64_t n0 = first_row<GS, R, WPB>();
+    const uint8_t* wr[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) wr[r] = w + (n0 + r < N ? n0 + r : N - 1) * ldw;
+
+    float acc[R][M];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+
+    const int64_t nchunk = K >> 4;  // 16 codes per chunk
+    const int64_t nsteps = (nchunk + GS - 1) / GS;
+    for (int64_t s = 0; s < nsteps; s += U) {
+        u32x4_t wv[U][R], xa[U][M], xb[U][M];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = (s + u) * GS + j;
+            const int64_t cc = c < nchunk ? c : nchunk - 1;
+#pragma unroll
+            for (int r = 0; r < R; ++r) wv[u][r] = ld_stream(wr[r] + cc * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = (s + u) * GS + j;
+            const int64_t cc = c < nchunk ? c : nchunk - 1;
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const uint16_t* xp = x + m * ldx + cc * 16;
+                const u32x4_t a = ld16(xp), b = ld16(xp + 8);
+                xa[u][m] = c < nchunk ? a : u32x4_t{0, 0, 0, 0};
+                xb[u][m] = c < nchunk ? b : u32x4_t{0, 0, 0, 0};
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                bf16x2_t wb[8];
+                e4m3x16(wv[u][r], wb);
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    float a = acc[r][m];
+                    a = dot2(wb[0], as_bf16x2(xa[u][m].x), a);
+                    a = dot2(wb[1], as_bf16x2(xa[u][m].y), a);
+                    a = dot2(wb[2], as_bf16x2(xa[u][m].z), a);
+                    a = dot2(wb[3], as_bf16x2(xa[u][m].w), a);
+                    a = dot2(wb[4], as_bf16x2(xb[u][m].x), a);
+                    a = dot2(wb[5], as_bf16x2(xb[u][m].y), a);
+                    a = dot2(wb[6], as_bf16x2(xb[u][m].z), a);
+                    a = dot2(wb[7], as_bf16x2(xb[u][m].w), a);
+                    acc[r][m] = a;
+                }
+            }
+    }
+
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = group_sum<GS>(acc[r][m]);
+
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const int v = r * M + m;
+            const int64_t n = n0 + r;
+            if ((v % GS) == j && n < N) y[m * ldy + n] = f32_to_bf16(acc[r][m] * ws[n * ws_step]);
+        }
+}
+
+// ------------------------------------------------------------------ block-scaled FP8
+// out = sum_kb (sum_{k in kb} xq*w) * 2^(xs-127) * 2^(ws-127).  A chunk of 16
+// codes lies inside one 128-wide block (kb = c/8), so each lane multiplies the
+// block scales into its own chunk partial before any reduction
+// [Z100 section 2.4: block formula and scale-folding identity].
+template <int M, int GS, int R, int U, int WPB>
+__global__ __launch_bounds__(64 * WPB) void gemv_fp8_blk_kernel(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, int64_t K,
+    const uint8_t* __restrict__ w, int64_t ldw, int64_t N,
+    const uint8_t* __restrict__ ws, uint16_t* __restrict__ y, int64_t ldy) {
+    const int j = (threadIdx.x & 63) % GS;
+    const int64_t n0 = first_row<GS, R, WPB>();
+    const int64_t nkb = K >> 7;
+    const uint8_t* wr[R];
+    const uint8_t* wsr[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t n = n0 + r < N ? n0 + r : N - 1;
+        wr[r] = w + n * ldw;
+        wsr[r] = ws + (n >> 7) * nkb;
+    }
+
+    float acc[R][M];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+
+    const int64_t nchunk = K >> 4;
+    const int64_t nsteps = (nchunk + GS - 1) / GS;
+    for (int64_t s = 0; s < nsteps; s += U) {
+        u32x4_t wv[U][R], xv[U][M];
+        float sw[U][R], sx[U][M];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = (s + u) * GS + j;
+            const bool ok = c < nchunk;
+            const int64_t cc = ok ? c : nchunk - 1;
+            const int64_t kb = cc >> 3;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                wv[u][r] = ld_stream(wr[r] + cc * 16);
+                sw[u][r] = ok ? ue8m0_to_f32(wsr[r][kb]) : 0.0f;  // an idle lane adds exactly 0
+            }
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                xv[u][m] = ld16(xq + m * K + cc * 16);
+                sx[u][m] = ok ? ue8m0_to_f32(xs[m * nkb + kb]) : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            bf16x2_t xb[M][8];
+#pragma unroll
+            for (int m = 0; m < M; ++m) e4m3x16(xv[u][m], xb[m]);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                bf16x2_t wb[8];
+                e4m3x16(wv[u][r], wb);
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    float loc = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) loc = dot2(wb[i], xb[m][i], loc);
+                    acc[r][m] += (loc * sx[u][m]) * sw[u][r];
+                }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = group_sum<GS>(acc[r][m]);
+
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const int v = r * M + m;
+            const int64_t n = n0 + r;
+            if ((v % GS) == j && n < N) y[m * ldy + n] = f32_to_bf16(acc[r][m]);
+        }
+}
+
+}  // namespace qlin
