@@ -161,7 +161,7 @@ def main():
     else:
         w0 = t(d["w"])
         ws_copies = [w0] + [w0.clone() for _ in range(B - 1)]
-    sc = t(d["ws"])
+    sc = t(d["ws"]) if "ws" in d else None
 
     # ---------------------------------------------------------------- per-call launch lists
     xq_buf = torch.empty((Mmax, K), dtype=torch.int8 if wl == "int8_decode" else torch.uint8, device=dev)

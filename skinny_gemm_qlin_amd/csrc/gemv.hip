@@ -12,6 +12,7 @@
 #include <algorithm>
 
 #include "gemv_kernels.hpp"
+#include "mfma_kernels.hpp"
 #include "qlin_launch.hpp"
 
 namespace qlin {
@@ -62,6 +63,44 @@ inline int steps64(int64_t K) { return (int)(((K >> 4) + 63) / 64); }
         default: return RUN<1, 64, 1, 8, 4>(a, st);                   \
     }
 
+
+// Matrix-core kernels: one workgroup of kMfmaKS waves per 16-row tile, U
+// chunks of 256 K per batch (U = the chunks of a wave's K slice, at most 5).
+inline int mfma_u(int64_t K) {
+    const int64_t nch = (K + 255) >> 8, per = (nch + kMfmaKS - 1) / kMfmaKS;
+    return (int)(per < 5 ? (per < 1 ? 1 : per) : 5);
+}
+
+#define QLIN_BY_U(KERNEL, U_, ...)                                                        \
+    switch (U_) {                                                                        \
+        case 1: hipLaunchKernelGGL((KERNEL<1>), __VA_ARGS__); break;                     \
+        case 2: hipLaunchKernelGGL((KERNEL<2>), __VA_ARGS__); break;                     \
+        case 3: hipLaunchKernelGGL((KERNEL<3>), __VA_ARGS__); break;                     \
+        case 4: hipLaunchKernelGGL((KERNEL<4>), __VA_ARGS__); break;                     \
+        default: hipLaunchKernelGGL((KERNEL<5>), __VA_ARGS__); break;                    \
+    }
+
+hipError_t run_i8_mfma(const I8Args& a, hipStream_t st) {
+    dim3 grid((unsigned)((a.N + 15) / 16)), block(64 * kMfmaKS);
+    QLIN_BY_U(gemv_i8_mfma_kernel, mfma_u(a.K), grid, block, 0, st, a.xq, a.ldxq, a.xs, a.xs_step, (int)a.M,
+              a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.bias, a.y, a.ldy, a.out_kind)
+    return hipGetLastError();
+}
+
+hipError_t run_fp8_mfma(const F8Args& a, hipStream_t st) {
+    dim3 grid((unsigned)((a.N + 15) / 16)), block(64 * kMfmaKS);
+    QLIN_BY_U(gemv_fp8_mfma_kernel, mfma_u(a.K), grid, block, 0, st, a.x, a.ldx, (int)a.M, a.K, a.w, a.ldw,
+              a.N, a.ws, a.ws_step, a.y, a.ldy)
+    return hipGetLastError();
+}
+
+hipError_t run_blk_mfma(const BlkArgs& a, hipStream_t st) {
+    dim3 grid((unsigned)((a.N + 15) / 16)), block(64 * kMfmaKS);
+    QLIN_BY_U(gemv_fp8_blk_mfma_kernel, mfma_u(a.K), grid, block, 0, st, a.xq, a.xs, (int)a.M, a.K, a.w,
+              a.ldw, a.N, a.ws, a.y, a.ldy)
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemv_i8(const I8Args& a, hipStream_t st) {
@@ -69,20 +108,7 @@ hipError_t launch_gemv_i8(const I8Args& a, hipStream_t st) {
         case 1: QLIN_M1_BY_STEPS(run_i8, a, st)
         case 2: return run_i8<2, 32, 2, 2, 1>(a, st);
         case 3: return run_i8<3, 32, 4, 1, 1>(a, st);
-        case 4: return run_i8<4, 32, 4, 1, 1>(a, st);
-        case 5: return run_i8<5, 16, 2, 2, 1>(a, st);
-        case 6: return run_i8<6, 16, 2, 2, 1>(a, st);
-        case 7: return run_i8<7, 16, 2, 2, 1>(a, st);
-        case 8: return run_i8<8, 16, 2, 2, 1>(a, st);
-        case 9: return run_i8<9, 16, 4, 1, 1>(a, st);
-        case 10: return run_i8<10, 16, 4, 1, 1>(a, st);
-        case 11: return run_i8<11, 16, 4, 1, 1>(a, st);
-        case 12: return run_i8<12, 16, 4, 1, 1>(a, st);
-        case 13: return run_i8<13, 16, 4, 1, 1>(a, st);
-        case 14: return run_i8<14, 16, 4, 1, 1>(a, st);
-        case 15: return run_i8<15, 16, 4, 1, 1>(a, st);
-        case 16: return run_i8<16, 16, 4, 1, 1>(a, st);
-        default: return hipErrorInvalidValue;
+        default: return run_i8_mfma(a, st);
     }
 }
 
@@ -91,42 +117,14 @@ hipError_t launch_gemv_fp8(const F8Args& a, hipStream_t st) {
         case 1: return run_fp8<1, 32, 2, 1, 1>(a, st);
         case 2: return run_fp8<2, 64, 4, 1, 1>(a, st);
         case 3: return run_fp8<3, 64, 4, 1, 1>(a, st);
-        case 4: return run_fp8<4, 64, 4, 1, 1>(a, st);
-        case 5: return run_fp8<5, 64, 4, 1, 1>(a, st);
-        case 6: return run_fp8<6, 64, 4, 1, 1>(a, st);
-        case 7: return run_fp8<7, 64, 4, 1, 1>(a, st);
-        case 8: return run_fp8<8, 64, 4, 1, 1>(a, st);
-        case 9: return run_fp8<9, 32, 2, 1, 1>(a, st);
-        case 10: return run_fp8<10, 32, 2, 1, 1>(a, st);
-        case 11: return run_fp8<11, 32, 2, 1, 1>(a, st);
-        case 12: return run_fp8<12, 32, 2, 1, 1>(a, st);
-        case 13: return run_fp8<13, 32, 2, 1, 1>(a, st);
-        case 14: return run_fp8<14, 32, 2, 1, 1>(a, st);
-        case 15: return run_fp8<15, 32, 2, 1, 1>(a, st);
-        case 16: return run_fp8<16, 32, 2, 1, 1>(a, st);
-        default: return hipErrorInvalidValue;
+        default: return run_fp8_mfma(a, st);
     }
 }
 
 hipError_t launch_gemv_fp8_blk(const BlkArgs& a, hipStream_t st) {
     switch (a.M) {
         case 1: return run_blk<1, 64, 1, 2, 4>(a, st);
-        case 2: return run_blk<2, 64, 1, 2, 4>(a, st);
-        case 3: return run_blk<3, 64, 2, 1, 4>(a, st);
-        case 4: return run_blk<4, 64, 2, 1, 4>(a, st);
-        case 5: return run_blk<5, 64, 2, 1, 4>(a, st);
-        case 6: return run_blk<6, 64, 2, 1, 4>(a, st);
-        case 7: return run_blk<7, 64, 2, 1, 4>(a, st);
-        case 8: return run_blk<8, 64, 2, 1, 4>(a, st);
-        case 9: return run_blk<9, 64, 2, 1, 4>(a, st);
-        case 10: return run_blk<10, 64, 2, 1, 4>(a, st);
-        case 11: return run_blk<11, 64, 2, 1, 4>(a, st);
-        case 12: return run_blk<12, 64, 2, 1, 4>(a, st);
-        case 13: return run_blk<13, 64, 2, 1, 4>(a, st);
-        case 14: return run_blk<14, 64, 2, 1, 4>(a, st);
-        case 15: return run_blk<15, 64, 2, 1, 4>(a, st);
-        case 16: return run_blk<16, 64, 2, 1, 4>(a, st);
-        default: return hipErrorInvalidValue;
+        default: return run_blk_mfma(a, st);
     }
 }
 
