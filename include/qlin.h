@@ -165,7 +165,8 @@ size_t qlin_moe_mxfp4_workspace_bytes(int64_t M, int64_t N, int64_t topk, int64_
  *   y         bf16 [M, ldy]
  *   workspace device buffer of at least qlin_moe_mxfp4_workspace_bytes(),
  *             16-byte aligned; its contents on entry do not matter.
- * Requires K % 32 == 0, K >= 32, 1 <= topk <= 16, E >= 1, ldx % 8 == 0. */
+ * Requires K % 32 == 0, 32 <= K <= 30720 (one staged activation row must fit
+ * the workgroup's 64 KiB LDS budget), 1 <= topk <= 16, E >= 1, ldx % 8 == 0. */
 int qlin_moe_mxfp4(const void* x, int64_t ldx, int64_t M, int64_t K,
                    const uint8_t* w_fp4, const uint8_t* s_ue8m0, int64_t E, int64_t N,
                    const int32_t* topk_ids, const float* topk_w, int64_t topk,

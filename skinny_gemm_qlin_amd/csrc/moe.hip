@@ -2,123 +2,200 @@
 // element/scale formats of the OCP MX spec: E2M1 elements, one UE8M0 scale
 // per 32 consecutive K elements].
 //
-// Stage 1+2 (moe_expert_kernel, persistent wavefronts):
-//   * every wave reads the M*topk routing ids into LDS and lists the live
-//     experts in order of first appearance (pairs whose id is out of range
-//     are dropped) -- the bucketing is recomputed per wave, so no host sync
-//     and no extra launch is needed;
-//   * work item = (live expert u, tile of 4 rows); waves stride over the
-//     items.  For an item, the pairs routed to the expert are gathered and
-//     the expert's rows are streamed once for up to T pairs at a time;
-//   * a 16-byte weight chunk is 32 E2M1 codes = exactly one UE8M0 block, so
-//     each lane folds its block scale into its chunk partial before the DPP
-//     row reduction; fp32 partial rows go to the workspace, one per pair.
+// Stage 1+2 (moe_expert_kernel): grid = (64-row tiles) x (expert slots).
+//   * bucketing, in every workgroup (no host synchronisation, no extra
+//     launch): thread p holds routing pair p (ids outside [0, E) dropped); the
+//     first pair of each expert is found with an LDS atomicMin table indexed
+//     by expert id (a v_readlane scan when E exceeds the table), live experts
+//     are ranked in order of first appearance, slot blockIdx.y takes the
+//     expert of that rank and a workgroup past the live count exits at once;
+//   * the pairs routed to the expert are listed in pair order and processed
+//     T at a time: their activation rows are staged in LDS once per
+//     workgroup, then each wave streams 16 weight rows (4 lane groups of 16
+//     lanes x 4 rows) with 128-bit loads, U steps of 256 bytes per row in
+//     flight, so the expert's weights are read from HBM once per T tokens;
+//   * a 16-byte chunk is 32 E2M1 codes = exactly one UE8M0 block; a lane
+//     widens its codes to bf16 (v_cvt_scalef32_pk_bf16_fp4, exact), dots them
+//     with the activations (v_dot2_f32_bf16, fp32) and folds the block scale
+//     into its own partial; DPP row reduction; one fp32 partial row per pair
+//     goes to the workspace.
 // Stage 3 (moe_combine_kernel): y[t,n] = bf16(sum_j g[t,j] * part[t,j,n]) in
 // slot order j = 0..topk-1 (deterministic).
-#include "qlin_device.hpp"
+#include "gemv_kernels.hpp"
 #include "qlin_launch.hpp"
 
 namespace qlin {
 
-constexpr int kMaxPairs = 256;  // M <= 16, topk <= 16
+constexpr int kMaxPairs = 256;    // M <= 16, topk <= 16
+constexpr int kMoeRows = 64;      // rows per workgroup: 4 waves x 4 groups x 4 rows
+constexpr int kMoeR = 4;          // rows per 16-lane group
+constexpr int64_t kMoeLdsBytes = 64 * 1024;  // activation staging budget per workgroup
+constexpr int kMoeTable = 1024;   // experts covered by the first-occurrence table
 
-template <int T>
-__global__ __launch_bounds__(64) void moe_expert_kernel(
+// Staged activation row layout in LDS: 16 bytes of padding after every 128
+// elements, so the 16 lanes of a group (64-byte stride) hit distinct banks.
+__host__ __device__ constexpr int64_t moe_pitch(int64_t K) { return K + ((K + 127) >> 7) * 8; }
+
+template <int T, int U, bool TABLE>
+__global__ __launch_bounds__(256) void moe_expert_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int M, int64_t K,
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ s, int64_t E, int64_t N,
     const int32_t* __restrict__ ids, int topk, float* __restrict__ part) {
-    __shared__ int32_t sid[kMaxPairs];
-    __shared__ int32_t live[kMaxPairs];
+    extern __shared__ __align__(16) uint16_t xl[];  // [T][pitch] activation rows of the current pairs
     __shared__ int32_t plist[kMaxPairs];
-    const int lane = threadIdx.x;
+    __shared__ int32_t firstpos[TABLE ? kMoeTable : 1];
+    __shared__ int32_t wcnt[4], hcnt[4];
+    __shared__ int32_t sh_e;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int g = lane >> 4, j = lane & 15;
-    const int npairs = M * topk;
+    const int npairs = M * topk;  // <= 256: thread p owns pair p
+    const uint64_t below = (1ull << lane) - 1ull;
 
-    for (int p = lane; p < npairs; p += 64) {
-        const int32_t e = ids[p];
-        sid[p] = (e >= 0 && e < E) ? e : -1;
+    int mine = -1;
+    if (tid < npairs) {
+        const int32_t id = ids[tid];
+        mine = (id >= 0 && id < E) ? id : -1;
     }
-    __syncthreads();
-    // live experts in order of first appearance
-    int nlive = 0;
-    for (int base = 0; base < npairs; base += 64) {
-        const int p = base + lane;
-        bool first = false;
-        if (p < npairs && sid[p] >= 0) {
-            first = true;
-            for (int q = 0; q < p; ++q) first = first && (sid[q] != sid[p]);
+    if (TABLE)
+        for (int i = tid; i < E; i += 256) firstpos[i] = 0x7fffffff;
+    if (tid == 0) sh_e = -1;
+    bool first;
+    if (TABLE) {
+        __syncthreads();
+        if (mine >= 0) atomicMin(&firstpos[mine], tid);
+        __syncthreads();
+        first = mine >= 0 && firstpos[mine] == tid;
+    } else {
+        // first appearance without a table: compare with every earlier pair,
+        // its id read back with v_readlane (wave w scans waves 0..w)
+        __shared__ int32_t sid[kMaxPairs];
+        sid[tid] = mine;
+        __syncthreads();
+        first = mine >= 0;
+        for (int q0 = 0; q0 <= wv * 64; q0 += 64) {
+            const int other = sid[q0 + lane];
+            const int lim = npairs - q0 < 64 ? npairs - q0 : 64;
+            for (int l = 0; l < lim; ++l) {
+                const int v = __builtin_amdgcn_readlane(other, l);
+                first = first && !(q0 + l < tid && v == mine);
+            }
         }
-        const uint64_t mask = __ballot(first);
-        const int rank = __popcll(mask & ((1ull << lane) - 1ull));
-        if (first) live[nlive + rank] = sid[p];
-        nlive += __popcll(mask);
     }
+    const uint64_t fm = __ballot(first);
+    if (lane == 0) wcnt[wv] = __popcll(fm);
     __syncthreads();
+    int base = 0;
+    for (int q = 0; q < wv; ++q) base += wcnt[q];
+    if (first && base + __popcll(fm & below) == (int)blockIdx.y) sh_e = mine;
+    __syncthreads();
+    const int e = sh_e;
+    if (e < 0) return;  // slot past the number of live experts (workgroup-uniform)
+    const bool h = mine == e;
+    const uint64_t hm = __ballot(h);
+    if (lane == 0) hcnt[wv] = __popcll(hm);
+    __syncthreads();
+    int hb = 0, cnt = 0;
+    for (int q = 0; q < 4; ++q) {
+        hb += q < wv ? hcnt[q] : 0;
+        cnt += hcnt[q];
+    }
+    if (h) plist[hb + __popcll(hm & below)] = tid;  // read after the barrier that opens each pass
 
-    const int64_t tiles = (N + 3) / 4;
-    const int64_t items = (int64_t)nlive * tiles;
-    const int64_t kchunks = K >> 5;  // 32 codes (16 bytes) per chunk
-    const int64_t wrow_bytes = K >> 1;
+    const int kchunks = (int)(K >> 5);  // 16-byte chunks (32 codes) per row
+    const int nsteps = (kchunks + 15) >> 4;
+    const int pitch = (int)moe_pitch(K);
+    const int64_t n0 = (int64_t)blockIdx.x * kMoeRows + wv * 16 + g * kMoeR;
+    const uint8_t* wr[kMoeR];
+    const uint8_t* sr[kMoeR];
+#pragma unroll
+    for (int r = 0; r < kMoeR; ++r) {
+        const int64_t n = n0 + r < N ? n0 + r : N - 1;
+        wr[r] = w + ((int64_t)e * N + n) * (K >> 1);
+        sr[r] = s + ((int64_t)e * N + n) * kchunks;
+    }
 
-    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-        const int u = (int)(it / tiles);
-        const int64_t n = (it % tiles) * 4 + g;
-        const int64_t nc = n < N ? n : N - 1;
-        const int e = live[u];
-        // pairs routed to expert e, in pair order
-        int cnt = 0;
-        for (int base = 0; base < npairs; base += 64) {
-            const int p = base + lane;
-            const bool hit = p < npairs && sid[p] == e;
-            const uint64_t mask = __ballot(hit);
-            const int rank = __popcll(mask & ((1ull << lane) - 1ull));
-            __syncthreads();
-            if (hit) plist[cnt + rank] = p;
-            cnt += __popcll(mask);
+    for (int pb = 0; pb < cnt; pb += T) {
+        const int nt = cnt - pb < T ? cnt - pb : T;
+        // stage the activation rows of pairs pb..pb+nt-1, 16 bytes per lane
+        __syncthreads();  // the previous pass is done reading xl
+        const int vec_per_row = (int)(K >> 3);
+        for (int i = tid; i < nt * vec_per_row; i += 256) {
+            const int t = i / vec_per_row;
+            const int v = i - t * vec_per_row;
+            const int64_t tok = plist[pb + t] / topk;
+            *(u32x4_t*)(xl + t * pitch + v * 8 + (v >> 4) * 8) = ld16(x + tok * ldx + (int64_t)v * 8);
         }
         __syncthreads();
 
-        const uint8_t* wr = w + ((int64_t)e * N + nc) * wrow_bytes;
-        const uint8_t* sr = s + ((int64_t)e * N + nc) * (K >> 5);
-        for (int pb = 0; pb < cnt; pb += T) {
-            float acc[T];
-            const uint16_t* xr[T];
+        float acc[kMoeR][T];
 #pragma unroll
-            for (int q = 0; q < T; ++q) {
-                acc[q] = 0.0f;
-                const int pq = pb + q < cnt ? plist[pb + q] : plist[pb];
-                xr[q] = x + (int64_t)(pq / topk) * ldx;
-            }
-            for (int64_t c = j; c < kchunks; c += 16) {
-                const u32x4_t wv = ld_stream(wr + c * 16);
-                const float sc = ue8m0_to_f32(sr[c]);
-                bf16x2_t wb[16];
-                e2m1x8_to_bf16(wv.x, wb + 0);
-                e2m1x8_to_bf16(wv.y, wb + 4);
-                e2m1x8_to_bf16(wv.z, wb + 8);
-                e2m1x8_to_bf16(wv.w, wb + 12);
+        for (int r = 0; r < kMoeR; ++r)
 #pragma unroll
-                for (int q = 0; q < T; ++q) {
-                    if (pb + q < cnt) {  // wave-uniform
-                        const uint16_t* xp = xr[q] + c * 32;
-                        const u32x4_t x0 = ld16(xp), x1 = ld16(xp + 8), x2 = ld16(xp + 16), x3 = ld16(xp + 24);
-                        const uint32_t xv[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
-                                                 x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
-                        float loc = 0.0f;
+            for (int t = 0; t < T; ++t) acc[r][t] = 0.0f;
+
+        for (int st = 0; st < nsteps; st += U) {
+            u32x4_t wv_[U][kMoeR];
+            uint32_t sb[U][kMoeR];
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) loc = dot2(wb[i], as_bf16x2(xv[i]), loc);
-                        acc[q] += loc * sc;
+            for (int u = 0; u < U; ++u) {
+                if (st + u < nsteps) {  // wave-uniform
+                    const int c = (st + u) * 16 + j;
+                    const int cc = c < kchunks ? c : kchunks - 1;
+#pragma unroll
+                    for (int r = 0; r < kMoeR; ++r) {
+                        wv_[u][r] = ld_stream(wr[r] + (int64_t)cc * 16);
+                        sb[u][r] = sr[r][cc];
                     }
                 }
             }
 #pragma unroll
-            for (int q = 0; q < T; ++q) {
-                if (pb + q < cnt) {
-                    const float v = row_sum_f32(acc[q]);
-                    if (j == (q & 15) && n < N) part[(int64_t)plist[pb + q] * N + n] = v;
+            for (int u = 0; u < U; ++u) {
+                if (st + u >= nsteps) break;  // wave-uniform
+                const int c = (st + u) * 16 + j;
+                const bool ok = c < kchunks;
+                const int cc = ok ? c : kchunks - 1;
+                // activations of this chunk: 32 bf16 per token from LDS
+                u32x4_t xa[T][4];
+#pragma unroll
+                for (int t = 0; t < T; ++t)
+                    if (t < nt) {
+                        const uint16_t* xp = xl + t * pitch + cc * 32 + (cc >> 2) * 8;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) xa[t][q] = *(const u32x4_t*)(xp + 8 * q);
+                    }
+#pragma unroll
+                for (int r = 0; r < kMoeR; ++r) {
+                    bf16x2_t wb[16];
+                    e2m1x8_to_bf16(wv_[u][r].x, wb + 0);
+                    e2m1x8_to_bf16(wv_[u][r].y, wb + 4);
+                    e2m1x8_to_bf16(wv_[u][r].z, wb + 8);
+                    e2m1x8_to_bf16(wv_[u][r].w, wb + 12);
+                    const float sc = ue8m0_to_f32(sb[u][r]);
+#pragma unroll
+                    for (int t = 0; t < T; ++t)
+                        if (t < nt) {
+                            float loc = 0.0f;
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                loc = dot2(wb[4 * q + 0], as_bf16x2(xa[t][q].x), loc);
+                                loc = dot2(wb[4 * q + 1], as_bf16x2(xa[t][q].y), loc);
+                                loc = dot2(wb[4 * q + 2], as_bf16x2(xa[t][q].z), loc);
+                                loc = dot2(wb[4 * q + 3], as_bf16x2(xa[t][q].w), loc);
+                            }
+                            acc[r][t] += ok ? loc * sc : 0.0f;  // a lane past the row end adds 0
+                        }
                 }
             }
         }
+#pragma unroll
+        for (int r = 0; r < kMoeR; ++r)
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+                if (t < nt) {
+                    const float v = group_sum<16>(acc[r][t]);
+                    const int64_t n = n0 + r;
+                    if (j == ((r * T + t) & 15) && n < N) part[(int64_t)plist[pb + t] * N + n] = v;
+                }
     }
 }
 
@@ -137,13 +214,13 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(
     y[t * ldy + n] = f32_to_bf16(acc);
 }
 
-template <int T>
-static hipError_t launch_moe_t(const MoeArgs& a, hipStream_t st) {
+template <int T, int U, bool TABLE>
+static hipError_t launch_moe_tu(const MoeArgs& a, hipStream_t st) {
     const int64_t npairs = a.M * a.topk;
-    const int64_t max_live = npairs < a.E ? npairs : a.E;
-    const int64_t items = max_live * ((a.N + 3) / 4);
-    const int64_t grid = items < 8192 ? items : 8192;
-    hipLaunchKernelGGL((moe_expert_kernel<T>), dim3((unsigned)grid), dim3(64), 0, st,
+    const int64_t slots = npairs < a.E ? npairs : a.E;
+    dim3 grid((unsigned)((a.N + kMoeRows - 1) / kMoeRows), (unsigned)slots);
+    const size_t lds = (size_t)T * moe_pitch(a.K) * 2;
+    hipLaunchKernelGGL((moe_expert_kernel<T, U, TABLE>), grid, dim3(256), lds, st,
                        a.x, a.ldx, (int)a.M, a.K, a.w, a.s, a.E, a.N, a.ids, (int)a.topk, a.part);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -153,11 +230,14 @@ static hipError_t launch_moe_t(const MoeArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Two tokens per pass (T = 2, U = 2: 122 VGPRs, four waves per SIMD) while
+// both staged rows fit the LDS budget, else one (K <= 30720 keeps one row
+// within it).  Four tokens per pass re-read fewer experts but halve the
+// resident waves, which costs more than the re-reads at decode batch sizes.
 hipError_t launch_moe_mxfp4(const MoeArgs& a, hipStream_t st) {
-    if (a.M <= 1) return launch_moe_t<1>(a, st);
-    if (a.M <= 2) return launch_moe_t<2>(a, st);
-    if (a.M <= 4) return launch_moe_t<4>(a, st);
-    return launch_moe_t<8>(a, st);
+    const bool two = 2 * moe_pitch(a.K) * 2 <= kMoeLdsBytes;
+    if (a.E <= kMoeTable) return two ? launch_moe_tu<2, 2, true>(a, st) : launch_moe_tu<1, 2, true>(a, st);
+    return two ? launch_moe_tu<2, 2, false>(a, st) : launch_moe_tu<1, 2, false>(a, st);
 }
 
 }  // namespace qlin

@@ -110,7 +110,8 @@ int qlin_moe_mxfp4(const void* x, int64_t ldx, int64_t M, int64_t K,
                    const int32_t* topk_ids, const float* topk_w, int64_t topk,
                    void* y, int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
     if (!x || !w_fp4 || !s_ue8m0 || !topk_ids || !topk_w || !y) return QLIN_ERR_NULL;
-    if (M < 1 || M > QLIN_MAX_M || N < 1 || E < 1 || K < 32 || K % 32 != 0 || topk < 1 || topk > 16)
+    if (M < 1 || M > QLIN_MAX_M || N < 1 || E < 1 || K < 32 || K % 32 != 0 || K > 30720 || topk < 1 ||
+        topk > 16)
         return QLIN_ERR_SHAPE;
     if (ldx < K || ldy < N) return QLIN_ERR_STRIDE;
     if (misaligned(x, 16) || ldx % 8 != 0 || misaligned(w_fp4, 16) || misaligned(topk_ids, 4) ||

@@ -134,6 +134,7 @@ def test_moe_errors(q):
     assert call(topk=17) == -2
     assert call(E=0) == -2
     assert call(K=7168 + 16, ldx=7184) == -2
+    assert call(K=30720 + 32, ldx=30752) == -2   # one staged activation row must fit 64 KiB of LDS
     assert call(ldy=100) == -3
     assert call(ws=None) == -5
     assert call(wsb=need - 1) == -5

@@ -58,7 +58,11 @@ def test_moe_full_config(ql, orc):
 
 @pytest.mark.parametrize("M,E,N,K,topk", [(1, 4, 64, 256, 1), (2, 8, 100, 512, 2), (3, 16, 37, 1024, 4),
                                           (5, 6, 130, 96, 3), (8, 64, 256, 7168, 6), (16, 32, 64, 2048, 8),
-                                          (16, 3, 40, 512, 16)])
+                                          (16, 3, 40, 512, 16),
+                                          # 2 and 1 tokens per LDS pass, then the largest K accepted
+                                          (6, 8, 70, 8192, 3), (5, 4, 33, 16384, 2), (3, 2, 16, 30720, 2),
+                                          # expert ids up to the first-occurrence table's size, then past it
+                                          (16, 1024, 24, 128, 16), (4, 1100, 16, 64, 8), (16, 1500, 8, 96, 16)])
 def test_moe_shapes(ql, orc, M, E, N, K, topk):
     if topk > E:
         d = gen_moe(M, E, N, K, 1, seed=M + N)
