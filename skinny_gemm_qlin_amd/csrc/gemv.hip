@@ -1,14 +1,14 @@
-// gemv.hip -- launchers of the VALU skinny-GEMV kernels (templates in
-// gemv_kernels.hpp) with the per-M tile configuration.
-//
-// Configuration per M (lanes per row GS, rows per group R, unrolled steps U,
-// waves per workgroup WPB) was chosen by measurement on MI355X at the decode
-// shapes (N=17408, K=5120 for INT8 / E4M3; N=4096, K=7168 for block FP8):
-//   * M = 1: one whole wavefront per row (GS=64), all K steps of the row in
-//     flight (U = number of steps, up to 8), 4 waves per workgroup;
-//   * larger M: smaller lane groups and more rows per group, so that each
-//     activation load feeds more weight rows, with fewer steps in flight to
-//     bound register pressure.
+// gemv.hip -- launchers of the skinny-GEMV kernels (VALU templates in
+// gemv_kernels.hpp, matrix-core templates in mfma_kernels.hpp) with the
+// per-M choice of kernel and tile, made by measurement on MI355X at the
+// decode shapes (N=17408, K=5120 for INT8 / E4M3; N=4096, K=7168 for block
+// FP8):
+//   * M = 1: VALU, one whole wavefront per row (GS=64), all K steps of the
+//     row in flight (up to 8), 4 waves per workgroup; block FP8 uses its own
+//     M = 1 kernel that shares the scale bytes of a batch across the wave;
+//   * M = 2 (INT8, E4M3): VALU with smaller lane groups and several rows per
+//     group, so that each activation load feeds more weight rows;
+//   * otherwise: the matrix-core kernels.
 #include <algorithm>
 
 #include "gemv_kernels.hpp"
@@ -65,39 +65,36 @@ inline int steps64(int64_t K) { return (int)(((K >> 4) + 63) / 64); }
 
 
 // Matrix-core kernels: one workgroup of kMfmaKS waves per 16-row tile, U
-// chunks of 256 K per batch (U = the chunks of a wave's K slice, at most 5).
-inline int mfma_u(int64_t K) {
-    const int64_t nch = (K + 255) >> 8, per = (nch + kMfmaKS - 1) / kMfmaKS;
-    return (int)(per < 5 ? (per < 1 ? 1 : per) : 5);
-}
-
-#define QLIN_BY_U(KERNEL, U_, ...)                                                        \
-    switch (U_) {                                                                        \
-        case 1: hipLaunchKernelGGL((KERNEL<1>), __VA_ARGS__); break;                     \
-        case 2: hipLaunchKernelGGL((KERNEL<2>), __VA_ARGS__); break;                     \
-        case 3: hipLaunchKernelGGL((KERNEL<3>), __VA_ARGS__); break;                     \
-        case 4: hipLaunchKernelGGL((KERNEL<4>), __VA_ARGS__); break;                     \
-        default: hipLaunchKernelGGL((KERNEL<5>), __VA_ARGS__); break;                    \
-    }
-
+// chunks of 256 K per batch.  Measured at the decode shapes: one chunk per
+// batch for INT8 and E4M3 (few registers, so the whole grid is resident at
+// once and waves overlap each other's latency), two for block FP8.
 hipError_t run_i8_mfma(const I8Args& a, hipStream_t st) {
     dim3 grid((unsigned)((a.N + 15) / 16)), block(64 * kMfmaKS);
-    QLIN_BY_U(gemv_i8_mfma_kernel, mfma_u(a.K), grid, block, 0, st, a.xq, a.ldxq, a.xs, a.xs_step, (int)a.M,
-              a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.bias, a.y, a.ldy, a.out_kind)
+    hipLaunchKernelGGL((gemv_i8_mfma_kernel<1>), grid, block, 0, st, a.xq, a.ldxq, a.xs, a.xs_step, (int)a.M,
+                       a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.bias, a.y, a.ldy, a.out_kind);
     return hipGetLastError();
 }
 
 hipError_t run_fp8_mfma(const F8Args& a, hipStream_t st) {
     dim3 grid((unsigned)((a.N + 15) / 16)), block(64 * kMfmaKS);
-    QLIN_BY_U(gemv_fp8_mfma_kernel, mfma_u(a.K), grid, block, 0, st, a.x, a.ldx, (int)a.M, a.K, a.w, a.ldw,
-              a.N, a.ws, a.ws_step, a.y, a.ldy)
+    hipLaunchKernelGGL((gemv_fp8_mfma_kernel<1>), grid, block, 0, st, a.x, a.ldx, (int)a.M, a.K, a.w, a.ldw,
+                       a.N, a.ws, a.ws_step, a.y, a.ldy);
     return hipGetLastError();
 }
 
 hipError_t run_blk_mfma(const BlkArgs& a, hipStream_t st) {
     dim3 grid((unsigned)((a.N + 15) / 16)), block(64 * kMfmaKS);
-    QLIN_BY_U(gemv_fp8_blk_mfma_kernel, mfma_u(a.K), grid, block, 0, st, a.xq, a.xs, (int)a.M, a.K, a.w,
-              a.ldw, a.N, a.ws, a.y, a.ldy)
+    hipLaunchKernelGGL((gemv_fp8_blk_mfma_kernel<2>), grid, block, 0, st, a.xq, a.xs, (int)a.M, a.K, a.w,
+                       a.ldw, a.N, a.ws, a.y, a.ldy);
+    return hipGetLastError();
+}
+
+template <int U>
+hipError_t run_blk_m1(const BlkArgs& a, hipStream_t st) {
+    constexpr int WPB = 4;
+    dim3 grid((unsigned)((a.N + WPB - 1) / WPB));
+    hipLaunchKernelGGL((gemv_fp8_blk_m1_kernel<U, WPB>), grid, dim3(64 * WPB), 0, st, a.xq, a.xs, a.K, a.w,
+                       a.ldw, a.N, a.ws, a.y);
     return hipGetLastError();
 }
 
@@ -107,7 +104,6 @@ hipError_t launch_gemv_i8(const I8Args& a, hipStream_t st) {
     switch (a.M) {
         case 1: QLIN_M1_BY_STEPS(run_i8, a, st)
         case 2: return run_i8<2, 32, 2, 2, 1>(a, st);
-        case 3: return run_i8<3, 32, 4, 1, 1>(a, st);
         default: return run_i8_mfma(a, st);
     }
 }
@@ -116,15 +112,21 @@ hipError_t launch_gemv_fp8(const F8Args& a, hipStream_t st) {
     switch (a.M) {
         case 1: return run_fp8<1, 32, 2, 1, 1>(a, st);
         case 2: return run_fp8<2, 64, 4, 1, 1>(a, st);
-        case 3: return run_fp8<3, 64, 4, 1, 1>(a, st);
         default: return run_fp8_mfma(a, st);
     }
 }
 
 hipError_t launch_gemv_fp8_blk(const BlkArgs& a, hipStream_t st) {
-    switch (a.M) {
-        case 1: return run_blk<1, 64, 1, 2, 4>(a, st);
-        default: return run_blk_mfma(a, st);
+    if (a.M > 1) return run_blk_mfma(a, st);
+    switch (std::min(steps64(a.K), 8)) {
+        case 1: return run_blk_m1<1>(a, st);
+        case 2: return run_blk_m1<2>(a, st);
+        case 3: return run_blk_m1<3>(a, st);
+        case 4: return run_blk_m1<4>(a, st);
+        case 5: return run_blk_m1<5>(a, st);
+        case 6: return run_blk_m1<6>(a, st);
+        case 7: return run_blk_m1<7>(a, st);
+        default: return run_blk_m1<8>(a, st);
     }
 }
 

@@ -301,4 +301,57 @@ __global__ __launch_bounds__(64 * WPB) void gemv_fp8_blk_kernel(
         }
 }
 
+// M = 1 block-scaled FP8 with the scale bytes fetched once per batch.  A wave
+// owns one row; a step is 64 lanes x 16 bytes = 8 K blocks of 128.  For a
+// batch of U <= 8 steps, lane l loads the weight and the activation scale of
+// K block (first block of the batch) + l, and in step u the lanes read the
+// scales of their own block (u*8 + lane/8) with a cross-lane shuffle instead
+// of two more byte loads per step.  Arithmetic and order as
+// gemv_fp8_blk_kernel: acc += (dot * 2^(xs-127)) * 2^(ws-127).
+template <int U, int WPB>
+__global__ __launch_bounds__(64 * WPB) void gemv_fp8_blk_m1_kernel(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, int64_t K,
+    const uint8_t* __restrict__ w, int64_t ldw, int64_t N,
+    const uint8_t* __restrict__ ws, uint16_t* __restrict__ y) {
+    static_assert(U >= 1 && U <= 8, "one scale byte per lane covers at most 8 steps");
+    const int j = threadIdx.x & 63;
+    const int64_t n = first_row<64, 1, WPB>();
+    if (n >= N) return;  // wave-uniform
+    const int64_t nkb = K >> 7;
+    const uint8_t* wr = w + n * ldw;
+    const uint8_t* wsr = ws + (n >> 7) * nkb;
+    const int64_t nchunk = K >> 4;
+    const int64_t nsteps = (nchunk + 63) >> 6;
+    float acc = 0.0f;
+    for (int64_t s = 0; s < nsteps; s += U) {
+        const int64_t kbl = s * 8 + j;
+        const bool okb = j < 8 * U && kbl < nkb;
+        const float swl = okb ? ue8m0_to_f32(wsr[kbl]) : 0.0f;
+        const float sxl = okb ? ue8m0_to_f32(xs[kbl]) : 0.0f;
+        u32x4_t wv[U], xv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = (s + u) * 64 + j;
+            const int64_t cc = c < nchunk ? c : nchunk - 1;
+            wv[u] = ld_stream(wr + cc * 16);
+            xv[u] = ld16(xq + cc * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool ok = (s + u) * 64 + j < nchunk;
+            const float sw = __shfl(swl, u * 8 + (j >> 3));
+            const float sx = __shfl(sxl, u * 8 + (j >> 3));
+            bf16x2_t xb[8], wb[8];
+            e4m3x16(xv[u], xb);
+            e4m3x16(wv[u], wb);
+            float loc = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) loc = dot2(wb[i], xb[i], loc);
+            acc += ok ? (loc * sx) * sw : 0.0f;  // a lane past the row end adds 0
+        }
+    }
+    acc = group_sum<64>(acc);
+    if (j == 0) y[n] = f32_to_bf16(acc);
+}
+
 }  // namespace qlin
