@@ -64,28 +64,44 @@ inline int steps64(int64_t K) { return (int)(((K >> 4) + 63) / 64); }
     }
 
 
-// Matrix-core kernels: one workgroup of kMfmaKS waves per 16-row tile, U
-// chunks of 256 K per batch.  Measured at the decode shapes: one chunk per
-// batch for INT8 and E4M3 (few registers, so the whole grid is resident at
-// once and waves overlap each other's latency), two for block FP8.
+// Matrix-core kernels: one workgroup of KS waves per 16-row tile, one chunk
+// of 256 K per wave per batch (few registers, so the whole grid is resident
+// and waves overlap each other's latency; measured at the decode shapes).
+// KS splits K so that the grid holds about 4096 waves: 4 when there are at
+// least 1024 row tiles, 8 from 512, else 16 -- never more waves than K has
+// chunks for, beyond the minimum of 4.
+inline int mfma_ks(int64_t N, int64_t K) {
+    const int64_t tiles = (N + 15) / 16, nch = (K + 255) >> 8;
+    int ks = tiles >= 1024 ? 4 : (tiles >= 512 ? 8 : 16);
+    while (ks > 4 && ks / 2 >= nch) ks /= 2;
+    return ks;
+}
+
+#define QLIN_BY_KS(KERNEL, KS_, GRID, ...)                                                 \
+    switch (KS_) {                                                                        \
+        case 16: hipLaunchKernelGGL((KERNEL<1, 16>), GRID, dim3(1024), __VA_ARGS__); break;  \
+        case 8: hipLaunchKernelGGL((KERNEL<1, 8>), GRID, dim3(512), __VA_ARGS__); break;     \
+        default: hipLaunchKernelGGL((KERNEL<1, 4>), GRID, dim3(256), __VA_ARGS__); break;    \
+    }
+
 hipError_t run_i8_mfma(const I8Args& a, hipStream_t st) {
-    dim3 grid((unsigned)((a.N + 15) / 16)), block(64 * kMfmaKS);
-    hipLaunchKernelGGL((gemv_i8_mfma_kernel<1>), grid, block, 0, st, a.xq, a.ldxq, a.xs, a.xs_step, (int)a.M,
-                       a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.bias, a.y, a.ldy, a.out_kind);
+    dim3 grid((unsigned)((a.N + 15) / 16));
+    QLIN_BY_KS(gemv_i8_mfma_kernel, mfma_ks(a.N, a.K), grid, 0, st, a.xq, a.ldxq, a.xs, a.xs_step, (int)a.M,
+               a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.bias, a.y, a.ldy, a.out_kind)
     return hipGetLastError();
 }
 
 hipError_t run_fp8_mfma(const F8Args& a, hipStream_t st) {
-    dim3 grid((unsigned)((a.N + 15) / 16)), block(64 * kMfmaKS);
-    hipLaunchKernelGGL((gemv_fp8_mfma_kernel<1>), grid, block, 0, st, a.x, a.ldx, (int)a.M, a.K, a.w, a.ldw,
-                       a.N, a.ws, a.ws_step, a.y, a.ldy);
+    dim3 grid((unsigned)((a.N + 15) / 16));
+    QLIN_BY_KS(gemv_fp8_mfma_kernel, mfma_ks(a.N, a.K), grid, 0, st, a.x, a.ldx, (int)a.M, a.K, a.w, a.ldw,
+               a.N, a.ws, a.ws_step, a.y, a.ldy)
     return hipGetLastError();
 }
 
 hipError_t run_blk_mfma(const BlkArgs& a, hipStream_t st) {
-    dim3 grid((unsigned)((a.N + 15) / 16)), block(64 * kMfmaKS);
-    hipLaunchKernelGGL((gemv_fp8_blk_mfma_kernel<2>), grid, block, 0, st, a.xq, a.xs, (int)a.M, a.K, a.w,
-                       a.ldw, a.N, a.ws, a.y, a.ldy);
+    dim3 grid((unsigned)((a.N + 15) / 16));
+    QLIN_BY_KS(gemv_fp8_blk_mfma_kernel, mfma_ks(a.N, a.K), grid, 0, st, a.xq, a.xs, (int)a.M, a.K, a.w,
+               a.ldw, a.N, a.ws, a.y, a.ldy)
     return hipGetLastError();
 }
 

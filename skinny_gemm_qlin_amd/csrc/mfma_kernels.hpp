@@ -25,7 +25,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kTilePitch = 256 + 16;  // LDS row pitch of the transpose tile (bytes); the pad spreads banks
-constexpr int kMfmaKS = 4;            // waves per workgroup (K split)
+constexpr int kMfmaKS = 4;            // default waves per workgroup (K split)
 
 // Load the 16 rows x 256 bytes of chunk c into registers (4 instructions,
 // each 4 rows x 256 contiguous bytes).  Past the end of K the address is
@@ -69,14 +69,14 @@ __device__ __forceinline__ u32x4_t tile_read(const uint8_t* t, int off) {
 
 // Sum the KS partial accumulator tiles of the workgroup in wave order; returns
 // true in wave 0, which then holds the total.
-template <class T>
+template <int KS, class T>
 __device__ __forceinline__ bool ks_reduce(T& acc, T (*red)[64]) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     red[wv][lane] = acc;
     __syncthreads();
     if (wv != 0) return false;
 #pragma unroll
-    for (int q = 1; q < kMfmaKS; ++q) acc += red[q][lane];
+    for (int q = 1; q < KS; ++q) acc += red[q][lane];
     return true;
 }
 
@@ -94,18 +94,18 @@ __device__ __forceinline__ void e4m3x16_to_bf16x8x2(const u32x4_t& c, bf16x8_t& 
 // ------------------------------------------------------------------ INT8 W8A8 (v_mfma_i32_16x16x64_i8)
 // acc exact in int32; epilogue bf16((acc*xs)*ws) (+ bias) as the VALU kernel
 // [Z100 operator-family table, INT8 row; section 2.1].
-template <int U>
-__global__ __launch_bounds__(64 * kMfmaKS) void gemv_i8_mfma_kernel(
+template <int U, int KS = kMfmaKS>
+__global__ __launch_bounds__(64 * KS) void gemv_i8_mfma_kernel(
     const int8_t* __restrict__ xq, int64_t ldxq, const float* __restrict__ xs, int xs_step, int M,
     int64_t K, const int8_t* __restrict__ w, int64_t ldw, int64_t N,
     const float* __restrict__ ws, int ws_step, const uint16_t* __restrict__ bias,
     void* __restrict__ y, int64_t ldy, int out_kind) {
-    __shared__ __align__(16) uint8_t tile[kMfmaKS][16 * kTilePitch];
-    __shared__ i32x4_t red[kMfmaKS][64];
+    __shared__ __align__(16) uint8_t tile[KS][16 * kTilePitch];
+    __shared__ i32x4_t red[KS][64];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int mi = lane & 15, mg = lane >> 4;
     const int64_t n0 = (int64_t)blockIdx.x * 16;
-    const int64_t nch = (K + 255) >> 8, per = (nch + kMfmaKS - 1) / kMfmaKS;
+    const int64_t nch = (K + 255) >> 8, per = (nch + KS - 1) / KS;
     const int64_t c0 = wv * per, c1 = c0 + per < nch ? c0 + per : nch;
     const TileLoader tl((const uint8_t*)w, ldw, n0, N);
     const bool xon = mi < M;
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(64 * kMfmaKS) void gemv_i8_mfma_kernel(
                                                            __builtin_bit_cast(i32x4_t, xb[u][h]), acc, 0, 0, 0);
         }
     }
-    if (!ks_reduce(acc, red)) return;
+    if (!ks_reduce<KS>(acc, red)) return;
     if (mi < M) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -160,17 +160,17 @@ __global__ __launch_bounds__(64 * kMfmaKS) void gemv_i8_mfma_kernel(
 // multiplied with the bf16 activations; fp32 accumulation; the weight scale
 // once in the epilogue [Z100 operator-family table, FP8 row; section 2.2].
 // MFMA (h, half) of a chunk covers K = c*256 + 64h + 16g + 8*half + [0, 8).
-template <int U>
-__global__ __launch_bounds__(64 * kMfmaKS) void gemv_fp8_mfma_kernel(
+template <int U, int KS = kMfmaKS>
+__global__ __launch_bounds__(64 * KS) void gemv_fp8_mfma_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int M, int64_t K,
     const uint8_t* __restrict__ w, int64_t ldw, int64_t N,
     const float* __restrict__ ws, int ws_step, uint16_t* __restrict__ y, int64_t ldy) {
-    __shared__ __align__(16) uint8_t tile[kMfmaKS][16 * kTilePitch];
-    __shared__ f32x4_t red[kMfmaKS][64];
+    __shared__ __align__(16) uint8_t tile[KS][16 * kTilePitch];
+    __shared__ f32x4_t red[KS][64];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int mi = lane & 15, mg = lane >> 4;
     const int64_t n0 = (int64_t)blockIdx.x * 16;
-    const int64_t nch = (K + 255) >> 8, per = (nch + kMfmaKS - 1) / kMfmaKS;
+    const int64_t nch = (K + 255) >> 8, per = (nch + KS - 1) / KS;
     const int64_t c0 = wv * per, c1 = c0 + per < nch ? c0 + per : nch;
     const TileLoader tl(w, ldw, n0, N);
     const bool xon = mi < M;
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(64 * kMfmaKS) void gemv_fp8_mfma_kernel(
             }
         }
     }
-    if (!ks_reduce(acc, red)) return;
+    if (!ks_reduce<KS>(acc, red)) return;
     if (mi < M) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -223,18 +223,18 @@ __global__ __launch_bounds__(64 * kMfmaKS) void gemv_fp8_mfma_kernel(
 //   acc += (D * 2^(ws[n/128, kb]-127)) * 2^(xs[token, kb]-127)
 // [Z100 section 2.4: block formula, fold per K block; DSV4 section 3.3].
 // The 16 rows of a tile share one 128-row scale block (tiles are 16-aligned).
-template <int U>
-__global__ __launch_bounds__(64 * kMfmaKS) void gemv_fp8_blk_mfma_kernel(
+template <int U, int KS = kMfmaKS>
+__global__ __launch_bounds__(64 * KS) void gemv_fp8_blk_mfma_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, int M, int64_t K,
     const uint8_t* __restrict__ w, int64_t ldw, int64_t N,
     const uint8_t* __restrict__ ws, uint16_t* __restrict__ y, int64_t ldy) {
-    __shared__ __align__(16) uint8_t tile[kMfmaKS][16 * kTilePitch];
-    __shared__ f32x4_t red[kMfmaKS][64];
+    __shared__ __align__(16) uint8_t tile[KS][16 * kTilePitch];
+    __shared__ f32x4_t red[KS][64];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int mi = lane & 15, mg = lane >> 4;
     const int64_t n0 = (int64_t)blockIdx.x * 16;
     const int64_t nkb = K >> 7;
-    const int64_t nch = (K + 255) >> 8, per = (nch + kMfmaKS - 1) / kMfmaKS;
+    const int64_t nch = (K + 255) >> 8, per = (nch + KS - 1) / KS;
     const int64_t c0 = wv * per, c1 = c0 + per < nch ? c0 + per : nch;
     const TileLoader tl(w, ldw, n0, N);
     const bool xon = mi < M;
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(64 * kMfmaKS) void gemv_fp8_blk_mfma_kernel(
             }
         }
     }
-    if (!ks_reduce(acc, red)) return;
+    if (!ks_reduce<KS>(acc, red)) return;
     if (mi < M) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {

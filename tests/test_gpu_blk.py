@@ -41,7 +41,9 @@ def test_blk_small_all_M(ql, orc, M):
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (2, 130, 384), (3, 257, 896), (9, 100, 640), (16, 555, 1152),
                                    # M = 1 kernel: partial step, two batches, three batches with a short last one
-                                   (1, 5, 1152), (1, 67, 9216), (1, 3, 16512)])
+                                   (1, 5, 1152), (1, 67, 9216), (1, 3, 16512),
+                                   # 512..1023 row tiles: eight waves split K
+                                   (4, 9000, 2048), (16, 8200, 2304)])
 def test_blk_ragged(ql, orc, M, N, K):
     d = gen_fp8_blk(M, N, K, seed=N + K)
     _check(orc, d, _gpu(ql, d))

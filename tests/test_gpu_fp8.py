@@ -47,7 +47,9 @@ def test_fp8_small_all_M(ql, orc, M, per_tensor):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 16), (2, 3, 48), (3, 37, 272), (4, 129, 1040),
-                                   (8, 255, 4112), (11, 17, 2064), (16, 1001, 784)])
+                                   (8, 255, 4112), (11, 17, 2064), (16, 1001, 784),
+                                   # 512..1023 row tiles: eight waves split K
+                                   (3, 9000, 2048), (16, 9001, 2320)])
 def test_fp8_ragged(ql, orc, M, N, K):
     d = gen_fp8(M, N, K, seed=N + K)
     y, ye, S = orc.gemv_fp8(d["x"], d["w"], d["ws"])

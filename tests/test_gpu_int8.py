@@ -46,7 +46,9 @@ def test_int8_small_all_M(ql, orc, M):
 
 # ragged shapes: N not a multiple of the row tile, K not a multiple of the K step
 @pytest.mark.parametrize("M,N,K", [(1, 1, 16), (2, 3, 48), (3, 37, 272), (5, 129, 1040),
-                                   (7, 255, 4112), (9, 61, 528), (13, 17, 2064), (16, 1001, 784)])
+                                   (7, 255, 4112), (9, 61, 528), (13, 17, 2064), (16, 1001, 784),
+                                   # 512..1023 row tiles: eight waves split K
+                                   (4, 9000, 2048), (16, 9001, 2320)])
 def test_int8_ragged(ql, orc, M, N, K):
     d = gen_int8(M, N, K, seed=M * 1000 + N)
     _check(orc, d["x"], d["w"], d["ws"], _run_full(ql, d["x"], d["w"], d["ws"]))
