@@ -199,18 +199,36 @@ __global__ __launch_bounds__(256) void moe_expert_kernel(
     }
 }
 
+// One thread per output (t, n).  All topk ids, gates and partials are loaded
+// before the sum (one memory latency instead of topk); a pair whose id is out
+// of range is skipped by a select, so its never-written partial row cannot
+// leak into the sum.
 __global__ __launch_bounds__(256) void moe_combine_kernel(
     const float* __restrict__ part, const int32_t* __restrict__ ids, const float* __restrict__ gw,
     int M, int topk, int64_t E, int64_t N, uint16_t* __restrict__ y, int64_t ldy) {
+    constexpr int kMaxTopk = 16;
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= (int64_t)M * N) return;
     const int t = (int)(i / N);
     const int64_t n = i % N;
-    float acc = 0.0f;
-    for (int jj = 0; jj < topk; ++jj) {
-        const int32_t e = ids[t * topk + jj];
-        if (e >= 0 && e < E) acc = fmaf(gw[t * topk + jj], part[(int64_t)(t * topk + jj) * N + n], acc);
+    bool ok[kMaxTopk];
+    float g[kMaxTopk], v[kMaxTopk];
+#pragma unroll
+    for (int jj = 0; jj < kMaxTopk; ++jj) {
+        ok[jj] = false;
+        g[jj] = v[jj] = 0.0f;
+        if (jj < topk) {
+            const int p = t * topk + jj;
+            const int32_t e = ids[p];
+            ok[jj] = e >= 0 && e < E;
+            g[jj] = gw[p];
+            v[jj] = part[(int64_t)p * N + n];
+        }
     }
+    float acc = 0.0f;
+#pragma unroll
+    for (int jj = 0; jj < kMaxTopk; ++jj)
+        if (jj < topk) acc = ok[jj] ? fmaf(g[jj], v[jj], acc) : acc;
     y[t * ldy + n] = f32_to_bf16(acc);
 }
 
