@@ -1,9 +1,12 @@
 """Pins of the oracle's MXFP4 top-k expert GEMV.
 
-References: a plain dense MXFP4 GEMV written with numpy over the OCP E2M1
-value table (one expert, weight 1), the weighted sum over experts done with
-numpy per expert, slot-order invariance, linearity in the routing weights,
-and the rule that out-of-range expert ids contribute nothing."""
+References: exact rational arithmetic on tiny inputs, a plain dense MXFP4
+GEMV written with numpy over the OCP E2M1 value table (one expert, weight 1),
+the weighted sum over experts done with numpy per expert, slot-order
+invariance, linearity in the routing weights, and the rule that out-of-range
+expert ids contribute nothing."""
+from fractions import Fraction
+
 import numpy as np
 
 from skinny_gemm_qlin_amd.inputs import bf16_values, gen_moe
@@ -19,6 +22,40 @@ def _dense_expert(w_e, s_e):
     vals[:, 0::2] = OCP_E2M1[w_e & 0xF]
     vals[:, 1::2] = OCP_E2M1[w_e >> 4]
     return vals * np.repeat(2.0 ** (s_e.astype(np.float64) - 127), 32, axis=1)
+
+
+def test_moe_exact_rational_tiny(orc):
+    # every product and sum in Fraction: y_exact, S and the rounded output
+    rng = np.random.default_rng(33)
+    for (M, E, N, K, topk) in [(1, 3, 2, 32, 2), (3, 4, 3, 64, 3), (2, 5, 2, 96, 1)]:
+        d = gen_moe(M, E, N, K, topk, seed=int(rng.integers(1 << 30)))
+        ids = d["ids"].copy()
+        ids[0, -1] = E  # one out-of-range id: contributes nothing
+        y, ye, S = orc.moe_mxfp4(d["x"], d["w"], d["s"], ids, d["gw"])
+        xf = bf16_values(d["x"])
+        for t in range(M):
+            for n in range(N):
+                ex = Fraction(0)
+                sa = Fraction(0)
+                for j in range(topk):
+                    e = int(ids[t, j])
+                    if not 0 <= e < E:
+                        continue
+                    g = Fraction(float(d["gw"][t, j]))
+                    dot = Fraction(0)
+                    adot = Fraction(0)
+                    for k in range(K):
+                        byte = int(d["w"][e, n, k // 2])
+                        code = byte & 0xF if k % 2 == 0 else byte >> 4
+                        wv = Fraction(float(OCP_E2M1[code])) * Fraction(2) ** (int(d["s"][e, n, k // 32]) - 127)
+                        p = wv * Fraction(float(xf[t, k]))
+                        dot += p
+                        adot += abs(p)
+                    ex += g * dot
+                    sa += abs(g) * adot
+                assert abs(Fraction(ye[t, n]) - ex) <= sa * Fraction(1, 2**44) + Fraction(1, 2**200)
+                assert abs(Fraction(S[t, n]) - sa) <= sa * Fraction(1, 2**44) + Fraction(1, 2**200)
+                assert y[t, n] == orc.f64_to_bf16(np.array([float(ex)]))[0]
 
 
 def test_single_expert_is_plain_mxfp4_gemv(orc):
