@@ -72,6 +72,14 @@ def _load():
     lib.orc_blk_act_quant.argtypes = [P, I64, I64, I64, P, P]
     lib.orc_gemv_fp8_blk.argtypes = [P, P, I64, I64, P, I64, I64, P, P, I64, P, P]
     lib.orc_moe_mxfp4.argtypes = [P, I64, I64, I64, P, P, I64, I64, P, P, I64, P, I64, P, P]
+    lib.orc_router_logits.argtypes = [P, I64, I64, I64, P, I64, P]
+    lib.orc_topk.argtypes = [P, I64, I64, I64, P]
+    lib.orc_topk_softmax.argtypes = [P, I64, I64, P, I64, P]
+    lib.orc_swiglu.argtypes = [ctypes.c_double] * 4
+    lib.orc_swiglu.restype = ctypes.c_double
+    lib.orc_swiglu_n.argtypes = [P, P, I64, ctypes.c_double, ctypes.c_double, P]
+    D = ctypes.c_double
+    lib.orc_moe_ffn_mxfp4.argtypes = [P, I64, I64, I64, P, P, P, P, I64, I64, P, P, I64, D, D, P, P, I64, P, P]
     _lib = lib
     return lib
 
@@ -253,3 +261,89 @@ def moe_mxfp4(x_bf16, w_fp4, s_ue8m0, topk_ids, topk_w):
     S = np.zeros((M, N), dtype=np.float64)
     _load().orc_moe_mxfp4(_p(x), K, M, K, _p(w), _p(s), E, N, _p(ids), _p(gw), topk, _p(y), N, _p(ye), _p(S))
     return y, ye, S
+
+
+# --------------------------------------------------------------------------- MoE expert FFN
+
+SWIGLU_ALPHA = 1.0   # [DSV4] sections 6.6 (J09) and 9.4
+SWIGLU_LIMIT = 10.0
+
+
+def router_logits(x_bf16, wr_bf16):
+    """logit[m, e] = sum_k x[m, k] * wr[e, k] in fp64 (bf16 inputs); router read as a plain bf16 linear."""
+    x = _c(x_bf16, np.uint16)
+    wr = _c(wr_bf16, np.uint16)
+    M, H = x.shape
+    E = wr.shape[0]
+    assert wr.shape == (E, H)
+    out = np.zeros((M, E), dtype=np.float64)
+    _load().orc_router_logits(_p(x), H, M, H, _p(wr), E, _p(out))
+    return out
+
+
+def topk(logits, k):
+    """The k largest logits per token, largest first; equal logits -> lower expert id."""
+    lg = _c(logits, np.float64)
+    M, E = lg.shape
+    ids = np.zeros((M, k), dtype=np.int32)
+    _load().orc_topk(_p(lg), M, E, k, _p(ids))
+    return ids
+
+
+def topk_softmax(logits, ids):
+    """Softmax over each token's selected logits (fp64)."""
+    lg = _c(logits, np.float64)
+    ids = _c(ids, np.int32)
+    M, E = lg.shape
+    k = ids.shape[1]
+    g = np.zeros((M, k), dtype=np.float64)
+    _load().orc_topk_softmax(_p(lg), M, E, _p(ids), k, _p(g))
+    return g
+
+
+def swiglu(gate, up, alpha=SWIGLU_ALPHA, limit=SWIGLU_LIMIT):
+    """silu(alpha * min(gate, limit)) * clamp(up, -limit, limit) elementwise, fp64."""
+    gt = _c(np.asarray(gate, dtype=np.float64), np.float64)
+    u = _c(np.asarray(up, dtype=np.float64), np.float64)
+    assert gt.shape == u.shape
+    out = np.zeros(gt.shape, dtype=np.float64)
+    _load().orc_swiglu_n(_p(gt), _p(u), gt.size, float(alpha), float(limit), _p(out))
+    return out
+
+
+def moe_ffn_mxfp4(x_bf16, w13, s13, w2, s2, ids, g, alpha=SWIGLU_ALPHA, limit=SWIGLU_LIMIT):
+    """Routed MXFP4 expert FFN for a given routing ([DSV4] sections 9.3, 6.6, 9.4).
+
+    w13 uint8 [E, 2I, H/2] (gate rows then up rows), s13 uint8 [E, 2I, H/32],
+    w2 uint8 [E, H, I/2], s2 uint8 [E, H, I/32]; ids int32 [M, k]; g float64 [M, k].
+    Returns (act uint16 [M*k, I], y uint16 [M, H], y_exact float64, S float64)."""
+    x = _c(x_bf16, np.uint16)
+    w13 = _c(w13, np.uint8)
+    s13 = _c(s13, np.uint8)
+    w2 = _c(w2, np.uint8)
+    s2 = _c(s2, np.uint8)
+    ids = _c(ids, np.int32)
+    g = _c(np.asarray(g, dtype=np.float64), np.float64)
+    M, H = x.shape
+    E, I2, Hh = w13.shape
+    I = I2 // 2
+    assert Hh * 2 == H and s13.shape == (E, 2 * I, H // 32)
+    assert w2.shape == (E, H, I // 2) and s2.shape == (E, H, I // 32)
+    k = ids.shape[1]
+    act = np.zeros((M * k, I), dtype=np.uint16)
+    y = np.zeros((M, H), dtype=np.uint16)
+    ye = np.zeros((M, H), dtype=np.float64)
+    S = np.zeros((M, H), dtype=np.float64)
+    _load().orc_moe_ffn_mxfp4(_p(x), H, M, H, _p(w13), _p(s13), _p(w2), _p(s2), E, I, _p(ids), _p(g), k,
+                              float(alpha), float(limit), _p(act), _p(y), H, _p(ye), _p(S))
+    return act, y, ye, S
+
+
+def moe_ffn_route_mxfp4(x_bf16, wr_bf16, k, w13, s13, w2, s2, alpha=SWIGLU_ALPHA, limit=SWIGLU_LIMIT):
+    """Whole routed FFN: router logits -> top-k -> softmax -> expert FFN.
+    Returns (ids, g, logits, act, y, y_exact, S)."""
+    lg = router_logits(x_bf16, wr_bf16)
+    ids = topk(lg, k)
+    g = topk_softmax(lg, ids)
+    act, y, ye, S = moe_ffn_mxfp4(x_bf16, w13, s13, w2, s2, ids, g, alpha, limit)
+    return ids, g, lg, act, y, ye, S

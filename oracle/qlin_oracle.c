@@ -362,6 +362,136 @@ void orc_moe_mxfp4(const uint16_t* x, int64_t ldx, int64_t M, int64_t K,
 }
 
 /* ------------------------------------------------------------------------ */
+/* MoE expert FFN with on-device routing: router logits -> top-k -> softmax  */
+/* over the selected logits -> per routed pair gate/up MXFP4 GEMVs ->        */
+/* clamped SwiGLU -> down MXFP4 GEMV -> weighted sum [DSV4 section 9.3 (the  */
+/* MXFP4 expert path), sections 6.6 (J09) and 9.4 (SwiGLU with alpha 1.0,    */
+/* limit 10.0)].                                                              */
+/* ------------------------------------------------------------------------ */
+
+/* logit[m][e] = sum_k x[m][k] * wr[e][k], bf16 inputs, fp64 sum.
+ * READING: the router is a plain bf16 linear layer without bias; the pages
+ * name the routing fast path but not its scoring function. */
+void orc_router_logits(const uint16_t* x, int64_t ldx, int64_t M, int64_t H,
+                       const uint16_t* wr, int64_t E, double* logits) {
+    int64_t e;
+#pragma omp parallel for schedule(static)
+    for (e = 0; e < E; ++e) {
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < H; ++k)
+                acc += (double)orc_bf16_to_f32(x[m * ldx + k]) * (double)orc_bf16_to_f32(wr[e * H + k]);
+            logits[m * E + e] = acc;
+        }
+    }
+}
+
+/* The k largest logits of each token, largest first.
+ * READING: equal logits go to the lower expert id (the first one met). */
+void orc_topk(const double* logits, int64_t M, int64_t E, int64_t k, int32_t* ids) {
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t j = 0; j < k; ++j) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < E; ++e) {
+                int taken = 0;
+                for (int64_t q = 0; q < j; ++q) taken |= ids[m * k + q] == e;
+                if (taken) continue;
+                if (best < 0 || logits[m * E + e] > logits[m * E + best]) best = e;
+            }
+            ids[m * k + j] = (int32_t)best;
+        }
+    }
+}
+
+/* Routing weights: softmax over the selected experts' logits.
+ * READING: renormalised over the top-k (as the routing weights of the
+ * expert GEMV are). */
+void orc_topk_softmax(const double* logits, int64_t M, int64_t E, const int32_t* ids, int64_t k,
+                      double* g) {
+    for (int64_t m = 0; m < M; ++m) {
+        double mx = -INFINITY, den = 0.0;
+        for (int64_t j = 0; j < k; ++j) mx = fmax(mx, logits[m * E + ids[m * k + j]]);
+        for (int64_t j = 0; j < k; ++j) den += exp(logits[m * E + ids[m * k + j]] - mx);
+        for (int64_t j = 0; j < k; ++j) g[m * k + j] = exp(logits[m * E + ids[m * k + j]] - mx) / den;
+    }
+}
+
+/* silu(alpha * min(gate, limit)) * clamp(up, -limit, limit), silu(z) = z / (1 + e^-z). */
+double orc_swiglu(double gate, double up, double alpha, double limit) {
+    const double gc = gate > limit ? limit : gate;
+    const double uc = up > limit ? limit : (up < -limit ? -limit : up);
+    const double z = alpha * gc;
+    return z / (1.0 + exp(-z)) * uc;
+}
+
+void orc_swiglu_n(const double* gate, const double* up, int64_t n, double alpha, double limit, double* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_swiglu(gate[i], up[i], alpha, limit);
+}
+
+/* One MXFP4 row (E2M1 codes, element 2i in the low nibble of byte i, one
+ * UE8M0 scale per 32) dotted with a bf16 vector of length K, fp64. */
+static double orc_mxfp4_row_dot(const uint8_t* wrow, const uint8_t* srow, const uint16_t* v, int64_t K,
+                                double* abs_sum) {
+    double dot = 0.0, dabs = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        uint8_t byte = wrow[k / 2];
+        uint8_t nib = (k % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+        double p = orc_e2m1_decode(nib) * orc_ue8m0_decode(srow[k / 32]) * (double)orc_bf16_to_f32(v[k]);
+        dot += p;
+        dabs += fabs(p);
+    }
+    if (abs_sum) *abs_sum = dabs;
+    return dot;
+}
+
+/* Expert FFN for a given routing (ids [M][k], weights g [M][k]):
+ *   gate = W13[e] rows 0..I-1 . x[t],  up = W13[e] rows I..2I-1 . x[t]
+ *   act[p][i] = bf16(swiglu(gate_i, up_i))        (p = t*k + j)
+ *   out[p][h] = W2[e] row h . act[p]
+ *   y[t][h]   = bf16(sum_j g[t][j] * out[p][h]),  S = sum_j |g| sum_i |w2 * act|
+ * w13 [E][2I][H/2], s13 [E][2I][H/32], w2 [E][H][I/2], s2 [E][H][I/32].
+ * READING: gate and up are fp32-or-better sums and the activation is rounded
+ * once to bf16, the input type of the down projection. */
+void orc_moe_ffn_mxfp4(const uint16_t* x, int64_t ldx, int64_t M, int64_t H,
+                       const uint8_t* w13, const uint8_t* s13, const uint8_t* w2, const uint8_t* s2,
+                       int64_t E, int64_t I, const int32_t* ids, const double* g, int64_t k,
+                       double alpha, double limit, uint16_t* act,
+                       uint16_t* y, int64_t ldy, double* y_exact, double* S) {
+    const int64_t P = M * k;
+    int64_t pi;
+#pragma omp parallel for schedule(static)
+    for (pi = 0; pi < P * I; ++pi) {
+        const int64_t p = pi / I, i = pi % I, t = p / k;
+        const int64_t e = ids[p];
+        if (e < 0 || e >= E) { act[p * I + i] = 0; continue; }
+        const double gate = orc_mxfp4_row_dot(w13 + (e * 2 * I + i) * (H / 2), s13 + (e * 2 * I + i) * (H / 32),
+                                              x + t * ldx, H, NULL);
+        const double up = orc_mxfp4_row_dot(w13 + (e * 2 * I + I + i) * (H / 2),
+                                            s13 + (e * 2 * I + I + i) * (H / 32), x + t * ldx, H, NULL);
+        act[p * I + i] = orc_f64_to_bf16(orc_swiglu(gate, up, alpha, limit));
+    }
+    int64_t h;
+#pragma omp parallel for schedule(static)
+    for (h = 0; h < H; ++h) {
+        for (int64_t t = 0; t < M; ++t) {
+            double tot = 0.0, sabs = 0.0;
+            for (int64_t j = 0; j < k; ++j) {
+                const int64_t p = t * k + j, e = ids[p];
+                if (e < 0 || e >= E) continue;
+                double dabs;
+                const double dot = orc_mxfp4_row_dot(w2 + (e * H + h) * (I / 2), s2 + (e * H + h) * (I / 32),
+                                                     act + p * I, I, &dabs);
+                tot += g[p] * dot;
+                sabs += fabs(g[p]) * dabs;
+            }
+            y[t * ldy + h] = orc_f64_to_bf16(tot);
+            if (y_exact) y_exact[t * H + h] = tot;
+            if (S) S[t * H + h] = sabs;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Array forms of the format helpers (loops over the scalar routines).      */
 /* ------------------------------------------------------------------------ */
 

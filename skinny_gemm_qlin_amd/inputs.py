@@ -94,6 +94,22 @@ def gen_moe(M: int, E: int, N: int, K: int, topk: int, seed: int = 0,
     return {"x": x, "w": w, "s": s, "ids": ids, "gw": gw}
 
 
+def gen_moe_ffn(M: int, E: int, H: int, I: int, topk: int, seed: int = 0,
+                s13_lo: int = 116, s13_hi: int = 122, s2_lo: int = 118, s2_hi: int = 124) -> dict:
+    """Routed MXFP4 expert FFN inputs.  Draw order: router weights, gate/up
+    codes and scales, down codes and scales, x.  Router weights are bf16
+    N(0, 1/H) so the logits are about N(0, 1); the gate/up scale range puts a
+    few gate/up values past the SwiGLU limit of 10."""
+    rng = np.random.default_rng(seed)
+    wr = bf16_bits((rng.standard_normal((E, H), dtype=np.float32) / np.float32(np.sqrt(H))).astype(np.float32))
+    w13 = rng.integers(0, 256, size=(E, 2 * I, H // 2), dtype=np.uint8)
+    s13 = rng.integers(s13_lo, s13_hi + 1, size=(E, 2 * I, H // 32)).astype(np.uint8)
+    w2 = rng.integers(0, 256, size=(E, H, I // 2), dtype=np.uint8)
+    s2 = rng.integers(s2_lo, s2_hi + 1, size=(E, H, I // 32)).astype(np.uint8)
+    x = bf16_bits(rng.standard_normal((M, H), dtype=np.float32))
+    return {"x": x, "wr": wr, "w13": w13, "s13": s13, "w2": w2, "s2": s2, "topk": topk}
+
+
 # Named workloads (shapes fixed by the published decode configurations).
 WORKLOADS = {
     "int8_small": {"kind": "int8", "N": 1024, "K": 1024, "Ms": [1]},
@@ -101,4 +117,5 @@ WORKLOADS = {
     "fp8_decode": {"kind": "fp8", "N": 17408, "K": 5120, "Ms": [1, 4, 8]},
     "fp8_blk": {"kind": "fp8_blk", "N": 4096, "K": 7168, "Ms": [1, 8, 16]},
     "moe_mxfp4": {"kind": "moe", "E": 64, "N": 2048, "K": 7168, "Ms": [8], "topk": 6},
+    "moe_ffn_mxfp4": {"kind": "moe_ffn", "E": 64, "H": 7168, "I": 2048, "Ms": [8], "topk": 6},
 }
