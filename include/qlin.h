@@ -173,6 +173,54 @@ int qlin_moe_mxfp4(const void* x, int64_t ldx, int64_t M, int64_t K,
                    void* y, int64_t ldy,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * (e) Routed MXFP4 expert FFN with on-device routing -- [DSV4] 9.3 (MXFP4
+ *     expert path), 6.6 (J09) and 9.4 (SwiGLU: alpha 1.0, limit 10.0),
+ *     0.1/0.2 (the routing fast path stays on the device)
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of device workspace qlin_moe_ffn_mxfp4 needs for these sizes: the
+ * router logits fp32 [M][E], then the SwiGLU activations bf16 [M*topk][I],
+ * then the down-projection partials fp32 [M*topk][H], each region starting
+ * on a 256-byte boundary (in that order, from the workspace base). */
+size_t qlin_moe_ffn_mxfp4_workspace_bytes(int64_t M, int64_t H, int64_t I, int64_t topk, int64_t E);
+
+/* For every token t (x row, H = hidden size):
+ *   logit[t,e] = sum_k x[t,k] * wr[e,k]            (bf16 router, fp32 sum)
+ *   ids[t,:]   = the topk largest logits, largest first; equal logits go to
+ *                the lower expert id; a NaN logit is never selected
+ *   g[t,j]     = exp(logit[t,ids[t,j]] - logit[t,ids[t,0]]) / sum over the
+ *                topk selected (softmax over the selected logits)
+ *   for each slot j, e = ids[t,j], i < I:
+ *     gate_i = w13[e, i, :] . x[t],  up_i = w13[e, I+i, :] . x[t]   (MXFP4)
+ *     act[t*topk+j, i] = bf16( silu(alpha * min(gate_i, limit))
+ *                              * clamp(up_i, -limit, limit) ),  silu(z) = z/(1+e^-z)
+ *   y[t,h] = bf16( sum_j g[t,j] * (w2[e, h, :] . act[t*topk+j]) )   (slot order)
+ * MXFP4 rows are E2M1 codes (element 2i in the LOW nibble of byte i) with
+ * one UE8M0 scale per 32 elements; every dot accumulates in fp32.  Five
+ * kernels on `stream`, no host synchronisation.
+ *   x        bf16 [M, ldx]
+ *   wr       bf16 [E, H] (row-major)
+ *   w13      uint8 [E, 2I, H/2]: gate rows 0..I-1, then up rows I..2I-1
+ *   s13      uint8 [E, 2I, H/32]
+ *   w2       uint8 [E, H, I/2];  s2 uint8 [E, H, I/32]
+ *   topk_ids int32 [M, topk] (output);  topk_w fp32 [M, topk] (output)
+ *   y        bf16 [M, ldy]
+ *   workspace device buffer of at least qlin_moe_ffn_mxfp4_workspace_bytes(),
+ *            16-byte aligned; contents on entry do not matter, on return it
+ *            holds the logits and activations described there.
+ * Requires 1 <= M <= 16, 1 <= E <= 1024, 1 <= topk <= min(16, E),
+ * H and I multiples of 32 in [32, 30720], ldx >= H with ldx % 8 == 0,
+ * ldy >= H. */
+int qlin_moe_ffn_mxfp4(const void* x, int64_t ldx, int64_t M, int64_t H,
+                       const void* wr, int64_t E, int64_t topk,
+                       const uint8_t* w13, const uint8_t* s13, int64_t I,
+                       const uint8_t* w2, const uint8_t* s2,
+                       float alpha, float limit,
+                       int32_t* topk_ids, float* topk_w,
+                       void* y, int64_t ldy,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -163,3 +163,55 @@ def qlin_moe_mxfp4(x, w, s, topk_ids, topk_w, y=None, workspace=None, stream=Non
                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                 _stream(x, stream)), "qlin_moe_mxfp4")
     return y
+
+
+def qlin_moe_ffn_mxfp4_workspace_bytes(M: int, H: int, I: int, topk: int, E: int) -> int:
+    return int(load().qlin_moe_ffn_mxfp4_workspace_bytes(M, H, I, topk, E))
+
+
+def _round256(b: int) -> int:
+    return (b + 255) // 256 * 256
+
+
+def qlin_moe_ffn_mxfp4(x, wr, w13, s13, w2, s2, topk, alpha=1.0, limit=10.0, y=None, workspace=None,
+                       stream=None, return_internals=False):
+    """Routed MXFP4 expert FFN with on-device routing.  x bf16 [M, H]; wr bf16
+    [E, H]; w13 uint8 [E, 2I, H/2] (gate rows then up rows); s13 [E, 2I, H/32];
+    w2 uint8 [E, H, I/2]; s2 [E, H, I/32].  Returns (y bf16 [M, H], topk_ids
+    int32 [M, topk], topk_w fp32 [M, topk]); with return_internals also the
+    router logits fp32 [M, E] and the activations bf16 [M*topk, I] read back
+    from the workspace (valid once the stream has run the call)."""
+    _need(x, "x", (torch.bfloat16,), 2)
+    _need(wr, "wr", (torch.bfloat16,), 2)
+    for name, t in (("w13", w13), ("s13", s13), ("w2", w2), ("s2", s2)):
+        _need(t, name, (torch.uint8,), 3)
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not wr.is_contiguous():
+        raise ValueError("wr must be contiguous")
+    M, H = x.shape
+    E = wr.shape[0]
+    I = w13.shape[1] // 2
+    if (tuple(wr.shape) != (E, H) or tuple(w13.shape) != (E, 2 * I, H // 2) or tuple(s13.shape) != (E, 2 * I, H // 32)
+            or tuple(w2.shape) != (E, H, I // 2) or tuple(s2.shape) != (E, H, I // 32)):
+        raise ValueError("router / expert tensor shapes do not match x")
+    need = qlin_moe_ffn_mxfp4_workspace_bytes(M, H, I, topk, E)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    if y is None:
+        y = torch.empty((M, H), dtype=torch.bfloat16, device=x.device)
+    _need(y, "y", (torch.bfloat16,), 2)
+    ids = torch.empty((M, topk), dtype=torch.int32, device=x.device)
+    gw = torch.empty((M, topk), dtype=torch.float32, device=x.device)
+    check(load().qlin_moe_ffn_mxfp4(x.data_ptr(), x.stride(0), M, H, wr.data_ptr(), E, topk,
+                                    w13.data_ptr(), s13.data_ptr(), I, w2.data_ptr(), s2.data_ptr(),
+                                    float(alpha), float(limit), ids.data_ptr(), gw.data_ptr(),
+                                    y.data_ptr(), y.stride(0), workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(), _stream(x, stream)),
+          "qlin_moe_ffn_mxfp4")
+    if not return_internals:
+        return y, ids, gw
+    o_act = _round256(M * E * 4)
+    logits = workspace[:M * E * 4].view(torch.float32).view(M, E)
+    act = workspace[o_act:o_act + M * topk * I * 2].view(torch.bfloat16).view(M * topk, I)
+    return y, ids, gw, logits, act

@@ -24,6 +24,7 @@ QLIN_ERR_LAUNCH = -7
 EXPORTS = (
     "qlin_status_str", "qlin_version", "qlin_act_quant_i8", "qlin_gemv_i8", "qlin_gemv_fp8",
     "qlin_gemv_fp8_blk", "qlin_moe_mxfp4_workspace_bytes", "qlin_moe_mxfp4",
+    "qlin_moe_ffn_mxfp4_workspace_bytes", "qlin_moe_ffn_mxfp4",
 )
 
 
@@ -60,6 +61,12 @@ def load() -> ctypes.CDLL:
     lib.qlin_moe_mxfp4_workspace_bytes.restype = SZ
     lib.qlin_moe_mxfp4.argtypes = [P, I64, I64, I64, P, P, I64, I64, P, P, I64, P, I64, P, SZ, P]
     lib.qlin_moe_mxfp4.restype = I
+    lib.qlin_moe_ffn_mxfp4_workspace_bytes.argtypes = [I64, I64, I64, I64, I64]
+    lib.qlin_moe_ffn_mxfp4_workspace_bytes.restype = SZ
+    F = ctypes.c_float
+    lib.qlin_moe_ffn_mxfp4.argtypes = [P, I64, I64, I64, P, I64, I64, P, P, I64, P, P, F, F, P, P, P, I64,
+                                       P, SZ, P]
+    lib.qlin_moe_ffn_mxfp4.restype = I
     _lib = lib
     return lib
 

@@ -124,4 +124,40 @@ int qlin_moe_mxfp4(const void* x, int64_t ldx, int64_t M, int64_t K,
     return launch_status(qlin::launch_moe_mxfp4(a, (hipStream_t)stream));
 }
 
+static size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+size_t qlin_moe_ffn_mxfp4_workspace_bytes(int64_t M, int64_t H, int64_t I, int64_t topk, int64_t E) {
+    if (M < 1 || H < 1 || I < 1 || topk < 1 || E < 1) return 0;
+    return round256((size_t)M * E * sizeof(float)) + round256((size_t)M * topk * I * sizeof(uint16_t)) +
+           round256((size_t)M * topk * H * sizeof(float));
+}
+
+int qlin_moe_ffn_mxfp4(const void* x, int64_t ldx, int64_t M, int64_t H,
+                       const void* wr, int64_t E, int64_t topk,
+                       const uint8_t* w13, const uint8_t* s13, int64_t I,
+                       const uint8_t* w2, const uint8_t* s2,
+                       float alpha, float limit,
+                       int32_t* topk_ids, float* topk_w,
+                       void* y, int64_t ldy,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    if (!x || !wr || !w13 || !s13 || !w2 || !s2 || !topk_ids || !topk_w || !y) return QLIN_ERR_NULL;
+    if (M < 1 || M > QLIN_MAX_M || E < 1 || E > 1024 || topk < 1 || topk > 16 || topk > E)
+        return QLIN_ERR_SHAPE;
+    if (H < 32 || H % 32 != 0 || H > 30720 || I < 32 || I % 32 != 0 || I > 30720) return QLIN_ERR_SHAPE;
+    if (ldx < H || ldy < H) return QLIN_ERR_STRIDE;
+    if (misaligned(x, 16) || ldx % 8 != 0 || misaligned(wr, 16) || misaligned(w13, 16) ||
+        misaligned(w2, 16) || misaligned(topk_ids, 4) || misaligned(topk_w, 4) || misaligned(y, 2))
+        return QLIN_ERR_ALIGN;
+    if (!workspace || workspace_bytes < qlin_moe_ffn_mxfp4_workspace_bytes(M, H, I, topk, E))
+        return QLIN_ERR_WORKSPACE;
+    if (misaligned(workspace, 16)) return QLIN_ERR_ALIGN;
+    char* ws = (char*)workspace;
+    float* logits = (float*)ws;
+    uint16_t* act = (uint16_t*)(ws + round256((size_t)M * E * sizeof(float)));
+    float* part = (float*)((char*)act + round256((size_t)M * topk * I * sizeof(uint16_t)));
+    qlin::MoeFfnArgs a{(const uint16_t*)x, ldx, M, H, (const uint16_t*)wr, E, topk, w13, s13, I, w2, s2,
+                       alpha, limit, topk_ids, topk_w, (uint16_t*)y, ldy, logits, act, part};
+    return launch_status(qlin::launch_moe_ffn_mxfp4(a, (hipStream_t)stream));
+}
+
 }  // extern "C"

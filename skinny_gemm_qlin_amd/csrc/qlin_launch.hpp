@@ -48,4 +48,20 @@ hipError_t launch_blk_act_quant(const BlkQuantArgs& a, hipStream_t st);
 hipError_t launch_gemv_fp8_blk(const BlkArgs& a, hipStream_t st);
 hipError_t launch_moe_mxfp4(const MoeArgs& a, hipStream_t st);
 
+struct MoeFfnArgs {
+    const uint16_t* x; int64_t ldx; int64_t M; int64_t H;
+    const uint16_t* wr; int64_t E; int64_t topk;
+    const uint8_t* w13; const uint8_t* s13; int64_t I;
+    const uint8_t* w2; const uint8_t* s2;
+    float alpha; float limit;
+    int32_t* ids; float* gw; uint16_t* y; int64_t ldy;
+    float* logits; uint16_t* act; float* part;  // workspace regions
+};
+
+hipError_t launch_router(const uint16_t* x, int64_t ldx, int64_t M, int64_t H, const uint16_t* wr, int64_t E,
+                         float* logits, hipStream_t st);
+hipError_t launch_topk_softmax(const float* logits, int64_t M, int64_t E, int64_t topk, int32_t* ids, float* gw,
+                               hipStream_t st);
+hipError_t launch_moe_ffn_mxfp4(const MoeFfnArgs& a, hipStream_t st);
+
 }  // namespace qlin

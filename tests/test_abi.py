@@ -140,3 +140,31 @@ def test_moe_errors(q):
     assert call(wsb=need - 1) == -5
     assert call(ws=A + 4) == -4
     assert call(w=A + 8) == -4
+
+
+def test_moe_ffn_errors(q):
+    need = q.qlin_moe_ffn_mxfp4_workspace_bytes(8, 7168, 2048, 6, 64)
+    assert need == 8 * 64 * 4 + 8 * 6 * 2048 * 2 + 8 * 6 * 7168 * 4  # every region a multiple of 256 here
+    assert q.qlin_moe_ffn_mxfp4_workspace_bytes(1, 32, 32, 1, 1) == 256 + 256 + 256
+    assert q.qlin_moe_ffn_mxfp4_workspace_bytes(0, 32, 32, 1, 1) == 0
+
+    def call(x=A, ldx=7168, M=8, H=7168, wr=A, E=64, topk=6, w13=A, s13=A, I=2048, w2=A, s2=A,
+             alpha=1.0, limit=10.0, ids=A, gw=A, y=A, ldy=7168, ws=A, wsb=need):
+        return q.qlin_moe_ffn_mxfp4(x, ldx, M, H, wr, E, topk, w13, s13, I, w2, s2, alpha, limit, ids, gw,
+                                    y, ldy, ws, wsb, None)
+    assert call(wr=None) == -1
+    assert call(s2=None) == -1
+    assert call(ids=None) == -1
+    assert call(M=0) == -2
+    assert call(M=17) == -2
+    assert call(E=1025) == -2
+    assert call(topk=17) == -2
+    assert call(E=4, topk=5) == -2           # more slots than experts
+    assert call(H=7168 + 16, ldx=7184, ldy=7184) == -2
+    assert call(I=30720 + 32) == -2
+    assert call(ldx=7000) == -3
+    assert call(ldy=100) == -3
+    assert call(x=A + 8) == -4
+    assert call(wr=A + 2) == -4
+    assert call(ws=None) == -5
+    assert call(wsb=need - 1) == -5

@@ -1,0 +1,136 @@
+"""GPU parity of the routed MXFP4 expert FFN (qlin_moe_ffn_mxfp4) against the
+CPU oracle.
+
+The device takes three decisions in fp32 that the exact oracle would take in
+fp64: which experts a token selects, the routing weights, and the bf16
+rounding of each SwiGLU activation.  The test therefore checks what is
+unique and that the rest is valid:
+  1. router logits: within the fp32 accumulation bound of the exact ones;
+  2. selected experts: a valid top-k of the exact logits (distinct, largest
+     first, every unselected logit below every selected one) up to the
+     measured logit error -- near-ties may go either way;
+  3. routing weights: the softmax of the exact logits of the selected
+     experts, to within what the measured logit error can move it;
+  4. activations: the exact clamped SwiGLU of the exact gate/up sums (the
+     oracle's expert GEMV of each routed pair), to within the fp32 error of
+     those sums propagated through the SwiGLU plus one bf16 rounding;
+  5. output: the float comparison rule against the exact down projection of
+     the device's own activations, weighted by the exact routing weights."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import dev, dev_bf16, host, host_bits, lib, need_gpu
+from parity import bf16_to_f64, bf16_ulp, check_float
+from skinny_gemm_qlin_amd.inputs import bf16_values, gen_moe_ffn
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ql():
+    need_gpu()
+    return lib()
+
+
+def _run(ql, d, alpha=1.0, limit=10.0):
+    y, ids, gw, logits, act = ql.qlin_moe_ffn_mxfp4(
+        dev_bf16(d["x"]), dev_bf16(d["wr"]), dev(d["w13"]), dev(d["s13"]), dev(d["w2"]), dev(d["s2"]),
+        d["topk"], alpha, limit, return_internals=True)
+    torch.cuda.synchronize()
+    return host_bits(y), host(ids), host(gw), host(logits).astype(np.float64), host_bits(act)
+
+
+def _check(orc, d, got, alpha=1.0, limit=10.0):
+    y, ids, gw, lg, act = got
+    k = d["topk"]
+    x = d["x"]
+    M, H = x.shape
+    E = d["wr"].shape[0]
+    I = d["w13"].shape[1] // 2
+    one = np.ones((1, 1), np.float32)
+
+    # 1. router logits
+    L = orc.router_logits(x, d["wr"])
+    SL = np.abs(bf16_values(x).astype(np.float64)) @ np.abs(bf16_values(d["wr"]).astype(np.float64)).T
+    assert np.all(np.abs(lg - L) <= (H / 8 + 32) * 2.0 ** -24 * SL + 1e-30), "router logits"
+
+    # 2. selected experts: a valid top-k of the exact logits
+    for t in range(M):
+        sel = ids[t].astype(np.int64)
+        assert len(set(sel.tolist())) == k and np.all((sel >= 0) & (sel < E)), f"token {t}: ids {sel}"
+        tie = 2.0 * np.max(np.abs(lg[t] - L[t])) + 1e-30
+        Ls = L[t, sel]
+        assert np.all(np.diff(Ls) <= tie), f"token {t}: not largest first {Ls}"
+        rest = np.setdiff1d(np.arange(E), sel)
+        if rest.size:
+            assert Ls.min() >= L[t, rest].max() - tie, f"token {t}: a larger logit was left out"
+
+    # 3. routing weights
+    g = orc.topk_softmax(L, ids)
+    dl = np.max(np.abs(lg - L), axis=1, keepdims=True)
+    assert np.all(np.abs(gw - g) <= g * (2.0 * dl * 1.01 + 4e-7) + 2e-7), "routing weights"
+
+    # 4. activations, from the exact gate/up sums of every routed pair
+    a_dev = bf16_to_f64(act)
+    for t in range(M):
+        for j in range(k):
+            p, e = t * k + j, int(ids[t, j])
+            _, gu, Sgu = orc.moe_mxfp4(x[t:t + 1], d["w13"], d["s13"], np.array([[e]], np.int32), one)
+            gate, up = gu[0, :I], gu[0, I:]
+            eg = (H / 8 + 32) * 2.0 ** -24 * Sgu[0, :I]
+            eu = (H / 8 + 32) * 2.0 ** -24 * Sgu[0, I:]
+            a_ex = orc.swiglu(gate, up, alpha, limit)
+            silu_g = np.abs(orc.swiglu(gate + eg, np.ones(I), alpha, limit)) + np.abs(orc.swiglu(gate - eg, np.ones(I), alpha, limit))
+            tol = (1.1 * abs(alpha) * np.minimum(np.abs(up) + eu, limit) * eg + silu_g * eu
+                   + bf16_ulp(a_ex) / 2 + 1e-6 * np.abs(a_ex) + 1e-30)
+            bad = np.abs(a_dev[p] - a_ex) > tol
+            assert not bad.any(), (f"pair {p} (token {t}, expert {e}): activation off at "
+                                   f"{np.argwhere(bad)[:5].ravel().tolist()}")
+
+    # 5. output: exact down projection of the device activations, exact weights
+    ye = np.zeros((M, H))
+    S = np.zeros((M, H))
+    for t in range(M):
+        for j in range(k):
+            p, e = t * k + j, int(ids[t, j])
+            _, o, So = orc.moe_mxfp4(act[p:p + 1], d["w2"], d["s2"], np.array([[e]], np.int32), one)
+            ye[t] += g[t, j] * o[0]
+            S[t] += abs(g[t, j]) * So[0]
+    return check_float(y, ye, S, I)
+
+
+@pytest.mark.parametrize("M,E,H,I,topk", [(1, 4, 256, 64, 2), (3, 8, 512, 96, 3), (16, 16, 128, 32, 16),
+                                          (5, 1024, 64, 64, 8), (2, 6, 1024, 160, 1), (7, 9, 96, 224, 4)])
+def test_ffn_shapes(ql, orc, M, E, H, I, topk):
+    d = gen_moe_ffn(M, E, H, I, topk, seed=M * 100 + E)
+    _check(orc, d, _run(ql, d))
+
+
+def test_ffn_full_config(ql, orc):
+    d = gen_moe_ffn(8, 64, 7168, 2048, 6, seed=0)
+    stats = _check(orc, d, _run(ql, d))
+    assert stats["ref_bits_equal"] > 0.99
+
+
+@pytest.mark.parametrize("alpha,limit", [(1.0, 1.0), (0.5, 10.0), (1.702, 3.0)])
+def test_ffn_swiglu_parameters(ql, orc, alpha, limit):
+    # a small limit clamps most gate/up values; alpha scales the gate inside the silu
+    d = gen_moe_ffn(4, 8, 512, 128, 3, seed=7)
+    _check(orc, d, _run(ql, d, alpha, limit), alpha, limit)
+
+
+def test_ffn_two_token_staging_for_long_rows(ql, orc):
+    # H = 16384 stages one token row per pass in the gate/up kernel
+    d = gen_moe_ffn(3, 4, 16384, 64, 2, seed=8)
+    _check(orc, d, _run(ql, d))
+
+
+def test_ffn_deterministic(ql):
+    d = gen_moe_ffn(8, 64, 1024, 256, 6, seed=9)
+    args = [dev_bf16(d["x"]), dev_bf16(d["wr"]), dev(d["w13"]), dev(d["s13"]), dev(d["w2"]), dev(d["s2"]), 6]
+    y0, i0, g0 = ql.qlin_moe_ffn_mxfp4(*args)
+    for _ in range(10):
+        y, i, g = ql.qlin_moe_ffn_mxfp4(*args)
+        assert torch.equal(y.view(torch.int16), y0.view(torch.int16))
+        assert torch.equal(i, i0) and torch.equal(g, g0)
