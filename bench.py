@@ -67,6 +67,12 @@ def bytes_moe_call(M, N, K, topk, live):
     return live * (N * K // 2 + N * K // 32) + 2 * M * K + 2 * M * N + 8 * M * topk
 
 
+def bytes_moe_ffn_call(M, H, I, E, topk, live):
+    # router rows, live experts' gate/up and down codes + scales, x, y, ids + weights
+    return (2 * E * H + live * (2 * I * (H // 2 + H // 32) + H * (I // 2 + I // 32))
+            + 2 * M * H + 2 * M * H + 8 * M * topk)
+
+
 # ----------------------------------------------------------------------------- workloads
 
 def src_hash():
@@ -97,7 +103,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="int8_decode",
-                    choices=["int8_decode", "fp8_decode", "fp8_blk", "moe_mxfp4"])
+                    choices=["int8_decode", "fp8_decode", "fp8_blk", "moe_mxfp4", "moe_ffn_mxfp4"])
     ap.add_argument("--ms", default=None, help="comma list of M values (default: the workload's)")
     ap.add_argument("--rotate", type=int, default=0, help="weight copies (0 = enough to defeat the MALL)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
@@ -131,7 +137,7 @@ def main():
     spec = inputs.WORKLOADS[wl]
     Ms = [int(m) for m in args.ms.split(",")] if args.ms else list(spec["Ms"])
     Mmax = max(Ms)
-    N, K = spec["N"], spec["K"]
+    N, K = spec.get("N", spec.get("H")), spec.get("K", spec.get("H"))  # the FFN maps H -> H
 
     # ---------------------------------------------------------------- inputs (seed 0)
     log(f"bench: generating {wl} inputs N={N} K={K} Ms={Ms}")
@@ -144,15 +150,25 @@ def main():
     elif wl == "fp8_blk":
         d = inputs.gen_fp8_blk(Mmax, N, K, seed=0)
         wbytes = N * K
-    else:
+    elif wl == "moe_mxfp4":
         E, topk = spec["E"], spec["topk"]
         d = inputs.gen_moe(Mmax, E, N, K, topk, seed=0)
         wbytes = E * N * K // 2
+    else:
+        E, topk, I = spec["E"], spec["topk"], spec["I"]
+        d = inputs.gen_moe_ffn(Mmax, E, N, I, topk, seed=0)
+        wbytes = E * 3 * I * N // 2
     B = args.rotate or max(1, -(-2 * MALL_BYTES // wbytes))
     log(f"bench: {B} rotating weight copies ({B * wbytes / 1e6:.0f} MB)")
 
     x = tb(d["x"])
-    if wl == "moe_mxfp4":
+    if wl == "moe_ffn_mxfp4":
+        wr = tb(d["wr"])
+        ffn = [(t(d["w13"]), t(d["s13"]), t(d["w2"]), t(d["s2"]))]
+        for i in range(1, B):
+            ffn.append(tuple(a.clone() for a in ffn[0]))
+        ws_copies = [None] * B
+    elif wl == "moe_mxfp4":
         ws_copies = [t(d["w"])] + [None] * (B - 1)
         s_copies = [t(d["s"])] + [None] * (B - 1)
         for i in range(1, B):
@@ -173,6 +189,17 @@ def main():
         ws_moe = torch.empty((ql.qlin_moe_mxfp4_workspace_bytes(Mmax, N, spec["topk"], spec["E"]),),
                              dtype=torch.uint8, device=dev)
         live = len(np.unique(d["ids"]))
+    if wl == "moe_ffn_mxfp4":
+        ws_ffn = torch.empty((ql.qlin_moe_ffn_mxfp4_workspace_bytes(Mmax, N, spec["I"], spec["topk"], spec["E"]),),
+                             dtype=torch.uint8, device=dev)
+        ids_buf = torch.empty((Mmax, spec["topk"]), dtype=torch.int32, device=dev)
+        gw_buf = torch.empty((Mmax, spec["topk"]), dtype=torch.float32, device=dev)
+        # live experts of the device's own routing (the same for every call)
+        ql.qlin_moe_ffn_mxfp4(x, wr, *ffn[0], spec["topk"], y=torch.empty((Mmax, N), dtype=torch.bfloat16, device=dev),
+                              workspace=ws_ffn, ids=ids_buf, gw=gw_buf)
+        torch.cuda.synchronize()
+        live_of = {M: len(np.unique(ids_buf[:M].cpu().numpy())) for M in Ms}
+        live = live_of[Mmax]
 
     def launches(M, ci):
         """[(kernel, bytes, fn)] for one call of the workload's entry point."""
@@ -188,11 +215,16 @@ def main():
         if wl == "fp8_blk":
             return [("act_quant_blk+gemv_fp8_blk", bytes_blk_call(M, N, K),
                      lambda: ql.qlin_gemv_fp8_blk(xm, w, sc, xq=xq_buf[:M], xs=xsb_buf[:M], y=y_buf[:M]))]
-        return [("moe_mxfp4", bytes_moe_call(M, N, K, spec["topk"], live),
-                 lambda: ql.qlin_moe_mxfp4(xm, w, s_copies[ci], ids, gw, y=y_buf[:M], workspace=ws_moe))]
+        if wl == "moe_mxfp4":
+            return [("moe_mxfp4", bytes_moe_call(M, N, K, spec["topk"], live),
+                     lambda: ql.qlin_moe_mxfp4(xm, w, s_copies[ci], ids, gw, y=y_buf[:M], workspace=ws_moe))]
+        return [("moe_ffn_mxfp4", bytes_moe_ffn_call(M, N, spec["I"], spec["E"], spec["topk"], live_of[M]),
+                 lambda: ql.qlin_moe_ffn_mxfp4(xm, wr, *ffn[ci], spec["topk"], y=y_buf[:M], workspace=ws_ffn,
+                                               ids=ids_buf[:M], gw=gw_buf[:M]))]
 
     dominant = {"int8_decode": "gemv_i8", "fp8_decode": "gemv_fp8",
-                "fp8_blk": "act_quant_blk+gemv_fp8_blk", "moe_mxfp4": "moe_mxfp4"}[wl]
+                "fp8_blk": "act_quant_blk+gemv_fp8_blk", "moe_mxfp4": "moe_mxfp4",
+                "moe_ffn_mxfp4": "moe_ffn_mxfp4"}[wl]
 
     def run_step(step):
         for i, M in enumerate(Ms):
@@ -297,7 +329,10 @@ def main():
                 elif wl == "fp8_blk":
                     oracle.fp8_blk(xm, d["w"], d["ws"])
                 else:
-                    oracle.moe_mxfp4(xm, d["w"], d["s"], d["ids"][:M], d["gw"][:M])
+                    if wl == "moe_mxfp4":
+                        oracle.moe_mxfp4(xm, d["w"], d["s"], d["ids"][:M], d["gw"][:M])
+                    else:
+                        oracle.moe_ffn_route_mxfp4(xm, d["wr"], spec["topk"], d["w13"], d["s13"], d["w2"], d["s2"])
 
         times = []
         t_begin = time.perf_counter()
@@ -315,8 +350,10 @@ def main():
         "fp8_decode": f"E4M3 weight-only GEMV ({'per-tensor' if args.per_tensor else 'per-channel'}) N={N} K={K}",
         "fp8_blk": f"128x128 block-scaled FP8 (act quant + GEMV) N={N} K={K}",
         "moe_mxfp4": f"MXFP4 top-{spec.get('topk')} expert GEMV E={spec.get('E')} N={N} K={K}",
+        "moe_ffn_mxfp4": f"MXFP4 top-{spec.get('topk')} expert FFN with routing E={spec.get('E')} "
+                         f"H={N} I={spec.get('I')} (router, gate/up+SwiGLU, down, combine)",
     }[wl], "N": N, "K": K, "Ms": Ms, "weight_copies": B, "cold_weights": B * wbytes >= 2 * MALL_BYTES}
-    if wl == "moe_mxfp4":
+    if wl in ("moe_mxfp4", "moe_ffn_mxfp4"):
         cfg["live_experts"] = int(live)
 
     out = {
@@ -331,7 +368,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"int8_decode": "int8", "fp8_decode": "fp8e4m3*bf16->f32",
-                  "fp8_blk": "fp8e4m3->f32", "moe_mxfp4": "fp4e2m1*bf16->f32"}[wl],
+                  "fp8_blk": "fp8e4m3->f32", "moe_mxfp4": "fp4e2m1*bf16->f32",
+                  "moe_ffn_mxfp4": "fp4e2m1*bf16->f32"}[wl],
         "data": "synthetic",
         "config": cfg,
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,

@@ -174,7 +174,7 @@ def _round256(b: int) -> int:
 
 
 def qlin_moe_ffn_mxfp4(x, wr, w13, s13, w2, s2, topk, alpha=1.0, limit=10.0, y=None, workspace=None,
-                       stream=None, return_internals=False):
+                       stream=None, return_internals=False, ids=None, gw=None):
     """Routed MXFP4 expert FFN with on-device routing.  x bf16 [M, H]; wr bf16
     [E, H]; w13 uint8 [E, 2I, H/2] (gate rows then up rows); s13 [E, 2I, H/32];
     w2 uint8 [E, H, I/2]; s2 [E, H, I/32].  Returns (y bf16 [M, H], topk_ids
@@ -201,8 +201,14 @@ def qlin_moe_ffn_mxfp4(x, wr, w13, s13, w2, s2, topk, alpha=1.0, limit=10.0, y=N
     if y is None:
         y = torch.empty((M, H), dtype=torch.bfloat16, device=x.device)
     _need(y, "y", (torch.bfloat16,), 2)
-    ids = torch.empty((M, topk), dtype=torch.int32, device=x.device)
-    gw = torch.empty((M, topk), dtype=torch.float32, device=x.device)
+    if ids is None:
+        ids = torch.empty((M, topk), dtype=torch.int32, device=x.device)
+    if gw is None:
+        gw = torch.empty((M, topk), dtype=torch.float32, device=x.device)
+    _need(ids, "ids", (torch.int32,), 2)
+    _need(gw, "gw", (torch.float32,), 2)
+    if tuple(ids.shape) != (M, topk) or tuple(gw.shape) != (M, topk) or not (ids.is_contiguous() and gw.is_contiguous()):
+        raise ValueError("ids / gw must be contiguous [M, topk]")
     check(load().qlin_moe_ffn_mxfp4(x.data_ptr(), x.stride(0), M, H, wr.data_ptr(), E, topk,
                                     w13.data_ptr(), s13.data_ptr(), I, w2.data_ptr(), s2.data_ptr(),
                                     float(alpha), float(limit), ids.data_ptr(), gw.data_ptr(),
