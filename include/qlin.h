@@ -188,7 +188,7 @@ size_t qlin_moe_ffn_mxfp4_workspace_bytes(int64_t M, int64_t H, int64_t I, int64
 /* For every token t (x row, H = hidden size):
  *   logit[t,e] = sum_k x[t,k] * wr[e,k]            (bf16 router, fp32 sum)
  *   ids[t,:]   = the topk largest logits, largest first; equal logits go to
- *                the lower expert id; a NaN logit is never selected
+ *                the lower expert id; a NaN logit ranks as -inf
  *   g[t,j]     = exp(logit[t,ids[t,j]] - logit[t,ids[t,0]]) / sum over the
  *                topk selected (softmax over the selected logits)
  *   for each slot j, e = ids[t,j], i < I:
