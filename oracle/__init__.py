@@ -66,6 +66,10 @@ def _load():
     lib.orc_f32_to_bf16_n.argtypes = [P, I64, P]
     lib.orc_e4m3_decode_n.argtypes = [P, I64, P]
     lib.orc_e4m3_encode_n.argtypes = [P, I64, P]
+    lib.orc_e5m2_decode_n.argtypes = [P, I64, P]
+    lib.orc_e5m2_encode_n.argtypes = [P, I64, P]
+    lib.orc_act_quant_fp8.argtypes = [P, I64, I64, I64, I, I, P, I64, P]
+    lib.orc_gemv_fp8_w8a8.argtypes = [P, I64, P, I, I, I64, I64, P, I64, I64, P, I, I, P, I64, P, P]
     lib.orc_act_quant_i8.argtypes = [P, I64, I64, I64, P, I64, P]
     lib.orc_gemv_i8.argtypes = [P, I64, P, I, I64, I64, P, I64, I64, P, I, P, P, P, I64]
     lib.orc_gemv_fp8.argtypes = [P, I64, I64, I64, P, I64, I64, P, I, P, I64, P, P]
@@ -132,6 +136,14 @@ def e4m3_decode(codes) -> np.ndarray:
 
 def e4m3_encode(values) -> np.ndarray:
     return _map("orc_e4m3_encode_n", values, np.float64, np.uint8)
+
+
+def e5m2_decode(codes) -> np.ndarray:
+    return _map("orc_e5m2_decode_n", codes, np.uint8, np.float64)
+
+
+def e5m2_encode(values) -> np.ndarray:
+    return _map("orc_e5m2_encode_n", values, np.float64, np.uint8)
 
 
 def e2m1_decode(nibbles) -> np.ndarray:
@@ -347,3 +359,38 @@ def moe_ffn_route_mxfp4(x_bf16, wr_bf16, k, w13, s13, w2, s2, alpha=SWIGLU_ALPHA
     g = topk_softmax(lg, ids)
     act, y, ye, S = moe_ffn_mxfp4(x_bf16, w13, s13, w2, s2, ids, g, alpha, limit)
     return ids, g, lg, act, y, ye, S
+
+
+# --------------------------------------------------------------------------- FP8 W8A8
+
+FMT_E4M3 = 0
+FMT_E5M2 = 1
+
+
+def act_quant_fp8(x_bf16, fmt=FMT_E4M3, per_token=True):
+    """Dynamic FP8 activation quantisation ([Z100] FP8 row): s = amax/fmax, q = enc(fl32(x/s)).
+    Returns (xq uint8 [M, K], xs float32 [M] or [1])."""
+    x = _c(x_bf16, np.uint16)
+    M, K = x.shape
+    xq = np.zeros((M, K), dtype=np.uint8)
+    xs = np.zeros((M if per_token else 1,), dtype=np.float32)
+    _load().orc_act_quant_fp8(_p(x), K, M, K, int(fmt), int(bool(per_token)), _p(xq), K, _p(xs))
+    return xq, xs
+
+
+def gemv_fp8_w8a8(xq, xs, x_fmt, w, ws, w_fmt):
+    """y = bf16(xs * ws * sum_k dec(xq) * dec(w)); xs [M] or [1], ws [N] or [1].
+    Returns (y uint16 [M, N], y_exact float64, S float64)."""
+    xq = _c(xq, np.uint8)
+    w = _c(w, np.uint8)
+    xs = _c(np.atleast_1d(xs).astype(np.float32), np.float32)
+    ws = _c(np.atleast_1d(ws).astype(np.float32), np.float32)
+    M, K = xq.shape
+    N = w.shape[0]
+    assert w.shape == (N, K) and xs.size in (1, M) and ws.size in (1, N)
+    y = np.zeros((M, N), dtype=np.uint16)
+    ye = np.zeros((M, N), dtype=np.float64)
+    S = np.zeros((M, N), dtype=np.float64)
+    _load().orc_gemv_fp8_w8a8(_p(xq), K, _p(xs), int(xs.size == M), int(x_fmt), M, K,
+                              _p(w), K, N, _p(ws), int(ws.size == N), int(w_fmt), _p(y), N, _p(ye), _p(S))
+    return y, ye, S

@@ -144,6 +144,40 @@ uint8_t orc_e4m3_encode(double v) {
     return (uint8_t)(sign | best);
 }
 
+/* OCP E5M2: 1 sign, 5 exponent bits (bias 15), 2 mantissa bits; exponent 0
+ * is subnormal (m/4 * 2^-14); exponent 31 holds +-inf (m = 0) and NaN.
+ * Largest finite magnitude 57344 (0x7B). */
+double orc_e5m2_decode(uint8_t c) {
+    int s = (c >> 7) & 1, e = (c >> 2) & 0x1F, m = c & 3;
+    double mag;
+    if (e == 31) mag = (m == 0) ? INFINITY : NAN;
+    else mag = (e == 0) ? ldexp((double)m, -16)             /* m/4 * 2^(1-15) */
+                        : ldexp((double)(4 + m), e - 17);  /* (1+m/4) * 2^(e-15) */
+    return s ? -mag : mag;
+}
+
+/* E5M2 encode: round to the nearest finite code, ties to the even mantissa
+ * (= even code), saturating to +-57344; NaN -> 0x7F.  READING: as for E4M3,
+ * RNE with saturation (the quantiser's values never exceed the maximum).
+ * Plain search over the 124 non-negative finite codes. */
+uint8_t orc_e5m2_encode(double v) {
+    if (isnan(v)) return 0x7F;
+    uint8_t sign = signbit(v) ? 0x80 : 0;
+    double a = fabs(v);
+    uint8_t best = 0;
+    for (int c = 0; c <= 0x7B; ++c) {
+        double lo = orc_e5m2_decode((uint8_t)c);
+        if (lo > a) break;
+        best = (uint8_t)c;
+    }
+    if (best < 0x7B) {
+        double lo = orc_e5m2_decode(best), hi = orc_e5m2_decode((uint8_t)(best + 1));
+        double dlo = a - lo, dhi = hi - a;
+        if (dhi < dlo || (dhi == dlo && ((best + 1) & 1) == 0)) best = (uint8_t)(best + 1);
+    }
+    return (uint8_t)(sign | best);
+}
+
 /* OCP E2M1 (MXFP4 element): 1 sign, 2 exponent bits (bias 1), 1 mantissa
  * bit; exponent field 0 is subnormal (m * 0.5). */
 double orc_e2m1_decode(uint8_t nib) {
@@ -234,6 +268,85 @@ void orc_gemv_fp8(const uint16_t* x, int64_t ldx, int64_t M, int64_t K,
             double acc = 0.0, sabs = 0.0;
             for (int64_t k = 0; k < K; ++k) {
                 double p = orc_e4m3_decode(w[n * ldw + k]) * (double)orc_bf16_to_f32(x[m * ldx + k]);
+                acc += p;
+                sabs += fabs(p);
+            }
+            double v = sc * acc;
+            y[m * ldy + n] = orc_f64_to_bf16(v);
+            if (y_exact) y_exact[m * N + n] = v;
+            if (S) S[m * N + n] = fabs(sc) * sabs;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* FP8 W8A8: e4m3fn or e5m2 codes for both operands, activation scale per   */
+/* token or per tensor, weight scale per channel or per tensor              */
+/* [Z100 operator-family table, FP8 row (W8A8; e4m3fn/e5m2;                 */
+/*  per-tensor/per-channel/per-token); section 2.2 (scale applied once)]    */
+/* ------------------------------------------------------------------------ */
+
+#define ORC_FMT_E4M3 0
+#define ORC_FMT_E5M2 1
+
+static double orc_fp8_decode(int fmt, uint8_t c) {
+    return fmt == ORC_FMT_E5M2 ? orc_e5m2_decode(c) : orc_e4m3_decode(c);
+}
+static uint8_t orc_fp8_encode(int fmt, double v) {
+    return fmt == ORC_FMT_E5M2 ? orc_e5m2_encode(v) : orc_e4m3_encode(v);
+}
+
+/* Dynamic activation quantisation: s = amax / fmax (fp32 IEEE division,
+ * fmax = 448 for E4M3, 57344 for E5M2), q = encode(fl32(x / s)) with x / s
+ * one fp32 division.  amax over the token's row (per_token) or over all M
+ * rows (one scale).  READING: the INT8 rule with the format's largest finite
+ * value in place of 127; amax == 0 gives s = 0 and zero codes. */
+void orc_act_quant_fp8(const uint16_t* x, int64_t ldx, int64_t M, int64_t K, int fmt, int per_token,
+                       uint8_t* xq, int64_t ldxq, float* xs) {
+    const float fmax = fmt == ORC_FMT_E5M2 ? 57344.0f : 448.0f;
+    float gmax = 0.0f;
+    if (!per_token)
+        for (int64_t m = 0; m < M; ++m)
+            for (int64_t k = 0; k < K; ++k) {
+                float a = fabsf(orc_bf16_to_f32(x[m * ldx + k]));
+                if (a > gmax) gmax = a;
+            }
+    for (int64_t m = 0; m < M; ++m) {
+        float amax = gmax;
+        if (per_token) {
+            amax = 0.0f;
+            for (int64_t k = 0; k < K; ++k) {
+                float a = fabsf(orc_bf16_to_f32(x[m * ldx + k]));
+                if (a > amax) amax = a;
+            }
+        }
+        float s = amax / fmax;
+        if (per_token || m == 0) xs[per_token ? m : 0] = s;
+        for (int64_t k = 0; k < K; ++k) {
+            uint8_t q = 0;
+            if (amax != 0.0f) {
+                float t = orc_bf16_to_f32(x[m * ldx + k]) / s; /* one fp32 division */
+                q = orc_fp8_encode(fmt, (double)t);
+            }
+            xq[m * ldxq + k] = q;
+        }
+    }
+}
+
+/* y = bf16( xs * ws * sum_k dec(xq[m,k]) * dec(w[n,k]) ), the sum and the
+ * scaling in fp64; xs is [M] or [1], ws is [N] or [1]. */
+void orc_gemv_fp8_w8a8(const uint8_t* xq, int64_t ldxq, const float* xs, int xs_per_token, int x_fmt,
+                       int64_t M, int64_t K, const uint8_t* w, int64_t ldw, int64_t N,
+                       const float* ws, int ws_per_row, int w_fmt,
+                       uint16_t* y, int64_t ldy, double* y_exact, double* S) {
+    int64_t n;
+#pragma omp parallel for schedule(static)
+    for (n = 0; n < N; ++n) {
+        for (int64_t m = 0; m < M; ++m) {
+            const double sc = (double)xs[xs_per_token ? m : 0] * (double)ws[ws_per_row ? n : 0];
+            double acc = 0.0, sabs = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double p = orc_fp8_decode(x_fmt, xq[m * ldxq + k]) * orc_fp8_decode(w_fmt, w[n * ldw + k]);
                 acc += p;
                 sabs += fabs(p);
             }
@@ -505,6 +618,14 @@ void orc_f32_to_bf16_n(const float* v, int64_t n, uint16_t* out) {
 
 void orc_e4m3_decode_n(const uint8_t* c, int64_t n, double* out) {
     for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_decode(c[i]);
+}
+
+void orc_e5m2_decode_n(const uint8_t* c, int64_t n, double* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_e5m2_decode(c[i]);
+}
+
+void orc_e5m2_encode_n(const double* v, int64_t n, uint8_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_e5m2_encode(v[i]);
 }
 
 void orc_e4m3_encode_n(const double* v, int64_t n, uint8_t* out) {

@@ -94,6 +94,22 @@ def gen_moe(M: int, E: int, N: int, K: int, topk: int, seed: int = 0,
     return {"x": x, "w": w, "s": s, "ids": ids, "gw": gw}
 
 
+def gen_fp8_w8a8(M: int, N: int, K: int, w_fmt: int = 0, per_channel: bool = True, seed: int = 0) -> dict:
+    """FP8 W8A8 inputs: W bf16 N(0, 0.02) -> per-row (or one) fp32 scale absmax/fmax
+    -> E4M3 (w_fmt 0) or E5M2 (w_fmt 1) codes by torch's cast; x bf16 N(0, 1)
+    (the activation codes are made by the quantiser under test)."""
+    rng = np.random.default_rng(seed)
+    w = bf16_values(bf16_bits(rng.normal(0.0, 0.02, size=(N, K)).astype(np.float32)))
+    fmax = 448.0 if w_fmt == 0 else 57344.0
+    amax = np.abs(w).max(axis=1) if per_channel else np.full(N, np.abs(w).max())
+    ws = (amax / np.float32(fmax)).astype(np.float32)
+    ws[ws == 0] = 1.0
+    dt = torch.float8_e4m3fn if w_fmt == 0 else torch.float8_e5m2
+    codes = (torch.from_numpy(w) / torch.from_numpy(ws)[:, None]).to(dt).view(torch.uint8).numpy()
+    x = bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    return {"x": x, "w": codes, "ws": ws if per_channel else ws[:1].copy(), "w_fmt": w_fmt}
+
+
 def gen_moe_ffn(M: int, E: int, H: int, I: int, topk: int, seed: int = 0,
                 s13_lo: int = 116, s13_hi: int = 122, s2_lo: int = 118, s2_hi: int = 124) -> dict:
     """Routed MXFP4 expert FFN inputs.  Draw order: router weights, gate/up
