@@ -16,7 +16,8 @@ All timed launches are replayed from HIP graphs, so the host's per-call
 overhead is not in the measurement.  `cpu_baseline` times the CPU oracle (oracle/, plain C,
 OpenMP over rows) on the host on the same workload.
 
-Other workloads (--workload fp8_decode | fp8_blk | moe_mxfp4) time the other
+Other workloads (--workload fp8_decode | fp8_w8a8 | fp8_blk | moe_mxfp4 |
+moe_ffn_mxfp4) time the other
 entry points the same way; they are used for profiling, the default run is
 the int8 one.
 """
@@ -26,6 +27,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -55,6 +57,14 @@ def bytes_gemv_fp8(M, N, K):
     return N * K + 4 * N + 2 * M * K + 2 * M * N               # W, ws (per row), x, y
 
 
+def bytes_act_quant_fp8(M, K):
+    return 2 * M * K + M * K + 4 * M                           # x, xq, xs
+
+
+def bytes_gemv_fp8_w8a8(M, N, K):
+    return N * K + 4 * N + M * K + 4 * M + 2 * M * N          # W, ws, xq, xs, y
+
+
 def bytes_blk_call(M, N, K):
     return N * K + ((N + 127) // 128) * (K // 128) + 2 * M * K + 2 * M * N   # W, ws, x, y
 
@@ -75,12 +85,35 @@ def bytes_moe_ffn_call(M, H, I, E, topk, live):
 
 # ----------------------------------------------------------------------------- workloads
 
-def src_hash():
-    h = hashlib.sha256()
+# translation units whose kernels each workload runs
+KERNEL_SOURCES = {
+    "int8_decode": ("act_quant.hip", "gemv.hip"),
+    "fp8_decode": ("gemv.hip",),
+    "fp8_w8a8": ("act_quant.hip", "gemv.hip"),
+    "fp8_blk": ("act_quant.hip", "gemv.hip"),
+    "moe_mxfp4": ("moe.hip",),
+    "moe_ffn_mxfp4": ("moe.hip", "routing.hip"),
+}
+
+
+def src_hash(workload):
+    """Hash of the device code a workload runs: its translation units and the
+    local headers they include, transitively.  qlin_launch.hpp (host-side
+    declarations of every launcher) is left out, so that adding an entry point
+    elsewhere does not invalidate this workload's counters."""
     csrc = os.path.join(ROOT, "skinny_gemm_qlin_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+    todo, seen = list(KERNEL_SOURCES[workload]), set()
+    while todo:
+        f = todo.pop()
+        if f in seen or f == "qlin_launch.hpp":
+            continue
+        seen.add(f)
+        text = open(os.path.join(csrc, f)).read()
+        todo += re.findall(r'^#include "([A-Za-z0-9_.]+)"', text, re.M)
+    h = hashlib.sha256()
+    for f in sorted(seen):
+        h.update(f.encode())
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -92,7 +125,7 @@ def load_traffic(workload):
         t = json.load(open(p)).get(workload)
     except Exception:
         return None
-    if not t or t.get("src_hash") != src_hash():
+    if not t or t.get("src_hash") != src_hash(workload):
         return None  # counters were taken on other kernel code
     return t.get("bytes_per_launch")
 
@@ -103,7 +136,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="int8_decode",
-                    choices=["int8_decode", "fp8_decode", "fp8_blk", "moe_mxfp4", "moe_ffn_mxfp4"])
+                    choices=["int8_decode", "fp8_decode", "fp8_w8a8", "fp8_blk", "moe_mxfp4", "moe_ffn_mxfp4"])
     ap.add_argument("--ms", default=None, help="comma list of M values (default: the workload's)")
     ap.add_argument("--rotate", type=int, default=0, help="weight copies (0 = enough to defeat the MALL)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
@@ -146,6 +179,9 @@ def main():
         wbytes = N * K
     elif wl == "fp8_decode":
         d = inputs.gen_fp8(Mmax, N, K, seed=0, per_tensor=args.per_tensor)
+        wbytes = N * K
+    elif wl == "fp8_w8a8":
+        d = inputs.gen_fp8_w8a8(Mmax, N, K, w_fmt=0, seed=0)
         wbytes = N * K
     elif wl == "fp8_blk":
         d = inputs.gen_fp8_blk(Mmax, N, K, seed=0)
@@ -212,6 +248,11 @@ def main():
                      lambda: ql.qlin_gemv_i8(xq_buf[:M], xs_buf[:M], w, sc, y=y_buf[:M]))]
         if wl == "fp8_decode":
             return [("gemv_fp8", bytes_gemv_fp8(M, N, K), lambda: ql.qlin_gemv_fp8(xm, w, sc, y=y_buf[:M]))]
+        if wl == "fp8_w8a8":
+            return [("act_quant_fp8", bytes_act_quant_fp8(M, K),
+                     lambda: ql.qlin_act_quant_fp8(xm, 0, True, xq_buf[:M], xs_buf[:M])),
+                    ("gemv_fp8_w8a8", bytes_gemv_fp8_w8a8(M, N, K),
+                     lambda: ql.qlin_gemv_fp8_w8a8(xq_buf[:M], xs_buf[:M], w, sc, 0, 0, y=y_buf[:M]))]
         if wl == "fp8_blk":
             return [("act_quant_blk+gemv_fp8_blk", bytes_blk_call(M, N, K),
                      lambda: ql.qlin_gemv_fp8_blk(xm, w, sc, xq=xq_buf[:M], xs=xsb_buf[:M], y=y_buf[:M]))]
@@ -222,7 +263,7 @@ def main():
                  lambda: ql.qlin_moe_ffn_mxfp4(xm, wr, *ffn[ci], spec["topk"], y=y_buf[:M], workspace=ws_ffn,
                                                ids=ids_buf[:M], gw=gw_buf[:M]))]
 
-    dominant = {"int8_decode": "gemv_i8", "fp8_decode": "gemv_fp8",
+    dominant = {"int8_decode": "gemv_i8", "fp8_decode": "gemv_fp8", "fp8_w8a8": "gemv_fp8_w8a8",
                 "fp8_blk": "act_quant_blk+gemv_fp8_blk", "moe_mxfp4": "moe_mxfp4",
                 "moe_ffn_mxfp4": "moe_ffn_mxfp4"}[wl]
 
@@ -326,6 +367,9 @@ def main():
                     oracle.gemv_i8(xq, xs, d["w"], d["ws"])
                 elif wl == "fp8_decode":
                     oracle.gemv_fp8(xm, d["w"], d["ws"])
+                elif wl == "fp8_w8a8":
+                    xq, xs = oracle.act_quant_fp8(xm, 0, True)
+                    oracle.gemv_fp8_w8a8(xq, xs, 0, d["w"], d["ws"], 0)
                 elif wl == "fp8_blk":
                     oracle.fp8_blk(xm, d["w"], d["ws"])
                 else:
@@ -348,6 +392,7 @@ def main():
     cfg = {"workload": {
         "int8_decode": f"W8A8 INT8 decode linear (act quant + GEMV, bf16 out) N={N} K={K}, one call per M",
         "fp8_decode": f"E4M3 weight-only GEMV ({'per-tensor' if args.per_tensor else 'per-channel'}) N={N} K={K}",
+        "fp8_w8a8": f"FP8 W8A8 E4M3 x E4M3 (per-token act quant + GEMV, per-channel ws) N={N} K={K}",
         "fp8_blk": f"128x128 block-scaled FP8 (act quant + GEMV) N={N} K={K}",
         "moe_mxfp4": f"MXFP4 top-{spec.get('topk')} expert GEMV E={spec.get('E')} N={N} K={K}",
         "moe_ffn_mxfp4": f"MXFP4 top-{spec.get('topk')} expert FFN with routing E={spec.get('E')} "
@@ -367,7 +412,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"int8_decode": "int8", "fp8_decode": "fp8e4m3*bf16->f32",
+        "dtype": {"int8_decode": "int8", "fp8_decode": "fp8e4m3*bf16->f32", "fp8_w8a8": "fp8e4m3*fp8e4m3->f32",
                   "fp8_blk": "fp8e4m3->f32", "moe_mxfp4": "fp4e2m1*bf16->f32",
                   "moe_ffn_mxfp4": "fp4e2m1*bf16->f32"}[wl],
         "data": "synthetic",

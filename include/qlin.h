@@ -3,8 +3,9 @@
  *
  *     y[M,N] = dequant(W[N,K]) . x[M,K],   M = 1..16 tokens
  *
- * in four variants: W8A8 INT8, FP8-E4M3 weight-only, 128x128 block-scaled
- * FP8 with UE8M0 scales, and the MXFP4 expert GEMV behind top-k routing.
+ * in four variants: W8A8 INT8, FP8-E4M3 weight-only (and FP8 W8A8 with
+ * E4M3 / E5M2 codes), 128x128 block-scaled FP8 with UE8M0 scales, and the
+ * MXFP4 expert GEMV behind top-k routing (also as a routed expert FFN).
  *
  * Sources (web pages, by title and section):
  *   [Z100] "Hygon Z100 (gfx906) vLLM adaptation: optimisation and operator
@@ -62,6 +63,12 @@ enum {
 
 #define QLIN_MAX_M 16
 
+/* FP8 code formats (OCP 8-bit floating point) of the W8A8 FP8 entry points. */
+enum {
+    QLIN_FMT_E4M3 = 0, /* e4m3fn: bias 7, no infinities, largest finite 448 */
+    QLIN_FMT_E5M2 = 1  /* e5m2: bias 15, +-inf and NaN, largest finite 57344 */
+};
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* qlin_status_str(int status);
 
@@ -114,6 +121,43 @@ int qlin_gemv_fp8(const void* x, int64_t ldx, int64_t M, int64_t K,
                   const uint8_t* w, int64_t ldw, int64_t N,
                   const float* ws, int ws_per_row,
                   void* y, int64_t ldy, void* stream);
+
+/* ------------------------------------------------------------------------
+ * (b') FP8 W8A8 -- [Z100] operator-family table (FP8 row: W8A8 with
+ *      e4m3fn or e5m2 codes, per-tensor / per-channel / per-token scales)
+ *      and 2.2 (the scale multiplies the accumulated sum once)
+ * ------------------------------------------------------------------------ */
+
+/* Dynamic FP8 activation quantisation (the INT8 rule with the format's
+ * largest finite value fmax = 448 (E4M3) or 57344 (E5M2) in place of 127):
+ *   per_token = 1:  s[m] = max_k |x[m,k]| / fmax,         xs fp32 [M]
+ *   per_token = 0:  s    = max_{m,k} |x[m,k]| / fmax,     xs fp32 [1]
+ *   xq[m,k] = fp8_rne(x[m,k] / s)   (codes of format fmt, uint8 [M, ldxq])
+ * Both divisions are IEEE fp32 (a reciprocal-multiply would change codes);
+ * fp8_rne rounds to the nearest finite code, ties to the even code, and a
+ * quotient above fmax (a rounding excess) saturates to +-fmax.  A zero
+ * amax gives s = 0 and codes 0.  Inputs must be finite.
+ * Requires K % 16 == 0, 16 <= K <= 2^24, ldx % 8 == 0, ldxq % 16 == 0;
+ * fmt is QLIN_FMT_E4M3 or QLIN_FMT_E5M2 and per_token 0 or 1 (else
+ * QLIN_ERR_ARG). */
+int qlin_act_quant_fp8(const void* x, int64_t ldx, int64_t M, int64_t K, int fmt, int per_token,
+                       uint8_t* xq, int64_t ldxq, float* xs, void* stream);
+
+/* FP8 x FP8 GEMV:
+ *   acc[m,n] = sum_k fp8(xq[m,k]) * fp8(w[n,k])      (fp32 accumulation)
+ *   y[m,n]   = bf16( (acc * xs[m]) * ws[n] )          (two fp32 products)
+ *   xq codes of format x_fmt [M, ldxq]; xs fp32 [M] (xs_per_token = 1) or
+ *   [1] (= 0); w codes of format w_fmt [N, ldw]; ws fp32 [N] (ws_per_row =
+ *   1, per-channel) or [1] (= 0, per-tensor); y bf16 [M, ldy].
+ * Both operands are widened to bf16 exactly, so each product is exact and
+ * only the running fp32 sum rounds.  Weight codes must be finite.
+ * Requires K % 16 == 0, 16 <= K <= 2^24, ldxq % 16 == 0, ldw % 16 == 0,
+ * N >= 1, ldy >= N; formats and flags as above (else QLIN_ERR_ARG). */
+int qlin_gemv_fp8_w8a8(const uint8_t* xq, int64_t ldxq, const float* xs, int xs_per_token, int x_fmt,
+                       int64_t M, int64_t K,
+                       const uint8_t* w, int64_t ldw, int64_t N,
+                       const float* ws, int ws_per_row, int w_fmt,
+                       void* y, int64_t ldy, void* stream);
 
 /* ------------------------------------------------------------------------
  * (c) Block-scaled FP8 -- [Z100] 2.4 (block formula, scale folding, padded

@@ -15,10 +15,11 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import QlinError, check, load, status_str  # noqa: F401
+from ._lib import QLIN_FMT_E4M3, QLIN_FMT_E5M2, QlinError, check, load, status_str  # noqa: F401
 
 __all__ = [
     "QlinError", "qlin_act_quant_i8", "qlin_gemv_i8", "qlin_gemv_fp8", "qlin_gemv_fp8_blk",
+    "qlin_act_quant_fp8", "qlin_gemv_fp8_w8a8", "QLIN_FMT_E4M3", "QLIN_FMT_E5M2",
     "qlin_moe_mxfp4", "qlin_moe_mxfp4_workspace_bytes", "status_str",
 ]
 
@@ -100,6 +101,59 @@ def qlin_gemv_fp8(x, w, ws, y=None, stream=None):
     check(load().qlin_gemv_fp8(x.data_ptr(), x.stride(0), M, K, w.data_ptr(), w.stride(0), N,
                                ws.data_ptr(), int(ws.numel() > 1), y.data_ptr(), y.stride(0),
                                _stream(x, stream)), "qlin_gemv_fp8")
+    return y
+
+
+_FP8_DT = {QLIN_FMT_E4M3: torch.float8_e4m3fn, QLIN_FMT_E5M2: torch.float8_e5m2}
+
+
+def _codes(t: torch.Tensor, name: str, fmt: int) -> torch.Tensor:
+    """FP8 codes as stored: torch.uint8, or the float8 dtype of the format."""
+    if fmt not in _FP8_DT:
+        raise ValueError(f"{name}: unknown FP8 format {fmt}")
+    _need(t, name, (torch.uint8, _FP8_DT[fmt]), 2)
+    return t
+
+
+def qlin_act_quant_fp8(x, fmt=QLIN_FMT_E4M3, per_token=True, xq=None, xs=None, stream=None):
+    """Dynamic FP8 quantisation of bf16 x [M, K] -> (xq uint8 codes [M, K] of
+    format fmt, xs fp32 [M] (per_token) or [1])."""
+    _need(x, "x", (torch.bfloat16,), 2)
+    M, K = x.shape
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if xs is None:
+        xs = torch.empty((M if per_token else 1,), dtype=torch.float32, device=x.device)
+    _codes(xq, "xq", fmt)
+    _need(xs, "xs", (torch.float32,), 1)
+    if xs.numel() < (M if per_token else 1):
+        raise ValueError(f"xs holds {xs.numel()} scales, needs {M if per_token else 1}")
+    check(load().qlin_act_quant_fp8(x.data_ptr(), x.stride(0), M, K, int(fmt), int(bool(per_token)),
+                                    xq.data_ptr(), xq.stride(0), xs.data_ptr(), _stream(x, stream)),
+          "qlin_act_quant_fp8")
+    return xq, xs
+
+
+def qlin_gemv_fp8_w8a8(xq, xs, w, ws, x_fmt=QLIN_FMT_E4M3, w_fmt=QLIN_FMT_E4M3, y=None, stream=None):
+    """FP8 W8A8 GEMV: xq codes [M, K] (format x_fmt), xs fp32 [M] or [1], w codes
+    [N, K] (format w_fmt, row pitch w.stride(0)), ws fp32 [N] or [1] -> y bf16 [M, N]."""
+    _codes(xq, "xq", x_fmt)
+    _codes(w, "w", w_fmt)
+    _need(xs, "xs", (torch.float32,), 1)
+    _need(ws, "ws", (torch.float32,), 1)
+    M, K = xq.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError(f"w has K={w.shape[1]}, xq has K={K}")
+    if xs.numel() not in (1, M) or ws.numel() not in (1, N):
+        raise ValueError(f"xs must hold 1 or M={M} scales, ws 1 or N={N}")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    _need(y, "y", (torch.bfloat16,), 2)
+    check(load().qlin_gemv_fp8_w8a8(xq.data_ptr(), xq.stride(0), xs.data_ptr(), int(xs.numel() > 1),
+                                    int(x_fmt), M, K, w.data_ptr(), w.stride(0), N, ws.data_ptr(),
+                                    int(ws.numel() > 1), int(w_fmt), y.data_ptr(), y.stride(0),
+                                    _stream(xq, stream)), "qlin_gemv_fp8_w8a8")
     return y
 
 

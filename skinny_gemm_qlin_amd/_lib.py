@@ -24,8 +24,11 @@ QLIN_ERR_LAUNCH = -7
 EXPORTS = (
     "qlin_status_str", "qlin_version", "qlin_act_quant_i8", "qlin_gemv_i8", "qlin_gemv_fp8",
     "qlin_gemv_fp8_blk", "qlin_moe_mxfp4_workspace_bytes", "qlin_moe_mxfp4",
-    "qlin_moe_ffn_mxfp4_workspace_bytes", "qlin_moe_ffn_mxfp4",
+    "qlin_moe_ffn_mxfp4_workspace_bytes", "qlin_moe_ffn_mxfp4", "qlin_act_quant_fp8", "qlin_gemv_fp8_w8a8",
 )
+
+QLIN_FMT_E4M3 = 0
+QLIN_FMT_E5M2 = 1
 
 
 class QlinError(RuntimeError):
@@ -55,6 +58,10 @@ def load() -> ctypes.CDLL:
     lib.qlin_gemv_i8.restype = I
     lib.qlin_gemv_fp8.argtypes = [P, I64, I64, I64, P, I64, I64, P, I, P, I64, P]
     lib.qlin_gemv_fp8.restype = I
+    lib.qlin_act_quant_fp8.argtypes = [P, I64, I64, I64, I, I, P, I64, P, P]
+    lib.qlin_act_quant_fp8.restype = I
+    lib.qlin_gemv_fp8_w8a8.argtypes = [P, I64, P, I, I, I64, I64, P, I64, I64, P, I, I, P, I64, P]
+    lib.qlin_gemv_fp8_w8a8.restype = I
     lib.qlin_gemv_fp8_blk.argtypes = [P, I64, I64, I64, P, I64, I64, P, P, P, P, I64, P]
     lib.qlin_gemv_fp8_blk.restype = I
     lib.qlin_moe_mxfp4_workspace_bytes.argtypes = [I64, I64, I64, I64]

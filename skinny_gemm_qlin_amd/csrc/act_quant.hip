@@ -4,6 +4,9 @@
 //                         [Z100 section 2.1; operator-family table, INT8 row]
 //   blk_act_quant_kernel  per (token, 128-wide K group) E4M3 codes with a
 //                         UE8M0 exponent [DSV4 section 3.3; Z100 section 2.4]
+//   act_quant_fp8_kernel  per-token or per-tensor E4M3 / E5M2 codes with an
+//                         fp32 scale amax/fmax [Z100 operator-family table,
+//                         FP8 row: W8A8, e4m3fn/e5m2, per-token/per-tensor]
 #include "qlin_device.hpp"
 #include "qlin_launch.hpp"
 
@@ -137,6 +140,113 @@ __global__ __launch_bounds__(64) void blk_act_quant_kernel(
         *(uint2*)(xq + m * K + kb * 128 + j * 8) = make_uint2((uint32_t)lo, (uint32_t)hi);
         if (j == 0) xs[m * nkb + kb] = (uint8_t)E;
     }
+}
+
+// ---------------------------------------------------------------- FP8 W8A8
+// The INT8 rule with the format's largest finite value fmax (448 for E4M3,
+// 57344 for E5M2) in place of 127: s = amax / fmax and q = rne(x / s), both
+// IEEE fp32 divisions.  |x / s| can exceed fmax by a rounding error (and by
+// more when s is an fp32 subnormal); such values saturate to +-fmax before
+// the convert, so every code is finite.  The comparisons keep a NaN (which
+// then converts to a NaN code).  amax == 0 gives s = 0 and zero codes.
+template <int F>
+__device__ __forceinline__ uint2 quant_fp8x8(const u32x4_t& v, float amax, float s) {
+    constexpr float fmax = F == kFmtE5M2 ? 57344.0f : 448.0f;
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+    float t[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t h = (e & 1) ? (d[e >> 1] >> 16) : (d[e >> 1] & 0xFFFFu);
+        float q = 0.0f;
+        if (amax != 0.0f) {
+            q = bf16_to_f32(h) / s;
+            q = q > fmax ? fmax : (q < -fmax ? -fmax : q);
+        }
+        t[e] = q;
+    }
+    int lo = 0, hi = 0;
+    lo = f32x2_to_fp8<F, false>(t[0], t[1], lo);
+    lo = f32x2_to_fp8<F, true>(t[2], t[3], lo);
+    hi = f32x2_to_fp8<F, false>(t[4], t[5], hi);
+    hi = f32x2_to_fp8<F, true>(t[6], t[7], hi);
+    return make_uint2((uint32_t)lo, (uint32_t)hi);
+}
+
+// One workgroup of T lanes quantises `rows` consecutive tokens with one
+// scale: rows = 1 and a grid of M workgroups for per-token scales, rows = M
+// and a single workgroup for the per-tensor scale.  The rows' 16-byte
+// vectors are numbered row-major; lane l takes vectors l, l + T, ...; the
+// first C of them stay in registers between the amax pass and the quantise
+// pass (M*K <= 8*T*C values are read from HBM once).  The amax is reduced
+// with DPP within a 16-lane row, shuffles across a wave and LDS across waves.
+template <int F, int T, int C>
+__global__ __launch_bounds__(T) void act_quant_fp8_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, int rows, int64_t K,
+    uint8_t* __restrict__ xq, int64_t ldxq, float* __restrict__ xs) {
+    constexpr int W = T / 64;
+    constexpr float fmax = F == kFmtE5M2 ? 57344.0f : 448.0f;
+    __shared__ float wave_max[W];
+    const int64_t m0 = (int64_t)blockIdx.x * rows;
+    const int tid = threadIdx.x;
+    const int nvec = (int)(K >> 3);  // 8 bf16 per vector
+    const int total = rows * nvec;
+
+    u32x4_t cache[C];
+    float a = 0.0f;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int i = tid + c * T;
+        if (i < total) {
+            const int r = i / nvec, v = i - r * nvec;
+            cache[c] = ld16(x + (m0 + r) * ldx + (int64_t)v * 8);
+        } else {
+            cache[c] = u32x4_t{0, 0, 0, 0};
+        }
+        a = absmax8(cache[c], a);
+    }
+    for (int i = tid + C * T; i < total; i += T) {
+        const int r = i / nvec, v = i - r * nvec;
+        a = absmax8(ld16(x + (m0 + r) * ldx + (int64_t)v * 8), a);
+    }
+    a = row_max_f32(a);
+    a = fmaxf(a, __shfl_xor(a, 16));
+    a = fmaxf(a, __shfl_xor(a, 32));
+    if ((tid & 63) == 0) wave_max[tid >> 6] = a;
+    __syncthreads();
+    float amax = wave_max[0];
+#pragma unroll
+    for (int q = 1; q < W; ++q) amax = fmaxf(amax, wave_max[q]);
+    const float s = amax / fmax;
+    if (tid == 0) xs[blockIdx.x] = s;
+
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int i = tid + c * T;
+        if (i < total) {
+            const int r = i / nvec, v = i - r * nvec;
+            *(uint2*)(xq + (m0 + r) * ldxq + (int64_t)v * 8) = quant_fp8x8<F>(cache[c], amax, s);
+        }
+    }
+    for (int i = tid + C * T; i < total; i += T) {
+        const int r = i / nvec, v = i - r * nvec;
+        *(uint2*)(xq + (m0 + r) * ldxq + (int64_t)v * 8) =
+            quant_fp8x8<F>(ld16(x + (m0 + r) * ldx + (int64_t)v * 8), amax, s);
+    }
+}
+
+template <int F>
+hipError_t launch_act_quant_fp8_fmt(const ActQuantF8Args& a, hipStream_t st) {
+    if (a.per_token)
+        hipLaunchKernelGGL((act_quant_fp8_kernel<F, 256, 4>), dim3((unsigned)a.M), dim3(256), 0, st, a.x, a.ldx, 1,
+                           a.K, a.xq, a.ldxq, a.xs);
+    else
+        hipLaunchKernelGGL((act_quant_fp8_kernel<F, 1024, 16>), dim3(1), dim3(1024), 0, st, a.x, a.ldx, (int)a.M,
+                           a.K, a.xq, a.ldxq, a.xs);
+    return hipGetLastError();
+}
+
+hipError_t launch_act_quant_fp8(const ActQuantF8Args& a, hipStream_t st) {
+    return a.fmt == kFmtE5M2 ? launch_act_quant_fp8_fmt<kFmtE5M2>(a, st) : launch_act_quant_fp8_fmt<kFmtE4M3>(a, st);
 }
 
 hipError_t launch_blk_act_quant(const BlkQuantArgs& a, hipStream_t st) {

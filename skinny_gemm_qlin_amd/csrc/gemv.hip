@@ -6,8 +6,9 @@
 //   * M = 1: VALU, one whole wavefront per row (GS=64), all K steps of the
 //     row in flight (up to 8), 4 waves per workgroup; block FP8 uses its own
 //     M = 1 kernel that shares the scale bytes of a batch across the wave;
-//   * M = 2 (INT8, E4M3): VALU with smaller lane groups and several rows per
-//     group, so that each activation load feeds more weight rows;
+//   * M = 2 (INT8, E4M3, FP8 W8A8): VALU with smaller lane groups (and, for
+//     INT8 / E4M3, several rows per group, so that each activation load feeds
+//     more weight rows);
 //   * otherwise: the matrix-core kernels.
 #include <algorithm>
 
@@ -36,6 +37,26 @@ hipError_t run_fp8(const F8Args& a, hipStream_t st) {
     hipLaunchKernelGGL((gemv_fp8_kernel<M, GS, R, U, WPB>), grid, dim3(64 * WPB), 0, st,
                        a.x, a.ldx, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.y, a.ldy);
     return hipGetLastError();
+}
+
+template <int M, int GS, int R, int U, int WPB, int XF, int WF>
+hipError_t run_w8a8_fmt(const W8A8F8Args& a, hipStream_t st) {
+    constexpr int rows_per_block = (64 / GS) * R * WPB;
+    dim3 grid((unsigned)((a.N + rows_per_block - 1) / rows_per_block));
+    hipLaunchKernelGGL((gemv_fp8_w8a8_kernel<M, GS, R, U, WPB, XF, WF>), grid, dim3(64 * WPB), 0, st,
+                       a.xq, a.ldxq, a.xs, a.xs_step, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.y, a.ldy);
+    return hipGetLastError();
+}
+
+// The two code formats are template arguments (the convert instruction
+// differs); the four combinations share every tile choice.
+template <int M, int GS, int R, int U, int WPB>
+hipError_t run_w8a8(const W8A8F8Args& a, hipStream_t st) {
+    if (a.x_fmt == kFmtE5M2)
+        return a.w_fmt == kFmtE5M2 ? run_w8a8_fmt<M, GS, R, U, WPB, kFmtE5M2, kFmtE5M2>(a, st)
+                                   : run_w8a8_fmt<M, GS, R, U, WPB, kFmtE5M2, kFmtE4M3>(a, st);
+    return a.w_fmt == kFmtE5M2 ? run_w8a8_fmt<M, GS, R, U, WPB, kFmtE4M3, kFmtE5M2>(a, st)
+                               : run_w8a8_fmt<M, GS, R, U, WPB, kFmtE4M3, kFmtE4M3>(a, st);
 }
 
 template <int M, int GS, int R, int U, int WPB>
@@ -105,6 +126,34 @@ hipError_t run_blk_mfma(const BlkArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <int XF, int WF>
+hipError_t run_w8a8_mfma_fmt(const W8A8F8Args& a, hipStream_t st) {
+    dim3 grid((unsigned)((a.N + 15) / 16));
+    switch (mfma_ks(a.N, a.K)) {
+        case 16:
+            hipLaunchKernelGGL((gemv_fp8_w8a8_mfma_kernel<1, 16, XF, WF>), grid, dim3(1024), 0, st, a.xq, a.ldxq,
+                               a.xs, a.xs_step, (int)a.M, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.y, a.ldy);
+            break;
+        case 8:
+            hipLaunchKernelGGL((gemv_fp8_w8a8_mfma_kernel<1, 8, XF, WF>), grid, dim3(512), 0, st, a.xq, a.ldxq,
+                               a.xs, a.xs_step, (int)a.M, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.y, a.ldy);
+            break;
+        default:
+            hipLaunchKernelGGL((gemv_fp8_w8a8_mfma_kernel<1, 4, XF, WF>), grid, dim3(256), 0, st, a.xq, a.ldxq,
+                               a.xs, a.xs_step, (int)a.M, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.y, a.ldy);
+            break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t run_w8a8_mfma(const W8A8F8Args& a, hipStream_t st) {
+    if (a.x_fmt == kFmtE5M2)
+        return a.w_fmt == kFmtE5M2 ? run_w8a8_mfma_fmt<kFmtE5M2, kFmtE5M2>(a, st)
+                                   : run_w8a8_mfma_fmt<kFmtE5M2, kFmtE4M3>(a, st);
+    return a.w_fmt == kFmtE5M2 ? run_w8a8_mfma_fmt<kFmtE4M3, kFmtE5M2>(a, st)
+                               : run_w8a8_mfma_fmt<kFmtE4M3, kFmtE4M3>(a, st);
+}
+
 template <int U>
 hipError_t run_blk_m1(const BlkArgs& a, hipStream_t st) {
     constexpr int WPB = 4;
@@ -130,6 +179,31 @@ hipError_t launch_gemv_fp8(const F8Args& a, hipStream_t st) {
         case 2: return run_fp8<2, 64, 4, 1, 1>(a, st);
         default: return run_fp8_mfma(a, st);
     }
+}
+
+// W8A8 FP8 widens both operands (16 converts per 16 code pairs), so the VALU
+// kernels keep fewer steps in flight than INT8 (measured at 17408 x 5120:
+// M = 1 best with 3 steps of one row per wave, M = 2 with 32-lane groups and
+// 5 steps); the matrix-core kernel from M = 3.
+hipError_t launch_gemv_fp8_w8a8(const W8A8F8Args& a, hipStream_t st) {
+    if (a.M == 1) {
+        switch (std::min(steps64(a.K), 3)) {
+            case 1: return run_w8a8<1, 64, 1, 1, 4>(a, st);
+            case 2: return run_w8a8<1, 64, 1, 2, 4>(a, st);
+            default: return run_w8a8<1, 64, 1, 3, 4>(a, st);
+        }
+    }
+    if (a.M == 2) {
+        const int steps32 = (int)(((a.K >> 4) + 31) / 32);
+        switch (std::min(steps32, 5)) {
+            case 1: return run_w8a8<2, 32, 1, 1, 2>(a, st);
+            case 2: return run_w8a8<2, 32, 1, 2, 2>(a, st);
+            case 3: return run_w8a8<2, 32, 1, 3, 2>(a, st);
+            case 4: return run_w8a8<2, 32, 1, 4, 2>(a, st);
+            default: return run_w8a8<2, 32, 1, 5, 2>(a, st);
+        }
+    }
+    return run_w8a8_mfma(a, st);
 }
 
 hipError_t launch_gemv_fp8_blk(const BlkArgs& a, hipStream_t st) {

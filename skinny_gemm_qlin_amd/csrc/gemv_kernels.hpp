@@ -216,6 +216,97 @@ __global__ __launch_bounds__(64 * WPB) void gemv_fp8_kernel(
         }
 }
 
+// ------------------------------------------------------------------ FP8 W8A8
+// Both operands are FP8 codes (activations XF, weights WF: E4M3 or E5M2),
+// each widened to bf16 exactly by the hardware convert; a product of two
+// such values is exact in fp32, so v_dot2 bf16 with fp32 accumulation only
+// rounds the running sum.  Epilogue as the INT8 path: bf16((acc*xs)*ws)
+// [Z100 operator-family table, FP8 row (W8A8); section 2.2].
+template <int F>
+__device__ __forceinline__ void fp8x16(const u32x4_t& v, bf16x2_t o[8]) {
+    fp8x4_to_bf16<F>(v.x, o[0], o[1]);
+    fp8x4_to_bf16<F>(v.y, o[2], o[3]);
+    fp8x4_to_bf16<F>(v.z, o[4], o[5]);
+    fp8x4_to_bf16<F>(v.w, o[6], o[7]);
+}
+
+template <int M, int GS, int R, int U, int WPB, int XF, int WF>
+__global__ __launch_bounds__(64 * WPB) void gemv_fp8_w8a8_kernel(
+    const uint8_t* __restrict__ xq, int64_t ldxq, const float* __restrict__ xs, int xs_step,
+    int64_t K, const uint8_t* __restrict__ w, int64_t ldw, int64_t N,
+    const float* __restrict__ ws, int ws_step, uint16_t* __restrict__ y, int64_t ldy) {
+    const int j = (threadIdx.x & 63) % GS;
+    const int64_t n0 = first_row<GS, R, WPB>();
+    const uint8_t* wr[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) wr[r] = w + (n0 + r < N ? n0 + r : N - 1) * ldw;
+
+    float acc[R][M];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+
+    const int64_t nchunk = K >> 4;  // 16 codes per chunk
+    const int64_t nsteps = (nchunk + GS - 1) / GS;
+    for (int64_t s = 0; s < nsteps; s += U) {
+        u32x4_t wv[U][R], xv[U][M];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = (s + u) * GS + j;
+            const int64_t cc = c < nchunk ? c : nchunk - 1;
+#pragma unroll
+            for (int r = 0; r < R; ++r) wv[u][r] = ld_stream(wr[r] + cc * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = (s + u) * GS + j;
+            const int64_t cc = c < nchunk ? c : nchunk - 1;
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const u32x4_t t = ld16(xq + m * ldxq + cc * 16);
+                xv[u][m] = c < nchunk ? t : u32x4_t{0, 0, 0, 0};  // code 0 decodes to +0 in both formats
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            bf16x2_t xb[M][8];
+#pragma unroll
+            for (int m = 0; m < M; ++m) fp8x16<XF>(xv[u][m], xb[m]);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                bf16x2_t wb[8];
+                fp8x16<WF>(wv[u][r], wb);
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    float a = acc[r][m];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) a = dot2(wb[i], xb[m][i], a);
+                    acc[r][m] = a;
+                }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = group_sum<GS>(acc[r][m]);
+
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const int v = r * M + m;
+            const int64_t n = n0 + r;
+            if ((v % GS) == j && n < N) {
+                float t = acc[r][m] * xs[m * xs_step];
+                t = t * ws[n * ws_step];
+                y[m * ldy + n] = f32_to_bf16(t);
+            }
+        }
+}
+
 // ------------------------------------------------------------------ block-scaled FP8
 // out = sum_kb (sum_{k in kb} xq*w) * 2^(xs-127) * 2^(ws-127).  A chunk of 16
 // codes lies inside one 128-wide block (kb = c/8), so each lane multiplies the

@@ -213,6 +213,80 @@ __global__ __launch_bounds__(64 * KS) void gemv_fp8_mfma_kernel(
     }
 }
 
+// ------------------------------------------------------------------ FP8 W8A8 (v_mfma_f32_16x16x32_bf16)
+// Weight codes (format WF) from the tile and activation codes (format XF)
+// straight from xq, each widened to bf16 (exact) for the bf16 matrix core
+// with fp32 accumulation; epilogue bf16((acc*xs)*ws) as the VALU kernel
+// [Z100 operator-family table, FP8 row (W8A8); section 2.2].
+template <int F>
+__device__ __forceinline__ void fp8x16_to_bf16x8x2(const u32x4_t& c, bf16x8_t& lo, bf16x8_t& hi) {
+    bf16x2_t b[8];
+    fp8x4_to_bf16<F>(c.x, b[0], b[1]);
+    fp8x4_to_bf16<F>(c.y, b[2], b[3]);
+    fp8x4_to_bf16<F>(c.z, b[4], b[5]);
+    fp8x4_to_bf16<F>(c.w, b[6], b[7]);
+    lo = bf16x8_t{b[0][0], b[0][1], b[1][0], b[1][1], b[2][0], b[2][1], b[3][0], b[3][1]};
+    hi = bf16x8_t{b[4][0], b[4][1], b[5][0], b[5][1], b[6][0], b[6][1], b[7][0], b[7][1]};
+}
+
+template <int U, int KS, int XF, int WF>
+__global__ __launch_bounds__(64 * KS) void gemv_fp8_w8a8_mfma_kernel(
+    const uint8_t* __restrict__ xq, int64_t ldxq, const float* __restrict__ xs, int xs_step, int M,
+    int64_t K, const uint8_t* __restrict__ w, int64_t ldw, int64_t N,
+    const float* __restrict__ ws, int ws_step, uint16_t* __restrict__ y, int64_t ldy) {
+    __shared__ __align__(16) uint8_t tile[KS][16 * kTilePitch];
+    __shared__ f32x4_t red[KS][64];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int mi = lane & 15, mg = lane >> 4;
+    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int64_t nch = (K + 255) >> 8, per = (nch + KS - 1) / KS;
+    const int64_t c0 = wv * per, c1 = c0 + per < nch ? c0 + per : nch;
+    const TileLoader tl(w, ldw, n0, N);
+    const bool xon = mi < M;
+    const uint8_t* xr = xq + (xon ? mi : 0) * ldxq;
+    uint8_t* t = tile[wv];
+
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t c = c0; c < c1; c += U) {
+        u32x4_t wv_[U][4], xb[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) tl.load(wv_[u], c + u < c1 ? c + u : c1 - 1, K);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                const int64_t k = (c + u) * 256 + 64 * s4 + 16 * mg;
+                const bool ok = (c + u < c1) && k < K && xon;
+                const u32x4_t v = ld16(xr + (ok ? k : 0));
+                xb[u][s4] = ok ? v : u32x4_t{0, 0, 0, 0};
+            }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            tile_store(t, wv_[u]);
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                bf16x8_t a0, a1, b0, b1;
+                fp8x16_to_bf16x8x2<WF>(tile_read(t, 64 * s4), a0, a1);
+                fp8x16_to_bf16x8x2<XF>(xb[u][s4], b0, b1);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc, 0, 0, 0);
+            }
+        }
+    }
+    if (!ks_reduce<KS>(acc, red)) return;
+    if (mi < M) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t n = n0 + 4 * mg + r;
+            if (n < N) {
+                float v = acc[r] * xs[mi * xs_step];
+                v = v * ws[n * ws_step];
+                y[mi * ldy + n] = f32_to_bf16(v);
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------------ block-scaled FP8 (v_mfma_f32_16x16x32_bf16)
 // Both operands are E4M3 codes (weights from the tile, activations from the
 // block quantiser); each is widened to bf16 (exact) and multiplied on the

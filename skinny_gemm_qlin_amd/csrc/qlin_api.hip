@@ -16,6 +16,7 @@ inline bool misaligned(const void* p, uintptr_t a) { return ((uintptr_t)p) % a !
 inline int launch_status(hipError_t e) { return e == hipSuccess ? QLIN_OK : QLIN_ERR_LAUNCH; }
 
 constexpr int64_t kMaxKInt8 = 131072;  // K * 127 * 128 < 2^31: int32 accumulation is exact
+constexpr int64_t kMaxKFp8 = 1 << 24;  // keeps the quantiser's 32-bit vector indexes in range
 
 }  // namespace
 
@@ -79,6 +80,35 @@ int qlin_gemv_fp8(const void* x, int64_t ldx, int64_t M, int64_t K,
         return QLIN_ERR_ALIGN;
     qlin::F8Args a{(const uint16_t*)x, ldx, M, K, w, ldw, N, ws, ws_per_row ? 1 : 0, (uint16_t*)y, ldy};
     return launch_status(qlin::launch_gemv_fp8(a, (hipStream_t)stream));
+}
+
+int qlin_act_quant_fp8(const void* x, int64_t ldx, int64_t M, int64_t K, int fmt, int per_token,
+                       uint8_t* xq, int64_t ldxq, float* xs, void* stream) {
+    if ((fmt != QLIN_FMT_E4M3 && fmt != QLIN_FMT_E5M2) || (per_token != 0 && per_token != 1)) return QLIN_ERR_ARG;
+    if (!x || !xq || !xs) return QLIN_ERR_NULL;
+    if (M < 1 || M > QLIN_MAX_M || K < 16 || K % 16 != 0 || K > kMaxKFp8) return QLIN_ERR_SHAPE;
+    if (ldx < K || ldxq < K) return QLIN_ERR_STRIDE;
+    if (misaligned(x, 16) || ldx % 8 != 0 || misaligned(xq, 16) || ldxq % 16 != 0 || misaligned(xs, 4))
+        return QLIN_ERR_ALIGN;
+    qlin::ActQuantF8Args a{(const uint16_t*)x, ldx, M, K, fmt, per_token, xq, ldxq, xs};
+    return launch_status(qlin::launch_act_quant_fp8(a, (hipStream_t)stream));
+}
+
+int qlin_gemv_fp8_w8a8(const uint8_t* xq, int64_t ldxq, const float* xs, int xs_per_token, int x_fmt,
+                       int64_t M, int64_t K, const uint8_t* w, int64_t ldw, int64_t N,
+                       const float* ws, int ws_per_row, int w_fmt, void* y, int64_t ldy, void* stream) {
+    if ((x_fmt != QLIN_FMT_E4M3 && x_fmt != QLIN_FMT_E5M2) || (w_fmt != QLIN_FMT_E4M3 && w_fmt != QLIN_FMT_E5M2))
+        return QLIN_ERR_ARG;
+    if ((xs_per_token != 0 && xs_per_token != 1) || (ws_per_row != 0 && ws_per_row != 1)) return QLIN_ERR_ARG;
+    if (!xq || !xs || !w || !ws || !y) return QLIN_ERR_NULL;
+    if (M < 1 || M > QLIN_MAX_M || N < 1 || K < 16 || K % 16 != 0 || K > kMaxKFp8) return QLIN_ERR_SHAPE;
+    if (ldxq < K || ldw < K || ldy < N) return QLIN_ERR_STRIDE;
+    if (misaligned(xq, 16) || ldxq % 16 != 0 || misaligned(w, 16) || ldw % 16 != 0 || misaligned(xs, 4) ||
+        misaligned(ws, 4) || misaligned(y, 2))
+        return QLIN_ERR_ALIGN;
+    qlin::W8A8F8Args a{xq, ldxq, xs, xs_per_token ? 1 : 0, x_fmt, M, K, w, ldw, N,
+                       ws, ws_per_row ? 1 : 0, w_fmt, (uint16_t*)y, ldy};
+    return launch_status(qlin::launch_gemv_fp8_w8a8(a, (hipStream_t)stream));
 }
 
 int qlin_gemv_fp8_blk(const void* x, int64_t ldx, int64_t M, int64_t K,

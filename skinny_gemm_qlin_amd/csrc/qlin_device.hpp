@@ -5,6 +5,8 @@
 //   E4M3   OCP fp8 (bias 7, no infinities, max 448), converted by the
 //          gfx950 hardware converts v_cvt_scalef32_pk_bf16_fp8 /
 //          v_cvt_pk_fp8_f32;
+//   E5M2   OCP bf8 (bias 15, max 57344), v_cvt_scalef32_pk_bf16_bf8 /
+//          v_cvt_pk_bf8_f32;
 //   E2M1   OCP fp4 element, converted by v_cvt_scalef32_pk_bf16_fp4;
 //   UE8M0  scale byte b meaning 2^(b-127) (byte 255 = NaN), built directly
 //          as fp32 bits.
@@ -42,6 +44,30 @@ __device__ __forceinline__ float ue8m0_to_f32(uint32_t b) {
 __device__ __forceinline__ void e4m3x4_to_bf16(uint32_t d, bf16x2_t& lo, bf16x2_t& hi) {
     lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.0f, false);
     hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.0f, true);
+}
+
+// FP8 code formats of the W8A8 path (values of the C ABI's fmt arguments).
+constexpr int kFmtE4M3 = 0;
+constexpr int kFmtE5M2 = 1;
+
+// Four FP8 codes of format F -> two bf16 pairs, exact (both formats embed in
+// bf16: at most 3 mantissa bits, exponents within bf16's normal range).
+template <int F>
+__device__ __forceinline__ void fp8x4_to_bf16(uint32_t d, bf16x2_t& lo, bf16x2_t& hi) {
+    if constexpr (F == kFmtE5M2) {
+        lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(d, 1.0f, false);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(d, 1.0f, true);
+    } else {
+        e4m3x4_to_bf16(d, lo, hi);
+    }
+}
+
+// Two fp32 values -> two FP8 codes of format F (round to nearest even) in
+// the low (HI = false) or high 16 bits of `old`.
+template <int F, bool HI>
+__device__ __forceinline__ int f32x2_to_fp8(float a, float b, int old) {
+    if constexpr (F == kFmtE5M2) return __builtin_amdgcn_cvt_pk_bf8_f32(a, b, old, HI);
+    else return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
 }
 
 // Eight E2M1 codes (one dword, element 2i in the low nibble of byte i) ->

@@ -13,6 +13,17 @@ struct ActQuantI8Args {
     int8_t* xq; int64_t ldxq; float* xs;
 };
 
+struct ActQuantF8Args {
+    const uint16_t* x; int64_t ldx; int64_t M; int64_t K; int fmt; int per_token;
+    uint8_t* xq; int64_t ldxq; float* xs;
+};
+
+struct W8A8F8Args {
+    const uint8_t* xq; int64_t ldxq; const float* xs; int xs_step; int x_fmt;
+    int64_t M; int64_t K; const uint8_t* w; int64_t ldw; int64_t N;
+    const float* ws; int ws_step; int w_fmt; uint16_t* y; int64_t ldy;
+};
+
 struct I8Args {
     const int8_t* xq; int64_t ldxq; const float* xs; int xs_step;
     int64_t M; int64_t K; const int8_t* w; int64_t ldw; int64_t N;
@@ -44,6 +55,8 @@ struct MoeArgs {
 hipError_t launch_act_quant_i8(const ActQuantI8Args& a, hipStream_t st);
 hipError_t launch_gemv_i8(const I8Args& a, hipStream_t st);
 hipError_t launch_gemv_fp8(const F8Args& a, hipStream_t st);
+hipError_t launch_act_quant_fp8(const ActQuantF8Args& a, hipStream_t st);
+hipError_t launch_gemv_fp8_w8a8(const W8A8F8Args& a, hipStream_t st);
 hipError_t launch_blk_act_quant(const BlkQuantArgs& a, hipStream_t st);
 hipError_t launch_gemv_fp8_blk(const BlkArgs& a, hipStream_t st);
 hipError_t launch_moe_mxfp4(const MoeArgs& a, hipStream_t st);

@@ -21,8 +21,8 @@ from typing import Optional, Tuple
 
 import torch
 
-from . import (qlin_act_quant_i8, qlin_gemv_fp8, qlin_gemv_fp8_blk, qlin_gemv_i8, qlin_moe_ffn_mxfp4,
-               qlin_moe_mxfp4)
+from . import (qlin_act_quant_fp8, qlin_act_quant_i8, qlin_gemv_fp8, qlin_gemv_fp8_blk, qlin_gemv_fp8_w8a8,
+               qlin_gemv_i8, qlin_moe_ffn_mxfp4, qlin_moe_mxfp4)
 
 hits = collections.Counter()
 
@@ -81,6 +81,46 @@ def gemv_fp8(x: torch.Tensor, w: torch.Tensor, ws: torch.Tensor) -> torch.Tensor
 
 @gemv_fp8.register_fake
 def _(x, w, ws):
+    return x.new_empty((x.shape[0], w.shape[0]), dtype=torch.bfloat16)
+
+
+# ----------------------------------------------------------------------------- FP8 W8A8 (fmt 0 = E4M3, 1 = E5M2)
+
+@torch.library.custom_op("qlin::act_quant_fp8", mutates_args=())
+def act_quant_fp8(x: torch.Tensor, fmt: int = 0, per_token: bool = True) -> Tuple[torch.Tensor, torch.Tensor]:
+    hits["act_quant_fp8"] += 1
+    return qlin_act_quant_fp8(x, fmt, per_token)
+
+
+@act_quant_fp8.register_fake
+def _(x, fmt=0, per_token=True):
+    M, K = x.shape
+    return x.new_empty((M, K), dtype=torch.uint8), x.new_empty((M if per_token else 1,), dtype=torch.float32)
+
+
+@torch.library.custom_op("qlin::gemv_fp8_w8a8", mutates_args=())
+def gemv_fp8_w8a8(xq: torch.Tensor, xs: torch.Tensor, w: torch.Tensor, ws: torch.Tensor, x_fmt: int = 0,
+                  w_fmt: int = 0) -> torch.Tensor:
+    hits["gemv_fp8_w8a8"] += 1
+    return qlin_gemv_fp8_w8a8(xq, xs, w, ws, x_fmt, w_fmt)
+
+
+@gemv_fp8_w8a8.register_fake
+def _(xq, xs, w, ws, x_fmt=0, w_fmt=0):
+    return xq.new_empty((xq.shape[0], w.shape[0]), dtype=torch.bfloat16)
+
+
+@torch.library.custom_op("qlin::linear_fp8_w8a8", mutates_args=())
+def linear_fp8_w8a8(x: torch.Tensor, w: torch.Tensor, ws: torch.Tensor, x_fmt: int = 0, w_fmt: int = 0,
+                    per_token: bool = True) -> torch.Tensor:
+    """Dynamic FP8 activation quantisation followed by the W8A8 GEMV (two kernels)."""
+    hits["linear_fp8_w8a8"] += 1
+    xq, xs = qlin_act_quant_fp8(x, x_fmt, per_token)
+    return qlin_gemv_fp8_w8a8(xq, xs, w, ws, x_fmt, w_fmt)
+
+
+@linear_fp8_w8a8.register_fake
+def _(x, w, ws, x_fmt=0, w_fmt=0, per_token=True):
     return x.new_empty((x.shape[0], w.shape[0]), dtype=torch.bfloat16)
 
 

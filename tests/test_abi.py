@@ -107,6 +107,55 @@ def test_gemv_fp8_errors(q):
     assert call(ldw=5120 + 4) == -4
 
 
+def test_act_quant_fp8_errors(q):
+    def call(x=A, ldx=1024, M=1, K=1024, fmt=0, pt=1, xq=A, ldxq=1024, xs=A):
+        return q.qlin_act_quant_fp8(x, ldx, M, K, fmt, pt, xq, ldxq, xs, None)
+    assert call(fmt=2) == -6
+    assert call(fmt=-1) == -6
+    assert call(pt=2) == -6
+    assert call(x=None) == -1
+    assert call(xq=None) == -1
+    assert call(xs=None) == -1
+    assert call(M=0) == -2
+    assert call(M=17) == -2
+    assert call(K=1000) == -2
+    assert call(K=(1 << 24) + 16, ldx=(1 << 24) + 16, ldxq=(1 << 24) + 16) == -2
+    assert call(ldx=512) == -3
+    assert call(ldxq=1000) == -3
+    assert call(x=A + 2) == -4
+    assert call(ldx=1028) == -4
+    assert call(xq=A + 8) == -4
+    assert call(ldxq=1032) == -4
+    assert call(xs=A + 2) == -4
+
+
+def test_gemv_fp8_w8a8_errors(q):
+    def call(xq=A, ldxq=1024, xs=A, xpt=1, xf=0, M=1, K=1024, w=A, ldw=1024, N=64, ws=A, wpr=1, wf=0,
+             y=A, ldy=64):
+        return q.qlin_gemv_fp8_w8a8(xq, ldxq, xs, xpt, xf, M, K, w, ldw, N, ws, wpr, wf, y, ldy, None)
+    assert call(xf=2) == -6
+    assert call(wf=7) == -6
+    assert call(xpt=-1) == -6
+    assert call(wpr=2) == -6
+    for name in ("xq", "xs", "w", "ws", "y"):
+        assert call(**{name: None}) == -1
+    assert call(M=0) == -2
+    assert call(M=17) == -2
+    assert call(N=0) == -2
+    assert call(K=8, ldxq=16, ldw=16) == -2
+    assert call(K=1032, ldxq=1040, ldw=1040) == -2
+    assert call(ldxq=1008) == -3
+    assert call(ldw=1008) == -3
+    assert call(ldy=63) == -3
+    assert call(xq=A + 8) == -4
+    assert call(ldxq=1032) == -4
+    assert call(w=A + 4) == -4
+    assert call(ldw=1024 + 4) == -4
+    assert call(xs=A + 1) == -4
+    assert call(ws=A + 2) == -4
+    assert call(y=A + 1) == -4
+
+
 def test_gemv_fp8_blk_errors(q):
     def call(x=A, ldx=7168, M=1, K=7168, w=A, ldw=7168, N=256, ws=A, xq=A, xs=A, y=A, ldy=256):
         return q.qlin_gemv_fp8_blk(x, ldx, M, K, w, ldw, N, ws, xq, xs, y, ldy, None)

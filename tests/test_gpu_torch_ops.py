@@ -8,7 +8,7 @@ import pytest
 import torch
 
 from gpu_util import dev, dev_bf16, lib, need_gpu
-from skinny_gemm_qlin_amd.inputs import gen_fp8, gen_fp8_blk, gen_int8, gen_moe, gen_moe_ffn
+from skinny_gemm_qlin_amd.inputs import gen_fp8, gen_fp8_blk, gen_fp8_w8a8, gen_int8, gen_moe, gen_moe_ffn
 
 pytestmark = pytest.mark.gpu
 
@@ -26,7 +26,9 @@ def args(ql):
     db = gen_fp8_blk(5, 256, 1024, seed=3)
     dm = gen_moe(4, 8, 128, 512, 2, seed=4)
     dn = gen_moe_ffn(4, 8, 256, 64, 2, seed=5)
+    dw = gen_fp8_w8a8(6, 256, 1024, w_fmt=1, seed=6)
     return {
+        "linear_fp8_w8a8": (dev_bf16(dw["x"]), dev(dw["w"]), dev(dw["ws"]), 0, 1, True),
         "linear_i8": (dev_bf16(d8["x"]), dev(d8["w"]), dev(d8["ws"])),
         "gemv_fp8": (dev_bf16(df["x"]), dev(df["w"]), dev(df["ws"])),
         "gemv_fp8_blk": (dev_bf16(db["x"]), dev(db["w"]), dev(db["ws"])),
@@ -44,7 +46,12 @@ def test_opcheck_every_operator(ql, args):
     import skinny_gemm_qlin_amd.torch_ops  # noqa: F401
     x8, w8, ws8 = args["linear_i8"]
     xq, xs = torch.ops.qlin.act_quant_i8(x8)
+    xw, ww, wsw = args["linear_fp8_w8a8"][:3]
+    xq8, xs8 = torch.ops.qlin.act_quant_fp8(xw, 0, True)
     cases = [(torch.ops.qlin.act_quant_i8.default, (x8,)),
+             (torch.ops.qlin.act_quant_fp8.default, (xw, 1, False)),
+             (torch.ops.qlin.gemv_fp8_w8a8.default, (xq8, xs8, ww, wsw, 0, 1)),
+             (torch.ops.qlin.linear_fp8_w8a8.default, args["linear_fp8_w8a8"]),
              (torch.ops.qlin.gemv_i8.default, (xq, xs, w8, ws8)),
              (torch.ops.qlin.linear_i8.default, args["linear_i8"]),
              (torch.ops.qlin.gemv_fp8.default, args["gemv_fp8"]),
@@ -58,15 +65,17 @@ def test_opcheck_every_operator(ql, args):
 def test_compiled_layer_equals_eager_and_reaches_every_kernel(ql, args):
     import skinny_gemm_qlin_amd.torch_ops as tops
 
-    def layer(a8, af, ab, am, an):
+    def layer(a8, af, ab, am, an, aw):
         r0 = torch.ops.qlin.linear_i8(*a8)
         r1 = torch.ops.qlin.gemv_fp8(*af)
         r2 = torch.ops.qlin.gemv_fp8_blk(*ab)
         r3 = torch.ops.qlin.moe_mxfp4(*am)
         y, ids, gw = torch.ops.qlin.moe_ffn_mxfp4(*an)
-        return r0, r1, r2, r3, y, ids, gw
+        r4 = torch.ops.qlin.linear_fp8_w8a8(*aw)
+        return r0, r1, r2, r3, y, ids, gw, r4
 
-    a = (args["linear_i8"], args["gemv_fp8"], args["gemv_fp8_blk"], args["moe_mxfp4"], args["moe_ffn_mxfp4"])
+    a = (args["linear_i8"], args["gemv_fp8"], args["gemv_fp8_blk"], args["moe_mxfp4"], args["moe_ffn_mxfp4"],
+         args["linear_fp8_w8a8"])
     eager = layer(*a)
     torch.cuda.synchronize()
 
@@ -76,6 +85,8 @@ def test_compiled_layer_equals_eager_and_reaches_every_kernel(ql, args):
     ref = [ql.qlin_gemv_i8(xq, xs, w8, ws8), ql.qlin_gemv_fp8(*args["gemv_fp8"]),
            ql.qlin_gemv_fp8_blk(*args["gemv_fp8_blk"])[0], ql.qlin_moe_mxfp4(*args["moe_mxfp4"]),
            *ql.qlin_moe_ffn_mxfp4(*args["moe_ffn_mxfp4"])]
+    xw, ww, wsw, xf, wf, pt = args["linear_fp8_w8a8"]
+    ref.append(ql.qlin_gemv_fp8_w8a8(*ql.qlin_act_quant_fp8(xw, xf, pt), ww, wsw, xf, wf))
     torch.cuda.synchronize()
     for e, r in zip(eager, ref):
         assert torch.equal(_bits(e), _bits(r))
@@ -90,7 +101,7 @@ def test_compiled_layer_equals_eager_and_reaches_every_kernel(ql, args):
         for e, c in zip(eager, out):
             assert torch.equal(_bits(e), _bits(c))
     assert dict(tops.hits) == {"linear_i8": 3, "gemv_fp8": 3, "gemv_fp8_blk": 3, "moe_mxfp4": 3,
-                               "moe_ffn_mxfp4": 3}
+                               "moe_ffn_mxfp4": 3, "linear_fp8_w8a8": 3}
 
 
 def test_one_dynamic_graph_serves_every_M(ql):

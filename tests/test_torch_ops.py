@@ -43,6 +43,14 @@ def test_fake_shapes_and_dtypes():
                   torch.ops.qlin.gemv_fp8_blk(d["x"], d["wf8"], d["wsb"]),
                   torch.ops.qlin.moe_mxfp4(d["x"], d["wm"], d["sm"], d["ids"], d["gw"])):
             assert y.shape == (3, 256) and y.dtype == torch.bfloat16
+        for fmt in (0, 1):
+            for per_token, ns in ((True, 3), (False, 1)):
+                xq8, xs8 = torch.ops.qlin.act_quant_fp8(d["x"], fmt, per_token)
+                assert xq8.shape == (3, 512) and xq8.dtype == torch.uint8
+                assert xs8.shape == (ns,) and xs8.dtype == torch.float32
+        for y in (torch.ops.qlin.gemv_fp8_w8a8(d["wf8"][:3], d["xs"], d["wf8"], d["ws"], 1, 0),
+                  torch.ops.qlin.linear_fp8_w8a8(d["x"], d["wf8"], d["ws"], 0, 1, False)):
+            assert y.shape == (3, 256) and y.dtype == torch.bfloat16
         y, ids, gw = torch.ops.qlin.moe_ffn_mxfp4(d["xh"], d["wr"], d["w13"], d["s13"], d["w2"], d["s2"], 2)
         assert y.shape == (3, 256) and y.dtype == torch.bfloat16
         assert ids.shape == (3, 2) and ids.dtype == torch.int32 and gw.shape == (3, 2) and gw.dtype == torch.float32
@@ -53,12 +61,13 @@ def test_traced_graph_keeps_the_operators_opaque():
 
     def layer(x, w8, ws, wf8, wsb):
         return torch.ops.qlin.linear_i8(x, w8, ws) + torch.ops.qlin.gemv_fp8(x, wf8, ws) \
-            + torch.ops.qlin.gemv_fp8_blk(x, wf8, wsb)
+            + torch.ops.qlin.gemv_fp8_blk(x, wf8, wsb) + torch.ops.qlin.linear_fp8_w8a8(x, wf8, ws)
 
     g = make_fx(layer, tracing_mode="fake")(d["x"], d["w8"], d["ws"], d["wf8"], d["wsb"])
     targets = [str(n.target) for n in g.graph.nodes if n.op == "call_function"]
     assert "qlin.linear_i8.default" in targets
     assert "qlin.gemv_fp8.default" in targets
     assert "qlin.gemv_fp8_blk.default" in targets
-    # nothing else computes the products: only the two adds remain
-    assert sorted(t for t in targets if not t.startswith("qlin.")) == ["aten.add.Tensor", "aten.add.Tensor"]
+    assert "qlin.linear_fp8_w8a8.default" in targets
+    # nothing else computes the products: only the three adds remain
+    assert sorted(t for t in targets if not t.startswith("qlin.")) == ["aten.add.Tensor"] * 3
