@@ -179,10 +179,11 @@ __device__ __forceinline__ uint2 quant_fp8x8(const u32x4_t& v, float amax, float
 // first C of them stay in registers between the amax pass and the quantise
 // pass (M*K <= 8*T*C values are read from HBM once).  The amax is reduced
 // with DPP within a 16-lane row, shuffles across a wave and LDS across waves.
-template <int F, int T, int C>
+template <int F, int T, int C, bool ONE_ROW>
 __global__ __launch_bounds__(T) void act_quant_fp8_kernel(
-    const uint16_t* __restrict__ x, int64_t ldx, int rows, int64_t K,
+    const uint16_t* __restrict__ x, int64_t ldx, int rows_arg, int64_t K,
     uint8_t* __restrict__ xq, int64_t ldxq, float* __restrict__ xs) {
+    const int rows = ONE_ROW ? 1 : rows_arg;  // per-token: no row split of the vector index
     constexpr int W = T / 64;
     constexpr float fmax = F == kFmtE5M2 ? 57344.0f : 448.0f;
     __shared__ float wave_max[W];
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(T) void act_quant_fp8_kernel(
     for (int c = 0; c < C; ++c) {
         const int i = tid + c * T;
         if (i < total) {
-            const int r = i / nvec, v = i - r * nvec;
+            const int r = ONE_ROW ? 0 : i / nvec, v = i - r * nvec;
             cache[c] = ld16(x + (m0 + r) * ldx + (int64_t)v * 8);
         } else {
             cache[c] = u32x4_t{0, 0, 0, 0};
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(T) void act_quant_fp8_kernel(
         a = absmax8(cache[c], a);
     }
     for (int i = tid + C * T; i < total; i += T) {
-        const int r = i / nvec, v = i - r * nvec;
+        const int r = ONE_ROW ? 0 : i / nvec, v = i - r * nvec;
         a = absmax8(ld16(x + (m0 + r) * ldx + (int64_t)v * 8), a);
     }
     a = row_max_f32(a);
@@ -223,12 +224,12 @@ __global__ __launch_bounds__(T) void act_quant_fp8_kernel(
     for (int c = 0; c < C; ++c) {
         const int i = tid + c * T;
         if (i < total) {
-            const int r = i / nvec, v = i - r * nvec;
+            const int r = ONE_ROW ? 0 : i / nvec, v = i - r * nvec;
             *(uint2*)(xq + (m0 + r) * ldxq + (int64_t)v * 8) = quant_fp8x8<F>(cache[c], amax, s);
         }
     }
     for (int i = tid + C * T; i < total; i += T) {
-        const int r = i / nvec, v = i - r * nvec;
+        const int r = ONE_ROW ? 0 : i / nvec, v = i - r * nvec;
         *(uint2*)(xq + (m0 + r) * ldxq + (int64_t)v * 8) =
             quant_fp8x8<F>(ld16(x + (m0 + r) * ldx + (int64_t)v * 8), amax, s);
     }
@@ -237,10 +238,10 @@ __global__ __launch_bounds__(T) void act_quant_fp8_kernel(
 template <int F>
 hipError_t launch_act_quant_fp8_fmt(const ActQuantF8Args& a, hipStream_t st) {
     if (a.per_token)
-        hipLaunchKernelGGL((act_quant_fp8_kernel<F, 256, 4>), dim3((unsigned)a.M), dim3(256), 0, st, a.x, a.ldx, 1,
+        hipLaunchKernelGGL((act_quant_fp8_kernel<F, 256, 4, true>), dim3((unsigned)a.M), dim3(256), 0, st, a.x, a.ldx, 1,
                            a.K, a.xq, a.ldxq, a.xs);
     else
-        hipLaunchKernelGGL((act_quant_fp8_kernel<F, 1024, 16>), dim3(1), dim3(1024), 0, st, a.x, a.ldx, (int)a.M,
+        hipLaunchKernelGGL((act_quant_fp8_kernel<F, 1024, 16, false>), dim3(1), dim3(1024), 0, st, a.x, a.ldx, (int)a.M,
                            a.K, a.xq, a.ldxq, a.xs);
     return hipGetLastError();
 }
