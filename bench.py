@@ -85,35 +85,40 @@ def bytes_moe_ffn_call(M, H, I, E, topk, live):
 
 # ----------------------------------------------------------------------------- workloads
 
-# translation units whose kernels each workload runs
+# translation units of the kernels the roofline's traffic figure covers (the
+# dominant kernel of each workload; the whole call for block FP8, the MoE
+# and the expert FFN)
 KERNEL_SOURCES = {
-    "int8_decode": ("act_quant.hip", "gemv.hip"),
+    "int8_decode": ("gemv.hip",),
     "fp8_decode": ("gemv.hip",),
-    "fp8_w8a8": ("act_quant.hip", "gemv.hip"),
+    "fp8_w8a8": ("gemv.hip",),
     "fp8_blk": ("act_quant.hip", "gemv.hip"),
     "moe_mxfp4": ("moe.hip",),
     "moe_ffn_mxfp4": ("moe.hip", "routing.hip"),
 }
 
 
-def src_hash(workload):
-    """Hash of the device code a workload runs: its translation units and the
-    local headers they include, transitively.  qlin_launch.hpp (host-side
-    declarations of every launcher) is left out, so that adding an entry point
-    elsewhere does not invalidate this workload's counters."""
+def src_hash(workload, read=None):
+    """Hash of the device code behind a workload's traffic figure: its
+    translation units and the local headers they include, transitively.
+    qlin_launch.hpp (host-side declarations of every launcher) is left out,
+    so that adding an entry point elsewhere does not invalidate the counters.
+    `read(name) -> bytes` reads a source file (default: the working tree)."""
     csrc = os.path.join(ROOT, "skinny_gemm_qlin_amd", "csrc")
-    todo, seen = list(KERNEL_SOURCES[workload]), set()
+    if read is None:
+        def read(name):
+            with open(os.path.join(csrc, name), "rb") as fh:
+                return fh.read()
+    todo, seen, h = list(KERNEL_SOURCES[workload]), set(), hashlib.sha256()
     while todo:
         f = todo.pop()
         if f in seen or f == "qlin_launch.hpp":
             continue
         seen.add(f)
-        text = open(os.path.join(csrc, f)).read()
-        todo += re.findall(r'^#include "([A-Za-z0-9_.]+)"', text, re.M)
-    h = hashlib.sha256()
+        todo += re.findall(r'^#include "([A-Za-z0-9_.]+)"', read(f).decode(), re.M)
     for f in sorted(seen):
         h.update(f.encode())
-        h.update(open(os.path.join(csrc, f), "rb").read())
+        h.update(read(f))
     return h.hexdigest()[:16]
 
 
