@@ -36,7 +36,11 @@
  *   output is touched.  QLIN_ERR_LAUNCH reports a HIP launch failure.
  * - Device-resident data is not validated (that would need a host sync):
  *   NaN/Inf inputs give unspecified outputs; see each call for the rest.
- * - M (tokens) must be in [1, 16].  Base pointers and row pitches of
+ * - M (tokens): the dense entry points (INT8, FP8, FP8 W8A8, block FP8 and
+ *   their quantisers) accept 1 <= M <= QLIN_MAX_M_PREFILL; up to 16 they run
+ *   the decode GEMV kernels, above 16 a tiled matrix-core GEMM with the same
+ *   arithmetic contract.  The MoE entry points and the per-tensor FP8
+ *   quantiser take 1 <= M <= QLIN_MAX_M.  Base pointers and row pitches of
  *   weights, codes and bf16 activations must be 16-byte aligned (128-bit
  *   loads); scale arrays must be naturally aligned.
  */
@@ -62,6 +66,7 @@ enum {
 };
 
 #define QLIN_MAX_M 16
+#define QLIN_MAX_M_PREFILL 16384
 
 /* FP8 code formats (OCP 8-bit floating point) of the W8A8 FP8 entry points. */
 enum {
@@ -137,8 +142,9 @@ int qlin_gemv_fp8(const void* x, int64_t ldx, int64_t M, int64_t K,
  * fp8_rne rounds to the nearest finite code, ties to the even code, and a
  * quotient above fmax (a rounding excess) saturates to +-fmax.  A zero
  * amax gives s = 0 and codes 0.  Inputs must be finite.
- * Requires K % 16 == 0, 16 <= K <= 2^24, ldx % 8 == 0, ldxq % 16 == 0;
- * fmt is QLIN_FMT_E4M3 or QLIN_FMT_E5M2 and per_token 0 or 1 (else
+ * Requires K % 16 == 0, 16 <= K <= 2^24, ldx % 8 == 0, ldxq % 16 == 0,
+ * M <= QLIN_MAX_M when per_token = 0 (one workgroup reduces the whole
+ * tensor); fmt is QLIN_FMT_E4M3 or QLIN_FMT_E5M2 and per_token 0 or 1 (else
  * QLIN_ERR_ARG). */
 int qlin_act_quant_fp8(const void* x, int64_t ldx, int64_t M, int64_t K, int fmt, int per_token,
                        uint8_t* xq, int64_t ldxq, float* xs, void* stream);

@@ -1,0 +1,48 @@
+// gemm.hip -- launchers of the prefill GEMM (gemm_kernels.hpp), used by the
+// dense entry points when M > 16.
+#include "gemm_kernels.hpp"
+#include "qlin_launch.hpp"
+
+namespace qlin {
+
+namespace {
+
+template <int WF, int ACT, int EPI>
+hipError_t run_gemm(const GemmParams& p, hipStream_t st) {
+    const int64_t tiles = ((p.M + kGemmBM - 1) / kGemmBM) * ((p.N + kGemmBN - 1) / kGemmBN);
+    const int64_t grid = (tiles + 7) / 8 * 8;  // the XCD remap needs a multiple of 8
+    hipLaunchKernelGGL((gemm_kernel<WF, ACT, EPI>), dim3((unsigned)grid), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_i8(const I8Args& a, hipStream_t st) {
+    GemmParams p{a.xq, a.ldxq, a.xs, a.xs_step, nullptr, a.M, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step,
+                 nullptr, a.bias, a.y, a.ldy, a.out_kind};
+    return run_gemm<kFmtE4M3, kActI8, kEpiI8>(p, st);
+}
+
+hipError_t launch_gemm_fp8(const F8Args& a, hipStream_t st) {
+    GemmParams p{a.x, a.ldx, nullptr, 0, nullptr, a.M, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step,
+                 nullptr, nullptr, a.y, a.ldy, 0};
+    return run_gemm<kFmtE4M3, kActBf16, kEpiWs>(p, st);
+}
+
+hipError_t launch_gemm_fp8_w8a8(const W8A8F8Args& a, hipStream_t st) {
+    GemmParams p{a.xq, a.ldxq, a.xs, a.xs_step, nullptr, a.M, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step,
+                 nullptr, nullptr, a.y, a.ldy, 0};
+    if (a.x_fmt == kFmtE5M2)
+        return a.w_fmt == kFmtE5M2 ? run_gemm<kFmtE5M2, kActE5M2, kEpiXsWs>(p, st)
+                                   : run_gemm<kFmtE4M3, kActE5M2, kEpiXsWs>(p, st);
+    return a.w_fmt == kFmtE5M2 ? run_gemm<kFmtE5M2, kActE4M3, kEpiXsWs>(p, st)
+                               : run_gemm<kFmtE4M3, kActE4M3, kEpiXsWs>(p, st);
+}
+
+hipError_t launch_gemm_fp8_blk(const BlkArgs& a, hipStream_t st) {
+    GemmParams p{a.xq, a.K, nullptr, 0, a.xs, a.M, a.K, a.w, a.ldw, a.N, nullptr, 0,
+                 a.ws, nullptr, a.y, a.ldy, 0};
+    return run_gemm<kFmtE4M3, kActE4M3, kEpiBlk>(p, st);
+}
+
+}  // namespace qlin

@@ -1,0 +1,241 @@
+// gemm_kernels.hpp -- tiled matrix-core GEMM for prefill-sized M (> 16),
+// the same four dense contracts as the decode kernels:
+//   INT8 W8A8        y = bf16((acc * xs[m]) * ws[n]) (+ bias), acc exact int32
+//                    [Z100 operator-family table, INT8 row; section 2.1]
+//   FP8 weight-only  y = bf16(ws[n] * sum_k fp8(w) * x)        [FP8 row; 2.2]
+//   FP8 W8A8         y = bf16((acc * xs[m]) * ws[n])           [FP8 row; 2.2]
+//   block FP8        y = bf16(sum_kb (D_kb * 2^(ws-127)) * 2^(xs-127))
+//                    [Z100 section 2.4: per-block fold; DSV4 section 3.3]
+//
+// Tiling: a 256-lane workgroup owns a 128 (weight rows n) x 128 (tokens m)
+// output tile; its 4 waves split it 2 x 2, each wave 64 x 64 = 4 x 4 MFMA
+// tiles of 16 x 16 (A operand = weight rows, B operand = token rows, so a
+// lane's 4 accumulator registers are 4 consecutive n of one token).  K runs
+// in tiles of 64 elements, double-buffered through LDS: the global loads of
+// tile k+1 (16 bytes per lane per load, row-contiguous) are in flight while
+// tile k is multiplied, then stored to the other LDS buffer; one barrier per
+// K tile.  FP8 codes are widened to bf16 (exact) as fragments are read from
+// LDS and multiplied on the bf16 matrix core with fp32 accumulation (the
+// fp8 matrix-core instructions sum with ~13 bits, see the decode kernels);
+// INT8 uses v_mfma_i32_16x16x64_i8 (exact).
+//
+// Rows past M or N are loaded clamped (results not stored); K chunks past K
+// are zero-filled (K % 16 == 0 keeps every 16-byte chunk whole).  Workgroup
+// ids are remapped so that each XCD (ids are dealt to the 8 XCDs round
+// robin) runs a contiguous range of tiles, M-fastest, so the workgroups
+// that share a weight tile share that XCD's L2.
+#pragma once
+#include <type_traits>
+
+#include "mfma_kernels.hpp"
+
+namespace qlin {
+
+enum GemmAct { kActBf16 = 0, kActE4M3 = 1, kActE5M2 = 2, kActI8 = 3 };
+enum GemmEpi { kEpiI8 = 0, kEpiWs = 1, kEpiXsWs = 2, kEpiBlk = 3 };
+
+struct GemmParams {
+    const void* x; int64_t ldx;          // activations [M][ldx]: bf16, FP8 or int8 codes
+    const float* xs; int xs_step;        // INT8 / W8A8: activation scale [M] or [1]
+    const uint8_t* xsb;                  // block FP8: UE8M0 [M][K/128]
+    int64_t M, K;
+    const void* w; int64_t ldw; int64_t N;  // weight codes [N][ldw]
+    const float* ws; int ws_step;        // weight scale [N] or [1]
+    const uint8_t* wsb;                  // block FP8: UE8M0 [ceil(N/128)][K/128]
+    const uint16_t* bias;                // INT8: bf16 [N] or null
+    void* y; int64_t ldy; int out_kind;  // bf16 [M][ldy] (INT8 out_kind 1: int32 acc)
+};
+
+constexpr int kGemmBM = 128, kGemmBN = 128, kGemmBK = 64;
+
+// 8 FP8 codes (one uint2) of format F -> bf16x8, exact.
+template <int F>
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint2 c) {
+    bf16x2_t b[4];
+    fp8x4_to_bf16<F>(c.x, b[0], b[1]);
+    fp8x4_to_bf16<F>(c.y, b[2], b[3]);
+    return bf16x8_t{b[0][0], b[0][1], b[1][0], b[1][1], b[2][0], b[2][1], b[3][0], b[3][1]};
+}
+
+template <int WF, int ACT, int EPI>
+__global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
+    constexpr bool kI8 = ACT == kActI8;
+    constexpr int XB = ACT == kActBf16 ? 2 : 1;       // bytes per activation element
+    constexpr int WP = kGemmBK + 16;                  // LDS row pitch, weight tile (bytes)
+    constexpr int XP = kGemmBK * XB + 16;             // LDS row pitch, activation tile
+    constexpr int WCH = kGemmBN * kGemmBK / 16 / 256; // 16-byte chunks per lane, weight tile
+    constexpr int XCH = kGemmBM * kGemmBK * XB / 16 / 256;
+    constexpr int WCPR = kGemmBK / 16;                // chunks per row
+    constexpr int XCPR = kGemmBK * XB / 16;
+    __shared__ __align__(16) uint8_t wt[2][kGemmBN * WP];
+    __shared__ __align__(16) uint8_t xt[2][kGemmBM * XP];
+
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const int64_t tiles_m = (M + kGemmBM - 1) / kGemmBM;
+    const int64_t tiles = tiles_m * ((N + kGemmBN - 1) / kGemmBN);
+    const int64_t per_xcd = (int64_t)gridDim.x / 8;  // the grid is a multiple of 8
+    const int64_t t = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (t >= tiles) return;  // workgroup-uniform
+    const int64_t n0 = (t / tiles_m) * kGemmBN, m0 = (t % tiles_m) * kGemmBM;
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int wn = wv & 1, wm = wv >> 1;
+    const int li = lane & 15, lg = lane >> 4;
+
+    // global sources of this lane's chunks
+    const uint8_t* wsrc[WCH];
+    int wdst[WCH], wcol[WCH];
+#pragma unroll
+    for (int i = 0; i < WCH; ++i) {
+        const int c = tid + i * 256, r = c / WCPR;
+        const int64_t n = n0 + r < N ? n0 + r : N - 1;
+        wcol[i] = (c % WCPR) * 16;
+        wsrc[i] = (const uint8_t*)p.w + n * p.ldw + wcol[i];
+        wdst[i] = r * WP + wcol[i];
+    }
+    const uint8_t* xsrc[XCH];
+    int xdst[XCH], xcol[XCH];
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+        const int c = tid + i * 256, r = c / XCPR;
+        const int64_t m = m0 + r < M ? m0 + r : M - 1;
+        xcol[i] = (c % XCPR) * 16;
+        xsrc[i] = (const uint8_t*)p.x + (m * p.ldx) * XB + xcol[i];
+        xdst[i] = r * XP + xcol[i];
+    }
+    const int64_t ktiles = (K + kGemmBK - 1) / kGemmBK;
+    u32x4_t wreg[WCH], xreg[XCH];
+    auto gload = [&](int64_t kt) {
+#pragma unroll
+        for (int i = 0; i < WCH; ++i) {
+            const int64_t kb = kt * kGemmBK + wcol[i];  // byte = element offset
+            wreg[i] = kb < K ? ld_stream(wsrc[i] + kt * kGemmBK) : u32x4_t{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < XCH; ++i) {
+            const int64_t ke = kt * kGemmBK + xcol[i] / XB;
+            xreg[i] = ke < K ? ld16(xsrc[i] + kt * kGemmBK * XB) : u32x4_t{0, 0, 0, 0};
+        }
+    };
+    auto lstore = [&](int b) {
+#pragma unroll
+        for (int i = 0; i < WCH; ++i) *(u32x4_t*)(wt[b] + wdst[i]) = wreg[i];
+#pragma unroll
+        for (int i = 0; i < XCH; ++i) *(u32x4_t*)(xt[b] + xdst[i]) = xreg[i];
+    };
+
+    typedef typename std::conditional<kI8, i32x4_t, f32x4_t>::type acc_t;
+    acc_t acc[4][4], dblk[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            acc[i][j] = acc_t{0, 0, 0, 0};
+            dblk[i][j] = acc_t{0, 0, 0, 0};
+        }
+    (void)dblk;
+
+    const int64_t nkb = K >> 7;
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int64_t kt = 0; kt < ktiles; ++kt) {
+        const int b = (int)(kt & 1);
+        if (kt + 1 < ktiles) gload(kt + 1);
+        const uint8_t* W = wt[b] + (wn * 64 + li) * WP;
+        const uint8_t* X = xt[b] + (wm * 64 + li) * XP;
+        if constexpr (kI8) {
+            i32x4_t a[4], bb[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = *(const i32x4_t*)(W + i * 16 * WP + lg * 16);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bb[j] = *(const i32x4_t*)(X + j * 16 * XP + lg * 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], bb[j], acc[i][j], 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < kGemmBK / 32; ++ks) {
+                bf16x8_t a[4], bb[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    a[i] = fp8x8_to_bf16x8<WF>(*(const uint2*)(W + i * 16 * WP + ks * 32 + lg * 8));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if constexpr (ACT == kActBf16)
+                        bb[j] = *(const bf16x8_t*)(X + j * 16 * XP + ks * 64 + lg * 16);
+                    else
+                        bb[j] = fp8x8_to_bf16x8<ACT == kActE5M2 ? kFmtE5M2 : kFmtE4M3>(
+                            *(const uint2*)(X + j * 16 * XP + ks * 32 + lg * 8));
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        if constexpr (EPI == kEpiBlk)
+                            dblk[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bb[j], dblk[i][j], 0, 0, 0);
+                        else
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
+                    }
+            }
+            if constexpr (EPI == kEpiBlk) {
+                if (kt & 1) {  // a 128-wide K block is complete: fold its two scales
+                    const int64_t kb = kt >> 1;
+                    const float sw = ue8m0_to_f32(p.wsb[(n0 >> 7) * nkb + kb]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int64_t m = m0 + wm * 64 + j * 16 + li;
+                        const float sx = ue8m0_to_f32(p.xsb[(m < M ? m : M - 1) * nkb + kb]);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            acc[i][j] += (dblk[i][j] * sw) * sx;
+                            dblk[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                        }
+                    }
+                }
+            }
+        }
+        if (kt + 1 < ktiles) lstore(b ^ 1);
+        __syncthreads();
+    }
+
+    // epilogue: lane holds D[n = 4*lg + r][m = li] of each 16 x 16 tile
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t m = m0 + wm * 64 + j * 16 + li;
+        if (m >= M) continue;
+        float xsv = 1.0f;
+        if constexpr (EPI == kEpiI8 || EPI == kEpiXsWs) xsv = p.xs[m * p.xs_step];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t n = n0 + wn * 64 + i * 16 + 4 * lg + r;
+                if (n >= N) continue;
+                if constexpr (EPI == kEpiI8) {
+                    if (p.out_kind == 1) {
+                        ((int32_t*)p.y)[m * p.ldy + n] = acc[i][j][r];
+                        continue;
+                    }
+                    float v = (float)acc[i][j][r];
+                    v = v * xsv;
+                    v = v * p.ws[n * p.ws_step];
+                    uint16_t o = f32_to_bf16(v);
+                    if (p.bias) o = f32_to_bf16(bf16_to_f32(o) + bf16_to_f32(p.bias[n]));
+                    ((uint16_t*)p.y)[m * p.ldy + n] = o;
+                } else if constexpr (EPI == kEpiWs) {
+                    ((uint16_t*)p.y)[m * p.ldy + n] = f32_to_bf16(acc[i][j][r] * p.ws[n * p.ws_step]);
+                } else if constexpr (EPI == kEpiXsWs) {
+                    float v = acc[i][j][r] * xsv;
+                    v = v * p.ws[n * p.ws_step];
+                    ((uint16_t*)p.y)[m * p.ldy + n] = f32_to_bf16(v);
+                } else {
+                    ((uint16_t*)p.y)[m * p.ldy + n] = f32_to_bf16(acc[i][j][r]);
+                }
+            }
+    }
+}
+
+}  // namespace qlin

@@ -9,7 +9,8 @@
 //   * M = 2 (INT8, E4M3, FP8 W8A8): VALU with smaller lane groups (and, for
 //     INT8 / E4M3, several rows per group, so that each activation load feeds
 //     more weight rows);
-//   * otherwise: the matrix-core kernels.
+//   * otherwise: the matrix-core kernels;
+//   * M > 16 (prefill): the tiled matrix-core GEMM of gemm.hip.
 #include <algorithm>
 
 #include "gemv_kernels.hpp"
@@ -17,6 +18,8 @@
 #include "qlin_launch.hpp"
 
 namespace qlin {
+
+constexpr int64_t kDecodeMaxM = 16;  // the decode kernels serve M <= 16, the tiled GEMM the rest
 
 namespace {
 
@@ -166,6 +169,7 @@ hipError_t run_blk_m1(const BlkArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_gemv_i8(const I8Args& a, hipStream_t st) {
+    if (a.M > kDecodeMaxM) return launch_gemm_i8(a, st);
     switch (a.M) {
         case 1: QLIN_M1_BY_STEPS(run_i8, a, st)
         case 2: return run_i8<2, 32, 2, 2, 1>(a, st);
@@ -174,6 +178,7 @@ hipError_t launch_gemv_i8(const I8Args& a, hipStream_t st) {
 }
 
 hipError_t launch_gemv_fp8(const F8Args& a, hipStream_t st) {
+    if (a.M > kDecodeMaxM) return launch_gemm_fp8(a, st);
     switch (a.M) {
         case 1: return run_fp8<1, 32, 2, 1, 1>(a, st);
         case 2: return run_fp8<2, 64, 4, 1, 1>(a, st);
@@ -186,6 +191,7 @@ hipError_t launch_gemv_fp8(const F8Args& a, hipStream_t st) {
 // M = 1 best with 3 steps of one row per wave, M = 2 with 32-lane groups and
 // 5 steps); the matrix-core kernel from M = 3.
 hipError_t launch_gemv_fp8_w8a8(const W8A8F8Args& a, hipStream_t st) {
+    if (a.M > kDecodeMaxM) return launch_gemm_fp8_w8a8(a, st);
     if (a.M == 1) {
         switch (std::min(steps64(a.K), 3)) {
             case 1: return run_w8a8<1, 64, 1, 1, 4>(a, st);
@@ -207,6 +213,7 @@ hipError_t launch_gemv_fp8_w8a8(const W8A8F8Args& a, hipStream_t st) {
 }
 
 hipError_t launch_gemv_fp8_blk(const BlkArgs& a, hipStream_t st) {
+    if (a.M > kDecodeMaxM) return launch_gemm_fp8_blk(a, st);
     if (a.M > 1) return run_blk_mfma(a, st);
     switch (std::min(steps64(a.K), 8)) {
         case 1: return run_blk_m1<1>(a, st);

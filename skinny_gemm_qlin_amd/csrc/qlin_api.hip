@@ -41,7 +41,7 @@ int qlin_version(void) { return 100; }  // 0.1.0
 int qlin_act_quant_i8(const void* x, int64_t ldx, int64_t M, int64_t K,
                       int8_t* xq, int64_t ldxq, float* xs, void* stream) {
     if (!x || !xq || !xs) return QLIN_ERR_NULL;
-    if (M < 1 || M > QLIN_MAX_M || K < 16 || K % 16 != 0 || K > kMaxKInt8) return QLIN_ERR_SHAPE;
+    if (M < 1 || M > QLIN_MAX_M_PREFILL || K < 16 || K % 16 != 0 || K > kMaxKInt8) return QLIN_ERR_SHAPE;
     if (ldx < K || ldxq < K) return QLIN_ERR_STRIDE;
     if (misaligned(x, 16) || ldx % 8 != 0 || misaligned(xq, 16) || ldxq % 16 != 0 || misaligned(xs, 4))
         return QLIN_ERR_ALIGN;
@@ -57,7 +57,7 @@ int qlin_gemv_i8(const int8_t* xq, int64_t ldxq, const float* xs, int xs_per_tok
     if ((xs_per_token != 0 && xs_per_token != 1) || (ws_per_row != 0 && ws_per_row != 1)) return QLIN_ERR_ARG;
     if (!xq || !w || !y) return QLIN_ERR_NULL;
     if (out_kind == 0 && (!xs || !ws)) return QLIN_ERR_NULL;
-    if (M < 1 || M > QLIN_MAX_M || N < 1 || K < 16 || K % 16 != 0 || K > kMaxKInt8) return QLIN_ERR_SHAPE;
+    if (M < 1 || M > QLIN_MAX_M_PREFILL || N < 1 || K < 16 || K % 16 != 0 || K > kMaxKInt8) return QLIN_ERR_SHAPE;
     if (ldxq < K || ldw < K || ldy < N) return QLIN_ERR_STRIDE;
     if (misaligned(xq, 16) || ldxq % 16 != 0 || misaligned(w, 16) || ldw % 16 != 0) return QLIN_ERR_ALIGN;
     if (misaligned(y, out_kind == 1 ? 4 : 2) || (xs && misaligned(xs, 4)) || (ws && misaligned(ws, 4)) ||
@@ -73,7 +73,7 @@ int qlin_gemv_fp8(const void* x, int64_t ldx, int64_t M, int64_t K,
                   void* y, int64_t ldy, void* stream) {
     if (ws_per_row != 0 && ws_per_row != 1) return QLIN_ERR_ARG;
     if (!x || !w || !ws || !y) return QLIN_ERR_NULL;
-    if (M < 1 || M > QLIN_MAX_M || N < 1 || K < 16 || K % 16 != 0) return QLIN_ERR_SHAPE;
+    if (M < 1 || M > QLIN_MAX_M_PREFILL || N < 1 || K < 16 || K % 16 != 0) return QLIN_ERR_SHAPE;
     if (ldx < K || ldw < K || ldy < N) return QLIN_ERR_STRIDE;
     if (misaligned(x, 16) || ldx % 8 != 0 || misaligned(w, 16) || ldw % 16 != 0 || misaligned(ws, 4) ||
         misaligned(y, 2))
@@ -86,7 +86,8 @@ int qlin_act_quant_fp8(const void* x, int64_t ldx, int64_t M, int64_t K, int fmt
                        uint8_t* xq, int64_t ldxq, float* xs, void* stream) {
     if ((fmt != QLIN_FMT_E4M3 && fmt != QLIN_FMT_E5M2) || (per_token != 0 && per_token != 1)) return QLIN_ERR_ARG;
     if (!x || !xq || !xs) return QLIN_ERR_NULL;
-    if (M < 1 || M > QLIN_MAX_M || K < 16 || K % 16 != 0 || K > kMaxKFp8) return QLIN_ERR_SHAPE;
+    if (M < 1 || M > (per_token ? QLIN_MAX_M_PREFILL : QLIN_MAX_M) || K < 16 || K % 16 != 0 || K > kMaxKFp8)
+        return QLIN_ERR_SHAPE;
     if (ldx < K || ldxq < K) return QLIN_ERR_STRIDE;
     if (misaligned(x, 16) || ldx % 8 != 0 || misaligned(xq, 16) || ldxq % 16 != 0 || misaligned(xs, 4))
         return QLIN_ERR_ALIGN;
@@ -101,7 +102,7 @@ int qlin_gemv_fp8_w8a8(const uint8_t* xq, int64_t ldxq, const float* xs, int xs_
         return QLIN_ERR_ARG;
     if ((xs_per_token != 0 && xs_per_token != 1) || (ws_per_row != 0 && ws_per_row != 1)) return QLIN_ERR_ARG;
     if (!xq || !xs || !w || !ws || !y) return QLIN_ERR_NULL;
-    if (M < 1 || M > QLIN_MAX_M || N < 1 || K < 16 || K % 16 != 0 || K > kMaxKFp8) return QLIN_ERR_SHAPE;
+    if (M < 1 || M > QLIN_MAX_M_PREFILL || N < 1 || K < 16 || K % 16 != 0 || K > kMaxKFp8) return QLIN_ERR_SHAPE;
     if (ldxq < K || ldw < K || ldy < N) return QLIN_ERR_STRIDE;
     if (misaligned(xq, 16) || ldxq % 16 != 0 || misaligned(w, 16) || ldw % 16 != 0 || misaligned(xs, 4) ||
         misaligned(ws, 4) || misaligned(y, 2))
@@ -115,7 +116,7 @@ int qlin_gemv_fp8_blk(const void* x, int64_t ldx, int64_t M, int64_t K,
                       const uint8_t* w, int64_t ldw, int64_t N, const uint8_t* ws,
                       uint8_t* xq, uint8_t* xs, void* y, int64_t ldy, void* stream) {
     if (!x || !w || !ws || !xq || !xs || !y) return QLIN_ERR_NULL;
-    if (M < 1 || M > QLIN_MAX_M || N < 1 || K < 128 || K % 128 != 0) return QLIN_ERR_SHAPE;
+    if (M < 1 || M > QLIN_MAX_M_PREFILL || N < 1 || K < 128 || K % 128 != 0) return QLIN_ERR_SHAPE;
     if (ldx < K || ldw < K || ldy < N) return QLIN_ERR_STRIDE;
     if (misaligned(x, 16) || ldx % 8 != 0 || misaligned(w, 16) || ldw % 16 != 0 || misaligned(xq, 16) ||
         misaligned(y, 2))

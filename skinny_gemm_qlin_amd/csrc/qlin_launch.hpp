@@ -61,6 +61,12 @@ hipError_t launch_blk_act_quant(const BlkQuantArgs& a, hipStream_t st);
 hipError_t launch_gemv_fp8_blk(const BlkArgs& a, hipStream_t st);
 hipError_t launch_moe_mxfp4(const MoeArgs& a, hipStream_t st);
 
+// prefill GEMM (M > 16), called by the launchers above
+hipError_t launch_gemm_i8(const I8Args& a, hipStream_t st);
+hipError_t launch_gemm_fp8(const F8Args& a, hipStream_t st);
+hipError_t launch_gemm_fp8_w8a8(const W8A8F8Args& a, hipStream_t st);
+hipError_t launch_gemm_fp8_blk(const BlkArgs& a, hipStream_t st);
+
 struct MoeFfnArgs {
     const uint16_t* x; int64_t ldx; int64_t M; int64_t H;
     const uint16_t* wr; int64_t E; int64_t topk;

@@ -55,7 +55,7 @@ def test_act_quant_errors(q):
     assert f(None, 1024, 1, 1024, A, 1024, A, None) == -1
     assert f(A, 1024, 1, 1024, None, 1024, A, None) == -1
     assert f(A, 1024, 0, 1024, A, 1024, A, None) == -2          # M = 0
-    assert f(A, 1024, 17, 1024, A, 1024, A, None) == -2         # M > 16
+    assert f(A, 1024, 16385, 1024, A, 1024, A, None) == -2      # M > QLIN_MAX_M_PREFILL
     assert f(A, 1024, 1, 1000, A, 1024, A, None) == -2          # K % 16
     assert f(A, 1 << 20, 1, 131088, A, 1 << 20, A, None) == -2  # K too large for exact int32
     assert f(A, 512, 1, 1024, A, 1024, A, None) == -3           # ldx < K
@@ -80,7 +80,7 @@ def test_gemv_i8_errors(q):
     assert call(xs=None) == -1
     assert call(ws=None) == -1
     assert call(M=0) == -2
-    assert call(M=17) == -2
+    assert call(M=16385) == -2
     assert call(N=0) == -2
     assert call(K=0) == -2
     assert call(K=1032, ldxq=1040, ldw=1040) == -2
@@ -100,6 +100,7 @@ def test_gemv_fp8_errors(q):
     assert call(wpr=3) == -6
     assert call(ws=None) == -1
     assert call(M=0) == -2
+    assert call(M=16385) == -2
     assert call(K=5128, ldx=5136, ldw=5136) == -2
     assert call(ldx=5000) == -3
     assert call(ldx=5124) == -4
@@ -117,7 +118,8 @@ def test_act_quant_fp8_errors(q):
     assert call(xq=None) == -1
     assert call(xs=None) == -1
     assert call(M=0) == -2
-    assert call(M=17) == -2
+    assert call(M=16385) == -2
+    assert call(M=17, pt=0) == -2  # the per-tensor scale: one workgroup, M <= 16
     assert call(K=1000) == -2
     assert call(K=(1 << 24) + 16, ldx=(1 << 24) + 16, ldxq=(1 << 24) + 16) == -2
     assert call(ldx=512) == -3
@@ -140,7 +142,7 @@ def test_gemv_fp8_w8a8_errors(q):
     for name in ("xq", "xs", "w", "ws", "y"):
         assert call(**{name: None}) == -1
     assert call(M=0) == -2
-    assert call(M=17) == -2
+    assert call(M=16385) == -2
     assert call(N=0) == -2
     assert call(K=8, ldxq=16, ldw=16) == -2
     assert call(K=1032, ldxq=1040, ldw=1040) == -2
@@ -163,7 +165,7 @@ def test_gemv_fp8_blk_errors(q):
     assert call(xs=None) == -1
     assert call(ws=None) == -1
     assert call(K=7168 + 16, ldx=7184, ldw=7184) == -2   # K % 128
-    assert call(M=17) == -2
+    assert call(M=16385) == -2
     assert call(ldw=7000) == -3
     assert call(xq=A + 8) == -4
 
