@@ -7,11 +7,12 @@ namespace qlin {
 
 namespace {
 
-template <int WF, int ACT, int EPI>
+template <int WF, int ACT, int EPI, int TN = 4, int TM = 4, int BK = 64>
 hipError_t run_gemm(const GemmParams& p, hipStream_t st) {
-    const int64_t tiles = ((p.M + kGemmBM - 1) / kGemmBM) * ((p.N + kGemmBN - 1) / kGemmBN);
+    constexpr int BN = GemmShape<TN, TM, BK>::BN, BM = GemmShape<TN, TM, BK>::BM;
+    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
     const int64_t grid = (tiles + 7) / 8 * 8;  // the XCD remap needs a multiple of 8
-    hipLaunchKernelGGL((gemm_kernel<WF, ACT, EPI>), dim3((unsigned)grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((gemm_kernel<WF, ACT, EPI, TN, TM, BK>), dim3((unsigned)grid), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 

@@ -46,7 +46,6 @@ struct GemmParams {
     void* y; int64_t ldy; int out_kind;  // bf16 [M][ldy] (INT8 out_kind 1: int32 acc)
 };
 
-constexpr int kGemmBM = 128, kGemmBN = 128, kGemmBK = 64;
 
 // 8 FP8 codes (one uint2) of format F -> bf16x8, exact.
 template <int F>
@@ -57,16 +56,26 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint2 c) {
     return bf16x8_t{b[0][0], b[0][1], b[1][0], b[1][1], b[2][0], b[2][1], b[3][0], b[3][1]};
 }
 
-template <int WF, int ACT, int EPI>
+// Tile shape: a wave computes TN x TM MFMA tiles (16 x 16 each), the 4 waves
+// of a workgroup 2 x 2 of those; K tiles of BK elements.
+template <int TN, int TM, int BK>
+struct GemmShape {
+    static constexpr int BN = 32 * TN, BM = 32 * TM;
+};
+
+template <int WF, int ACT, int EPI, int TN, int TM, int BK>
 __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
     constexpr bool kI8 = ACT == kActI8;
+    constexpr int kGemmBN = 32 * TN, kGemmBM = 32 * TM, kGemmBK = BK;
     constexpr int XB = ACT == kActBf16 ? 2 : 1;       // bytes per activation element
     constexpr int WP = kGemmBK + 16;                  // LDS row pitch, weight tile (bytes)
     constexpr int XP = kGemmBK * XB + 16;             // LDS row pitch, activation tile
-    constexpr int WCH = kGemmBN * kGemmBK / 16 / 256; // 16-byte chunks per lane, weight tile
-    constexpr int XCH = kGemmBM * kGemmBK * XB / 16 / 256;
-    constexpr int WCPR = kGemmBK / 16;                // chunks per row
+    constexpr int WCPR = kGemmBK / 16;                // 16-byte chunks per row
     constexpr int XCPR = kGemmBK * XB / 16;
+    constexpr int WTOT = kGemmBN * WCPR, XTOT = kGemmBM * XCPR;  // chunks per tile
+    constexpr int WCH = (WTOT + 255) / 256, XCH = (XTOT + 255) / 256;  // per lane
+    static_assert(EPI != kEpiBlk || (128 % (16 * TN) == 0 && BK <= 128 && 128 % BK == 0),
+                  "block FP8: a wave's rows lie in one 128-row scale block, K tiles divide 128");
     __shared__ __align__(16) uint8_t wt[2][kGemmBN * WP];
     __shared__ __align__(16) uint8_t xt[2][kGemmBM * XP];
 
@@ -87,7 +96,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
     int wdst[WCH], wcol[WCH];
 #pragma unroll
     for (int i = 0; i < WCH; ++i) {
-        const int c = tid + i * 256, r = c / WCPR;
+        const int c = (tid + i * 256) % WTOT, r = c / WCPR;  // lanes past WTOT repeat a chunk (not stored)
         const int64_t n = n0 + r < N ? n0 + r : N - 1;
         wcol[i] = (c % WCPR) * 16;
         wsrc[i] = (const uint8_t*)p.w + n * p.ldw + wcol[i];
@@ -97,7 +106,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
     int xdst[XCH], xcol[XCH];
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
-        const int c = tid + i * 256, r = c / XCPR;
+        const int c = (tid + i * 256) % XTOT, r = c / XCPR;
         const int64_t m = m0 + r < M ? m0 + r : M - 1;
         xcol[i] = (c % XCPR) * 16;
         xsrc[i] = (const uint8_t*)p.x + (m * p.ldx) * XB + xcol[i];
@@ -119,17 +128,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
     };
     auto lstore = [&](int b) {
 #pragma unroll
-        for (int i = 0; i < WCH; ++i) *(u32x4_t*)(wt[b] + wdst[i]) = wreg[i];
+        for (int i = 0; i < WCH; ++i)
+            if (WTOT % 256 == 0 || tid + i * 256 < WTOT) *(u32x4_t*)(wt[b] + wdst[i]) = wreg[i];
 #pragma unroll
-        for (int i = 0; i < XCH; ++i) *(u32x4_t*)(xt[b] + xdst[i]) = xreg[i];
+        for (int i = 0; i < XCH; ++i)
+            if (XTOT % 256 == 0 || tid + i * 256 < XTOT) *(u32x4_t*)(xt[b] + xdst[i]) = xreg[i];
     };
 
     typedef typename std::conditional<kI8, i32x4_t, f32x4_t>::type acc_t;
-    acc_t acc[4][4], dblk[4][4];
+    acc_t acc[TN][TM], dblk[TN][TM];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TN; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < TM; ++j) {
             acc[i][j] = acc_t{0, 0, 0, 0};
             dblk[i][j] = acc_t{0, 0, 0, 0};
         }
@@ -142,28 +153,31 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
     for (int64_t kt = 0; kt < ktiles; ++kt) {
         const int b = (int)(kt & 1);
         if (kt + 1 < ktiles) gload(kt + 1);
-        const uint8_t* W = wt[b] + (wn * 64 + li) * WP;
-        const uint8_t* X = xt[b] + (wm * 64 + li) * XP;
+        const uint8_t* W = wt[b] + (wn * TN * 16 + li) * WP;
+        const uint8_t* X = xt[b] + (wm * TM * 16 + li) * XP;
         if constexpr (kI8) {
-            i32x4_t a[4], bb[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = *(const i32x4_t*)(W + i * 16 * WP + lg * 16);
+            for (int ks = 0; ks < kGemmBK / 64; ++ks) {
+                i32x4_t a[TN], bb[TM];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) bb[j] = *(const i32x4_t*)(X + j * 16 * XP + lg * 16);
+                for (int i = 0; i < TN; ++i) a[i] = *(const i32x4_t*)(W + i * 16 * WP + ks * 64 + lg * 16);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+                for (int j = 0; j < TM; ++j) bb[j] = *(const i32x4_t*)(X + j * 16 * XP + ks * 64 + lg * 16);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], bb[j], acc[i][j], 0, 0, 0);
+                for (int i = 0; i < TN; ++i)
+#pragma unroll
+                    for (int j = 0; j < TM; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], bb[j], acc[i][j], 0, 0, 0);
+            }
         } else {
 #pragma unroll
             for (int ks = 0; ks < kGemmBK / 32; ++ks) {
-                bf16x8_t a[4], bb[4];
+                bf16x8_t a[TN], bb[TM];
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < TN; ++i)
                     a[i] = fp8x8_to_bf16x8<WF>(*(const uint2*)(W + i * 16 * WP + ks * 32 + lg * 8));
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < TM; ++j) {
                     if constexpr (ACT == kActBf16)
                         bb[j] = *(const bf16x8_t*)(X + j * 16 * XP + ks * 64 + lg * 16);
                     else
@@ -171,9 +185,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
                             *(const uint2*)(X + j * 16 * XP + ks * 32 + lg * 8));
                 }
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < TN; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
+                    for (int j = 0; j < TM; ++j) {
                         if constexpr (EPI == kEpiBlk)
                             dblk[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bb[j], dblk[i][j], 0, 0, 0);
                         else
@@ -181,15 +195,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
                     }
             }
             if constexpr (EPI == kEpiBlk) {
-                if (kt & 1) {  // a 128-wide K block is complete: fold its two scales
-                    const int64_t kb = kt >> 1;
-                    const float sw = ue8m0_to_f32(p.wsb[(n0 >> 7) * nkb + kb]);
+                if (((kt + 1) * kGemmBK) % 128 == 0) {  // a 128-wide K block is complete: fold its scales
+                    const int64_t kb = ((kt + 1) * kGemmBK >> 7) - 1;
+                    const float sw = ue8m0_to_f32(p.wsb[((n0 + wn * TN * 16) >> 7) * nkb + kb]);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int64_t m = m0 + wm * 64 + j * 16 + li;
+                    for (int j = 0; j < TM; ++j) {
+                        const int64_t m = m0 + wm * TM * 16 + j * 16 + li;
                         const float sx = ue8m0_to_f32(p.xsb[(m < M ? m : M - 1) * nkb + kb]);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
+                        for (int i = 0; i < TN; ++i) {
                             acc[i][j] += (dblk[i][j] * sw) * sx;
                             dblk[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
                         }
@@ -203,16 +217,16 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
 
     // epilogue: lane holds D[n = 4*lg + r][m = li] of each 16 x 16 tile
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t m = m0 + wm * 64 + j * 16 + li;
+    for (int j = 0; j < TM; ++j) {
+        const int64_t m = m0 + wm * TM * 16 + j * 16 + li;
         if (m >= M) continue;
         float xsv = 1.0f;
         if constexpr (EPI == kEpiI8 || EPI == kEpiXsWs) xsv = p.xs[m * p.xs_step];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < TN; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t n = n0 + wn * 64 + i * 16 + 4 * lg + r;
+                const int64_t n = n0 + wn * TN * 16 + i * 16 + 4 * lg + r;
                 if (n >= N) continue;
                 if constexpr (EPI == kEpiI8) {
                     if (p.out_kind == 1) {
