@@ -94,6 +94,11 @@ inline int steps64(int64_t K) { return (int)(((K >> 4) + 63) / 64); }
 // KS splits K so that the grid holds about 4096 waves: 4 when there are at
 // least 1024 row tiles, 8 from 512, else 16 -- never more waves than K has
 // chunks for, beyond the minimum of 4.
+// From 12 tokens the INT8 kernel stages the activation rows through LDS like
+// the weights (row-contiguous loads; measured 23.9 -> 22.4 us at M = 16,
+// slower below 12 tokens).
+constexpr int64_t kStageXMinM = 12;
+
 inline int mfma_ks(int64_t N, int64_t K) {
     const int64_t tiles = (N + 15) / 16, nch = (K + 255) >> 8;
     int ks = tiles >= 1024 ? 4 : (tiles >= 512 ? 8 : 16);
@@ -110,8 +115,13 @@ inline int mfma_ks(int64_t N, int64_t K) {
 
 hipError_t run_i8_mfma(const I8Args& a, hipStream_t st) {
     dim3 grid((unsigned)((a.N + 15) / 16));
-    QLIN_BY_KS(gemv_i8_mfma_kernel, mfma_ks(a.N, a.K), grid, 0, st, a.xq, a.ldxq, a.xs, a.xs_step, (int)a.M,
-               a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.bias, a.y, a.ldy, a.out_kind)
+    if (a.M >= kStageXMinM) {
+        QLIN_BY_KS(gemv_i8_mfma_xl_kernel, mfma_ks(a.N, a.K), grid, 0, st, a.xq, a.ldxq, a.xs, a.xs_step,
+                   (int)a.M, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.bias, a.y, a.ldy, a.out_kind)
+    } else {
+        QLIN_BY_KS(gemv_i8_mfma_kernel, mfma_ks(a.N, a.K), grid, 0, st, a.xq, a.ldxq, a.xs, a.xs_step, (int)a.M,
+                   a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.bias, a.y, a.ldy, a.out_kind)
+    }
     return hipGetLastError();
 }
 

@@ -155,6 +155,107 @@ __global__ __launch_bounds__(64 * KS) void gemv_i8_mfma_kernel(
     }
 }
 
+// Activation rows staged like the weights: 16 token rows x 256 bytes per
+// chunk, loaded 4 rows x 256 contiguous bytes per instruction (rows past M
+// repeat row M-1: their output columns are not stored; bytes past K are 0).
+struct XTileLoader {
+    const uint8_t* row[4];
+    int lp;
+    __device__ XTileLoader(const uint8_t* x, int64_t ldx, int M) {
+        const int lane = threadIdx.x & 63;
+        const int lr = lane >> 4;
+        lp = lane & 15;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int m = 4 * q + lr;
+            row[q] = x + (int64_t)(m < M ? m : M - 1) * ldx;
+        }
+    }
+    __device__ __forceinline__ void load(u32x4_t v[4], int64_t c, int64_t K, bool live) const {
+        const int64_t k = c * 256 + lp * 16;
+        const bool ok = live && k < K;
+        const int64_t kc = ok ? k : 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x4_t t = ld16(row[q] + kc);
+            v[q] = ok ? t : u32x4_t{0, 0, 0, 0};
+        }
+    }
+};
+
+// INT8 with the activation operand staged through a second per-wave LDS tile
+// (row-contiguous loads instead of a 16-token gather per MFMA), shared by
+// RT row tiles of 16 weight rows per wave.
+template <int U, int KS = kMfmaKS, int RT = 1>
+__global__ __launch_bounds__(64 * KS) void gemv_i8_mfma_xl_kernel(
+    const int8_t* __restrict__ xq, int64_t ldxq, const float* __restrict__ xs, int xs_step, int M,
+    int64_t K, const int8_t* __restrict__ w, int64_t ldw, int64_t N,
+    const float* __restrict__ ws, int ws_step, const uint16_t* __restrict__ bias,
+    void* __restrict__ y, int64_t ldy, int out_kind) {
+    __shared__ __align__(16) uint8_t tile[KS][RT][16 * kTilePitch];
+    __shared__ __align__(16) uint8_t xtile[KS][16 * kTilePitch];
+    __shared__ i32x4_t red[KS][64];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int mi = lane & 15, mg = lane >> 4;
+    const int64_t nb = (int64_t)blockIdx.x * 16 * RT;
+    const int64_t nch = (K + 255) >> 8, per = (nch + KS - 1) / KS;
+    const int64_t c0 = wv * per, c1 = c0 + per < nch ? c0 + per : nch;
+    const XTileLoader xl((const uint8_t*)xq, ldxq, M);
+    uint8_t* xt = xtile[wv];
+
+    i32x4_t acc[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) acc[r] = i32x4_t{0, 0, 0, 0};
+    for (int64_t c = c0; c < c1; c += U) {
+        u32x4_t wv_[U][RT][4], xv_[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                const TileLoader tl((const uint8_t*)w, ldw, nb + 16 * r, N);
+                tl.load(wv_[u][r], c + u < c1 ? c + u : c1 - 1, K);
+            }
+#pragma unroll
+        for (int u = 0; u < U; ++u) xl.load(xv_[u], c + u, K, c + u < c1);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            tile_store(xt, xv_[u]);
+#pragma unroll
+            for (int r = 0; r < RT; ++r) tile_store(tile[wv][r], wv_[u][r]);
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const i32x4_t bx = __builtin_bit_cast(i32x4_t, tile_read(xt, 64 * h));
+#pragma unroll
+                for (int r = 0; r < RT; ++r)
+                    acc[r] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                        __builtin_bit_cast(i32x4_t, tile_read(tile[wv][r], 64 * h)), bx, acc[r], 0, 0, 0);
+            }
+        }
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        if (rt) __syncthreads();  // wave 0 is done reading red
+        if (!ks_reduce<KS>(acc[rt], red)) continue;
+        if (mi < M) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t n = nb + 16 * rt + 4 * mg + r;
+                if (n >= N) continue;
+                if (out_kind == 1) {
+                    ((int32_t*)y)[mi * ldy + n] = acc[rt][r];
+                } else {
+                    float v = (float)acc[rt][r];
+                    v = v * xs[mi * xs_step];
+                    v = v * ws[n * ws_step];
+                    uint16_t o = f32_to_bf16(v);
+                    if (bias) o = f32_to_bf16(bf16_to_f32(o) + bf16_to_f32(bias[n]));
+                    ((uint16_t*)y)[mi * ldy + n] = o;
+                }
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------------ FP8-E4M3 weight-only (v_mfma_f32_16x16x32_bf16)
 // The E4M3 codes read back from the tile are converted to bf16 (exact) and
 // multiplied with the bf16 activations; fp32 accumulation; the weight scale
