@@ -36,6 +36,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
+PEAK_INT8_TOPS = 5000.0  # MI355X dense int8 matrix-core peak
 MALL_BYTES = 256 << 20  # Infinity Cache
 
 
@@ -90,6 +92,8 @@ def bytes_moe_ffn_call(M, H, I, E, topk, live):
 # and the expert FFN)
 KERNEL_SOURCES = {
     "int8_decode": ("gemv.hip",),
+    "int8_prefill": ("gemm.hip",),
+    "fp8_prefill": ("gemm.hip",),
     "fp8_decode": ("gemv.hip",),
     "fp8_w8a8": ("gemv.hip",),
     "fp8_blk": ("act_quant.hip", "gemv.hip"),
@@ -141,7 +145,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="int8_decode",
-                    choices=["int8_decode", "fp8_decode", "fp8_w8a8", "fp8_blk", "moe_mxfp4", "moe_ffn_mxfp4"])
+                    choices=["int8_decode", "fp8_decode", "fp8_w8a8", "fp8_blk", "moe_mxfp4", "moe_ffn_mxfp4",
+                             "int8_prefill", "fp8_prefill"])
     ap.add_argument("--ms", default=None, help="comma list of M values (default: the workload's)")
     ap.add_argument("--rotate", type=int, default=0, help="weight copies (0 = enough to defeat the MALL)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
@@ -179,10 +184,10 @@ def main():
 
     # ---------------------------------------------------------------- inputs (seed 0)
     log(f"bench: generating {wl} inputs N={N} K={K} Ms={Ms}")
-    if wl == "int8_decode":
+    if wl in ("int8_decode", "int8_prefill"):
         d = inputs.gen_int8(Mmax, N, K, seed=0)
         wbytes = N * K
-    elif wl == "fp8_decode":
+    elif wl in ("fp8_decode", "fp8_prefill"):
         d = inputs.gen_fp8(Mmax, N, K, seed=0, per_tensor=args.per_tensor)
         wbytes = N * K
     elif wl == "fp8_w8a8":
@@ -221,7 +226,7 @@ def main():
     sc = t(d["ws"]) if "ws" in d else None
 
     # ---------------------------------------------------------------- per-call launch lists
-    xq_buf = torch.empty((Mmax, K), dtype=torch.int8 if wl == "int8_decode" else torch.uint8, device=dev)
+    xq_buf = torch.empty((Mmax, K), dtype=torch.int8 if wl.startswith("int8") else torch.uint8, device=dev)
     xs_buf = torch.empty((Mmax,), dtype=torch.float32, device=dev)
     xsb_buf = torch.empty((Mmax, K // 128), dtype=torch.uint8, device=dev)
     y_buf = torch.empty((Mmax, N), dtype=torch.bfloat16, device=dev)
@@ -246,12 +251,12 @@ def main():
         """[(kernel, bytes, fn)] for one call of the workload's entry point."""
         w = ws_copies[ci]
         xm = x[:M]
-        if wl == "int8_decode":
+        if wl in ("int8_decode", "int8_prefill"):
             return [("act_quant_i8", bytes_act_quant_i8(M, K),
                      lambda: ql.qlin_act_quant_i8(xm, xq_buf[:M], xs_buf[:M])),
                     ("gemv_i8", bytes_gemv_i8(M, N, K),
                      lambda: ql.qlin_gemv_i8(xq_buf[:M], xs_buf[:M], w, sc, y=y_buf[:M]))]
-        if wl == "fp8_decode":
+        if wl in ("fp8_decode", "fp8_prefill"):
             return [("gemv_fp8", bytes_gemv_fp8(M, N, K), lambda: ql.qlin_gemv_fp8(xm, w, sc, y=y_buf[:M]))]
         if wl == "fp8_w8a8":
             return [("act_quant_fp8", bytes_act_quant_fp8(M, K),
@@ -269,6 +274,7 @@ def main():
                                                ids=ids_buf[:M], gw=gw_buf[:M]))]
 
     dominant = {"int8_decode": "gemv_i8", "fp8_decode": "gemv_fp8", "fp8_w8a8": "gemv_fp8_w8a8",
+                "int8_prefill": "gemv_i8", "fp8_prefill": "gemv_fp8",
                 "fp8_blk": "act_quant_blk+gemv_fp8_blk", "moe_mxfp4": "moe_mxfp4",
                 "moe_ffn_mxfp4": "moe_ffn_mxfp4"}[wl]
 
@@ -322,7 +328,7 @@ def main():
     # -> mean launch duration of that kernel.
     reps = max(20, args.steps)
     per_m = {}
-    dom_bytes, dom_ms, dom_n = 0, 0.0, 0
+    dom_bytes, dom_ms, dom_n, dom_flops = 0, 0.0, 0, 0
     for i, M in enumerate(Ms):
         ent = per_m.setdefault(str(M), {})
         for kidx in range(len(launches(M, 0))):
@@ -341,6 +347,8 @@ def main():
             ent[kname] = {"us": round(us, 3), "GBps": round(nb / (us * 1e-6) / 1e9, 1),
                           "frac": round(nb / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
             if kname == dominant:
+                dom_flops += 2 * M * N * K * reps
+                ent[kname]["TFLOPs"] = round(2 * M * N * K / (us * 1e-6) / 1e12, 1)
                 dom_bytes += nb * reps
                 dom_ms += ms * reps
                 dom_n += reps
@@ -354,6 +362,19 @@ def main():
 
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = load_traffic(wl)
+    if wl.endswith("_prefill"):
+        # compute-bound: algorithmic MACs x 2 per launch / launch duration, against
+        # the dense matrix-core peak of the instruction's type (int8 5.0 POP/s,
+        # bf16 2.5 PFLOP/s)
+        peak = PEAK_INT8_TOPS if wl.startswith("int8") else PEAK_BF16_TFLOPS
+        tf = dom_flops / (dom_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(tf, 1), "peak": peak,
+                    "unit": "TOP/s" if wl.startswith("int8") else "TFLOP/s", "frac": round(tf / peak, 4),
+                    "traffic": traffic, "launches": dom_n}
+    else:
+        roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                    "launches": dom_n}
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
@@ -367,10 +388,10 @@ def main():
         def oracle_step():
             for M in Ms:
                 xm = d["x"][:M]
-                if wl == "int8_decode":
+                if wl in ("int8_decode", "int8_prefill"):
                     xq, xs = oracle.act_quant_i8(xm)
                     oracle.gemv_i8(xq, xs, d["w"], d["ws"])
-                elif wl == "fp8_decode":
+                elif wl in ("fp8_decode", "fp8_prefill"):
                     oracle.gemv_fp8(xm, d["w"], d["ws"])
                 elif wl == "fp8_w8a8":
                     xq, xs = oracle.act_quant_fp8(xm, 0, True)
@@ -397,6 +418,8 @@ def main():
     cfg = {"workload": {
         "int8_decode": f"W8A8 INT8 decode linear (act quant + GEMV, bf16 out) N={N} K={K}, one call per M",
         "fp8_decode": f"E4M3 weight-only GEMV ({'per-tensor' if args.per_tensor else 'per-channel'}) N={N} K={K}",
+        "int8_prefill": f"W8A8 INT8 prefill linear (act quant + tiled GEMM, bf16 out) N={N} K={K}, one call per M",
+        "fp8_prefill": f"E4M3 weight-only prefill GEMM (per-channel) N={N} K={K}, one call per M",
         "fp8_w8a8": f"FP8 W8A8 E4M3 x E4M3 (per-token act quant + GEMV, per-channel ws) N={N} K={K}",
         "fp8_blk": f"128x128 block-scaled FP8 (act quant + GEMV) N={N} K={K}",
         "moe_mxfp4": f"MXFP4 top-{spec.get('topk')} expert GEMV E={spec.get('E')} N={N} K={K}",
@@ -418,13 +441,12 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"int8_decode": "int8", "fp8_decode": "fp8e4m3*bf16->f32", "fp8_w8a8": "fp8e4m3*fp8e4m3->f32",
+                  "int8_prefill": "int8", "fp8_prefill": "fp8e4m3*bf16->f32",
                   "fp8_blk": "fp8e4m3->f32", "moe_mxfp4": "fp4e2m1*bf16->f32",
                   "moe_ffn_mxfp4": "fp4e2m1*bf16->f32"}[wl],
         "data": "synthetic",
         "config": cfg,
-        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "launches": dom_n},
+        "roofline": roofline,
         "cpu_baseline": cpu,
         "per_m": per_m,
     }

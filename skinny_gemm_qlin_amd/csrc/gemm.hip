@@ -18,32 +18,48 @@ hipError_t run_gemm(const GemmParams& p, hipStream_t st) {
 
 }  // namespace
 
+// Tile choice (measured at N = 17408, K = 5120): up to 256 tokens the 64 x 64
+// tiles give 4x more workgroups (the GEMM is latency-bound there); above,
+// 128 x 128 tiles.  INT8 takes K tiles of 128 (one 64-deep MFMA step per
+// 64 bytes would double the barriers per MFMA).
+constexpr int64_t kSmallTileMaxM = 256;
+
 hipError_t launch_gemm_i8(const I8Args& a, hipStream_t st) {
     GemmParams p{a.xq, a.ldxq, a.xs, a.xs_step, nullptr, a.M, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step,
                  nullptr, a.bias, a.y, a.ldy, a.out_kind};
-    return run_gemm<kFmtE4M3, kActI8, kEpiI8>(p, st);
+    if (a.M <= kSmallTileMaxM) return run_gemm<kFmtE4M3, kActI8, kEpiI8, 2, 2, 128>(p, st);
+    return run_gemm<kFmtE4M3, kActI8, kEpiI8, 4, 4, 128>(p, st);
 }
 
 hipError_t launch_gemm_fp8(const F8Args& a, hipStream_t st) {
     GemmParams p{a.x, a.ldx, nullptr, 0, nullptr, a.M, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step,
                  nullptr, nullptr, a.y, a.ldy, 0};
-    return run_gemm<kFmtE4M3, kActBf16, kEpiWs>(p, st);
+    if (a.M <= kSmallTileMaxM) return run_gemm<kFmtE4M3, kActBf16, kEpiWs, 2, 2, 64>(p, st);
+    return run_gemm<kFmtE4M3, kActBf16, kEpiWs, 4, 4, 64>(p, st);
 }
 
 hipError_t launch_gemm_fp8_w8a8(const W8A8F8Args& a, hipStream_t st) {
     GemmParams p{a.xq, a.ldxq, a.xs, a.xs_step, nullptr, a.M, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step,
                  nullptr, nullptr, a.y, a.ldy, 0};
-    if (a.x_fmt == kFmtE5M2)
-        return a.w_fmt == kFmtE5M2 ? run_gemm<kFmtE5M2, kActE5M2, kEpiXsWs>(p, st)
-                                   : run_gemm<kFmtE4M3, kActE5M2, kEpiXsWs>(p, st);
-    return a.w_fmt == kFmtE5M2 ? run_gemm<kFmtE5M2, kActE4M3, kEpiXsWs>(p, st)
-                               : run_gemm<kFmtE4M3, kActE4M3, kEpiXsWs>(p, st);
+    const bool small = a.M <= kSmallTileMaxM;
+    if (a.x_fmt == kFmtE5M2) {
+        if (a.w_fmt == kFmtE5M2)
+            return small ? run_gemm<kFmtE5M2, kActE5M2, kEpiXsWs, 2, 2, 64>(p, st)
+                         : run_gemm<kFmtE5M2, kActE5M2, kEpiXsWs, 4, 4, 128>(p, st);
+        return small ? run_gemm<kFmtE4M3, kActE5M2, kEpiXsWs, 2, 2, 64>(p, st)
+                     : run_gemm<kFmtE4M3, kActE5M2, kEpiXsWs, 4, 4, 128>(p, st);
+    }
+    if (a.w_fmt == kFmtE5M2)
+        return small ? run_gemm<kFmtE5M2, kActE4M3, kEpiXsWs, 2, 2, 64>(p, st)
+                     : run_gemm<kFmtE5M2, kActE4M3, kEpiXsWs, 4, 4, 128>(p, st);
+    return small ? run_gemm<kFmtE4M3, kActE4M3, kEpiXsWs, 2, 2, 64>(p, st)
+                 : run_gemm<kFmtE4M3, kActE4M3, kEpiXsWs, 4, 4, 128>(p, st);
 }
 
 hipError_t launch_gemm_fp8_blk(const BlkArgs& a, hipStream_t st) {
     GemmParams p{a.xq, a.K, nullptr, 0, a.xs, a.M, a.K, a.w, a.ldw, a.N, nullptr, 0,
                  a.ws, nullptr, a.y, a.ldy, 0};
-    return run_gemm<kFmtE4M3, kActE4M3, kEpiBlk>(p, st);
+    return run_gemm<kFmtE4M3, kActE4M3, kEpiBlk, 2, 2, 128>(p, st);
 }
 
 }  // namespace qlin

@@ -7,14 +7,16 @@
 //   block FP8        y = bf16(sum_kb (D_kb * 2^(ws-127)) * 2^(xs-127))
 //                    [Z100 section 2.4: per-block fold; DSV4 section 3.3]
 //
-// Tiling: a 256-lane workgroup owns a 128 (weight rows n) x 128 (tokens m)
-// output tile; its 4 waves split it 2 x 2, each wave 64 x 64 = 4 x 4 MFMA
-// tiles of 16 x 16 (A operand = weight rows, B operand = token rows, so a
-// lane's 4 accumulator registers are 4 consecutive n of one token).  K runs
-// in tiles of 64 elements, double-buffered through LDS: the global loads of
+// Tiling: a 256-lane workgroup owns a (32*TN weight rows n) x (32*TM tokens
+// m) output tile; its 4 waves split it 2 x 2, each wave TN x TM MFMA tiles of
+// 16 x 16 (A operand = weight rows, B operand = token rows, so a lane's 4
+// accumulator registers are 4 consecutive n of one token).  K runs in tiles
+// of BK elements, double-buffered through LDS: the global loads of
 // tile k+1 (16 bytes per lane per load, row-contiguous) are in flight while
 // tile k is multiplied, then stored to the other LDS buffer; one barrier per
-// K tile.  FP8 codes are widened to bf16 (exact) as fragments are read from
+// K tile; whole K tiles are loaded without bounds checks.  (Measured: the
+// 32 x 32 MFMAs, deeper prefetch and other LDS paddings do not change the
+// throughput of this design; it is bound by the tile traffic through LDS.)  FP8 codes are widened to bf16 (exact) as fragments are read from
 // LDS and multiplied on the bf16 matrix core with fp32 accumulation (the
 // fp8 matrix-core instructions sum with ~13 bits, see the decode kernels);
 // INT8 uses v_mfma_i32_16x16x64_i8 (exact).
@@ -63,13 +65,13 @@ struct GemmShape {
     static constexpr int BN = 32 * TN, BM = 32 * TM;
 };
 
-template <int WF, int ACT, int EPI, int TN, int TM, int BK>
+template <int WF, int ACT, int EPI, int TN, int TM, int BK, int PAD = 16>
 __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
     constexpr bool kI8 = ACT == kActI8;
     constexpr int kGemmBN = 32 * TN, kGemmBM = 32 * TM, kGemmBK = BK;
     constexpr int XB = ACT == kActBf16 ? 2 : 1;       // bytes per activation element
-    constexpr int WP = kGemmBK + 16;                  // LDS row pitch, weight tile (bytes)
-    constexpr int XP = kGemmBK * XB + 16;             // LDS row pitch, activation tile
+    constexpr int WP = kGemmBK + PAD;                 // LDS row pitch, weight tile (bytes)
+    constexpr int XP = kGemmBK * XB + PAD;            // LDS row pitch, activation tile
     constexpr int WCPR = kGemmBK / 16;                // 16-byte chunks per row
     constexpr int XCPR = kGemmBK * XB / 16;
     constexpr int WTOT = kGemmBN * WCPR, XTOT = kGemmBM * XCPR;  // chunks per tile
@@ -113,8 +115,16 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
         xdst[i] = r * XP + xcol[i];
     }
     const int64_t ktiles = (K + kGemmBK - 1) / kGemmBK;
+    const int64_t kfull = K / kGemmBK;  // tiles that lie wholly inside K: loaded without checks
     u32x4_t wreg[WCH], xreg[XCH];
     auto gload = [&](int64_t kt) {
+        if (kt < kfull) {
+#pragma unroll
+            for (int i = 0; i < WCH; ++i) wreg[i] = ld_stream(wsrc[i] + kt * kGemmBK);
+#pragma unroll
+            for (int i = 0; i < XCH; ++i) xreg[i] = ld16(xsrc[i] + kt * kGemmBK * XB);
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < WCH; ++i) {
             const int64_t kb = kt * kGemmBK + wcol[i];  // byte = element offset
