@@ -75,6 +75,8 @@ def _load():
     lib.orc_gemv_fp8.argtypes = [P, I64, I64, I64, P, I64, I64, P, I, P, I64, P, P]
     lib.orc_blk_act_quant.argtypes = [P, I64, I64, I64, P, P]
     lib.orc_gemv_fp8_blk.argtypes = [P, P, I64, I64, P, I64, I64, P, P, I64, P, P]
+    lib.orc_blk_act_quant_g.argtypes = [P, I64, I64, I64, I64, P, P]
+    lib.orc_gemv_fp8_blk_g.argtypes = [P, P, I64, I64, P, I64, I64, P, I64, I64, P, I64, P, P]
     lib.orc_moe_mxfp4.argtypes = [P, I64, I64, I64, P, P, I64, I64, P, P, I64, P, I64, P, P]
     lib.orc_router_logits.argtypes = [P, I64, I64, I64, P, I64, P]
     lib.orc_topk.argtypes = [P, I64, I64, I64, P]
@@ -212,20 +214,20 @@ def gemv_fp8(x_bf16, w_e4m3, ws):
 
 # --------------------------------------------------------------------------- (c) block-scaled FP8
 
-def blk_act_quant(x_bf16):
-    """Per-token, per-128-group E4M3 quantisation with a UE8M0 scale
-    ([DSV4] section 3.3).  Returns (xq uint8 [M, K], xs uint8 [M, K/128])."""
+def blk_act_quant(x_bf16, block_k=BLK):
+    """Per-token, per-block_k-group E4M3 quantisation with a UE8M0 scale
+    ([DSV4] section 3.3; block_k 128 there).  Returns (xq uint8 [M, K], xs uint8 [M, K/block_k])."""
     x = _c(x_bf16, np.uint16)
     M, K = x.shape
-    assert K % BLK == 0
+    assert K % block_k == 0
     xq = np.zeros((M, K), dtype=np.uint8)
-    xs = np.zeros((M, K // BLK), dtype=np.uint8)
-    _load().orc_blk_act_quant(_p(x), K, M, K, _p(xq), _p(xs))
+    xs = np.zeros((M, K // block_k), dtype=np.uint8)
+    _load().orc_blk_act_quant_g(_p(x), K, M, K, int(block_k), _p(xq), _p(xs))
     return xq, xs
 
 
-def gemv_fp8_blk(xq, xs, w_e4m3, ws_blk):
-    """Block-scaled GEMV core ([Z100] section 2.4).  ws_blk is [ceil(N/128), K/128].
+def gemv_fp8_blk(xq, xs, w_e4m3, ws_blk, block_n=BLK, block_k=BLK):
+    """Block-scaled GEMV core ([Z100] section 2.4).  ws_blk is [ceil(N/block_n), K/block_k].
 
     Returns (y uint16 [M, N], y_exact float64, S float64)."""
     xq = _c(xq, np.uint8)
@@ -234,20 +236,21 @@ def gemv_fp8_blk(xq, xs, w_e4m3, ws_blk):
     wsb = _c(ws_blk, np.uint8)
     M, K = xq.shape
     N = w.shape[0]
-    assert wsb.shape == ((N + BLK - 1) // BLK, K // BLK)
+    assert wsb.shape == ((N + block_n - 1) // block_n, K // block_k) and xs.shape == (M, K // block_k)
     y = np.zeros((M, N), dtype=np.uint16)
     ye = np.zeros((M, N), dtype=np.float64)
     S = np.zeros((M, N), dtype=np.float64)
-    _load().orc_gemv_fp8_blk(_p(xq), _p(xs), M, K, _p(w), K, N, _p(wsb), _p(y), N, _p(ye), _p(S))
+    _load().orc_gemv_fp8_blk_g(_p(xq), _p(xs), M, K, _p(w), K, N, _p(wsb), int(block_n), int(block_k),
+                               _p(y), N, _p(ye), _p(S))
     return y, ye, S
 
 
-def fp8_blk(x_bf16, w_e4m3, ws_blk):
+def fp8_blk(x_bf16, w_e4m3, ws_blk, block_n=BLK, block_k=BLK):
     """Whole block-scaled path: activation quantisation then GEMV.
 
     Returns (xq, xs, y, y_exact, S)."""
-    xq, xs = blk_act_quant(x_bf16)
-    y, ye, S = gemv_fp8_blk(xq, xs, w_e4m3, ws_blk)
+    xq, xs = blk_act_quant(x_bf16, block_k)
+    y, ye, S = gemv_fp8_blk(xq, xs, w_e4m3, ws_blk, block_n, block_k)
     return xq, xs, y, ye, S
 
 

@@ -373,13 +373,15 @@ void orc_gemv_fp8_w8a8(const uint8_t* xq, int64_t ldxq, const float* xs, int xs_
  * two is exact).  READING: the pages fix the scale format (UE8M0) and the
  * grouping but not the exponent rule; rounding the scale up to the next
  * power of two is the plainest rule that never overflows E4M3. */
-void orc_blk_act_quant(const uint16_t* x, int64_t ldx, int64_t M, int64_t K,
-                       uint8_t* xq /* [M][K] */, uint8_t* xs /* [M][K/128] */) {
-    int64_t nkb = K / ORC_BLK;
+/* Activation quantisation per token and block_k-wide K group (block_k a
+ * multiple of 32; 128 in the configuration the pages tested). */
+void orc_blk_act_quant_g(const uint16_t* x, int64_t ldx, int64_t M, int64_t K, int64_t bk,
+                         uint8_t* xq /* [M][K] */, uint8_t* xs /* [M][K/bk] */) {
+    int64_t nkb = K / bk;
     for (int64_t m = 0; m < M; ++m) {
         for (int64_t kb = 0; kb < nkb; ++kb) {
             double amax = 0.0;
-            for (int64_t k = kb * ORC_BLK; k < (kb + 1) * ORC_BLK; ++k) {
+            for (int64_t k = kb * bk; k < (kb + 1) * bk; ++k) {
                 double a = fabs((double)orc_bf16_to_f32(x[m * ldx + k]));
                 if (a > amax) amax = a;
             }
@@ -392,7 +394,7 @@ void orc_blk_act_quant(const uint16_t* x, int64_t ldx, int64_t M, int64_t K,
                 if (E > 254) E = 254;
             }
             xs[m * nkb + kb] = (uint8_t)E;
-            for (int64_t k = kb * ORC_BLK; k < (kb + 1) * ORC_BLK; ++k) {
+            for (int64_t k = kb * bk; k < (kb + 1) * bk; ++k) {
                 double v = ldexp((double)orc_bf16_to_f32(x[m * ldx + k]), -(E - 127));
                 xq[m * K + k] = orc_e4m3_encode(v);
             }
@@ -400,12 +402,21 @@ void orc_blk_act_quant(const uint16_t* x, int64_t ldx, int64_t M, int64_t K,
     }
 }
 
+void orc_blk_act_quant(const uint16_t* x, int64_t ldx, int64_t M, int64_t K,
+                       uint8_t* xq /* [M][K] */, uint8_t* xs /* [M][K/128] */) {
+    orc_blk_act_quant_g(x, ldx, M, K, ORC_BLK, xq, xs);
+}
+
 /* out[m,n] = sum_kb ( sum_{k in kb} xq[m,k] * w[n,k] ) * a_s[m,kb] * w_s[n/128, kb]
  * with every code and scale decoded exactly; ws is [ceil(N/128)][K/128]. */
-void orc_gemv_fp8_blk(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
-                      const uint8_t* w, int64_t ldw, int64_t N, const uint8_t* ws,
-                      uint16_t* y, int64_t ldy, double* y_exact, double* S) {
-    int64_t nkb = K / ORC_BLK;
+/* Block-scaled GEMV with block_n x block_k weight blocks (weight scale row
+ * n / block_n) and block_k-wide activation groups: per K block the two
+ * power-of-two scales multiply that block's exact partial sum [Z100 section
+ * 2.4: block formula; block_n, block_k runtime parameters, block_k % 32]. */
+void orc_gemv_fp8_blk_g(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
+                        const uint8_t* w, int64_t ldw, int64_t N, const uint8_t* ws, int64_t bn, int64_t bk,
+                        uint16_t* y, int64_t ldy, double* y_exact, double* S) {
+    int64_t nkb = K / bk;
     int64_t n;
 #pragma omp parallel for schedule(static)
     for (n = 0; n < N; ++n) {
@@ -413,13 +424,12 @@ void orc_gemv_fp8_blk(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K
             double tot = 0.0, sabs = 0.0;
             for (int64_t kb = 0; kb < nkb; ++kb) {
                 double part = 0.0, pabs = 0.0;
-                for (int64_t k = kb * ORC_BLK; k < (kb + 1) * ORC_BLK; ++k) {
+                for (int64_t k = kb * bk; k < (kb + 1) * bk; ++k) {
                     double p = orc_e4m3_decode(xq[m * K + k]) * orc_e4m3_decode(w[n * ldw + k]);
                     part += p;
                     pabs += fabs(p);
                 }
-                double sc = orc_ue8m0_decode(xs[m * nkb + kb]) *
-                            orc_ue8m0_decode(ws[(n / ORC_BLK) * nkb + kb]);
+                double sc = orc_ue8m0_decode(xs[m * nkb + kb]) * orc_ue8m0_decode(ws[(n / bn) * nkb + kb]);
                 tot += part * sc;
                 sabs += pabs * fabs(sc);
             }
@@ -428,6 +438,12 @@ void orc_gemv_fp8_blk(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K
             if (S) S[m * N + n] = sabs;
         }
     }
+}
+
+void orc_gemv_fp8_blk(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
+                      const uint8_t* w, int64_t ldw, int64_t N, const uint8_t* ws,
+                      uint16_t* y, int64_t ldy, double* y_exact, double* S) {
+    orc_gemv_fp8_blk_g(xq, xs, M, K, w, ldw, N, ws, ORC_BLK, ORC_BLK, y, ldy, y_exact, S);
 }
 
 /* ------------------------------------------------------------------------ */

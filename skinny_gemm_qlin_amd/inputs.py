@@ -72,11 +72,15 @@ def gen_fp8(M: int, N: int, K: int, seed: int = 0, per_tensor: bool = False) -> 
     return {"w": codes, "ws": ws, "x": x}
 
 
-def gen_fp8_blk(M: int, N: int, K: int, seed: int = 0, scale_lo: int = 115, scale_hi: int = 125) -> dict:
+def gen_fp8_blk(M: int, N: int, K: int, seed: int = 0, scale_lo: int = 115, scale_hi: int = 125,
+                block_n: int = 128, block_k: int = 128) -> dict:
+    """Block-scaled FP8 inputs: W codes uniform over the finite E4M3 codes, one
+    UE8M0 byte U{scale_lo..scale_hi} per block_n x block_k weight block
+    ([ceil(N/block_n)][K/block_k]), x bf16 N(0, 1)."""
     rng = np.random.default_rng(seed)
     w = _E4M3_FINITE[rng.integers(0, _E4M3_FINITE.size, size=(N, K))]
-    nb = (N + 127) // 128
-    ws = rng.integers(scale_lo, scale_hi + 1, size=(nb, K // 128)).astype(np.uint8)
+    nb = (N + block_n - 1) // block_n
+    ws = rng.integers(scale_lo, scale_hi + 1, size=(nb, K // block_k)).astype(np.uint8)
     x = bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
     return {"w": w, "ws": ws, "x": x}
 
