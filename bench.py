@@ -67,8 +67,8 @@ def bytes_gemv_fp8_w8a8(M, N, K):
     return N * K + 4 * N + M * K + 4 * M + 2 * M * N          # W, ws, xq, xs, y
 
 
-def bytes_blk_call(M, N, K):
-    return N * K + ((N + 127) // 128) * (K // 128) + 2 * M * K + 2 * M * N   # W, ws, x, y
+def bytes_blk_call(M, N, K, bn=128, bk=128):
+    return N * K + ((N + bn - 1) // bn) * (K // bk) + 2 * M * K + 2 * M * N   # W, ws, x, y
 
 
 def bytes_blk_gemv(M, N, K):
@@ -151,6 +151,7 @@ def main():
     ap.add_argument("--rotate", type=int, default=0, help="weight copies (0 = enough to defeat the MALL)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--per-tensor", action="store_true", help="fp8_decode: per-tensor weight scale")
+    ap.add_argument("--block", default="128,128", help="fp8_blk: block_n,block_k of the weight scales")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -194,7 +195,8 @@ def main():
         d = inputs.gen_fp8_w8a8(Mmax, N, K, w_fmt=0, seed=0)
         wbytes = N * K
     elif wl == "fp8_blk":
-        d = inputs.gen_fp8_blk(Mmax, N, K, seed=0)
+        bn, bk = (int(v) for v in args.block.split(","))
+        d = inputs.gen_fp8_blk(Mmax, N, K, seed=0, block_n=bn, block_k=bk)
         wbytes = N * K
     elif wl == "moe_mxfp4":
         E, topk = spec["E"], spec["topk"]
@@ -228,7 +230,7 @@ def main():
     # ---------------------------------------------------------------- per-call launch lists
     xq_buf = torch.empty((Mmax, K), dtype=torch.int8 if wl.startswith("int8") else torch.uint8, device=dev)
     xs_buf = torch.empty((Mmax,), dtype=torch.float32, device=dev)
-    xsb_buf = torch.empty((Mmax, K // 128), dtype=torch.uint8, device=dev)
+    xsb_buf = torch.empty((Mmax, K // (bk if wl == "fp8_blk" else 128)), dtype=torch.uint8, device=dev)
     y_buf = torch.empty((Mmax, N), dtype=torch.bfloat16, device=dev)
     if wl == "moe_mxfp4":
         ids, gw = t(d["ids"]), t(d["gw"])
@@ -264,8 +266,8 @@ def main():
                     ("gemv_fp8_w8a8", bytes_gemv_fp8_w8a8(M, N, K),
                      lambda: ql.qlin_gemv_fp8_w8a8(xq_buf[:M], xs_buf[:M], w, sc, 0, 0, y=y_buf[:M]))]
         if wl == "fp8_blk":
-            return [("act_quant_blk+gemv_fp8_blk", bytes_blk_call(M, N, K),
-                     lambda: ql.qlin_gemv_fp8_blk(xm, w, sc, xq=xq_buf[:M], xs=xsb_buf[:M], y=y_buf[:M]))]
+            return [("act_quant_blk+gemv_fp8_blk", bytes_blk_call(M, N, K, bn, bk),
+                     lambda: ql.qlin_gemv_fp8_blk_ex(xm, w, sc, bn, bk, xq=xq_buf[:M], xs=xsb_buf[:M], y=y_buf[:M]))]
         if wl == "moe_mxfp4":
             return [("moe_mxfp4", bytes_moe_call(M, N, K, spec["topk"], live),
                      lambda: ql.qlin_moe_mxfp4(xm, w, s_copies[ci], ids, gw, y=y_buf[:M], workspace=ws_moe))]
@@ -397,7 +399,7 @@ def main():
                     xq, xs = oracle.act_quant_fp8(xm, 0, True)
                     oracle.gemv_fp8_w8a8(xq, xs, 0, d["w"], d["ws"], 0)
                 elif wl == "fp8_blk":
-                    oracle.fp8_blk(xm, d["w"], d["ws"])
+                    oracle.fp8_blk(xm, d["w"], d["ws"], bn, bk)
                 else:
                     if wl == "moe_mxfp4":
                         oracle.moe_mxfp4(xm, d["w"], d["s"], d["ids"][:M], d["gw"][:M])
@@ -421,7 +423,7 @@ def main():
         "int8_prefill": f"W8A8 INT8 prefill linear (act quant + tiled GEMM, bf16 out) N={N} K={K}, one call per M",
         "fp8_prefill": f"E4M3 weight-only prefill GEMM (per-channel) N={N} K={K}, one call per M",
         "fp8_w8a8": f"FP8 W8A8 E4M3 x E4M3 (per-token act quant + GEMV, per-channel ws) N={N} K={K}",
-        "fp8_blk": f"128x128 block-scaled FP8 (act quant + GEMV) N={N} K={K}",
+        "fp8_blk": f"{args.block.replace(',', 'x')} block-scaled FP8 (act quant + GEMV) N={N} K={K}",
         "moe_mxfp4": f"MXFP4 top-{spec.get('topk')} expert GEMV E={spec.get('E')} N={N} K={K}",
         "moe_ffn_mxfp4": f"MXFP4 top-{spec.get('topk')} expert FFN with routing E={spec.get('E')} "
                          f"H={N} I={spec.get('I')} (router, gate/up+SwiGLU, down, combine)",

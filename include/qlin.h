@@ -192,6 +192,24 @@ int qlin_gemv_fp8_blk(const void* x, int64_t ldx, int64_t M, int64_t K,
                       uint8_t* xq, uint8_t* xs,
                       void* y, int64_t ldy, void* stream);
 
+/* The same block-scaled path at any block shape: block_n x block_k weight
+ * blocks and block_k-wide activation groups, block_k a multiple of 32 and
+ * block_n >= 1 (block_n = 1, block_k = 32 is the MX layout: one UE8M0 scale
+ * per row and 32 K elements).  [Z100] 2.4 gives block_n and block_k as
+ * run-time parameters with block_k % 32 == 0 (tested there at 128 x 128 only).
+ * Arithmetic as qlin_gemv_fp8_blk with 128 replaced by the block sizes:
+ *   ws UE8M0 [ceil(N/block_n), K/block_k]; xq uint8 [M, K];
+ *   xs uint8 [M, K/block_k]; out[m,n] = sum_kb 2^(xs[m,kb]-127) *
+ *   2^(ws[n/block_n,kb]-127) * sum_{k in kb} xq[m,k] * w[n,k].
+ * block_n = block_k = 128 is exactly qlin_gemv_fp8_blk.  Other shapes run a
+ * matrix-core GEMV over 16 tokens per launch (M > 16 reads the weights once
+ * per 16 tokens) and require K <= 32768 (the tile's scale bytes are staged in
+ * LDS).  Requires K % block_k == 0, ldx % 8 == 0, ldw % 16 == 0, ldy >= N. */
+int qlin_gemv_fp8_blk_ex(const void* x, int64_t ldx, int64_t M, int64_t K,
+                         const uint8_t* w, int64_t ldw, int64_t N, const uint8_t* ws,
+                         int64_t block_n, int64_t block_k,
+                         uint8_t* xq, uint8_t* xs, void* y, int64_t ldy, void* stream);
+
 /* ------------------------------------------------------------------------
  * (d) MXFP4 expert GEMV behind top-k routing -- [DSV4] 9.3; element and
  *     scale formats of the OCP MX spec (E2M1, one UE8M0 per 32 elements)

@@ -19,7 +19,7 @@ from ._lib import QLIN_FMT_E4M3, QLIN_FMT_E5M2, QlinError, check, load, status_s
 
 __all__ = [
     "QlinError", "qlin_act_quant_i8", "qlin_gemv_i8", "qlin_gemv_fp8", "qlin_gemv_fp8_blk",
-    "qlin_act_quant_fp8", "qlin_gemv_fp8_w8a8", "QLIN_FMT_E4M3", "QLIN_FMT_E5M2",
+    "qlin_act_quant_fp8", "qlin_gemv_fp8_w8a8", "QLIN_FMT_E4M3", "QLIN_FMT_E5M2", "qlin_gemv_fp8_blk_ex",
     "qlin_moe_mxfp4", "qlin_moe_mxfp4_workspace_bytes", "status_str",
 ]
 
@@ -181,6 +181,33 @@ def qlin_gemv_fp8_blk(x, w, ws, xq=None, xs=None, y=None, stream=None):
     check(load().qlin_gemv_fp8_blk(x.data_ptr(), x.stride(0), M, K, w.data_ptr(), w.stride(0), N,
                                    ws.data_ptr(), xq.data_ptr(), xs.data_ptr(), y.data_ptr(),
                                    y.stride(0), _stream(x, stream)), "qlin_gemv_fp8_blk")
+    return y, xq, xs
+
+
+def qlin_gemv_fp8_blk_ex(x, w, ws, block_n, block_k, xq=None, xs=None, y=None, stream=None):
+    """Block-scaled FP8 at any block shape: x bf16 [M, K], w E4M3 [N, K], ws UE8M0
+    [ceil(N/block_n), K/block_k].  Returns (y bf16 [M, N], xq E4M3 [M, K], xs UE8M0 [M, K/block_k])."""
+    _need(x, "x", (torch.bfloat16,), 2)
+    _need(w, "w", _U8, 2)
+    _need(ws, "ws", (torch.uint8,), 2)
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K or K % block_k:
+        raise ValueError(f"w has K={w.shape[1]}, x has K={K}, block_k={block_k}")
+    if tuple(ws.shape) != ((N + block_n - 1) // block_n, K // block_k) or not ws.is_contiguous():
+        raise ValueError(f"ws must be contiguous [{(N + block_n - 1) // block_n}, {K // block_k}], got {tuple(ws.shape)}")
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if xs is None:
+        xs = torch.empty((M, K // block_k), dtype=torch.uint8, device=x.device)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    if not xq.is_contiguous() or not xs.is_contiguous():
+        raise ValueError("xq / xs must be contiguous")
+    _need(y, "y", (torch.bfloat16,), 2)
+    check(load().qlin_gemv_fp8_blk_ex(x.data_ptr(), x.stride(0), M, K, w.data_ptr(), w.stride(0), N,
+                                      ws.data_ptr(), int(block_n), int(block_k), xq.data_ptr(), xs.data_ptr(),
+                                      y.data_ptr(), y.stride(0), _stream(x, stream)), "qlin_gemv_fp8_blk_ex")
     return y, xq, xs
 
 

@@ -4,6 +4,8 @@
 //                         [Z100 section 2.1; operator-family table, INT8 row]
 //   blk_act_quant_kernel  per (token, 128-wide K group) E4M3 codes with a
 //                         UE8M0 exponent [DSV4 section 3.3; Z100 section 2.4]
+//   blkg_act_quant_kernel the same per (token, block_k-wide group), any
+//                         block_k that is a multiple of 32 [Z100 section 2.4]
 //   act_quant_fp8_kernel  per-token or per-tensor E4M3 / E5M2 codes with an
 //                         fp32 scale amax/fmax [Z100 operator-family table,
 //                         FP8 row: W8A8, e4m3fn/e5m2, per-token/per-tensor]
@@ -248,6 +250,57 @@ hipError_t launch_act_quant_fp8_fmt(const ActQuantF8Args& a, hipStream_t st) {
 
 hipError_t launch_act_quant_fp8(const ActQuantF8Args& a, hipStream_t st) {
     return a.fmt == kFmtE5M2 ? launch_act_quant_fp8_fmt<kFmtE5M2>(a, st) : launch_act_quant_fp8_fmt<kFmtE4M3>(a, st);
+}
+
+// Any block_k (a multiple of 32): one workgroup per token, one lane per
+// K group (groups g, g + 256, ...).  Pass 1 takes the group's amax with
+// 16-byte loads, pass 2 re-reads the group (a cache hit) and converts
+// x * 2^(127-E) to E4M3 (exact scaling, RNE convert); E follows the same
+// rule as blk_act_quant_kernel.
+__global__ __launch_bounds__(256) void blkg_act_quant_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, int64_t K, int64_t bk,
+    uint8_t* __restrict__ xq, uint8_t* __restrict__ xs) {
+    const int64_t m = blockIdx.x;
+    const int64_t nkb = K / bk;
+    const uint16_t* row = x + m * ldx;
+    for (int64_t g = threadIdx.x; g < nkb; g += 256) {
+        float a = 0.0f;
+        for (int64_t v = 0; v < bk; v += 8) a = absmax8(ld16(row + g * bk + v), a);
+        int E = 127;
+        if (a != 0.0f) {
+            const uint32_t bits = __float_as_uint(a);
+            const int ex = (int)(bits >> 23);
+            int p;
+            if (ex == 0) p = -200;
+            else p = (ex - 127) - (((bits & 0x7FFFFFu) <= 0x600000u) ? 8 : 7);
+            E = 127 + p;
+            E = E < 1 ? 1 : (E > 254 ? 254 : E);
+        }
+        const int inv = 254 - E;
+        const float sc = inv == 0 ? __uint_as_float(0x00400000u) : __uint_as_float((uint32_t)inv << 23);
+        xs[m * nkb + g] = (uint8_t)E;
+        for (int64_t v = 0; v < bk; v += 8) {
+            const u32x4_t d = ld16(row + g * bk + v);
+            const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+            float f[8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                f[2 * q] = bf16_to_f32(w[q] & 0xFFFFu) * sc;
+                f[2 * q + 1] = bf16_to_f32(w[q] >> 16) * sc;
+            }
+            int lo = 0, hi = 0;
+            lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], lo, false);
+            lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
+            hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], hi, false);
+            hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
+            *(uint2*)(xq + m * K + g * bk + v) = make_uint2((uint32_t)lo, (uint32_t)hi);
+        }
+    }
+}
+
+hipError_t launch_blkg_act_quant(const BlkQuantArgs& a, int64_t bk, hipStream_t st) {
+    hipLaunchKernelGGL(blkg_act_quant_kernel, dim3((unsigned)a.M), dim3(256), 0, st, a.x, a.ldx, a.K, bk, a.xq, a.xs);
+    return hipGetLastError();
 }
 
 hipError_t launch_blk_act_quant(const BlkQuantArgs& a, hipStream_t st) {

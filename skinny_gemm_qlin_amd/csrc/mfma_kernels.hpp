@@ -80,6 +80,14 @@ __device__ __forceinline__ bool ks_reduce(T& acc, T (*red)[64]) {
     return true;
 }
 
+// 8 E4M3 codes (one uint2) -> one bf16x8 MFMA operand, exact.
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8_e4m3(uint2 c) {
+    bf16x2_t b[4];
+    e4m3x4_to_bf16(c.x, b[0], b[1]);
+    e4m3x4_to_bf16(c.y, b[2], b[3]);
+    return bf16x8_t{b[0][0], b[0][1], b[1][0], b[1][1], b[2][0], b[2][1], b[3][0], b[3][1]};
+}
+
 // 16 E4M3 codes -> two bf16x8 MFMA operands (bytes 0-7, bytes 8-15), exact.
 __device__ __forceinline__ void e4m3x16_to_bf16x8x2(const u32x4_t& c, bf16x8_t& lo, bf16x8_t& hi) {
     bf16x2_t b[8];
@@ -462,6 +470,88 @@ __global__ __launch_bounds__(64 * KS) void gemv_fp8_blk_mfma_kernel(
             }
         }
     }
+    if (!ks_reduce<KS>(acc, red)) return;
+    if (mi < M) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t n = n0 + 4 * mg + r;
+            if (n < N) y[mi * ldy + n] = f32_to_bf16(acc[r]);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ block-scaled FP8, any block shape
+// block_n x block_k weight blocks (block_k a multiple of 32, block_n >= 1,
+// down to one scale per row) and block_k-wide activation groups.  Here the
+// K slots of each MFMA are 32 contiguous K (lane group g takes 8g .. 8g+7),
+// so one 16 x 16 x 32 MFMA lies inside one K block; its result accumulates
+// in a block partial D that is folded when the block ends (or the wave's K
+// range does): acc += (D * 2^(ws[row]-127)) * 2^(xs[token]-127), with a
+// per-row weight scale (the 4 rows of a lane's D registers) and a per-token
+// activation scale [Z100 section 2.4: block formula, fold per K block;
+// block_n, block_k run-time parameters, block_k % 32].  The tile's scale
+// bytes are staged once in LDS, transposed to [K block][16] so that a lane's
+// 4 row scales are one 32-bit LDS word.
+template <int KS>
+__global__ __launch_bounds__(64 * KS) void gemv_fp8_blkg_mfma_kernel(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, int M, int64_t K,
+    const uint8_t* __restrict__ w, int64_t ldw, int64_t N,
+    const uint8_t* __restrict__ ws, int64_t bn, int64_t bk, uint16_t* __restrict__ y, int64_t ldy) {
+    __shared__ __align__(16) uint8_t tile[KS][16 * kTilePitch];
+    __shared__ f32x4_t red[KS][64];
+    extern __shared__ __align__(16) uint8_t sct[];  // [nkb][16] weight scales, then [nkb][16] token scales
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int mi = lane & 15, mg = lane >> 4;
+    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int64_t nkb = K / bk;
+    uint8_t* swt = sct;
+    uint8_t* sxt = sct + nkb * 16;
+    for (int64_t i = threadIdx.x; i < nkb * 16; i += 64 * KS) {
+        const int r = (int)(i & 15);
+        const int64_t kb = i >> 4;
+        const int64_t n = n0 + r < N ? n0 + r : N - 1;
+        swt[i] = ws[(n / bn) * nkb + kb];
+        sxt[i] = r < M ? xs[r * nkb + kb] : (uint8_t)127;
+    }
+    __syncthreads();
+
+    const int64_t nch = (K + 255) >> 8, per = (nch + KS - 1) / KS;
+    const int64_t c0 = wv * per, c1 = c0 + per < nch ? c0 + per : nch;
+    const TileLoader tl(w, ldw, n0, N);
+    const uint8_t* xr = xq + (int64_t)(mi < M ? mi : M - 1) * K;
+    uint8_t* t = tile[wv];
+
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, d = {0.f, 0.f, 0.f, 0.f};
+    int64_t kb_cur = -1, kb_end = 0;  // current K block and its end (K index)
+    auto fold = [&]() {
+        const uint32_t s4 = *(const uint32_t*)(swt + kb_cur * 16 + 4 * mg);
+        const float sx = ue8m0_to_f32(sxt[kb_cur * 16 + mi]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] += (d[r] * ue8m0_to_f32((s4 >> (8 * r)) & 0xFFu)) * sx;
+        d = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    };
+    for (int64_t c = c0; c < c1; ++c) {
+        u32x4_t wv_[4];
+        tl.load(wv_, c, K);
+        tile_store(t, wv_);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t k0 = c * 256 + 32 * j;
+            if (k0 >= K) break;  // wave-uniform; K % 32 == 0
+            if (kb_cur < 0) {  // first step of this wave's K range
+                kb_cur = k0 / bk;
+                kb_end = (kb_cur + 1) * bk;
+            } else if (k0 >= kb_end) {  // steps of 32 cross at most one block boundary
+                fold();
+                ++kb_cur;
+                kb_end += bk;
+            }
+            const bf16x8_t a = fp8x8_to_bf16x8_e4m3(*(const uint2*)(t + mi * kTilePitch + 32 * j + 8 * mg));
+            const bf16x8_t b = fp8x8_to_bf16x8_e4m3(*(const uint2*)(xr + k0 + 8 * mg));
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, d, 0, 0, 0);
+        }
+    }
+    if (kb_cur >= 0) fold();
     if (!ks_reduce<KS>(acc, red)) return;
     if (mi < M) {
 #pragma unroll

@@ -17,6 +17,7 @@ inline int launch_status(hipError_t e) { return e == hipSuccess ? QLIN_OK : QLIN
 
 constexpr int64_t kMaxKInt8 = 131072;  // K * 127 * 128 < 2^31: int32 accumulation is exact
 constexpr int64_t kMaxKFp8 = 1 << 24;  // keeps the quantiser's 32-bit vector indexes in range
+constexpr int64_t kMaxKBlkGeneral = 32768;  // the general block GEMV stages K/32 x 32 scale bytes in LDS
 
 }  // namespace
 
@@ -127,6 +128,32 @@ int qlin_gemv_fp8_blk(const void* x, int64_t ldx, int64_t M, int64_t K,
     if (e != hipSuccess) return QLIN_ERR_LAUNCH;
     qlin::BlkArgs a{xq, xs, M, K, w, ldw, N, ws, (uint16_t*)y, ldy};
     return launch_status(qlin::launch_gemv_fp8_blk(a, st));
+}
+
+int qlin_gemv_fp8_blk_ex(const void* x, int64_t ldx, int64_t M, int64_t K,
+                         const uint8_t* w, int64_t ldw, int64_t N, const uint8_t* ws,
+                         int64_t block_n, int64_t block_k,
+                         uint8_t* xq, uint8_t* xs, void* y, int64_t ldy, void* stream) {
+    if (!x || !w || !ws || !xq || !xs || !y) return QLIN_ERR_NULL;
+    if (block_n < 1 || block_k < 32 || block_k % 32 != 0) return QLIN_ERR_SHAPE;
+    if (block_n == 128 && block_k == 128)  // the tested configuration keeps its own kernels
+        return qlin_gemv_fp8_blk(x, ldx, M, K, w, ldw, N, ws, xq, xs, y, ldy, stream);
+    if (M < 1 || M > QLIN_MAX_M_PREFILL || N < 1 || K < block_k || K % block_k != 0 || K > kMaxKBlkGeneral)
+        return QLIN_ERR_SHAPE;
+    if (ldx < K || ldw < K || ldy < N) return QLIN_ERR_STRIDE;
+    if (misaligned(x, 16) || ldx % 8 != 0 || misaligned(w, 16) || ldw % 16 != 0 || misaligned(xq, 16) ||
+        misaligned(y, 2))
+        return QLIN_ERR_ALIGN;
+    hipStream_t st = (hipStream_t)stream;
+    qlin::BlkQuantArgs qa{(const uint16_t*)x, ldx, M, K, xq, xs};
+    if (qlin::launch_blkg_act_quant(qa, block_k, st) != hipSuccess) return QLIN_ERR_LAUNCH;
+    const int64_t nkb = K / block_k;
+    for (int64_t m0 = 0; m0 < M; m0 += QLIN_MAX_M) {  // 16 tokens per launch
+        const int64_t mc = M - m0 < QLIN_MAX_M ? M - m0 : QLIN_MAX_M;
+        qlin::BlkArgs a{xq + m0 * K, xs + m0 * nkb, mc, K, w, ldw, N, ws, (uint16_t*)y + m0 * ldy, ldy};
+        if (qlin::launch_gemv_fp8_blkg(a, block_n, block_k, st) != hipSuccess) return QLIN_ERR_LAUNCH;
+    }
+    return QLIN_OK;
 }
 
 size_t qlin_moe_mxfp4_workspace_bytes(int64_t M, int64_t N, int64_t topk, int64_t E) {

@@ -170,6 +170,25 @@ def test_gemv_fp8_blk_errors(q):
     assert call(xq=A + 8) == -4
 
 
+def test_gemv_fp8_blk_ex_errors(q):
+    def call(x=A, ldx=1024, M=1, K=1024, w=A, ldw=1024, N=64, ws=A, bn=1, bk=32, xq=A, xs=A, y=A, ldy=64):
+        return q.qlin_gemv_fp8_blk_ex(x, ldx, M, K, w, ldw, N, ws, bn, bk, xq, xs, y, ldy, None)
+    for name in ("x", "w", "ws", "xq", "xs", "y"):
+        assert call(**{name: None}) == -1
+    assert call(bn=0) == -2
+    assert call(bk=48) == -2            # block_k % 32
+    assert call(bk=16) == -2
+    assert call(K=1056, ldx=1056, ldw=1056, bk=64) == -2  # K % block_k
+    assert call(M=0) == -2
+    assert call(M=16385) == -2
+    assert call(K=32800, ldx=32800, ldw=32800) == -2  # K > 32768 for the general shapes
+    assert call(ldx=512) == -3
+    assert call(ldy=63) == -3
+    assert call(x=A + 2) == -4
+    assert call(ldw=1024 + 8) == -4
+    assert call(bn=128, bk=128, K=1000, ldx=1000, ldw=1000) == -2  # forwarded to qlin_gemv_fp8_blk
+
+
 def test_moe_errors(q):
     assert q.qlin_moe_mxfp4_workspace_bytes(8, 2048, 6, 64) == 8 * 6 * 2048 * 4
     assert q.qlin_moe_mxfp4_workspace_bytes(1, 3, 1, 1) == 256
