@@ -222,24 +222,29 @@ hipError_t launch_gemv_fp8_w8a8(const W8A8F8Args& a, hipStream_t st) {
     return run_w8a8_mfma(a, st);
 }
 
-hipError_t launch_gemv_fp8_blkg(const BlkArgs& a, int64_t bn, int64_t bk, hipStream_t st) {
+template <bool PAIR>
+hipError_t run_blkg(const BlkArgs& a, int64_t bn, int64_t bk, hipStream_t st) {
     dim3 grid((unsigned)((a.N + 15) / 16));
     const size_t lds = (size_t)(a.K / bk) * 32;  // transposed weight and token scale tables
     switch (mfma_ks(a.N, a.K)) {
         case 16:
-            hipLaunchKernelGGL(gemv_fp8_blkg_mfma_kernel<16>, grid, dim3(1024), lds, st, a.xq, a.xs, (int)a.M, a.K,
-                               a.w, a.ldw, a.N, a.ws, bn, bk, a.y, a.ldy);
+            hipLaunchKernelGGL((gemv_fp8_blkg_mfma_kernel<16, PAIR>), grid, dim3(1024), lds, st, a.xq, a.xs, (int)a.M,
+                               a.K, a.w, a.ldw, a.N, a.ws, bn, bk, a.y, a.ldy);
             break;
         case 8:
-            hipLaunchKernelGGL(gemv_fp8_blkg_mfma_kernel<8>, grid, dim3(512), lds, st, a.xq, a.xs, (int)a.M, a.K,
-                               a.w, a.ldw, a.N, a.ws, bn, bk, a.y, a.ldy);
+            hipLaunchKernelGGL((gemv_fp8_blkg_mfma_kernel<8, PAIR>), grid, dim3(512), lds, st, a.xq, a.xs, (int)a.M,
+                               a.K, a.w, a.ldw, a.N, a.ws, bn, bk, a.y, a.ldy);
             break;
         default:
-            hipLaunchKernelGGL(gemv_fp8_blkg_mfma_kernel<4>, grid, dim3(256), lds, st, a.xq, a.xs, (int)a.M, a.K,
-                               a.w, a.ldw, a.N, a.ws, bn, bk, a.y, a.ldy);
+            hipLaunchKernelGGL((gemv_fp8_blkg_mfma_kernel<4, PAIR>), grid, dim3(256), lds, st, a.xq, a.xs, (int)a.M,
+                               a.K, a.w, a.ldw, a.N, a.ws, bn, bk, a.y, a.ldy);
             break;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_gemv_fp8_blkg(const BlkArgs& a, int64_t bn, int64_t bk, hipStream_t st) {
+    return bk % 64 == 0 ? run_blkg<true>(a, bn, bk, st) : run_blkg<false>(a, bn, bk, st);
 }
 
 hipError_t launch_gemv_fp8_blk(const BlkArgs& a, hipStream_t st) {

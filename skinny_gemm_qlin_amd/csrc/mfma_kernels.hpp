@@ -492,7 +492,10 @@ __global__ __launch_bounds__(64 * KS) void gemv_fp8_blk_mfma_kernel(
 // block_n, block_k run-time parameters, block_k % 32].  The tile's scale
 // bytes are staged once in LDS, transposed to [K block][16] so that a lane's
 // 4 row scales are one 32-bit LDS word.
-template <int KS>
+// PAIR (block_k a multiple of 64): the K slots of two MFMAs are paired over
+// 64 K as in gemv_fp8_blk_mfma_kernel (16-byte loads of both operands per
+// lane for two MFMAs); a 64-K step still lies in one block.
+template <int KS, bool PAIR>
 __global__ __launch_bounds__(64 * KS) void gemv_fp8_blkg_mfma_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, int M, int64_t K,
     const uint8_t* __restrict__ w, int64_t ldw, int64_t N,
@@ -530,25 +533,34 @@ __global__ __launch_bounds__(64 * KS) void gemv_fp8_blkg_mfma_kernel(
         for (int r = 0; r < 4; ++r) acc[r] += (d[r] * ue8m0_to_f32((s4 >> (8 * r)) & 0xFFu)) * sx;
         d = f32x4_t{0.f, 0.f, 0.f, 0.f};
     };
+    constexpr int STEP = PAIR ? 64 : 32;
     for (int64_t c = c0; c < c1; ++c) {
         u32x4_t wv_[4];
         tl.load(wv_, c, K);
         tile_store(t, wv_);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int64_t k0 = c * 256 + 32 * j;
-            if (k0 >= K) break;  // wave-uniform; K % 32 == 0
+        for (int j = 0; j < 256 / STEP; ++j) {
+            const int64_t k0 = c * 256 + STEP * j;
+            if (k0 >= K) break;  // wave-uniform; K % STEP == 0
             if (kb_cur < 0) {  // first step of this wave's K range
                 kb_cur = k0 / bk;
                 kb_end = (kb_cur + 1) * bk;
-            } else if (k0 >= kb_end) {  // steps of 32 cross at most one block boundary
+            } else if (k0 >= kb_end) {  // a step crosses at most one block boundary
                 fold();
                 ++kb_cur;
                 kb_end += bk;
             }
-            const bf16x8_t a = fp8x8_to_bf16x8_e4m3(*(const uint2*)(t + mi * kTilePitch + 32 * j + 8 * mg));
-            const bf16x8_t b = fp8x8_to_bf16x8_e4m3(*(const uint2*)(xr + k0 + 8 * mg));
-            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, d, 0, 0, 0);
+            if constexpr (PAIR) {
+                bf16x8_t a0, a1, b0, b1;
+                e4m3x16_to_bf16x8x2(tile_read(t, 64 * j), a0, a1);
+                e4m3x16_to_bf16x8x2(ld16(xr + k0 + 16 * mg), b0, b1);
+                d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, d, 0, 0, 0);
+                d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, d, 0, 0, 0);
+            } else {
+                const bf16x8_t a = fp8x8_to_bf16x8_e4m3(*(const uint2*)(t + mi * kTilePitch + 32 * j + 8 * mg));
+                const bf16x8_t b = fp8x8_to_bf16x8_e4m3(*(const uint2*)(xr + k0 + 8 * mg));
+                d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, d, 0, 0, 0);
+            }
         }
     }
     if (kb_cur >= 0) fold();
