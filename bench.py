@@ -98,6 +98,7 @@ KERNEL_SOURCES = {
     "fp8_w8a8": ("gemv.hip",),
     "fp8_blk": ("act_quant.hip", "gemv.hip"),
     "moe_mxfp4": ("moe.hip",),
+    "moe_prefill": ("moe.hip", "moe_prefill.hip"),
     "moe_ffn_mxfp4": ("moe.hip", "routing.hip"),
 }
 
@@ -146,7 +147,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="int8_decode",
                     choices=["int8_decode", "fp8_decode", "fp8_w8a8", "fp8_blk", "moe_mxfp4", "moe_ffn_mxfp4",
-                             "int8_prefill", "fp8_prefill"])
+                             "int8_prefill", "fp8_prefill", "moe_prefill"])
     ap.add_argument("--ms", default=None, help="comma list of M values (default: the workload's)")
     ap.add_argument("--rotate", type=int, default=0, help="weight copies (0 = enough to defeat the MALL)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
@@ -198,7 +199,7 @@ def main():
         bn, bk = (int(v) for v in args.block.split(","))
         d = inputs.gen_fp8_blk(Mmax, N, K, seed=0, block_n=bn, block_k=bk)
         wbytes = N * K
-    elif wl == "moe_mxfp4":
+    elif wl in ("moe_mxfp4", "moe_prefill"):
         E, topk = spec["E"], spec["topk"]
         d = inputs.gen_moe(Mmax, E, N, K, topk, seed=0)
         wbytes = E * N * K // 2
@@ -216,7 +217,7 @@ def main():
         for i in range(1, B):
             ffn.append(tuple(a.clone() for a in ffn[0]))
         ws_copies = [None] * B
-    elif wl == "moe_mxfp4":
+    elif wl in ("moe_mxfp4", "moe_prefill"):
         ws_copies = [t(d["w"])] + [None] * (B - 1)
         s_copies = [t(d["s"])] + [None] * (B - 1)
         for i in range(1, B):
@@ -232,11 +233,12 @@ def main():
     xs_buf = torch.empty((Mmax,), dtype=torch.float32, device=dev)
     xsb_buf = torch.empty((Mmax, K // (bk if wl == "fp8_blk" else 128)), dtype=torch.uint8, device=dev)
     y_buf = torch.empty((Mmax, N), dtype=torch.bfloat16, device=dev)
-    if wl == "moe_mxfp4":
+    if wl in ("moe_mxfp4", "moe_prefill"):
         ids, gw = t(d["ids"]), t(d["gw"])
         ws_moe = torch.empty((ql.qlin_moe_mxfp4_workspace_bytes(Mmax, N, spec["topk"], spec["E"]),),
                              dtype=torch.uint8, device=dev)
         live = len(np.unique(d["ids"]))
+        live_of = {M: len(np.unique(d["ids"][:M])) for M in Ms}
     if wl == "moe_ffn_mxfp4":
         ws_ffn = torch.empty((ql.qlin_moe_ffn_mxfp4_workspace_bytes(Mmax, N, spec["I"], spec["topk"], spec["E"]),),
                              dtype=torch.uint8, device=dev)
@@ -268,16 +270,17 @@ def main():
         if wl == "fp8_blk":
             return [("act_quant_blk+gemv_fp8_blk", bytes_blk_call(M, N, K, bn, bk),
                      lambda: ql.qlin_gemv_fp8_blk_ex(xm, w, sc, bn, bk, xq=xq_buf[:M], xs=xsb_buf[:M], y=y_buf[:M]))]
-        if wl == "moe_mxfp4":
-            return [("moe_mxfp4", bytes_moe_call(M, N, K, spec["topk"], live),
-                     lambda: ql.qlin_moe_mxfp4(xm, w, s_copies[ci], ids, gw, y=y_buf[:M], workspace=ws_moe))]
+        if wl in ("moe_mxfp4", "moe_prefill"):
+            return [("moe_mxfp4", bytes_moe_call(M, N, K, spec["topk"], live_of[M]),
+                     lambda: ql.qlin_moe_mxfp4(xm, w, s_copies[ci], ids[:M], gw[:M], y=y_buf[:M],
+                                               workspace=ws_moe))]
         return [("moe_ffn_mxfp4", bytes_moe_ffn_call(M, N, spec["I"], spec["E"], spec["topk"], live_of[M]),
                  lambda: ql.qlin_moe_ffn_mxfp4(xm, wr, *ffn[ci], spec["topk"], y=y_buf[:M], workspace=ws_ffn,
                                                ids=ids_buf[:M], gw=gw_buf[:M]))]
 
     dominant = {"int8_decode": "gemv_i8", "fp8_decode": "gemv_fp8", "fp8_w8a8": "gemv_fp8_w8a8",
                 "int8_prefill": "gemv_i8", "fp8_prefill": "gemv_fp8",
-                "fp8_blk": "act_quant_blk+gemv_fp8_blk", "moe_mxfp4": "moe_mxfp4",
+                "fp8_blk": "act_quant_blk+gemv_fp8_blk", "moe_mxfp4": "moe_mxfp4", "moe_prefill": "moe_mxfp4",
                 "moe_ffn_mxfp4": "moe_ffn_mxfp4"}[wl]
 
     def run_step(step):
@@ -364,7 +367,7 @@ def main():
 
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = load_traffic(wl)
-    if wl.endswith("_prefill"):
+    if wl in ("int8_prefill", "fp8_prefill"):
         # compute-bound: algorithmic MACs x 2 per launch / launch duration, against
         # the dense matrix-core peak of the instruction's type (int8 5.0 POP/s,
         # bf16 2.5 PFLOP/s)
@@ -401,7 +404,7 @@ def main():
                 elif wl == "fp8_blk":
                     oracle.fp8_blk(xm, d["w"], d["ws"], bn, bk)
                 else:
-                    if wl == "moe_mxfp4":
+                    if wl in ("moe_mxfp4", "moe_prefill"):
                         oracle.moe_mxfp4(xm, d["w"], d["s"], d["ids"][:M], d["gw"][:M])
                     else:
                         oracle.moe_ffn_route_mxfp4(xm, d["wr"], spec["topk"], d["w13"], d["s13"], d["w2"], d["s2"])
@@ -425,10 +428,12 @@ def main():
         "fp8_w8a8": f"FP8 W8A8 E4M3 x E4M3 (per-token act quant + GEMV, per-channel ws) N={N} K={K}",
         "fp8_blk": f"{args.block.replace(',', 'x')} block-scaled FP8 (act quant + GEMV) N={N} K={K}",
         "moe_mxfp4": f"MXFP4 top-{spec.get('topk')} expert GEMV E={spec.get('E')} N={N} K={K}",
+        "moe_prefill": f"MXFP4 top-{spec.get('topk')} expert GEMM, prefill (pair sort + grouped GEMM + combine) "
+                       f"E={spec.get('E')} N={N} K={K}",
         "moe_ffn_mxfp4": f"MXFP4 top-{spec.get('topk')} expert FFN with routing E={spec.get('E')} "
                          f"H={N} I={spec.get('I')} (router, gate/up+SwiGLU, down, combine)",
     }[wl], "N": N, "K": K, "Ms": Ms, "weight_copies": B, "cold_weights": B * wbytes >= 2 * MALL_BYTES}
-    if wl in ("moe_mxfp4", "moe_ffn_mxfp4"):
+    if wl in ("moe_mxfp4", "moe_ffn_mxfp4", "moe_prefill"):
         cfg["live_experts"] = int(live)
 
     out = {
@@ -444,7 +449,7 @@ def main():
         "vs_baseline": None,
         "dtype": {"int8_decode": "int8", "fp8_decode": "fp8e4m3*bf16->f32", "fp8_w8a8": "fp8e4m3*fp8e4m3->f32",
                   "int8_prefill": "int8", "fp8_prefill": "fp8e4m3*bf16->f32",
-                  "fp8_blk": "fp8e4m3->f32", "moe_mxfp4": "fp4e2m1*bf16->f32",
+                  "fp8_blk": "fp8e4m3->f32", "moe_mxfp4": "fp4e2m1*bf16->f32", "moe_prefill": "fp4e2m1*bf16->f32",
                   "moe_ffn_mxfp4": "fp4e2m1*bf16->f32"}[wl],
         "data": "synthetic",
         "config": cfg,

@@ -37,10 +37,10 @@
  * - Device-resident data is not validated (that would need a host sync):
  *   NaN/Inf inputs give unspecified outputs; see each call for the rest.
  * - M (tokens): the dense entry points (INT8, FP8, FP8 W8A8, block FP8 and
- *   their quantisers) accept 1 <= M <= QLIN_MAX_M_PREFILL; up to 16 they run
- *   the decode GEMV kernels, above 16 a tiled matrix-core GEMM with the same
- *   arithmetic contract.  The MoE entry points and the per-tensor FP8
- *   quantiser take 1 <= M <= QLIN_MAX_M.  Base pointers and row pitches of
+ *   their quantisers) and qlin_moe_mxfp4 accept 1 <= M <= QLIN_MAX_M_PREFILL;
+ *   up to 16 they run the decode kernels, above 16 a tiled (grouped, for
+ *   the MoE) matrix-core GEMM with the same arithmetic contract.  The routed
+ *   expert FFN and the per-tensor FP8 quantiser take 1 <= M <= QLIN_MAX_M.  Base pointers and row pitches of
  *   weights, codes and bf16 activations must be 16-byte aligned (128-bit
  *   loads); scale arrays must be naturally aligned.
  */
@@ -215,8 +215,10 @@ int qlin_gemv_fp8_blk_ex(const void* x, int64_t ldx, int64_t M, int64_t K,
  *     scale formats of the OCP MX spec (E2M1, one UE8M0 per 32 elements)
  * ------------------------------------------------------------------------ */
 
-/* Bytes of device workspace qlin_moe_mxfp4 needs for these sizes
- * (per-(token, slot) fp32 partial rows, M * topk * N * 4, rounded up). */
+/* Bytes of device workspace qlin_moe_mxfp4 needs for these sizes: the
+ * per-(token, slot) fp32 partial rows, M * topk * N * 4 rounded up to 256;
+ * for M > 16 followed by the pair sort: int32 pair offsets [E+1], tile
+ * offsets [E+1] and pair order [M * topk], rounded up to 256. */
 size_t qlin_moe_mxfp4_workspace_bytes(int64_t M, int64_t N, int64_t topk, int64_t E);
 
 /* y[t,n] = bf16( sum_{j < topk} g[t,j] * sum_k e2m1(W[e,n,k]) * 2^(S[e,n,k/32]-127) * x[t,k] ),
@@ -224,7 +226,11 @@ size_t qlin_moe_mxfp4_workspace_bytes(int64_t M, int64_t N, int64_t topk, int64_
  * Steps: every (token, slot) pair is bucketed by its expert on the device;
  * each live expert's weights are streamed once for all its tokens (fp32
  * partial per pair into the workspace); then the partials are combined in
- * slot order j = 0..topk-1.  No host synchronisation.
+ * slot order j = 0..topk-1.  No host synchronisation.  For M > 16 (prefill)
+ * the pairs are sorted by expert and a grouped matrix-core GEMM computes
+ * 64 pairs x 64 rows per workgroup; there the block scale is applied in the
+ * E2M1 -> bf16 convert, exact for scale bytes 2..252 (values within bf16's
+ * normal range; the M <= 16 path folds the scale in fp32 at any byte).
  *   x         bf16 [M, ldx]
  *   w_fp4     uint8 [E, N, K/2]: element 2i of a row in the LOW nibble of byte i
  *   s_ue8m0   uint8 [E, N, K/32]
@@ -234,7 +240,8 @@ size_t qlin_moe_mxfp4_workspace_bytes(int64_t M, int64_t N, int64_t topk, int64_
  *   workspace device buffer of at least qlin_moe_mxfp4_workspace_bytes(),
  *             16-byte aligned; its contents on entry do not matter.
  * Requires K % 32 == 0, 32 <= K <= 30720 (one staged activation row must fit
- * the workgroup's 64 KiB LDS budget), 1 <= topk <= 16, E >= 1, ldx % 8 == 0. */
+ * the workgroup's 64 KiB LDS budget), 1 <= topk <= 16, E >= 1, ldx % 8 == 0,
+ * M <= QLIN_MAX_M_PREFILL, and E <= 1024 when M > 16. */
 int qlin_moe_mxfp4(const void* x, int64_t ldx, int64_t M, int64_t K,
                    const uint8_t* w_fp4, const uint8_t* s_ue8m0, int64_t E, int64_t N,
                    const int32_t* topk_ids, const float* topk_w, int64_t topk,

@@ -313,8 +313,17 @@ static hipError_t launch_combine(const float* part, const int32_t* ids, const fl
 }
 
 hipError_t launch_moe_mxfp4(const MoeArgs& a, hipStream_t st) {
+    hipError_t err;
+    if (a.M > 16) {  // prefill: sort the pairs by expert, grouped GEMM (moe_prefill.hip)
+        int32_t* offs = a.sort;
+        int32_t* toffs = offs + a.E + 1;
+        int32_t* perm = toffs + a.E + 1;
+        err = launch_moe_prefill_mxfp4(a, offs, toffs, perm, st);
+        if (err != hipSuccess) return err;
+        return launch_combine(a.part, a.ids, a.gw, a.M, a.topk, a.E, a.N, a.y, a.ldy, st);
+    }
     MoeKParams p{a.x, a.ldx, (int)a.M, a.K, a.w, a.s, a.E, a.N, a.ids, (int)a.topk, a.part, nullptr, 0.f, 0.f};
-    hipError_t err = launch_expert_any<kMoePlain>(p, st);
+    err = launch_expert_any<kMoePlain>(p, st);
     if (err != hipSuccess) return err;
     return launch_combine(a.part, a.ids, a.gw, a.M, a.topk, a.E, a.N, a.y, a.ldy, st);
 }

@@ -17,7 +17,8 @@ inline int launch_status(hipError_t e) { return e == hipSuccess ? QLIN_OK : QLIN
 
 constexpr int64_t kMaxKInt8 = 131072;  // K * 127 * 128 < 2^31: int32 accumulation is exact
 constexpr int64_t kMaxKFp8 = 1 << 24;  // keeps the quantiser's 32-bit vector indexes in range
-constexpr int64_t kMaxKBlkGeneral = 32768;  // the general block GEMV stages K/32 x 32 scale bytes in LDS
+constexpr int64_t kMaxKBlkGeneral = 32768;
+constexpr int64_t kMaxEPrefill = 1024;  // the pair sort counts experts in one workgroup's LDS  // the general block GEMV stages K/32 x 32 scale bytes in LDS
 
 }  // namespace
 
@@ -157,10 +158,12 @@ int qlin_gemv_fp8_blk_ex(const void* x, int64_t ldx, int64_t M, int64_t K,
 }
 
 size_t qlin_moe_mxfp4_workspace_bytes(int64_t M, int64_t N, int64_t topk, int64_t E) {
-    (void)E;
-    if (M < 1 || N < 1 || topk < 1) return 0;
-    const size_t b = (size_t)M * (size_t)topk * (size_t)N * sizeof(float);
-    return (b + 255) & ~(size_t)255;
+    if (M < 1 || N < 1 || topk < 1 || E < 1) return 0;
+    const size_t b = ((size_t)M * (size_t)topk * (size_t)N * sizeof(float) + 255) & ~(size_t)255;
+    if (M <= QLIN_MAX_M) return b;
+    // prefill: + pair offsets [E+1], tile offsets [E+1], pair order [M*topk] (int32)
+    const size_t s = ((size_t)(2 * (E + 1) + M * topk) * sizeof(int32_t) + 255) & ~(size_t)255;
+    return b + s;
 }
 
 int qlin_moe_mxfp4(const void* x, int64_t ldx, int64_t M, int64_t K,
@@ -168,17 +171,19 @@ int qlin_moe_mxfp4(const void* x, int64_t ldx, int64_t M, int64_t K,
                    const int32_t* topk_ids, const float* topk_w, int64_t topk,
                    void* y, int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
     if (!x || !w_fp4 || !s_ue8m0 || !topk_ids || !topk_w || !y) return QLIN_ERR_NULL;
-    if (M < 1 || M > QLIN_MAX_M || N < 1 || E < 1 || K < 32 || K % 32 != 0 || K > 30720 || topk < 1 ||
+    if (M < 1 || M > QLIN_MAX_M_PREFILL || N < 1 || E < 1 || K < 32 || K % 32 != 0 || K > 30720 || topk < 1 ||
         topk > 16)
         return QLIN_ERR_SHAPE;
+    if (M > QLIN_MAX_M && E > kMaxEPrefill) return QLIN_ERR_SHAPE;
     if (ldx < K || ldy < N) return QLIN_ERR_STRIDE;
     if (misaligned(x, 16) || ldx % 8 != 0 || misaligned(w_fp4, 16) || misaligned(topk_ids, 4) ||
         misaligned(topk_w, 4) || misaligned(y, 2))
         return QLIN_ERR_ALIGN;
     if (!workspace || workspace_bytes < qlin_moe_mxfp4_workspace_bytes(M, N, topk, E)) return QLIN_ERR_WORKSPACE;
     if (misaligned(workspace, 16)) return QLIN_ERR_ALIGN;
+    const size_t part_bytes = ((size_t)M * topk * N * sizeof(float) + 255) & ~(size_t)255;
     qlin::MoeArgs a{(const uint16_t*)x, ldx, M, K, w_fp4, s_ue8m0, E, N, topk_ids, topk_w, topk,
-                    (uint16_t*)y, ldy, (float*)workspace};
+                    (uint16_t*)y, ldy, (float*)workspace, (int32_t*)((char*)workspace + part_bytes)};
     return launch_status(qlin::launch_moe_mxfp4(a, (hipStream_t)stream));
 }
 

@@ -33,11 +33,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
-// UE8M0 byte -> fp32 scale 2^(b-127).  b = 0 is the fp32 subnormal 2^-127.
+// UE8M0 byte -> fp32 scale 2^(b-127).  b = 0 is the fp32 subnormal 2^-127,
+// b = 255 is NaN.  Selects, not branches (the compiler would otherwise put an
+// exec-mask branch around every scale in a kernel's inner loop).
 __device__ __forceinline__ float ue8m0_to_f32(uint32_t b) {
-    if (b == 0u) return __uint_as_float(0x00400000u);
-    if (b == 255u) return __uint_as_float(0x7FC00000u);
-    return __uint_as_float(b << 23);
+    uint32_t u = b << 23;
+    u = b == 0u ? 0x00400000u : u;
+    u = b == 255u ? 0x7FC00000u : u;
+    return __uint_as_float(u);
 }
 
 // Four E4M3 codes (one dword) -> two bf16 pairs, exact (E4M3 embeds in bf16).

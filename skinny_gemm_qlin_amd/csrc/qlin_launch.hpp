@@ -50,6 +50,7 @@ struct MoeArgs {
     const uint8_t* w; const uint8_t* s; int64_t E; int64_t N;
     const int32_t* ids; const float* gw; int64_t topk;
     uint16_t* y; int64_t ldy; float* part;
+    int32_t* sort;  // M > 16: pair offsets [E+1], tile offsets [E+1], pair order [M*topk]
 };
 
 hipError_t launch_act_quant_i8(const ActQuantI8Args& a, hipStream_t st);
@@ -63,6 +64,7 @@ hipError_t launch_gemv_fp8_blk(const BlkArgs& a, hipStream_t st);
 hipError_t launch_blkg_act_quant(const BlkQuantArgs& a, int64_t bk, hipStream_t st);
 hipError_t launch_gemv_fp8_blkg(const BlkArgs& a, int64_t bn, int64_t bk, hipStream_t st);
 hipError_t launch_moe_mxfp4(const MoeArgs& a, hipStream_t st);
+hipError_t launch_moe_prefill_mxfp4(const MoeArgs& a, int32_t* offs, int32_t* toffs, int32_t* perm, hipStream_t st);
 
 // prefill GEMM (M > 16), called by the launchers above
 hipError_t launch_gemm_i8(const I8Args& a, hipStream_t st);

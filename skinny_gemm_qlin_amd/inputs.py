@@ -140,5 +140,6 @@ WORKLOADS = {
     "fp8_prefill": {"kind": "fp8", "N": 17408, "K": 5120, "Ms": [128, 512, 2048]},
     "fp8_blk": {"kind": "fp8_blk", "N": 4096, "K": 7168, "Ms": [1, 8, 16]},
     "moe_mxfp4": {"kind": "moe", "E": 64, "N": 2048, "K": 7168, "Ms": [8], "topk": 6},
+    "moe_prefill": {"kind": "moe", "E": 64, "N": 2048, "K": 7168, "Ms": [64, 512], "topk": 6},
     "moe_ffn_mxfp4": {"kind": "moe_ffn", "E": 64, "H": 7168, "I": 2048, "Ms": [8], "topk": 6},
 }

@@ -21,8 +21,8 @@ from typing import Optional, Tuple
 
 import torch
 
-from . import (qlin_act_quant_fp8, qlin_act_quant_i8, qlin_gemv_fp8, qlin_gemv_fp8_blk, qlin_gemv_fp8_w8a8,
-               qlin_gemv_i8, qlin_moe_ffn_mxfp4, qlin_moe_mxfp4)
+from . import (qlin_act_quant_fp8, qlin_act_quant_i8, qlin_gemv_fp8, qlin_gemv_fp8_blk, qlin_gemv_fp8_blk_ex,
+               qlin_gemv_fp8_w8a8, qlin_gemv_i8, qlin_moe_ffn_mxfp4, qlin_moe_mxfp4)
 
 hits = collections.Counter()
 
@@ -132,6 +132,17 @@ def gemv_fp8_blk(x: torch.Tensor, w: torch.Tensor, ws: torch.Tensor) -> torch.Te
 
 @gemv_fp8_blk.register_fake
 def _(x, w, ws):
+    return x.new_empty((x.shape[0], w.shape[0]), dtype=torch.bfloat16)
+
+
+@torch.library.custom_op("qlin::gemv_fp8_blk_ex", mutates_args=())
+def gemv_fp8_blk_ex(x: torch.Tensor, w: torch.Tensor, ws: torch.Tensor, block_n: int, block_k: int) -> torch.Tensor:
+    hits["gemv_fp8_blk_ex"] += 1
+    return qlin_gemv_fp8_blk_ex(x, w, ws, block_n, block_k)[0]
+
+
+@gemv_fp8_blk_ex.register_fake
+def _(x, w, ws, block_n, block_k):
     return x.new_empty((x.shape[0], w.shape[0]), dtype=torch.bfloat16)
 
 

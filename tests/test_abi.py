@@ -210,6 +210,13 @@ def test_moe_errors(q):
     assert call(wsb=need - 1) == -5
     assert call(ws=A + 4) == -4
     assert call(w=A + 8) == -4
+    # prefill (M > 16): the workspace also holds the pair sort (offsets and order)
+    big = q.qlin_moe_mxfp4_workspace_bytes(512, 2048, 6, 64)
+    part = 512 * 6 * 2048 * 4
+    assert big == part + (((2 * 65 + 512 * 6) * 4 + 255) // 256) * 256
+    assert call(M=512, wsb=part) == -5
+    assert call(M=16385, wsb=big) == -2
+    assert call(M=17, E=1025, wsb=q.qlin_moe_mxfp4_workspace_bytes(17, 2048, 6, 1025)) == -2
 
 
 def test_moe_ffn_errors(q):

@@ -27,7 +27,9 @@ def args(ql):
     dm = gen_moe(4, 8, 128, 512, 2, seed=4)
     dn = gen_moe_ffn(4, 8, 256, 64, 2, seed=5)
     dw = gen_fp8_w8a8(6, 256, 1024, w_fmt=1, seed=6)
+    dx = gen_fp8_blk(3, 256, 1024, seed=7, block_n=1, block_k=32)
     return {
+        "gemv_fp8_blk_ex": (dev_bf16(dx["x"]), dev(dx["w"]), dev(dx["ws"]), 1, 32),
         "linear_fp8_w8a8": (dev_bf16(dw["x"]), dev(dw["w"]), dev(dw["ws"]), 0, 1, True),
         "linear_i8": (dev_bf16(d8["x"]), dev(d8["w"]), dev(d8["ws"])),
         "gemv_fp8": (dev_bf16(df["x"]), dev(df["w"]), dev(df["ws"])),
@@ -56,6 +58,7 @@ def test_opcheck_every_operator(ql, args):
              (torch.ops.qlin.linear_i8.default, args["linear_i8"]),
              (torch.ops.qlin.gemv_fp8.default, args["gemv_fp8"]),
              (torch.ops.qlin.gemv_fp8_blk.default, args["gemv_fp8_blk"]),
+             (torch.ops.qlin.gemv_fp8_blk_ex.default, args["gemv_fp8_blk_ex"]),
              (torch.ops.qlin.moe_mxfp4.default, args["moe_mxfp4"]),
              (torch.ops.qlin.moe_ffn_mxfp4.default, args["moe_ffn_mxfp4"])]
     for op, a in cases:

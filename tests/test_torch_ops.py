@@ -19,6 +19,7 @@ def _inputs(M=3, N=256, K=512, E=8, H=256, I=64):
         "wf8": torch.empty((N, K), dtype=torch.uint8),
         "ws": torch.empty((N,), dtype=torch.float32),
         "wsb": torch.empty(((N + 127) // 128, K // 128), dtype=torch.uint8),
+        "wsmx": torch.empty((N, K // 32), dtype=torch.uint8),
         "wm": torch.empty((E, N, K // 2), dtype=torch.uint8),
         "sm": torch.empty((E, N, K // 32), dtype=torch.uint8),
         "ids": torch.empty((M, 2), dtype=torch.int32),
@@ -41,6 +42,7 @@ def test_fake_shapes_and_dtypes():
                   torch.ops.qlin.linear_i8(d["x"], d["w8"], d["ws"]),
                   torch.ops.qlin.gemv_fp8(d["x"], d["wf8"], d["ws"]),
                   torch.ops.qlin.gemv_fp8_blk(d["x"], d["wf8"], d["wsb"]),
+                  torch.ops.qlin.gemv_fp8_blk_ex(d["x"], d["wf8"], d["wsmx"], 1, 32),
                   torch.ops.qlin.moe_mxfp4(d["x"], d["wm"], d["sm"], d["ids"], d["gw"])):
             assert y.shape == (3, 256) and y.dtype == torch.bfloat16
         for fmt in (0, 1):
