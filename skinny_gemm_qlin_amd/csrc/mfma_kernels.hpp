@@ -338,12 +338,15 @@ __device__ __forceinline__ void fp8x16_to_bf16x8x2(const u32x4_t& c, bf16x8_t& l
     hi = bf16x8_t{b[4][0], b[4][1], b[5][0], b[5][1], b[6][0], b[6][1], b[7][0], b[7][1]};
 }
 
-template <int U, int KS, int XF, int WF>
+// XL: the activation codes are staged through a per-wave LDS tile like the
+// weights (row-contiguous loads), for the larger token counts.
+template <int U, int KS, int XF, int WF, bool XL = false>
 __global__ __launch_bounds__(64 * KS) void gemv_fp8_w8a8_mfma_kernel(
     const uint8_t* __restrict__ xq, int64_t ldxq, const float* __restrict__ xs, int xs_step, int M,
     int64_t K, const uint8_t* __restrict__ w, int64_t ldw, int64_t N,
     const float* __restrict__ ws, int ws_step, uint16_t* __restrict__ y, int64_t ldy) {
     __shared__ __align__(16) uint8_t tile[KS][16 * kTilePitch];
+    __shared__ __align__(16) uint8_t xtile[XL ? KS : 1][16 * kTilePitch];
     __shared__ f32x4_t red[KS][64];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int mi = lane & 15, mg = lane >> 4;
@@ -356,27 +359,34 @@ __global__ __launch_bounds__(64 * KS) void gemv_fp8_w8a8_mfma_kernel(
     uint8_t* t = tile[wv];
 
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    const XTileLoader xtl(xq, ldxq, M);
     for (int64_t c = c0; c < c1; c += U) {
         u32x4_t wv_[U][4], xb[U][4];
 #pragma unroll
         for (int u = 0; u < U; ++u) tl.load(wv_[u], c + u < c1 ? c + u : c1 - 1, K);
+        if constexpr (XL) {
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+            for (int u = 0; u < U; ++u) xtl.load(xb[u], c + u, K, c + u < c1);
+        } else {
 #pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) {
-                const int64_t k = (c + u) * 256 + 64 * s4 + 16 * mg;
-                const bool ok = (c + u < c1) && k < K && xon;
-                const u32x4_t v = ld16(xr + (ok ? k : 0));
-                xb[u][s4] = ok ? v : u32x4_t{0, 0, 0, 0};
-            }
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    const int64_t k = (c + u) * 256 + 64 * s4 + 16 * mg;
+                    const bool ok = (c + u < c1) && k < K && xon;
+                    const u32x4_t v = ld16(xr + (ok ? k : 0));
+                    xb[u][s4] = ok ? v : u32x4_t{0, 0, 0, 0};
+                }
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             tile_store(t, wv_[u]);
+            if constexpr (XL) tile_store(xtile[wv], xb[u]);
 #pragma unroll
             for (int s4 = 0; s4 < 4; ++s4) {
                 bf16x8_t a0, a1, b0, b1;
                 fp8x16_to_bf16x8x2<WF>(tile_read(t, 64 * s4), a0, a1);
-                fp8x16_to_bf16x8x2<XF>(xb[u][s4], b0, b1);
+                fp8x16_to_bf16x8x2<XF>(XL ? tile_read(xtile[wv], 64 * s4) : xb[u][s4], b0, b1);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, acc, 0, 0, 0);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc, 0, 0, 0);
             }
