@@ -177,7 +177,10 @@ int qlin_gemv_fp8_w8a8(const uint8_t* xq, int64_t ldxq, const float* xs, int xs_
  *      clamped to [1, 254] (E = 127 for an all-zero group);
  *      xq[m,k] = e4m3_rne(x[m,k] / 2^(E-127)),  xs[m,kb] = E.
  *    xq / xs are written to the caller's buffers (they are also the exported
- *    quantised activations).
+ *    quantised activations).  For M = 1 and K <= 32768 both steps run in one
+ *    kernel (each workgroup quantises the row into its LDS, and each group is
+ *    written to xq / xs by exactly one workgroup); otherwise the step-2
+ *    kernel reads xq / xs back.  The results are the same either way.
  * 2. out[m,n] = sum_kb ( sum_{k in kb} xq[m,k] * w[n,k] )
  *                     * 2^(xs[m,kb]-127) * 2^(ws[n/128, kb]-127)
  *    The block scales multiply each lane's partial sum of the current block

@@ -120,18 +120,8 @@ __global__ __launch_bounds__(64) void blk_act_quant_kernel(
     for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(f[e]));
     a = row_max_f32(a);
 
-    int E = 127;
-    if (a != 0.0f) {
-        const uint32_t bits = __float_as_uint(a);
-        const int ex = (int)(bits >> 23);  // biased exponent; 0 for a subnormal amax
-        int p;
-        if (ex == 0) p = -200;             // amax < 2^-126: clamps to E = 1 below
-        else p = (ex - 127) - (((bits & 0x7FFFFFu) <= 0x600000u) ? 8 : 7);
-        E = 127 + p;
-        E = E < 1 ? 1 : (E > 254 ? 254 : E);
-    }
-    const int inv = 254 - E;  // biased exponent of 2^(127-E)
-    const float sc = inv == 0 ? __uint_as_float(0x00400000u) : __uint_as_float((uint32_t)inv << 23);
+    const int E = blk_group_exp(a);
+    const float sc = blk_group_inv_scale(E);
 
     int lo = 0, hi = 0;
     lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0] * sc, f[1] * sc, lo, false);
@@ -266,18 +256,8 @@ __global__ __launch_bounds__(256) void blkg_act_quant_kernel(
     for (int64_t g = threadIdx.x; g < nkb; g += 256) {
         float a = 0.0f;
         for (int64_t v = 0; v < bk; v += 8) a = absmax8(ld16(row + g * bk + v), a);
-        int E = 127;
-        if (a != 0.0f) {
-            const uint32_t bits = __float_as_uint(a);
-            const int ex = (int)(bits >> 23);
-            int p;
-            if (ex == 0) p = -200;
-            else p = (ex - 127) - (((bits & 0x7FFFFFu) <= 0x600000u) ? 8 : 7);
-            E = 127 + p;
-            E = E < 1 ? 1 : (E > 254 ? 254 : E);
-        }
-        const int inv = 254 - E;
-        const float sc = inv == 0 ? __uint_as_float(0x00400000u) : __uint_as_float((uint32_t)inv << 23);
+        const int E = blk_group_exp(a);
+        const float sc = blk_group_inv_scale(E);
         xs[m * nkb + g] = (uint8_t)E;
         for (int64_t v = 0; v < bk; v += 8) {
             const u32x4_t d = ld16(row + g * bk + v);

@@ -445,4 +445,128 @@ __global__ __launch_bounds__(64 * WPB) void gemv_fp8_blk_m1_kernel(
     if (j == 0) y[n] = f32_to_bf16(acc);
 }
 
+// M = 1 block-scaled FP8 with the activation quantisation fused in (one
+// launch instead of two).  Each wave first issues the loads of its row's
+// first batch of weights (after its first activation load), then the
+// workgroup quantises the token's row into
+// LDS (a 16-lane DPP row per 128-group, 8 values per lane, the rule of
+// blk_act_quant_kernel: bit-identical codes) with the decoded group scales
+// 2^(E-127), so the quantisation runs under the weights' HBM latency.  After
+// one barrier each wave runs the gemv_fp8_blk_m1_kernel loop on its row with
+// codes and scales read from LDS.  Group g is exported to xq / xs by
+// workgroup g % gridDim.x alone.  Dynamic LDS: K code bytes, then K/128
+// floats.
+template <int U, int WPB>
+__global__ __launch_bounds__(64 * WPB) void gemv_fp8_blk_m1_fq_kernel(
+    const uint16_t* __restrict__ x, int64_t K,
+    const uint8_t* __restrict__ w, int64_t ldw, int64_t N, const uint8_t* __restrict__ ws,
+    uint8_t* __restrict__ xq, uint8_t* __restrict__ xs, uint16_t* __restrict__ y) {
+    static_assert(U >= 1 && U <= 8, "one scale per lane covers at most 8 steps");
+    extern __shared__ __align__(16) uint8_t lds[];
+    uint8_t* xl = lds;
+    float* sl = (float*)(lds + K);  // K % 128 == 0 keeps it aligned
+    const int64_t nkb = K >> 7;
+    const int j = threadIdx.x & 63;
+    const int64_t n = first_row<64, 1, WPB>();
+    const bool live = n < N;  // wave-uniform
+    const uint8_t* wr = w + (live ? n : N - 1) * ldw;
+    const int64_t nchunk = K >> 4;
+    const int64_t nsteps = (nchunk + 63) >> 6;
+    auto load_w = [&](u32x4_t (&wv)[U], int64_t s) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = (s + u) * 64 + j;
+            wv[u] = ld_stream(wr + (c < nchunk ? c : nchunk - 1) * 16);
+        }
+    };
+    const int64_t ngl = nkb * 16;  // one lane per 8 values (K >= 128: ngl >= 16)
+    auto ld_x = [&](int64_t i0) {
+        const int64_t i = i0 + threadIdx.x;
+        return ld16(x + (i < ngl ? i : ngl - 1) * 8);
+    };
+    auto quant_pass = [&](int64_t i0, const u32x4_t& v) {
+        const int64_t i = i0 + threadIdx.x;
+        const bool ok = i < ngl;
+        const int64_t g = ok ? (i >> 4) : nkb - 1;
+        const int jj = (int)(i & 15);
+        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+        float f[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            f[2 * q] = bf16_to_f32(d[q] & 0xFFFFu);
+            f[2 * q + 1] = bf16_to_f32(d[q] >> 16);
+        }
+        float a = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(f[e]));
+        a = row_max_f32(a);  // the 16 lanes of a DPP row hold one group
+        const int E = blk_group_exp(a);
+        const float sc = blk_group_inv_scale(E);
+        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0] * sc, f[1] * sc, 0, false);
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2] * sc, f[3] * sc, lo, true);
+        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4] * sc, f[5] * sc, 0, false);
+        hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6] * sc, f[7] * sc, hi, true);
+        if (ok) {
+            const uint2 c = make_uint2((uint32_t)lo, (uint32_t)hi);
+            *(uint2*)(xl + g * 128 + jj * 8) = c;
+            if (jj == 0) sl[g] = ue8m0_to_f32((uint32_t)E);
+            if ((uint32_t)g % gridDim.x == blockIdx.x) {
+                *(uint2*)(xq + g * 128 + jj * 8) = c;
+                if (jj == 0) xs[g] = (uint8_t)E;
+            }
+        }
+    };
+    // the first pass's activations are requested before the weights: loads
+    // complete in issue order, so its quantisation runs while the weight
+    // batch is still in flight
+    const u32x4_t x0 = ld_x(0);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* wsr = ws + ((live ? n : N - 1) >> 7) * nkb;
+    auto ld_sw = [&](int64_t s) {  // lane j: weight scale byte of K block s*8 + j
+        const int64_t kbl = s * 8 + j;
+        return wsr[j < 8 * U && kbl < nkb ? kbl : 0];
+    };
+    u32x4_t wv[U];
+    load_w(wv, 0);
+    uint8_t swb = ld_sw(0);
+    __builtin_amdgcn_sched_barrier(0);
+    quant_pass(0, x0);
+    for (int64_t i0 = 64 * WPB; i0 < ngl; i0 += 64 * WPB) quant_pass(i0, ld_x(i0));  // uniform trip count
+    __syncthreads();
+    if (!live) return;  // no barrier follows
+
+    float acc = 0.0f;
+    for (int64_t s = 0; s < nsteps; s += U) {
+        if (s > 0) {
+            load_w(wv, s);
+            swb = ld_sw(s);
+        }
+        const int64_t kbl = s * 8 + j;
+        const bool okb = j < 8 * U && kbl < nkb;
+        const float swl = okb ? ue8m0_to_f32(swb) : 0.0f;
+        const float sxl = okb ? sl[okb ? kbl : 0] : 0.0f;
+        u32x4_t xv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = (s + u) * 64 + j;
+            xv[u] = *(const u32x4_t*)(xl + (c < nchunk ? c : nchunk - 1) * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool ok = (s + u) * 64 + j < nchunk;
+            const float sw = __shfl(swl, u * 8 + (j >> 3));
+            const float sx = __shfl(sxl, u * 8 + (j >> 3));
+            bf16x2_t xb[8], wb[8];
+            e4m3x16(xv[u], xb);
+            e4m3x16(wv[u], wb);
+            float loc = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) loc = dot2(wb[i], xb[i], loc);
+            acc += ok ? (loc * sx) * sw : 0.0f;  // a lane past the row end adds 0
+        }
+    }
+    acc = group_sum<64>(acc);
+    if (j == 0) y[n] = f32_to_bf16(acc);
+}
+
 }  // namespace qlin

@@ -125,9 +125,11 @@ int qlin_gemv_fp8_blk(const void* x, int64_t ldx, int64_t M, int64_t K,
         return QLIN_ERR_ALIGN;
     hipStream_t st = (hipStream_t)stream;
     qlin::BlkQuantArgs qa{(const uint16_t*)x, ldx, M, K, xq, xs};
+    qlin::BlkArgs a{xq, xs, M, K, w, ldw, N, ws, (uint16_t*)y, ldy};
+    if (M == 1 && K <= qlin::kBlkFusedMaxK)  // one launch
+        return launch_status(qlin::launch_gemv_fp8_blk_fq(qa, a, st));
     hipError_t e = qlin::launch_blk_act_quant(qa, st);
     if (e != hipSuccess) return QLIN_ERR_LAUNCH;
-    qlin::BlkArgs a{xq, xs, M, K, w, ldw, N, ws, (uint16_t*)y, ldy};
     return launch_status(qlin::launch_gemv_fp8_blk(a, st));
 }
 

@@ -43,6 +43,28 @@ __device__ __forceinline__ float ue8m0_to_f32(uint32_t b) {
     return __uint_as_float(u);
 }
 
+// UE8M0 exponent byte of an activation group whose absolute maximum is amax:
+// E = 127 + p for the smallest integer p with amax <= 448 * 2^p, clamped to
+// [1, 254]; amax = 0 gives 127 [DSV4 section 3.3: power-of-two block scales;
+// Z100 section 2.4].  With amax = (1 + f) * 2^(e-127), 448 = 1.75 * 2^8 gives
+// p = e - 135 when 1 + f <= 1.75 and e - 134 otherwise; a subnormal amax
+// (e = 0) lands below 1 and clamps to 1.
+__device__ __forceinline__ int blk_group_exp(float amax) {
+    const uint32_t bits = __float_as_uint(amax);
+    const int ex = (int)(bits >> 23);
+    int E = ex - (((bits & 0x7FFFFFu) <= 0x600000u) ? 8 : 7);
+    E = E < 1 ? 1 : (E > 254 ? 254 : E);
+    return amax == 0.0f ? 127 : E;
+}
+
+// 2^(127 - E) for E in [1, 254], the factor that maps a group onto the E4M3
+// range (E = 254 gives the fp32 subnormal 2^-127; every product stays exact
+// wherever the E4M3 rounding can see it).
+__device__ __forceinline__ float blk_group_inv_scale(int E) {
+    const int inv = 254 - E;
+    return inv == 0 ? __uint_as_float(0x00400000u) : __uint_as_float((uint32_t)inv << 23);
+}
+
 // Four E4M3 codes (one dword) -> two bf16 pairs, exact (E4M3 embeds in bf16).
 __device__ __forceinline__ void e4m3x4_to_bf16(uint32_t d, bf16x2_t& lo, bf16x2_t& hi) {
     lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.0f, false);

@@ -60,6 +60,9 @@ hipError_t launch_act_quant_fp8(const ActQuantF8Args& a, hipStream_t st);
 hipError_t launch_gemv_fp8_w8a8(const W8A8F8Args& a, hipStream_t st);
 hipError_t launch_blk_act_quant(const BlkQuantArgs& a, hipStream_t st);
 hipError_t launch_gemv_fp8_blk(const BlkArgs& a, hipStream_t st);
+// act quant + GEMV in one launch (M = 1, K <= kBlkFusedMaxK)
+constexpr int64_t kBlkFusedMaxK = 32768;
+hipError_t launch_gemv_fp8_blk_fq(const BlkQuantArgs& q, const BlkArgs& a, hipStream_t st);
 // any block shape (block_k a multiple of 32), M <= 16 per launch
 hipError_t launch_blkg_act_quant(const BlkQuantArgs& a, int64_t bk, hipStream_t st);
 hipError_t launch_gemv_fp8_blkg(const BlkArgs& a, int64_t bn, int64_t bk, hipStream_t st);

@@ -43,7 +43,9 @@ def test_blk_small_all_M(ql, orc, M):
                                    # M = 1 kernel: partial step, two batches, three batches with a short last one
                                    (1, 5, 1152), (1, 67, 9216), (1, 3, 16512),
                                    # 512..1023 row tiles: eight waves split K
-                                   (4, 9000, 2048), (16, 8200, 2304)])
+                                   (4, 9000, 2048), (16, 8200, 2304),
+                                   # one workgroup exports every group; M = 1 past the fused path's K limit
+                                   (7, 1, 2048), (16, 9, 1280), (1, 3, 33024), (2, 3, 33024)])
 def test_blk_ragged(ql, orc, M, N, K):
     d = gen_fp8_blk(M, N, K, seed=N + K)
     _check(orc, d, _gpu(ql, d))
@@ -112,3 +114,12 @@ def test_blk_deterministic(ql):
     ref = ql.qlin_gemv_fp8_blk(x, w, ws)[0]
     for _ in range(10):
         assert torch.equal(ql.qlin_gemv_fp8_blk(x, w, ws)[0].view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("M", [1, 5, 16])
+def test_blk_padded_activation_stride(ql, orc, M):
+    d = gen_fp8_blk(M, 300, 1024, seed=44 + M)
+    xp = padded(d["x"].view(np.int16), 40).view(torch.bfloat16)  # row pitch 1064 elements
+    y, xq, xs = ql.qlin_gemv_fp8_blk(xp, dev(d["w"]), dev(d["ws"]))
+    torch.cuda.synchronize()
+    _check(orc, d, (host_bits(y), host(xq), host(xs)))
