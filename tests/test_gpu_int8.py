@@ -54,6 +54,15 @@ def test_int8_ragged(ql, orc, M, N, K):
     _check(orc, d["x"], d["w"], d["ws"], _run_full(ql, d["x"], d["w"], d["ws"]))
 
 
+# >= 1024 row tiles (four waves split K) and M >= 12: every 256-K chunk of a
+# wave in flight at once for 1..5 chunks per wave, the chunk loop above that;
+# ragged K tails inside the last chunk
+@pytest.mark.parametrize("M,K", [(12, 768), (12, 1040), (16, 2064), (13, 3072), (16, 4096), (16, 5008), (12, 5376)])
+def test_int8_large_n_chunks_in_flight(ql, orc, M, K):
+    d = gen_int8(M, 16400, K, seed=M + K)
+    _check(orc, d["x"], d["w"], d["ws"], _run_full(ql, d["x"], d["w"], d["ws"]))
+
+
 # decode config: N=17408, K=5120, every M of the workload, full comparison
 @pytest.fixture(scope="module")
 def decode_w():
