@@ -16,6 +16,24 @@ hipError_t run_gemm(const GemmParams& p, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <int WF, int ACT, int EPI, int BN, int BM>
+hipError_t run_gemm_dma(const GemmParams& p, hipStream_t st) {
+    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+    const int64_t grid = (tiles + 7) / 8 * 8;
+    hipLaunchKernelGGL((gemm_dma_kernel<WF, ACT, EPI, BN, BM>), dim3((unsigned)grid), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+// Direct-to-LDS kernel, one-byte operands, K % 128 == 0.  Tiles (weight rows
+// x tokens, measured with INT8 at N = 17408, K = 5120): 64 x 64 up to 256
+// tokens, 64 x 128 up to 1024, 128 x 128 above.
+template <int WF, int ACT, int EPI>
+hipError_t run_dma(const GemmParams& p, hipStream_t st) {
+    if (p.M <= 256) return run_gemm_dma<WF, ACT, EPI, 64, 64>(p, st);
+    if (p.M <= 1024) return run_gemm_dma<WF, ACT, EPI, 64, 128>(p, st);
+    return run_gemm_dma<WF, ACT, EPI, 128, 128>(p, st);
+}
+
 }  // namespace
 
 // Tile choice (measured at N = 17408, K = 5120): up to 256 tokens the 64 x 64
@@ -27,6 +45,7 @@ constexpr int64_t kSmallTileMaxM = 256;
 hipError_t launch_gemm_i8(const I8Args& a, hipStream_t st) {
     GemmParams p{a.xq, a.ldxq, a.xs, a.xs_step, nullptr, a.M, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step,
                  nullptr, a.bias, a.y, a.ldy, a.out_kind};
+    if (a.K % 128 == 0) return run_dma<kFmtE4M3, kActI8, kEpiI8>(p, st);
     if (a.M <= kSmallTileMaxM) return run_gemm<kFmtE4M3, kActI8, kEpiI8, 2, 2, 128>(p, st);
     return run_gemm<kFmtE4M3, kActI8, kEpiI8, 4, 4, 128>(p, st);
 }
@@ -41,6 +60,13 @@ hipError_t launch_gemm_fp8(const F8Args& a, hipStream_t st) {
 hipError_t launch_gemm_fp8_w8a8(const W8A8F8Args& a, hipStream_t st) {
     GemmParams p{a.xq, a.ldxq, a.xs, a.xs_step, nullptr, a.M, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step,
                  nullptr, nullptr, a.y, a.ldy, 0};
+    if (a.K % 128 == 0) {
+        if (a.x_fmt == kFmtE5M2)
+            return a.w_fmt == kFmtE5M2 ? run_dma<kFmtE5M2, kActE5M2, kEpiXsWs>(p, st)
+                                       : run_dma<kFmtE4M3, kActE5M2, kEpiXsWs>(p, st);
+        return a.w_fmt == kFmtE5M2 ? run_dma<kFmtE5M2, kActE4M3, kEpiXsWs>(p, st)
+                                   : run_dma<kFmtE4M3, kActE4M3, kEpiXsWs>(p, st);
+    }
     const bool small = a.M <= kSmallTileMaxM;
     if (a.x_fmt == kFmtE5M2) {
         if (a.w_fmt == kFmtE5M2)
@@ -59,7 +85,7 @@ hipError_t launch_gemm_fp8_w8a8(const W8A8F8Args& a, hipStream_t st) {
 hipError_t launch_gemm_fp8_blk(const BlkArgs& a, hipStream_t st) {
     GemmParams p{a.xq, a.K, nullptr, 0, a.xs, a.M, a.K, a.w, a.ldw, a.N, nullptr, 0,
                  a.ws, nullptr, a.y, a.ldy, 0};
-    return run_gemm<kFmtE4M3, kActE4M3, kEpiBlk, 2, 2, 128>(p, st);
+    return run_dma<kFmtE4M3, kActE4M3, kEpiBlk>(p, st);  // K % 128 == 0 by contract
 }
 
 }  // namespace qlin

@@ -262,4 +262,240 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
     }
 }
 
+// ------------------------------------------------------------------ direct-to-LDS variant
+// For one-byte operands on both sides (INT8, FP8 W8A8, block FP8) and K a
+// multiple of 128.  The tiles travel global -> LDS with
+// global_load_lds_dwordx4 (no VGPR staging, no LDS store instructions) into a
+// two-stage ring of 128-byte-deep K tiles: one load instruction covers 8 rows
+// x 128 bytes, i.e. whole 128-byte lines (64-byte row pieces measured 40%
+// slower through L2).  In LDS a row's 16-byte chunk c sits at position
+// c ^ ((row >> 1) & 7), so the 32x32 MFMA fragment reads (16 bytes of 32
+// consecutive rows per half-wave) spread over all banks; a lane picks the
+// global chunk that lands on its fixed LDS slot.  Each wave waits for its own
+// loads with an explicit vmcnt, then one barrier publishes the stage to the
+// workgroup (a __syncthreads() would make the compiler drain every
+// outstanding load first).  4 waves, 2 x 2, each (BN/2) x (BM/2) of 32 x 32
+// MFMA tiles: v_mfma_i32_32x32x32_i8 for INT8; FP8 codes are widened to bf16
+// as fragments are read (exact) for v_mfma_f32_32x32x16_bf16.  The block-FP8
+// epilogue folds both scales per K tile (= one 128-wide K block).
+// Measured at N = 17408, K = 5120 (INT8): M = 128 / 512 / 2048 / 4096 about
+// 8 / 20 / 11 / 10% faster than gemm_kernel.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef int i32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+template <int N_>
+__device__ __forceinline__ void wait_vmcnt() {  // s_waitcnt vmcnt(N_), other counters untouched
+    static_assert(N_ >= 0 && N_ < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((N_ & 15) | ((N_ >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// Workgroup barrier that does not wait for outstanding global loads: the
+// signal fences keep the compiler from moving memory operations across it.
+__device__ __forceinline__ void stage_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+__device__ __forceinline__ int dma_swz(int row) { return (row >> 1) & 7; }
+
+template <int WF, int ACT, int EPI, int BN, int BM>
+__global__ __launch_bounds__(256) void gemm_dma_kernel(const GemmParams p) {
+    constexpr bool kI8 = ACT == kActI8;
+    static_assert(ACT != kActBf16, "one-byte activation codes");
+    static_assert(BN % 64 == 0 && BM % 64 == 0 && BN <= 128 && BM <= 128, "tile");
+    constexpr int BK = 128;                                // bytes = K elements per stage
+    constexpr int WT = BN * BK, XT = BM * BK, ST = WT + XT;
+    constexpr int WI = BN / 8 / 4, XI = BM / 8 / 4;        // load instructions per wave and stage
+    constexpr int LPS = WI + XI;
+    constexpr int TN = BN / 64, TM = BM / 64;              // 32 x 32 tiles per wave
+    __shared__ __align__(16) uint8_t lds[2 * ST];
+
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const int64_t tiles_m = (M + BM - 1) / BM;
+    const int64_t tiles = tiles_m * ((N + BN - 1) / BN);
+    const int64_t per_xcd = (int64_t)gridDim.x / 8;  // the grid is a multiple of 8
+    const int64_t t = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (t >= tiles) return;  // workgroup-uniform
+    const int64_t n0 = (t / tiles_m) * BN, m0 = (t % tiles_m) * BM;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+
+    // this lane's load sources: row (wv*WI + i)*8 + lane/8, the chunk that
+    // belongs in LDS slot lane%8 of that row
+    const uint8_t* wsrc[WI];
+    const uint8_t* xsrc[XI];
+#pragma unroll
+    for (int i = 0; i < WI; ++i) {
+        const int r = (wv * WI + i) * 8 + (lane >> 3);
+        const int64_t n = n0 + r < N ? n0 + r : N - 1;  // rows past N: clamped, not stored
+        wsrc[i] = (const uint8_t*)p.w + n * p.ldw + (((lane & 7) ^ dma_swz(r)) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < XI; ++i) {
+        const int r = (wv * XI + i) * 8 + (lane >> 3);
+        const int64_t m = m0 + r < M ? m0 + r : M - 1;
+        xsrc[i] = (const uint8_t*)p.x + m * p.ldx + (((lane & 7) ^ dma_swz(r)) * 16);
+    }
+    auto issue = [&](int64_t kt, int slot) {
+        uint8_t* base = lds + slot * ST;
+#pragma unroll
+        for (int i = 0; i < WI; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(wsrc[i] + kt * BK),
+                                             (lds_void_t*)(base + (wv * WI + i) * 1024), 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < XI; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(xsrc[i] + kt * BK),
+                                             (lds_void_t*)(base + WT + (wv * XI + i) * 1024), 16, 0, 0);
+    };
+
+    const int wn = wv & 1, wm = wv >> 1;
+    const int row = lane & 31, half = lane >> 5;
+    typedef typename std::conditional<kI8, i32x16_t, f32x16_t>::type acc_t;
+    acc_t acc[TN][TM], dblk[TN][TM];
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+            acc[i][j] = acc_t{};
+            dblk[i][j] = acc_t{};
+        }
+    (void)dblk;
+
+    const int64_t ktiles = K / BK, nkb = K >> 7;
+    // block FP8: the scale bytes of K block kb are requested one tile ahead,
+    // together with that tile, so the wait at the top of the loop covers them
+    uint32_t swb = 0, sxb[TM];
+    auto load_scales = [&](int64_t kb) {
+        if constexpr (EPI == kEpiBlk) {
+            swb = p.wsb[(n0 >> 7) * nkb + kb];
+#pragma unroll
+            for (int j = 0; j < TM; ++j) {
+                const int64_t m = m0 + wm * (BM / 2) + j * 32 + row;
+                sxb[j] = p.xsb[(m < M ? m : M - 1) * nkb + kb];
+            }
+        }
+    };
+    load_scales(0);
+    issue(0, 0);
+    for (int64_t kt = 0; kt < ktiles; ++kt) {
+        wait_vmcnt<0>();  // this wave's loads of tile kt (and its scales), the only ones outstanding
+        stage_barrier();  // tile kt complete for everyone; everyone is done with tile kt-1
+        float sw = 1.0f, sx[TM];
+        if constexpr (EPI == kEpiBlk) {
+            // decoded here, before the next bytes are requested: the empty asm
+            // pins the value, so the compiler cannot sink the decode to the fold
+            // (that would keep the byte register live across its reload and
+            // make it wait for every outstanding load)
+            sw = ue8m0_to_f32(swb);
+            asm volatile("" : "+v"(sw));
+#pragma unroll
+            for (int j = 0; j < TM; ++j) {
+                sx[j] = ue8m0_to_f32(sxb[j]);
+                asm volatile("" : "+v"(sx[j]));
+            }
+        }
+        (void)sw;
+        (void)sx;
+        load_scales(kt + 1 < ktiles ? kt + 1 : kt);
+        __builtin_amdgcn_sched_barrier(0);  // the scale loads stay ahead of the tile loads
+        // unconditional, so the scale loads above complete before it on every
+        // path (a conditional issue makes the compiler wait for everything);
+        // the last tile reloads itself into the idle slot
+        issue(kt + 1 < ktiles ? kt + 1 : kt, (int)((kt + 1) & 1));
+        const uint8_t* Wt = lds + (kt & 1) * ST;
+        const uint8_t* Xt = Wt + WT;
+#pragma unroll
+        for (int ks = 0; ks < BK / 32; ++ks) {
+            const int c = 2 * ks + half;
+            u32x4_t a[TN], b[TM];
+#pragma unroll
+            for (int i = 0; i < TN; ++i) {
+                const int r = wn * (BN / 2) + i * 32 + row;
+                a[i] = *(const u32x4_t*)(Wt + r * BK + ((c ^ dma_swz(r)) * 16));
+            }
+#pragma unroll
+            for (int j = 0; j < TM; ++j) {
+                const int r = wm * (BM / 2) + j * 32 + row;
+                b[j] = *(const u32x4_t*)(Xt + r * BK + ((c ^ dma_swz(r)) * 16));
+            }
+            if constexpr (kI8) {
+#pragma unroll
+                for (int i = 0; i < TN; ++i)
+#pragma unroll
+                    for (int j = 0; j < TM; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4_t, a[i]),
+                                                                         __builtin_bit_cast(i32x4_t, b[j]),
+                                                                         acc[i][j], 0, 0, 0);
+            } else {
+                constexpr int XF = ACT == kActE5M2 ? kFmtE5M2 : kFmtE4M3;
+                bf16x8_t a0[TN], a1[TN], b0[TM], b1[TM];
+#pragma unroll
+                for (int i = 0; i < TN; ++i) {
+                    a0[i] = fp8x8_to_bf16x8<WF>(make_uint2(a[i].x, a[i].y));
+                    a1[i] = fp8x8_to_bf16x8<WF>(make_uint2(a[i].z, a[i].w));
+                }
+#pragma unroll
+                for (int j = 0; j < TM; ++j) {
+                    b0[j] = fp8x8_to_bf16x8<XF>(make_uint2(b[j].x, b[j].y));
+                    b1[j] = fp8x8_to_bf16x8<XF>(make_uint2(b[j].z, b[j].w));
+                }
+#pragma unroll
+                for (int i = 0; i < TN; ++i)
+#pragma unroll
+                    for (int j = 0; j < TM; ++j) {
+                        acc_t& d = EPI == kEpiBlk ? dblk[i][j] : acc[i][j];
+                        d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], b0[j], d, 0, 0, 0);
+                        d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1[j], d, 0, 0, 0);
+                    }
+            }
+        }
+        if constexpr (EPI == kEpiBlk) {  // the tile is one 128-wide K block: fold its scales
+#pragma unroll
+            for (int i = 0; i < TN; ++i)
+#pragma unroll
+                for (int j = 0; j < TM; ++j) {
+                    acc[i][j] += (dblk[i][j] * sw) * sx[j];
+                    dblk[i][j] = acc_t{};
+                }
+        }
+    }
+
+    wait_vmcnt<0>();  // no load into LDS outlives the workgroup
+
+    // epilogue: register r of a 32 x 32 tile holds weight row 8(r/4) + 4*half + r%4, token lane%32
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+        const int64_t m = m0 + wm * (BM / 2) + j * 32 + row;
+        if (m >= M) continue;
+        float xsv = 1.0f;
+        if constexpr (EPI == kEpiI8 || EPI == kEpiXsWs) xsv = p.xs[m * p.xs_step];
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t n = n0 + wn * (BN / 2) + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                if (n >= N) continue;
+                if constexpr (EPI == kEpiI8) {
+                    if (p.out_kind == 1) {
+                        ((int32_t*)p.y)[m * p.ldy + n] = acc[i][j][r];
+                        continue;
+                    }
+                    float v = (float)acc[i][j][r];
+                    v = v * xsv;
+                    v = v * p.ws[n * p.ws_step];
+                    uint16_t o = f32_to_bf16(v);
+                    if (p.bias) o = f32_to_bf16(bf16_to_f32(o) + bf16_to_f32(p.bias[n]));
+                    ((uint16_t*)p.y)[m * p.ldy + n] = o;
+                } else if constexpr (EPI == kEpiXsWs) {
+                    float v = acc[i][j][r] * xsv;
+                    v = v * p.ws[n * p.ws_step];
+                    ((uint16_t*)p.y)[m * p.ldy + n] = f32_to_bf16(v);
+                } else {
+                    ((uint16_t*)p.y)[m * p.ldy + n] = f32_to_bf16(acc[i][j][r]);
+                }
+            }
+    }
+}
+
 }  // namespace qlin

@@ -67,6 +67,40 @@ def test_prefill_int8_extreme_accumulators(ql, orc):
     assert np.array_equal(host(acc), oacc) and oacc[0, 0] == -127 * 127 * K
 
 
+# K % 128 == 0: the direct-to-LDS kernel (64 x 64 tiles up to 256 tokens,
+# 64 x 128 up to 1024, 128 x 128 above); ragged M and N in every tile size
+DMA_SHAPES = [(17, 64, 128), (33, 129, 256), (100, 250, 1024), (256, 64, 384), (257, 1000, 768),
+              (600, 65, 640), (1024, 130, 256), (1030, 200, 384), (1100, 383, 512)]
+
+
+@pytest.mark.parametrize("M,N,K", DMA_SHAPES)
+def test_prefill_int8_dma_bit_exact(ql, orc, M, N, K):
+    d = gen_int8(M, N, K, seed=M * 3 + N + K)
+    rng = np.random.default_rng(M)
+    bias = bf16_bits(rng.standard_normal(N).astype(np.float32))
+    xq, xs = ql.qlin_act_quant_i8(dev_bf16(d["x"]))
+    acc = ql.qlin_gemv_i8(xq, xs, dev(d["w"]), dev(d["ws"]), out_kind=1)
+    y = ql.qlin_gemv_i8(xq, xs, padded(d["w"], 128), dev(d["ws"]), bias=dev_bf16(bias))
+    torch.cuda.synchronize()
+    oxq, oxs = orc.act_quant_i8(d["x"])
+    oacc, oy = orc.gemv_i8(oxq, oxs, d["w"], d["ws"], bias=bias)
+    assert np.array_equal(host(acc), oacc)
+    assert np.array_equal(host_bits(y), oy)
+
+
+@pytest.mark.parametrize("M,N,K", DMA_SHAPES)
+@pytest.mark.parametrize("x_fmt,w_fmt", [(0, 0), (1, 1), (0, 1), (1, 0)])
+def test_prefill_fp8_w8a8_dma(ql, orc, M, N, K, x_fmt, w_fmt):
+    d = gen_fp8_w8a8(M, N, K, w_fmt=w_fmt, seed=M + 5 * N + K)
+    xq, xs = ql.qlin_act_quant_fp8(dev_bf16(d["x"]), x_fmt, True)
+    y = ql.qlin_gemv_fp8_w8a8(xq, xs, dev(d["w"]), dev(d["ws"]), x_fmt, w_fmt)
+    torch.cuda.synchronize()
+    oxq, oxs = orc.act_quant_fp8(d["x"], x_fmt, True)
+    assert np.array_equal(host(xq), oxq)
+    _, ye, S = orc.gemv_fp8_w8a8(oxq, oxs, x_fmt, d["w"], d["ws"], w_fmt)
+    check_float(host_bits(y), ye, S, K)
+
+
 # ----------------------------------------------------------------------------- FP8 weight-only
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -109,7 +143,7 @@ def test_prefill_fp8_w8a8_static_per_tensor_scale(ql, orc):
 # ----------------------------------------------------------------------------- block FP8
 
 @pytest.mark.parametrize("M,N,K", [(17, 128, 128), (33, 129, 256), (100, 250, 1024), (129, 383, 512),
-                                   (300, 77, 2048), (257, 1000, 768)])
+                                   (300, 77, 2048), (257, 1000, 768), (1030, 200, 384), (1100, 130, 640)])
 def test_prefill_fp8_blk(ql, orc, M, N, K):
     d = gen_fp8_blk(M, N, K, seed=M + N)
     y, xq, xs = ql.qlin_gemv_fp8_blk(dev_bf16(d["x"]), dev(d["w"]), dev(d["ws"]))
