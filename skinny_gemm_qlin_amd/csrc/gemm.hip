@@ -53,6 +53,13 @@ hipError_t launch_gemm_i8(const I8Args& a, hipStream_t st) {
 hipError_t launch_gemm_fp8(const F8Args& a, hipStream_t st) {
     GemmParams p{a.x, a.ldx, nullptr, 0, nullptr, a.M, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step,
                  nullptr, nullptr, a.y, a.ldy, 0};
+    if (a.K % 128 == 0) {
+        // bf16 activation rows are twice as wide, so the token side of the
+        // tile stays at 64 (measured: M = 128 / 512 / 2048 64.3 / 172 / 603 us
+        // against 80.2 / 221 / 648 us for the register-staged kernel)
+        if (a.M <= kSmallTileMaxM) return run_gemm_dma<kFmtE4M3, kActBf16, kEpiWs, 64, 64>(p, st);
+        return run_gemm_dma<kFmtE4M3, kActBf16, kEpiWs, 128, 64>(p, st);
+    }
     if (a.M <= kSmallTileMaxM) return run_gemm<kFmtE4M3, kActBf16, kEpiWs, 2, 2, 64>(p, st);
     return run_gemm<kFmtE4M3, kActBf16, kEpiWs, 4, 4, 64>(p, st);
 }

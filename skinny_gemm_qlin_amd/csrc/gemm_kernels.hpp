@@ -263,8 +263,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
 }
 
 // ------------------------------------------------------------------ direct-to-LDS variant
-// For one-byte operands on both sides (INT8, FP8 W8A8, block FP8) and K a
-// multiple of 128.  The tiles travel global -> LDS with
+// For one-byte weight codes and K a multiple of 128 (INT8, FP8 weight-only
+// with bf16 activations, FP8 W8A8, block FP8).  The tiles travel global -> LDS with
 // global_load_lds_dwordx4 (no VGPR staging, no LDS store instructions) into a
 // two-stage ring of 128-byte-deep K tiles: one load instruction covers 8 rows
 // x 128 bytes, i.e. whole 128-byte lines (64-byte row pieces measured 40%
@@ -299,16 +299,22 @@ __device__ __forceinline__ void stage_barrier() {
 }
 
 __device__ __forceinline__ int dma_swz(int row) { return (row >> 1) & 7; }
+// activation rows: 8 chunks (one-byte codes, as the weights) or 16 (bf16:
+// 32 lanes read one chunk of 32 consecutive rows; chunk ^ (row & 15) spreads
+// every 16 of them over all banks)
+template <int XB>
+__device__ __forceinline__ int dma_xswz(int row) { return XB == 2 ? (row & 15) : dma_swz(row); }
 
 template <int WF, int ACT, int EPI, int BN, int BM>
 __global__ __launch_bounds__(256) void gemm_dma_kernel(const GemmParams p) {
     constexpr bool kI8 = ACT == kActI8;
-    static_assert(ACT != kActBf16, "one-byte activation codes");
     static_assert(BN % 64 == 0 && BM % 64 == 0 && BN <= 128 && BM <= 128, "tile");
-    constexpr int BK = 128;                                // bytes = K elements per stage
-    constexpr int WT = BN * BK, XT = BM * BK, ST = WT + XT;
-    constexpr int WI = BN / 8 / 4, XI = BM / 8 / 4;        // load instructions per wave and stage
-    constexpr int LPS = WI + XI;
+    constexpr int BK = 128;                                // K elements per stage (= weight bytes per row)
+    constexpr int XB = ACT == kActBf16 ? 2 : 1;            // bytes per activation element
+    constexpr int XRB = BK * XB, XRPI = 1024 / XRB;        // activation row bytes, rows per load instruction
+    constexpr int WT = BN * BK, XT = BM * XRB, ST = WT + XT;
+    constexpr int WI = BN / 8 / 4, XI = BM / XRPI / 4;     // load instructions per wave and stage
+    static_assert(WI >= 1 && XI >= 1, "load split");
     constexpr int TN = BN / 64, TM = BM / 64;              // 32 x 32 tiles per wave
     __shared__ __align__(16) uint8_t lds[2 * ST];
 
@@ -333,9 +339,9 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const GemmParams p) {
     }
 #pragma unroll
     for (int i = 0; i < XI; ++i) {
-        const int r = (wv * XI + i) * 8 + (lane >> 3);
+        const int r = (wv * XI + i) * XRPI + lane / (XRB / 16);
         const int64_t m = m0 + r < M ? m0 + r : M - 1;
-        xsrc[i] = (const uint8_t*)p.x + m * p.ldx + (((lane & 7) ^ dma_swz(r)) * 16);
+        xsrc[i] = (const uint8_t*)p.x + m * p.ldx * XB + (((lane % (XRB / 16)) ^ dma_xswz<XB>(r)) * 16);
     }
     auto issue = [&](int64_t kt, int slot) {
         uint8_t* base = lds + slot * ST;
@@ -345,7 +351,7 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const GemmParams p) {
                                              (lds_void_t*)(base + (wv * WI + i) * 1024), 16, 0, 0);
 #pragma unroll
         for (int i = 0; i < XI; ++i)
-            __builtin_amdgcn_global_load_lds((const void*)(xsrc[i] + kt * BK),
+            __builtin_amdgcn_global_load_lds((const void*)(xsrc[i] + kt * XRB),
                                              (lds_void_t*)(base + WT + (wv * XI + i) * 1024), 16, 0, 0);
     };
 
@@ -408,7 +414,7 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const GemmParams p) {
 #pragma unroll
         for (int ks = 0; ks < BK / 32; ++ks) {
             const int c = 2 * ks + half;
-            u32x4_t a[TN], b[TM];
+            u32x4_t a[TN], b[TM][XB];
 #pragma unroll
             for (int i = 0; i < TN; ++i) {
                 const int r = wn * (BN / 2) + i * 32 + row;
@@ -417,7 +423,9 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const GemmParams p) {
 #pragma unroll
             for (int j = 0; j < TM; ++j) {
                 const int r = wm * (BM / 2) + j * 32 + row;
-                b[j] = *(const u32x4_t*)(Xt + r * BK + ((c ^ dma_swz(r)) * 16));
+#pragma unroll
+                for (int h = 0; h < XB; ++h)  // bf16: the two chunks of the same 16 K
+                    b[j][h] = *(const u32x4_t*)(Xt + r * XRB + (((XB * c + h) ^ dma_xswz<XB>(r)) * 16));
             }
             if constexpr (kI8) {
 #pragma unroll
@@ -425,7 +433,7 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const GemmParams p) {
 #pragma unroll
                     for (int j = 0; j < TM; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4_t, a[i]),
-                                                                         __builtin_bit_cast(i32x4_t, b[j]),
+                                                                         __builtin_bit_cast(i32x4_t, b[j][0]),
                                                                          acc[i][j], 0, 0, 0);
             } else {
                 constexpr int XF = ACT == kActE5M2 ? kFmtE5M2 : kFmtE4M3;
@@ -437,8 +445,13 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const GemmParams p) {
                 }
 #pragma unroll
                 for (int j = 0; j < TM; ++j) {
-                    b0[j] = fp8x8_to_bf16x8<XF>(make_uint2(b[j].x, b[j].y));
-                    b1[j] = fp8x8_to_bf16x8<XF>(make_uint2(b[j].z, b[j].w));
+                    if constexpr (XB == 2) {
+                        b0[j] = __builtin_bit_cast(bf16x8_t, b[j][0]);
+                        b1[j] = __builtin_bit_cast(bf16x8_t, b[j][XB - 1]);
+                    } else {
+                        b0[j] = fp8x8_to_bf16x8<XF>(make_uint2(b[j][0].x, b[j][0].y));
+                        b1[j] = fp8x8_to_bf16x8<XF>(make_uint2(b[j][0].z, b[j][0].w));
+                    }
                 }
 #pragma unroll
                 for (int i = 0; i < TN; ++i)
@@ -470,6 +483,7 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const GemmParams p) {
         if (m >= M) continue;
         float xsv = 1.0f;
         if constexpr (EPI == kEpiI8 || EPI == kEpiXsWs) xsv = p.xs[m * p.xs_step];
+        (void)xsv;
 #pragma unroll
         for (int i = 0; i < TN; ++i)
 #pragma unroll
@@ -491,6 +505,8 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const GemmParams p) {
                     float v = acc[i][j][r] * xsv;
                     v = v * p.ws[n * p.ws_step];
                     ((uint16_t*)p.y)[m * p.ldy + n] = f32_to_bf16(v);
+                } else if constexpr (EPI == kEpiWs) {
+                    ((uint16_t*)p.y)[m * p.ldy + n] = f32_to_bf16(acc[i][j][r] * p.ws[n * p.ws_step]);
                 } else {
                     ((uint16_t*)p.y)[m * p.ldy + n] = f32_to_bf16(acc[i][j][r]);
                 }

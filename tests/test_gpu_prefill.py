@@ -89,6 +89,17 @@ def test_prefill_int8_dma_bit_exact(ql, orc, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", DMA_SHAPES)
+@pytest.mark.parametrize("per_tensor", [False, True])
+def test_prefill_fp8_dma(ql, orc, M, N, K, per_tensor):
+    d = gen_fp8(M, N, K, seed=M * 11 + N + K, per_tensor=per_tensor)
+    y = ql.qlin_gemv_fp8(padded(d["x"].view(np.int16), 64).view(torch.bfloat16), padded(d["w"], 128),
+                         dev(d["ws"]))
+    torch.cuda.synchronize()
+    _, ye, S = orc.gemv_fp8(d["x"], d["w"], d["ws"])
+    check_float(host_bits(y), ye, S, K)
+
+
+@pytest.mark.parametrize("M,N,K", DMA_SHAPES)
 @pytest.mark.parametrize("x_fmt,w_fmt", [(0, 0), (1, 1), (0, 1), (1, 0)])
 def test_prefill_fp8_w8a8_dma(ql, orc, M, N, K, x_fmt, w_fmt):
     d = gen_fp8_w8a8(M, N, K, w_fmt=w_fmt, seed=M + 5 * N + K)
