@@ -34,16 +34,19 @@ def _check(orc, ql, d, ids=None, gw=None):
 
 @pytest.mark.parametrize("M,E,N,K,topk", [(17, 8, 128, 256, 2), (33, 4, 200, 512, 2), (64, 16, 130, 1056, 4),
                                           (100, 64, 256, 512, 6), (257, 8, 64, 320, 8), (40, 1, 96, 128, 1),
-                                          (300, 32, 1000, 256, 3)])
+                                          (300, 32, 1000, 256, 3),
+                                          # many pair tiles per expert
+                                          (512, 16, 300, 512, 4), (260, 4, 129, 768, 2)])
 def test_moe_prefill_shapes(ql, orc, M, E, N, K, topk):
     d = gen_moe(M, E, N, K, topk, seed=M + E + N)
     _check(orc, ql, d)
 
 
-def test_moe_prefill_skewed_routing_and_bad_ids(ql, orc):
+@pytest.mark.parametrize("K", [256, 320])
+def test_moe_prefill_skewed_routing_and_bad_ids(ql, orc, K):
     # every token routes slot 0 to expert 3 (one expert holds > 64 pairs: several
     # pair tiles), slot 1 spread, slot 2 out of range (-1 and E): contributes nothing
-    M, E, N, K, topk = 150, 12, 192, 256, 3
+    M, E, N, topk = 150, 12, 192, 3
     d = gen_moe(M, E, N, K, topk, seed=5)
     ids = d["ids"].copy()
     ids[:, 0] = 3
@@ -53,11 +56,12 @@ def test_moe_prefill_skewed_routing_and_bad_ids(ql, orc):
     _check(orc, ql, d, ids=ids)
 
 
+@pytest.mark.parametrize("K", [128, 256])  # register-staged and direct-to-LDS kernels
 @pytest.mark.parametrize("byte,x_exp", [(2, 0), (252, -40)])
-def test_moe_prefill_edge_scale_bytes(ql, orc, byte, x_exp):
+def test_moe_prefill_edge_scale_bytes(ql, orc, byte, x_exp, K):
     # the grouped GEMM applies the block scale in the E2M1 -> bf16 convert:
     # exact for scale bytes 2..252 (x scaled so that y stays finite in bf16)
-    M, E, N, K, topk = 20, 2, 64, 128, 2
+    M, E, N, topk = 20, 2, 64, 2
     d = gen_moe(M, E, N, K, topk, seed=6)
     d["s"][:] = byte
     d["x"] = bf16_bits(bf16_values(d["x"]) * np.float32(2.0 ** x_exp))
