@@ -68,6 +68,22 @@ def test_moe_prefill_edge_scale_bytes(ql, orc, byte, x_exp, K):
     _check(orc, ql, d)
 
 
+def test_moe_prefill_unaligned_scales_fall_back(ql, orc):
+    # scale rows that do not start on a 4-byte boundary cannot use the 4-byte
+    # direct loads: the register-staged kernel runs instead, same results
+    M, E, N, K, topk = 70, 8, 160, 512, 2
+    d = gen_moe(M, E, N, K, topk, seed=9)
+    flat = torch.empty(d["s"].size + 1, dtype=torch.uint8, device="cuda")
+    flat[1:] = dev(d["s"].reshape(-1))
+    s_off = flat[1:].view(E, N, K // 32)
+    assert s_off.data_ptr() % 4 == 1
+    y = ql.qlin_moe_mxfp4(dev_bf16(d["x"]), dev(d["w"]), s_off, dev(d["ids"]), dev(d["gw"]))
+    torch.cuda.synchronize()
+    _, ye, S = orc.moe_mxfp4(d["x"], d["w"], d["s"], d["ids"], d["gw"])
+    check_float(host_bits(y), ye, S, K)
+    check_float(_run(ql, d), ye, S, K)  # the aligned call (direct-to-LDS kernel)
+
+
 def test_moe_prefill_full_expert_shape(ql, orc):
     # 64 experts of 2048 x 7168, 64 tokens, top-6, compared on every output
     d = gen_moe(64, 64, 2048, 7168, 6, seed=0)
