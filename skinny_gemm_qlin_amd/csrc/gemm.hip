@@ -16,11 +16,11 @@ hipError_t run_gemm(const GemmParams& p, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int WF, int ACT, int EPI, int BN, int BM>
+template <int WF, int ACT, int EPI, int BN, int BM, int NW = 4>
 hipError_t run_gemm_dma(const GemmParams& p, hipStream_t st) {
     const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
     const int64_t grid = (tiles + 7) / 8 * 8;
-    hipLaunchKernelGGL((gemm_dma_kernel<WF, ACT, EPI, BN, BM>), dim3((unsigned)grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((gemm_dma_kernel<WF, ACT, EPI, BN, BM, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, st, p);
     return hipGetLastError();
 }
 
@@ -55,10 +55,12 @@ hipError_t launch_gemm_fp8(const F8Args& a, hipStream_t st) {
                  nullptr, nullptr, a.y, a.ldy, 0};
     if (a.K % 128 == 0) {
         // bf16 activation rows are twice as wide, so the token side of the
-        // tile stays at 64 (measured: M = 128 / 512 / 2048 64.3 / 172 / 603 us
-        // against 80.2 / 221 / 648 us for the register-staged kernel)
+        // tile stays at 64; above 256 tokens 8 waves of 32 x 32 share a
+        // 128 x 64 tile (measured: M = 128 / 512 / 2048 / 4096 63.9 / 157.5 /
+        // 572 / 1084 us; 4 waves on 128 x 64: 172 / 612 / 1121 us at the
+        // larger M; the register-staged kernel 80 / 219 / 645 / 1220 us)
         if (a.M <= kSmallTileMaxM) return run_gemm_dma<kFmtE4M3, kActBf16, kEpiWs, 64, 64>(p, st);
-        return run_gemm_dma<kFmtE4M3, kActBf16, kEpiWs, 128, 64>(p, st);
+        return run_gemm_dma<kFmtE4M3, kActBf16, kEpiWs, 128, 64, 8>(p, st);
     }
     if (a.M <= kSmallTileMaxM) return run_gemm<kFmtE4M3, kActBf16, kEpiWs, 2, 2, 64>(p, st);
     return run_gemm<kFmtE4M3, kActBf16, kEpiWs, 4, 4, 64>(p, st);

@@ -274,7 +274,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
 // global chunk that lands on its fixed LDS slot.  Each wave waits for its own
 // loads with an explicit vmcnt, then one barrier publishes the stage to the
 // workgroup (a __syncthreads() would make the compiler drain every
-// outstanding load first).  4 waves, 2 x 2, each (BN/2) x (BM/2) of 32 x 32
+// outstanding load first).  NW = 4 or 8 waves, (NW/2) x 2, each
+// (BN/(NW/2)) x (BM/2) of 32 x 32
 // MFMA tiles: v_mfma_i32_32x32x32_i8 for INT8; FP8 codes are widened to bf16
 // as fragments are read (exact) for v_mfma_f32_32x32x16_bf16.  The block-FP8
 // epilogue folds both scales per K tile (= one 128-wide K block).
@@ -305,17 +306,19 @@ __device__ __forceinline__ int dma_swz(int row) { return (row >> 1) & 7; }
 template <int XB>
 __device__ __forceinline__ int dma_xswz(int row) { return XB == 2 ? (row & 15) : dma_swz(row); }
 
-template <int WF, int ACT, int EPI, int BN, int BM>
-__global__ __launch_bounds__(256) void gemm_dma_kernel(const GemmParams p) {
+template <int WF, int ACT, int EPI, int BN, int BM, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const GemmParams p) {
     constexpr bool kI8 = ACT == kActI8;
-    static_assert(BN % 64 == 0 && BM % 64 == 0 && BN <= 128 && BM <= 128, "tile");
+    static_assert(NW == 4 || NW == 8, "waves");
+    constexpr int WGN = NW / 2, WGM = 2;                   // wave grid (weight rows x tokens)
+    static_assert(BN % (32 * WGN) == 0 && BM % 64 == 0 && BN <= 32 * WGN * 2 && BM <= 128, "tile");
     constexpr int BK = 128;                                // K elements per stage (= weight bytes per row)
     constexpr int XB = ACT == kActBf16 ? 2 : 1;            // bytes per activation element
     constexpr int XRB = BK * XB, XRPI = 1024 / XRB;        // activation row bytes, rows per load instruction
     constexpr int WT = BN * BK, XT = BM * XRB, ST = WT + XT;
-    constexpr int WI = BN / 8 / 4, XI = BM / XRPI / 4;     // load instructions per wave and stage
+    constexpr int WI = BN / 8 / NW, XI = BM / XRPI / NW;   // load instructions per wave and stage
     static_assert(WI >= 1 && XI >= 1, "load split");
-    constexpr int TN = BN / 64, TM = BM / 64;              // 32 x 32 tiles per wave
+    constexpr int TN = BN / WGN / 32, TM = BM / WGM / 32;  // 32 x 32 tiles per wave
     __shared__ __align__(16) uint8_t lds[2 * ST];
 
     const int64_t M = p.M, N = p.N, K = p.K;
@@ -355,7 +358,7 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const GemmParams p) {
                                              (lds_void_t*)(base + WT + (wv * XI + i) * 1024), 16, 0, 0);
     };
 
-    const int wn = wv & 1, wm = wv >> 1;
+    const int wn = wv % WGN, wm = wv / WGN;
     const int row = lane & 31, half = lane >> 5;
     typedef typename std::conditional<kI8, i32x16_t, f32x16_t>::type acc_t;
     acc_t acc[TN][TM], dblk[TN][TM];
@@ -377,7 +380,7 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const GemmParams p) {
             swb = p.wsb[(n0 >> 7) * nkb + kb];
 #pragma unroll
             for (int j = 0; j < TM; ++j) {
-                const int64_t m = m0 + wm * (BM / 2) + j * 32 + row;
+                const int64_t m = m0 + wm * (BM / WGM) + j * 32 + row;
                 sxb[j] = p.xsb[(m < M ? m : M - 1) * nkb + kb];
             }
         }
@@ -417,12 +420,12 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const GemmParams p) {
             u32x4_t a[TN], b[TM][XB];
 #pragma unroll
             for (int i = 0; i < TN; ++i) {
-                const int r = wn * (BN / 2) + i * 32 + row;
+                const int r = wn * (BN / WGN) + i * 32 + row;
                 a[i] = *(const u32x4_t*)(Wt + r * BK + ((c ^ dma_swz(r)) * 16));
             }
 #pragma unroll
             for (int j = 0; j < TM; ++j) {
-                const int r = wm * (BM / 2) + j * 32 + row;
+                const int r = wm * (BM / WGM) + j * 32 + row;
 #pragma unroll
                 for (int h = 0; h < XB; ++h)  // bf16: the two chunks of the same 16 K
                     b[j][h] = *(const u32x4_t*)(Xt + r * XRB + (((XB * c + h) ^ dma_xswz<XB>(r)) * 16));
@@ -479,7 +482,7 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const GemmParams p) {
     // epilogue: register r of a 32 x 32 tile holds weight row 8(r/4) + 4*half + r%4, token lane%32
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
-        const int64_t m = m0 + wm * (BM / 2) + j * 32 + row;
+        const int64_t m = m0 + wm * (BM / WGM) + j * 32 + row;
         if (m >= M) continue;
         float xsv = 1.0f;
         if constexpr (EPI == kEpiI8 || EPI == kEpiXsWs) xsv = p.xs[m * p.xs_step];
@@ -488,7 +491,7 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const GemmParams p) {
         for (int i = 0; i < TN; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t n = n0 + wn * (BN / 2) + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                const int64_t n = n0 + wn * (BN / WGN) + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
                 if (n >= N) continue;
                 if constexpr (EPI == kEpiI8) {
                     if (p.out_kind == 1) {
