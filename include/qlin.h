@@ -204,9 +204,16 @@ int qlin_gemv_fp8_blk(const void* x, int64_t ldx, int64_t M, int64_t K,
  *   ws UE8M0 [ceil(N/block_n), K/block_k]; xq uint8 [M, K];
  *   xs uint8 [M, K/block_k]; out[m,n] = sum_kb 2^(xs[m,kb]-127) *
  *   2^(ws[n/block_n,kb]-127) * sum_{k in kb} xq[m,k] * w[n,k].
- * block_n = block_k = 128 is exactly qlin_gemv_fp8_blk.  Other shapes run a
- * matrix-core GEMV over 16 tokens per launch (M > 16 reads the weights once
- * per 16 tokens) and require K <= 32768 (the tile's scale bytes are staged in
+ * block_n = block_k = 128 is exactly qlin_gemv_fp8_blk.  Other shapes, up to
+ * 16 tokens, run a matrix-core GEMV that folds both scales into each block's
+ * partial sum.  Above 16 tokens with K % 128 == 0 one tiled GEMM covers all
+ * tokens and applies both scales inside the E4M3 -> bf16 operand converts,
+ * so the fp32 sum is over exactly scaled products: exact while every scaled
+ * value is a normal bf16 number, i.e. weight scale bytes 10..246 and
+ * activation groups whose amax exceeds about 2^-109 (the float comparison
+ * rule holds either way only inside that range).  Above 16 tokens with
+ * K % 128 != 0 the GEMV runs once per 16 tokens (the weights are read once
+ * per 16 tokens).  K <= 32768 (the GEMV stages a tile's scale bytes in
  * LDS).  Requires K % block_k == 0, ldx % 8 == 0, ldw % 16 == 0, ldy >= N. */
 int qlin_gemv_fp8_blk_ex(const void* x, int64_t ldx, int64_t M, int64_t K,
                          const uint8_t* w, int64_t ldw, int64_t N, const uint8_t* ws,

@@ -91,6 +91,17 @@ hipError_t launch_gemm_fp8_w8a8(const W8A8F8Args& a, hipStream_t st) {
                  : run_gemm<kFmtE4M3, kActE4M3, kEpiXsWs, 4, 4, 128>(p, st);
 }
 
+// Block FP8 at any block shape (block_k a multiple of 32; K % 128 == 0).
+hipError_t launch_gemm_fp8_blkg(const BlkArgs& a, int64_t bn, int64_t bk, hipStream_t st) {
+    GemmParams p{a.xq, a.K, nullptr, 0, a.xs, a.M, a.K, a.w, a.ldw, a.N, nullptr, 0,
+                 a.ws, nullptr, a.y, a.ldy, 0, bn, bk};
+    const bool word = (((uintptr_t)a.ws | (uintptr_t)a.xs) & 3) == 0, half = (((uintptr_t)a.ws | (uintptr_t)a.xs) & 1) == 0;
+    if (bk == 32 && word) return run_dma<kFmtE4M3, kActE4M3, kEpiBlkGW>(p, st);
+    if (bk == 64 && half) return run_dma<kFmtE4M3, kActE4M3, kEpiBlkGH>(p, st);
+    if (bk % 128 == 0) return run_dma<kFmtE4M3, kActE4M3, kEpiBlkGT>(p, st);
+    return run_dma<kFmtE4M3, kActE4M3, kEpiBlkG>(p, st);
+}
+
 hipError_t launch_gemm_fp8_blk(const BlkArgs& a, hipStream_t st) {
     GemmParams p{a.xq, a.K, nullptr, 0, a.xs, a.M, a.K, a.w, a.ldw, a.N, nullptr, 0,
                  a.ws, nullptr, a.y, a.ldy, 0};

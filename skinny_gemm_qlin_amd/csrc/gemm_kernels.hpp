@@ -34,7 +34,12 @@
 namespace qlin {
 
 enum GemmAct { kActBf16 = 0, kActE4M3 = 1, kActE5M2 = 2, kActI8 = 3 };
-enum GemmEpi { kEpiI8 = 0, kEpiWs = 1, kEpiXsWs = 2, kEpiBlk = 3 };
+// kEpiBlkG*: block FP8 at any block shape; the suffix is how a row's scale
+// bytes of one K tile are fetched (a byte per 32-K step, one 32-bit word for
+// block_k 32, one 16-bit half for block_k 64, one byte per tile for block_k
+// a multiple of 128)
+enum GemmEpi { kEpiI8 = 0, kEpiWs = 1, kEpiXsWs = 2, kEpiBlk = 3, kEpiBlkG = 4, kEpiBlkGW = 5, kEpiBlkGH = 6,
+               kEpiBlkGT = 7 };
 
 struct GemmParams {
     const void* x; int64_t ldx;          // activations [M][ldx]: bf16, FP8 or int8 codes
@@ -46,6 +51,7 @@ struct GemmParams {
     const uint8_t* wsb;                  // block FP8: UE8M0 [ceil(N/128)][K/128]
     const uint16_t* bias;                // INT8: bf16 [N] or null
     void* y; int64_t ldy; int out_kind;  // bf16 [M][ldy] (INT8 out_kind 1: int32 acc)
+    int64_t bn = 128, bk = 128;          // block FP8, any shape: scale blocks (wsb [ceil(N/bn)][K/bk], xsb [M][K/bk])
 };
 
 
@@ -300,6 +306,16 @@ __device__ __forceinline__ void stage_barrier() {
 }
 
 __device__ __forceinline__ int dma_swz(int row) { return (row >> 1) & 7; }
+
+// 8 E4M3 codes times a power-of-two scale -> bf16x8 (the scale is applied
+// inside the convert; exact while the results stay in bf16's normal range).
+__device__ __forceinline__ bf16x8_t e4m3x8_scaled(uint2 c, float sc) {
+    const bf16x2_t b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, sc, false);
+    const bf16x2_t b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, sc, true);
+    const bf16x2_t b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, sc, false);
+    const bf16x2_t b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, sc, true);
+    return bf16x8_t{b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
+}
 // activation rows: 8 chunks (one-byte codes, as the weights) or 16 (bf16:
 // 32 lanes read one chunk of 32 consecutive rows; chunk ^ (row & 15) spreads
 // every 16 of them over all banks)
@@ -371,7 +387,78 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const GemmParams p) {
         }
     (void)dblk;
 
+    constexpr bool kBG = EPI >= kEpiBlkG;  // block FP8, any shape
+    constexpr int GM = EPI - kEpiBlkG;    // scale fetch: 0 bytes, 1 word, 2 half, 3 one byte per tile
+    static_assert(!kBG || (ACT == kActE4M3 && WF == kFmtE4M3), "block FP8 codes");
     const int64_t ktiles = K / BK, nkb = K >> 7;
+    // block FP8 at any block shape: a lane's A row and B token are fixed, so
+    // each 32-K step needs one weight scale per row tile and one activation
+    // scale per token tile; they are folded into the E4M3 -> bf16 converts
+    // (exact while the scaled values stay in bf16's normal range) and the
+    // products accumulate straight into fp32.  The scale bytes of the next
+    // K tile are requested ahead of its loads, as for the 128 x 128 fold.
+    constexpr int KSS = BK / 32;  // 32-K steps per tile
+    uint32_t gswb[TN][KSS], gsxb[TM][KSS];
+    const uint8_t* gsw_row[TN];
+    const uint8_t* gsx_row[TM];
+    (void)gswb;
+    (void)gsxb;
+    (void)gsw_row;
+    (void)gsx_row;
+    if constexpr (kBG) {
+        const int64_t nkbg = K / p.bk;
+#pragma unroll
+        for (int i = 0; i < TN; ++i) {
+            const int64_t n = n0 + wn * (BN / WGN) + i * 32 + row;
+            gsw_row[i] = p.wsb + ((n < N ? n : N - 1) / p.bn) * nkbg;
+        }
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+            const int64_t m = m0 + wm * (BM / WGM) + j * 32 + row;
+            gsx_row[j] = p.xsb + (m < M ? m : M - 1) * nkbg;
+        }
+    }
+    // block_k 32 / 64 (GM 1 / 2): a row's scale bytes of one K tile are
+    // contiguous (4 / 2 bytes at an aligned offset, K % 128 == 0), so one
+    // load per row replaces 4 byte loads, each of which touches 32 rows'
+    // cache lines; other block_k load a byte per 32-K step (GM 0).  Words are
+    // split at the top of the next step.
+    auto load_gscales = [&](int64_t kt) {
+        if constexpr (kBG && GM == 1) {
+#pragma unroll
+            for (int i = 0; i < TN; ++i) gswb[i][0] = *(const uint32_t*)(gsw_row[i] + kt * 4);
+#pragma unroll
+            for (int j = 0; j < TM; ++j) gsxb[j][0] = *(const uint32_t*)(gsx_row[j] + kt * 4);
+        } else if constexpr (kBG && GM == 2) {
+#pragma unroll
+            for (int i = 0; i < TN; ++i) gswb[i][0] = *(const uint16_t*)(gsw_row[i] + kt * 2);
+#pragma unroll
+            for (int j = 0; j < TM; ++j) gsxb[j][0] = *(const uint16_t*)(gsx_row[j] + kt * 2);
+        } else if constexpr (kBG && GM == 3) {
+            const int kb = (int)(kt * BK / p.bk);
+#pragma unroll
+            for (int i = 0; i < TN; ++i) gswb[i][0] = gsw_row[i][kb];
+#pragma unroll
+            for (int j = 0; j < TM; ++j) gsxb[j][0] = gsx_row[j][kb];
+        } else if constexpr (kBG) {
+#pragma unroll
+            for (int ks = 0; ks < KSS; ++ks) {
+                const int kb = (int)((kt * BK + ks * 32) / p.bk);
+#pragma unroll
+                for (int i = 0; i < TN; ++i) gswb[i][ks] = gsw_row[i][kb];
+#pragma unroll
+                for (int j = 0; j < TM; ++j) gsxb[j][ks] = gsx_row[j][kb];
+            }
+        }
+    };
+    // scale byte of 32-K step ks from what load_gscales fetched
+    auto gbyte = [&](const uint32_t (&v)[KSS], int ks) -> uint32_t {
+        if constexpr (GM == 1) return (v[0] >> (8 * ks)) & 0xFFu;
+        else if constexpr (GM == 2) return (v[0] >> (8 * (ks >> 1))) & 0xFFu;
+        else if constexpr (GM == 3) return v[0];
+        else return v[ks];
+    };
+    (void)gbyte;
     // block FP8: the scale bytes of K block kb are requested one tile ahead,
     // together with that tile, so the wait at the top of the loop covers them
     uint32_t swb = 0, sxb[TM];
@@ -386,6 +473,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const GemmParams p) {
         }
     };
     load_scales(0);
+    load_gscales(0);
     issue(0, 0);
     for (int64_t kt = 0; kt < ktiles; ++kt) {
         wait_vmcnt<0>();  // this wave's loads of tile kt (and its scales), the only ones outstanding
@@ -406,7 +494,26 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const GemmParams p) {
         }
         (void)sw;
         (void)sx;
+        float gsw[TN][KSS], gsx[TM][KSS];
+        (void)gsw;
+        (void)gsx;
+        if constexpr (kBG) {
+#pragma unroll
+            for (int ks = 0; ks < KSS; ++ks) {
+#pragma unroll
+                for (int i = 0; i < TN; ++i) {
+                    gsw[i][ks] = ue8m0_to_f32(gbyte(gswb[i], ks));
+                    asm volatile("" : "+v"(gsw[i][ks]));
+                }
+#pragma unroll
+                for (int j = 0; j < TM; ++j) {
+                    gsx[j][ks] = ue8m0_to_f32(gbyte(gsxb[j], ks));
+                    asm volatile("" : "+v"(gsx[j][ks]));
+                }
+            }
+        }
         load_scales(kt + 1 < ktiles ? kt + 1 : kt);
+        load_gscales(kt + 1 < ktiles ? kt + 1 : kt);
         __builtin_amdgcn_sched_barrier(0);  // the scale loads stay ahead of the tile loads
         // unconditional, so the scale loads above complete before it on every
         // path (a conditional issue makes the compiler wait for everything);
@@ -443,14 +550,22 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const GemmParams p) {
                 bf16x8_t a0[TN], a1[TN], b0[TM], b1[TM];
 #pragma unroll
                 for (int i = 0; i < TN; ++i) {
-                    a0[i] = fp8x8_to_bf16x8<WF>(make_uint2(a[i].x, a[i].y));
-                    a1[i] = fp8x8_to_bf16x8<WF>(make_uint2(a[i].z, a[i].w));
+                    if constexpr (kBG) {
+                        a0[i] = e4m3x8_scaled(make_uint2(a[i].x, a[i].y), gsw[i][ks]);
+                        a1[i] = e4m3x8_scaled(make_uint2(a[i].z, a[i].w), gsw[i][ks]);
+                    } else {
+                        a0[i] = fp8x8_to_bf16x8<WF>(make_uint2(a[i].x, a[i].y));
+                        a1[i] = fp8x8_to_bf16x8<WF>(make_uint2(a[i].z, a[i].w));
+                    }
                 }
 #pragma unroll
                 for (int j = 0; j < TM; ++j) {
                     if constexpr (XB == 2) {
                         b0[j] = __builtin_bit_cast(bf16x8_t, b[j][0]);
                         b1[j] = __builtin_bit_cast(bf16x8_t, b[j][XB - 1]);
+                    } else if constexpr (kBG) {
+                        b0[j] = e4m3x8_scaled(make_uint2(b[j][0].x, b[j][0].y), gsx[j][ks]);
+                        b1[j] = e4m3x8_scaled(make_uint2(b[j][0].z, b[j][0].w), gsx[j][ks]);
                     } else {
                         b0[j] = fp8x8_to_bf16x8<XF>(make_uint2(b[j][0].x, b[j][0].y));
                         b1[j] = fp8x8_to_bf16x8<XF>(make_uint2(b[j][0].z, b[j][0].w));

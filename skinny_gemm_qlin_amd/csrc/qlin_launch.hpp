@@ -74,6 +74,7 @@ hipError_t launch_gemm_i8(const I8Args& a, hipStream_t st);
 hipError_t launch_gemm_fp8(const F8Args& a, hipStream_t st);
 hipError_t launch_gemm_fp8_w8a8(const W8A8F8Args& a, hipStream_t st);
 hipError_t launch_gemm_fp8_blk(const BlkArgs& a, hipStream_t st);
+hipError_t launch_gemm_fp8_blkg(const BlkArgs& a, int64_t bn, int64_t bk, hipStream_t st);
 
 struct MoeFfnArgs {
     const uint16_t* x; int64_t ldx; int64_t M; int64_t H;

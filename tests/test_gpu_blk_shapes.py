@@ -50,6 +50,39 @@ def test_blk_shapes_ragged_and_prefill(ql, orc, M, N, K, bn, bk):
     _check(orc, d, bn, bk, _run(ql, d, bn, bk), K)
 
 
+# above 16 tokens with K % 128 == 0: one tiled GEMM with the scales applied in
+# the operand converts; (800, 1, 32) has K % 128 != 0 (GEMV per 16 tokens)
+@pytest.mark.parametrize("bn,bk", [(1, 32), (16, 32), (32, 128), (64, 64), (7, 32), (128, 256), (3, 96),
+                                   (128, 64), (1, 128)])
+@pytest.mark.parametrize("M", [17, 100, 300])
+def test_blk_shapes_prefill_gemm(ql, orc, bn, bk, M):
+    N, K = 300, 768
+    d = gen_fp8_blk(M, N, K, seed=bn * 7 + bk + M, scale_lo=110, scale_hi=135, block_n=bn, block_k=bk)
+    _check(orc, d, bn, bk, _run(ql, d, bn, bk), K)
+
+
+def test_blk_shapes_prefill_k_not_multiple_of_128(ql, orc):
+    d = gen_fp8_blk(40, 150, 800, seed=3, block_n=1, block_k=32)
+    _check(orc, d, 1, 32, _run(ql, d, 1, 32), 800)
+
+
+def test_blk_shapes_prefill_full_mx_shape(ql, orc):
+    # the 4096 x 7168 block-FP8 matrix with MX-style 1 x 32 scales, 128 tokens
+    d = gen_fp8_blk(128, 4096, 7168, seed=4, block_n=1, block_k=32)
+    _check(orc, d, 1, 32, _run(ql, d, 1, 32), 7168)
+
+
+@pytest.mark.parametrize("byte,x_exp", [(10, 0), (246, -100)])
+def test_blk_shapes_prefill_scale_range_ends(ql, orc, byte, x_exp):
+    # the ends of the weight-scale range in which the GEMM's scaled converts are
+    # exact (x scaled so that the outputs stay finite)
+    M, N, K, bn, bk = 40, 64, 256, 1, 32
+    d = gen_fp8_blk(M, N, K, seed=6, block_n=bn, block_k=bk)
+    d["ws"][:] = byte
+    d["x"] = bf16_bits(bf16_values(d["x"]) * np.float32(2.0 ** x_exp))
+    _check(orc, d, bn, bk, _run(ql, d, bn, bk), K)
+
+
 def test_blk_shapes_edge_scales(ql, orc):
     # scale bytes at the ends of their range (2^-127 and large) and a zero group
     M, N, K, bn, bk = 3, 64, 256, 1, 32
