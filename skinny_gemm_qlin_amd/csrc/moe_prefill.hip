@@ -320,9 +320,11 @@ __global__ __launch_bounds__(256) void moe_gemm_dma_kernel(const MoeGemmParams p
 
     const int row = lane & 31, half = lane >> 5;
     const int ar = wv * 32 + row;  // this lane's weight row in the tile
-    f32x16_t acc[TM];
+    // two accumulators per tile (the two 16-K halves of each step) so that a
+    // wave has two independent MFMA chains; summed once at the end
+    f32x16_t acc[TM][2];
 #pragma unroll
-    for (int j = 0; j < TM; ++j) acc[j] = f32x16_t{};
+    for (int j = 0; j < TM; ++j) acc[j][0] = acc[j][1] = f32x16_t{};
     const int64_t ktiles = K / kPdBK;
     issue(0, 0);
     for (int64_t kt = 0; kt < ktiles; ++kt) {
@@ -343,8 +345,8 @@ __global__ __launch_bounds__(256) void moe_gemm_dma_kernel(const MoeGemmParams p
                 const int xr = j * 32 + row;
                 const bf16x8_t b0 = *(const bf16x8_t*)(Xt + xr * XRB + ((c0 ^ (xr & 15)) * 16));
                 const bf16x8_t b1 = *(const bf16x8_t*)(Xt + xr * XRB + (((c0 + 1) ^ (xr & 15)) * 16));
-                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[j], 0, 0, 0);
-                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[j], 0, 0, 0);
+                acc[j][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[j][0], 0, 0, 0);
+                acc[j][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[j][1], 0, 0, 0);
             }
         }
     }
@@ -356,10 +358,11 @@ __global__ __launch_bounds__(256) void moe_gemm_dma_kernel(const MoeGemmParams p
         const int pr = j * 32 + row;
         if (pr >= cnt) continue;
         float* out = p.part + (int64_t)prow[pr] * N;
+        const f32x16_t v = acc[j][0] + acc[j][1];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int64_t n = n0 + wv * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (n < N) out[n] = acc[j][r];
+            if (n < N) out[n] = v[r];
         }
     }
 }
