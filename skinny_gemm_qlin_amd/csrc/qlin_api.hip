@@ -17,8 +17,8 @@ inline int launch_status(hipError_t e) { return e == hipSuccess ? QLIN_OK : QLIN
 
 constexpr int64_t kMaxKInt8 = 131072;  // K * 127 * 128 < 2^31: int32 accumulation is exact
 constexpr int64_t kMaxKFp8 = 1 << 24;  // keeps the quantiser's 32-bit vector indexes in range
-constexpr int64_t kMaxKBlkGeneral = 32768;
-constexpr int64_t kMaxEPrefill = 1024;  // the pair sort counts experts in one workgroup's LDS  // the general block GEMV stages K/32 x 32 scale bytes in LDS
+constexpr int64_t kMaxKBlkGeneral = 32768;  // the general block GEMV stages K/32 x 32 scale bytes in LDS
+constexpr int64_t kMaxEPrefill = 1024;      // the pair sort counts experts in one workgroup's LDS
 
 }  // namespace
 
