@@ -40,9 +40,10 @@
  *   their quantisers) and qlin_moe_mxfp4 accept 1 <= M <= QLIN_MAX_M_PREFILL;
  *   up to 16 they run the decode kernels, above 16 a tiled (grouped, for
  *   the MoE) matrix-core GEMM with the same arithmetic contract.  The routed
- *   expert FFN and the per-tensor FP8 quantiser take 1 <= M <= QLIN_MAX_M.  Base pointers and row pitches of
- *   weights, codes and bf16 activations must be 16-byte aligned (128-bit
- *   loads); scale arrays must be naturally aligned.
+ *   expert FFN and the per-tensor FP8 quantiser take 1 <= M <= QLIN_MAX_M.
+ * - Base pointers and row pitches of weights, codes and bf16 activations must
+ *   be 16-byte aligned (128-bit loads); scale arrays must be naturally
+ *   aligned.
  */
 #ifndef QLIN_H
 #define QLIN_H
