@@ -156,8 +156,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(the per-GPU kernel at a shard's shape is what one GPU measures).", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
+              "(one GPU measures the per-GPU kernel at a shard's shape).", file=sys.stderr)
         sys.exit(1)
 
     import numpy as np
