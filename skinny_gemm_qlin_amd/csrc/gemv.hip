@@ -253,6 +253,9 @@ hipError_t launch_gemv_fp8_w8a8(const W8A8F8Args& a, hipStream_t st) {
     // at N=17408, K=5120: 16.4 us against 17.7-18.5 us for one row per group
     // with 2-5 steps in flight)
     if (a.M == 2) return run_w8a8<2, 32, 2, 1, 1>(a, st);
+    // three rows per group at three tokens (17.8-17.9 us against 19.1-19.3 us
+    // for the matrix-core kernel); from four tokens the matrix core wins
+    if (a.M == 3) return run_w8a8<3, 32, 3, 1, 1>(a, st);
     return run_w8a8_mfma(a, st);
 }
 
