@@ -23,7 +23,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqlin.so")
 
 SOURCES = ["qlin_api.hip", "act_quant.hip", "gemv.hip", "gemm.hip", "moe.hip", "moe_prefill.hip", "routing.hip"]
-HEADERS = ["qlin_device.hpp", "qlin_launch.hpp", "gemv_kernels.hpp", "mfma_kernels.hpp", "gemm_kernels.hpp"]
+HEADERS = ["qlin_device.hpp", "qlin_launch.hpp", "gemv_kernels.hpp", "mfma_kernels.hpp", "ks_kernels.hpp", "gemm_kernels.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -6,14 +6,21 @@
 //   * M = 1: VALU, one whole wavefront per row (GS=64), all K steps of the
 //     row in flight (up to 8), 4 waves per workgroup; block FP8 uses its own
 //     M = 1 kernel that shares the scale bytes of a batch across the wave;
-//   * M = 2 (INT8, E4M3, FP8 W8A8): VALU with smaller lane groups (and, for
-//     INT8 / E4M3, several rows per group, so that each activation load feeds
-//     more weight rows);
-//   * otherwise: the matrix-core kernels;
+//   * M = 2 (INT8, FP8 W8A8, and E4M3 where the next item does not apply):
+//     VALU with smaller lane groups (and, for INT8 / E4M3, several rows per
+//     group, so that each activation load feeds more weight rows);
+//   * K a multiple of 1024 (at most 8192 for INT8, 5120 for the E4M3 kinds),
+//     from M = 3 (E4M3 weight-only from M = 2; W8A8 for E4M3 x E4M3 only):
+//     the K-slice matrix-core kernels of ks_kernels.hpp (INT8 at M = 4 / 8 /
+//     16: 16.5 / 17.0 / 18.4 us against 17.5 / 19.1 / 21.4 us for one
+//     workgroup per 16-row tile);
+//   * otherwise: the matrix-core kernels of mfma_kernels.hpp;
 //   * M > 16 (prefill): the tiled matrix-core GEMM of gemm.hip.
 #include <algorithm>
+#include <atomic>
 
 #include "gemv_kernels.hpp"
+#include "ks_kernels.hpp"
 #include "mfma_kernels.hpp"
 #include "qlin_launch.hpp"
 
@@ -194,6 +201,73 @@ hipError_t run_w8a8_mfma(const W8A8F8Args& a, hipStream_t st) {
                                : run_w8a8_mfma_fmt<kFmtE4M3, kFmtE4M3>(a, st);
 }
 
+// ---- K-slice kernels: the plan and the launch
+// Compute units of the current device (queried once per device).
+int cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+struct KsPlan { int L, T; unsigned G; int64_t R; };
+
+// K = 1024 * L with L in [2, lmax]; G = one workgroup per compute unit, or
+// one per 16 rows when N is small, or more when a workgroup would get more
+// than kKsMaxTiles tiles; R = rows per workgroup, T = its tiles.
+bool ks_plan(int64_t N, int64_t K, int lmax, KsPlan& p) {
+    if (N < 1 || K % 1024 != 0 || K / 1024 < 2 || K / 1024 > lmax) return false;
+    int64_t G = std::min<int64_t>(cu_count(), (N + 15) / 16);
+    int64_t R = (N + G - 1) / G;
+    if ((R + 15) / 16 > kKsMaxTiles) {
+        G = (N + 16 * kKsMaxTiles - 1) / (16 * kKsMaxTiles);
+        R = (N + G - 1) / G;
+    }
+    p = {(int)(K / 1024), (int)((R + 15) / 16), (unsigned)G, R};
+    return true;
+}
+
+constexpr int kKsMaxLI8 = 8;     // INT8 holds 2L + 3 * 2L 16-byte registers per lane
+constexpr int kKsMaxLFloat = 5;  // the float kinds hold 4L + 2 * 2L
+
+template <int KIND, int L>
+hipError_t run_ks_t(const KsArgs& a, const KsPlan& p, hipStream_t st) {
+    const dim3 grid(p.G), block(64 * kKsWaves);
+    switch (p.T) {
+        case 1: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 1>), grid, block, 0, st, a); break;
+        case 2: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 2>), grid, block, 0, st, a); break;
+        case 3: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 3>), grid, block, 0, st, a); break;
+        case 4: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 4>), grid, block, 0, st, a); break;
+        case 5: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 5>), grid, block, 0, st, a); break;
+        default: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 6>), grid, block, 0, st, a); break;
+    }
+    return hipGetLastError();
+}
+
+template <int KIND>
+hipError_t run_ks(const KsArgs& a, const KsPlan& p, hipStream_t st) {
+    switch (p.L) {
+        case 2: return run_ks_t<KIND, 2>(a, p, st);
+        case 3: return run_ks_t<KIND, 3>(a, p, st);
+        case 4: return run_ks_t<KIND, 4>(a, p, st);
+        case 5: return run_ks_t<KIND, 5>(a, p, st);
+        default:
+            if constexpr (KIND == kKsI8) {
+                switch (p.L) {
+                    case 6: return run_ks_t<KIND, 6>(a, p, st);
+                    case 7: return run_ks_t<KIND, 7>(a, p, st);
+                    default: return run_ks_t<KIND, 8>(a, p, st);
+                }
+            }
+            return hipErrorInvalidValue;  // not reached: ks_plan caps L per kind
+    }
+}
+
 template <int U>
 hipError_t run_blk_m1(const BlkArgs& a, hipStream_t st) {
     constexpr int WPB = 4;
@@ -223,7 +297,15 @@ hipError_t launch_gemv_i8(const I8Args& a, hipStream_t st) {
     switch (a.M) {
         case 1: QLIN_M1_BY_STEPS(run_i8, a, st)
         case 2: return run_i8<2, 32, 2, 2, 1>(a, st);
-        default: return run_i8_mfma(a, st);
+        default: {
+            KsPlan p;
+            if (ks_plan(a.N, a.K, kKsMaxLI8, p)) {
+                const KsArgs k{a.xq, a.ldxq, a.xs, a.xs_step, (int)a.M, (const uint8_t*)a.w, a.ldw, a.N, p.R,
+                               a.ws, a.ws_step, a.bias, a.y, a.ldy, a.out_kind};
+                return run_ks<kKsI8>(k, p, st);
+            }
+            return run_i8_mfma(a, st);
+        }
     }
 }
 
@@ -231,8 +313,18 @@ hipError_t launch_gemv_fp8(const F8Args& a, hipStream_t st) {
     if (a.M > kDecodeMaxM) return launch_gemm_fp8(a, st);
     switch (a.M) {
         case 1: return run_fp8<1, 32, 2, 1, 1>(a, st);
-        case 2: return run_fp8<2, 64, 4, 1, 1>(a, st);
-        default: return run_fp8_mfma(a, st);
+        default: {
+            // K-slice kernels from M = 2 (17408 x 5120: 17.4 against 18.2 us
+            // for the VALU kernel at M = 2)
+            KsPlan p;
+            if (ks_plan(a.N, a.K, kKsMaxLFloat, p)) {
+                const KsArgs k{a.x, a.ldx, nullptr, 0, (int)a.M, a.w, a.ldw, a.N, p.R,
+                               a.ws, a.ws_step, nullptr, a.y, a.ldy, 0};
+                return run_ks<kKsF8>(k, p, st);
+            }
+            if (a.M == 2) return run_fp8<2, 64, 4, 1, 1>(a, st);
+            return run_fp8_mfma(a, st);
+        }
     }
 }
 
@@ -253,6 +345,14 @@ hipError_t launch_gemv_fp8_w8a8(const W8A8F8Args& a, hipStream_t st) {
     // at N=17408, K=5120: 16.4 us against 17.7-18.5 us for one row per group
     // with 2-5 steps in flight)
     if (a.M == 2) return run_w8a8<2, 32, 2, 1, 1>(a, st);
+    // from three tokens the K-slice kernels where they apply (E4M3 x E4M3,
+    // 17408 x 5120: 16.8 against 18.3 us for the VALU kernel below at M = 3)
+    KsPlan p;
+    if (a.x_fmt == kFmtE4M3 && a.w_fmt == kFmtE4M3 && ks_plan(a.N, a.K, kKsMaxLFloat, p)) {
+        const KsArgs k{a.xq, a.ldxq, a.xs, a.xs_step, (int)a.M, a.w, a.ldw, a.N, p.R,
+                       a.ws, a.ws_step, nullptr, a.y, a.ldy, 0};
+        return run_ks<kKsW8A8>(k, p, st);
+    }
     // three rows per group at three tokens (17.8-17.9 us against 19.1-19.3 us
     // for the matrix-core kernel); from four tokens the matrix core wins
     if (a.M == 3) return run_w8a8<3, 32, 3, 1, 1>(a, st);

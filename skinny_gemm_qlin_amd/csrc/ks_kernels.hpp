@@ -1,0 +1,175 @@
+// ks_kernels.hpp -- K-slice matrix-core decode kernels for gfx950: one
+// workgroup per compute unit, each wave owning a fixed slice of K (see below).
+#pragma once
+#include <type_traits>
+
+#include "mfma_kernels.hpp"
+
+namespace qlin {
+
+// ------------------------------------------------------------------ K-slice kernels (decode shapes)
+// For K a multiple of 1024 the dense decode paths (INT8, E4M3 weight-only,
+// E4M3 x E4M3 W8A8) also have kernels laid out for the whole chip rather than
+// for one row tile.  The grid holds one workgroup per compute unit (fewer when
+// N is small); workgroup b owns rows n = j*G + b for j < R (one row in every
+// G, so that no workgroup has more than one row above another), taken as T
+// tiles of 16.  Each of its 8 waves owns one eighth of K (L lines of 128
+// bytes) for the whole kernel: it loads its slice of the M token rows once,
+// into registers in the MFMA B layout, then streams its slice of the T weight
+// tiles with the following tiles' loads in flight (8 rows x 128 bytes per
+// load instruction), transposing each 128-byte line of a tile through a
+// 16-row LDS column into the MFMA A layout.  The 8 partial tiles are summed in
+// wave order after one barrier (deterministic; exact for INT8).  Against one
+// workgroup per 16-row tile, the activations are read once per wave instead
+// of once per tile, and no compute unit is left with an extra tile.  The tile
+// loop is unrolled at compile time and no load sits under a branch, so the
+// compiler's load counters stay exact and each wait covers one tile only.
+constexpr int kKsI8 = 0;      // INT8 codes x INT8 codes, int32 sums
+constexpr int kKsF8 = 1;      // E4M3 weights x bf16 activations, fp32 sums
+constexpr int kKsW8A8 = 2;    // E4M3 weights x E4M3 activation codes, fp32 sums
+constexpr int kKsWaves = 8;   // waves per workgroup = K slices
+constexpr int kKsMaxTiles = 6;
+constexpr int kKsPitch = 128 + 16;  // LDS row pitch of the transpose column (the pad spreads banks)
+
+struct KsArgs {
+    const void* x; int64_t ldx;      // INT8 / E4M3 codes, or bf16 activations (elements)
+    const float* xs; int xs_step;    // token scales (INT8, W8A8)
+    int M;
+    const uint8_t* w; int64_t ldw; int64_t N; int64_t R;
+    const float* ws; int ws_step;
+    const uint16_t* bias;            // INT8: optional bf16 bias
+    void* y; int64_t ldy; int out_kind;  // INT8: out_kind 1 stores the raw int32 sums
+};
+
+template <int KIND, int L, int T>
+__global__ __launch_bounds__(64 * kKsWaves) void gemv_ks_kernel(const KsArgs a) {
+    constexpr bool I8 = KIND == kKsI8;
+    constexpr int NQ = 2 * L;                  // loads per tile = 64-K steps of the slice
+    constexpr int NX = I8 ? NQ : 2 * NQ;       // B operand registers (16 bytes each) of the slice
+    constexpr int DMAX = (I8 && L <= 6) ? 3 : 2;
+    constexpr int D = T < DMAX ? T : DMAX;     // tiles in flight per wave
+    typedef typename std::conditional<I8, i32x4_t, f32x4_t>::type acc_t;
+    __shared__ __align__(16) uint8_t col[kKsWaves][16 * kKsPitch];
+    __shared__ acc_t part[T][kKsWaves][64];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int mi = lane & 15, mg = lane >> 4, lr = lane >> 3, lp = lane & 7;
+    const int64_t G = gridDim.x, wg = blockIdx.x;
+    // row of the workgroup's j-th row, or -1 past its range
+    auto row = [&](int64_t j) -> int64_t {
+        const int64_t n = j * G + wg;
+        return (j < a.R && n < a.N) ? n : -1;
+    };
+    const int64_t k0 = (int64_t)wv * (L * 128);
+    const uint8_t* wb = a.w + k0 + 16 * lp;
+    uint8_t* cp = col[wv];
+    // load j of a tile: line j/2 of rows 8*(j%2) + lane/8.  Rows past the
+    // range read the tile's first row instead (the same lines as a lane of
+    // the same or the previous load, so no extra HBM traffic), or row wg when
+    // the whole tile is past the range; they are never stored.
+    auto load_tile = [&](u32x4_t (&buf)[NQ], int t) {
+        const int64_t r0 = row(16 * t), fb = r0 >= 0 ? r0 : wg;
+        const int64_t ra = row(16 * t + lr), rb = row(16 * t + 8 + lr);
+        const uint8_t* p0 = wb + (ra >= 0 ? ra : fb) * a.ldw;
+        const uint8_t* p1 = wb + (rb >= 0 ? rb : fb) * a.ldw;
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            buf[2 * j] = ld_stream(p0 + 128 * j);
+            buf[2 * j + 1] = ld_stream(p1 + 128 * j);
+        }
+    };
+
+    u32x4_t bufs[D][NQ];
+    load_tile(bufs[0], 0);
+    // the wave's K slice of token lane%16 (zero past M): 64-K step s covers
+    // K = k0 + 64s + 16*(lane/16) + [0, 16)
+    u32x4_t xb[NX];
+    {
+        const bool xon = mi < a.M;
+        const int64_t m = xon ? mi : 0;
+        if constexpr (KIND == kKsF8) {
+            const uint16_t* xr = (const uint16_t*)a.x + m * a.ldx + k0 + 16 * mg;
+#pragma unroll
+            for (int h = 0; h < NX; ++h) {  // h = 2s + half
+                const u32x4_t v = ld16(xr + 64 * (h >> 1) + 8 * (h & 1));
+                xb[h] = xon ? v : u32x4_t{0, 0, 0, 0};
+            }
+        } else {
+            const uint8_t* xr = (const uint8_t*)a.x + m * a.ldx + k0 + 16 * mg;
+#pragma unroll
+            for (int s = 0; s < NQ; ++s) {
+                const u32x4_t v = ld16(xr + 64 * s);
+                const u32x4_t c = xon ? v : u32x4_t{0, 0, 0, 0};
+                if constexpr (I8) {
+                    xb[s] = c;
+                } else {
+                    bf16x8_t lo, hi;
+                    fp8x16_to_bf16x8x2<kFmtE4M3>(c, lo, hi);
+                    xb[2 * s] = __builtin_bit_cast(u32x4_t, lo);
+                    xb[2 * s + 1] = __builtin_bit_cast(u32x4_t, hi);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int d = 1; d < D; ++d) load_tile(bufs[d], d);
+
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        u32x4_t (&buf)[NQ] = bufs[t % D];
+        acc_t acc = {};
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            *(u32x4_t*)(cp + lr * kKsPitch + 16 * lp) = buf[2 * j];
+            *(u32x4_t*)(cp + (8 + lr) * kKsPitch + 16 * lp) = buf[2 * j + 1];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int s = 2 * j + h;
+                const u32x4_t wa = *(const u32x4_t*)(cp + mi * kKsPitch + 64 * h + 16 * mg);
+                if constexpr (I8) {
+                    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, wa),
+                                                               __builtin_bit_cast(i32x4_t, xb[s]), acc, 0, 0, 0);
+                } else {
+                    bf16x8_t a0, a1;
+                    e4m3x16_to_bf16x8x2(wa, a0, a1);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(bf16x8_t, xb[2 * s]), acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(bf16x8_t, xb[2 * s + 1]), acc, 0, 0, 0);
+                }
+            }
+        }
+        part[t][wv][lane] = acc;
+        if (t + D < T) load_tile(buf, t + D);
+    }
+    __syncthreads();
+
+    for (int t = wv; t < T; t += kKsWaves) {
+        acc_t acc = part[t][0][lane];
+#pragma unroll
+        for (int q = 1; q < kKsWaves; ++q) acc += part[t][q][lane];
+        if (mi >= a.M) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t n = row(16 * t + 4 * mg + r);
+            if (n < 0) continue;
+            if constexpr (I8) {
+                if (a.out_kind == 1) {
+                    ((int32_t*)a.y)[mi * a.ldy + n] = acc[r];
+                } else {
+                    float v = (float)acc[r];
+                    v = v * a.xs[mi * a.xs_step];
+                    v = v * a.ws[n * a.ws_step];
+                    uint16_t o = f32_to_bf16(v);
+                    if (a.bias) o = f32_to_bf16(bf16_to_f32(o) + bf16_to_f32(a.bias[n]));
+                    ((uint16_t*)a.y)[mi * a.ldy + n] = o;
+                }
+            } else if constexpr (KIND == kKsW8A8) {
+                float v = acc[r] * a.xs[mi * a.xs_step];
+                v = v * a.ws[n * a.ws_step];
+                ((uint16_t*)a.y)[mi * a.ldy + n] = f32_to_bf16(v);
+            } else {
+                ((uint16_t*)a.y)[mi * a.ldy + n] = f32_to_bf16(acc[r] * a.ws[n * a.ws_step]);
+            }
+        }
+    }
+}
+
+}  // namespace qlin

@@ -1,0 +1,133 @@
+"""GPU parity of the K-slice decode kernels (K a multiple of 1024, M <= 16:
+INT8 from M = 3, E4M3 weight-only from M = 2, E4M3 x E4M3 W8A8 from M = 3)
+against the CPU oracle, over every slice length L = K/1024 and every tile
+count T per workgroup they are built for.  The (L, T) noted per case is what a 256-compute-unit device runs: one
+workgroup per compute unit, or one per 16 rows when N < 4096, or N/96 of them
+when a workgroup would get more than six tiles; parity does not depend on it.
+INT8 is compared bit-exactly (codes, int32 sums, bf16 outputs), the float
+kinds under the comparison rules of tests/parity.py."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import dev, dev_bf16, host, host_bits, lib, need_gpu, padded
+from parity import check_float
+from skinny_gemm_qlin_amd.inputs import bf16_bits, gen_fp8, gen_fp8_w8a8, gen_int8
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ql():
+    need_gpu()
+    return lib()
+
+
+# ----------------------------------------------------------------------------- INT8
+
+def _i8(ql, orc, M, N, K, seed, w_pad=0, bias=False):
+    d = gen_int8(M, N, K, seed=seed)
+    b = bf16_bits(np.random.default_rng(seed).standard_normal(N).astype(np.float32)) if bias else None
+    xq, xs = orc.act_quant_i8(d["x"])
+    wd = dev(d["w"]) if w_pad == 0 else padded(d["w"], w_pad)
+    acc = ql.qlin_gemv_i8(dev(xq), dev(xs), wd, dev(d["ws"]), out_kind=1)
+    y = ql.qlin_gemv_i8(dev(xq), dev(xs), wd, dev(d["ws"]), bias=None if b is None else dev_bf16(b))
+    torch.cuda.synchronize()
+    oacc, oy = orc.gemv_i8(xq, xs, d["w"], d["ws"], bias=b)
+    assert np.array_equal(host(acc), oacc), "int32 sums differ"
+    assert np.array_equal(host_bits(y), oy), "bf16 outputs differ"
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (3, 100, 2048),     # L=2, T=1, 7 workgroups
+    (16, 4096, 3072),   # L=3, T=1
+    (5, 5000, 4096),    # L=4, T=2
+    (8, 9001, 5120),    # L=5, T=3
+    (12, 13000, 6144),  # L=6, T=4
+    (16, 17000, 7168),  # L=7, T=5
+    (4, 21000, 8192),   # L=8, T=6
+    (7, 30000, 2048),   # more than six tiles per unit: 313 workgroups of 96 rows
+    (16, 1, 2048),      # one row
+    (3, 17, 2048),      # two workgroups, 9 and 8 rows
+])
+def test_ks_int8_tiles_and_slices(ql, orc, M, N, K):
+    _i8(ql, orc, M, N, K, seed=M * 7 + N)
+
+
+@pytest.mark.parametrize("M", list(range(3, 17)))
+def test_ks_int8_every_m(ql, orc, M):
+    _i8(ql, orc, M, 2000, 2048, seed=M)
+
+
+def test_ks_int8_padded_pitch_and_bias(ql, orc):
+    _i8(ql, orc, 6, 3000, 2048, seed=3, w_pad=256, bias=True)
+
+
+def test_ks_int8_decode_shape_is_deterministic(ql):
+    d = gen_int8(16, 17408, 5120, seed=21)
+    xq, xs = ql.qlin_act_quant_i8(dev_bf16(d["x"]))
+    w, ws = dev(d["w"]), dev(d["ws"])
+    ref = ql.qlin_gemv_i8(xq, xs, w, ws, out_kind=1)
+    for _ in range(10):
+        assert torch.equal(ql.qlin_gemv_i8(xq, xs, w, ws, out_kind=1), ref)
+
+
+# ----------------------------------------------------------------------------- E4M3 weight-only
+
+@pytest.mark.parametrize("M,N,K", [
+    (3, 100, 2048),     # L=2, T=1
+    (16, 4096, 3072),   # L=3, T=1
+    (5, 5000, 4096),    # L=4, T=2
+    (8, 9001, 5120),    # L=5, T=3
+    (11, 13000, 2048),  # L=2, T=4
+    (16, 16500, 2048),  # L=2, T=5
+    (4, 21000, 2048),   # L=2, T=6
+    (7, 30000, 2048),   # 313 workgroups
+    (9, 1, 5120),
+])
+def test_ks_fp8_tiles_and_slices(ql, orc, M, N, K):
+    d = gen_fp8(M, N, K, seed=M + N)
+    y = ql.qlin_gemv_fp8(dev_bf16(d["x"]), dev(d["w"]), dev(d["ws"]))
+    torch.cuda.synchronize()
+    _, ye, S = orc.gemv_fp8(d["x"], d["w"], d["ws"])
+    check_float(host_bits(y), ye, S, K)
+
+
+@pytest.mark.parametrize("M", list(range(2, 17)))
+def test_ks_fp8_every_m(ql, orc, M):
+    d = gen_fp8(M, 1500, 3072, seed=M, per_tensor=M % 2 == 0)
+    y = ql.qlin_gemv_fp8(dev_bf16(d["x"]), padded(d["w"], 128), dev(d["ws"]))
+    torch.cuda.synchronize()
+    _, ye, S = orc.gemv_fp8(d["x"], d["w"], d["ws"])
+    check_float(host_bits(y), ye, S, 3072)
+
+
+# ----------------------------------------------------------------------------- W8A8 E4M3 x E4M3
+
+def _w8a8(ql, orc, M, N, K, seed, per_channel=True, per_token=True, w_pad=0):
+    d = gen_fp8_w8a8(M, N, K, w_fmt=0, per_channel=per_channel, seed=seed)
+    xq, xs = orc.act_quant_fp8(d["x"], 0, per_token)
+    wd = dev(d["w"]) if w_pad == 0 else padded(d["w"], w_pad)
+    y = ql.qlin_gemv_fp8_w8a8(dev(xq), dev(xs), wd, dev(d["ws"]), 0, 0)
+    torch.cuda.synchronize()
+    _, ye, S = orc.gemv_fp8_w8a8(xq, xs, 0, d["w"], d["ws"], 0)
+    check_float(host_bits(y), ye, S, K)
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (4, 100, 2048),     # L=2, T=1
+    (16, 4096, 3072),   # L=3, T=1
+    (5, 5000, 4096),    # L=4, T=2
+    (8, 9001, 5120),    # L=5, T=3
+    (11, 13000, 2048),  # L=2, T=4
+    (16, 16500, 2048),  # L=2, T=5
+    (4, 21000, 2048),   # L=2, T=6
+    (7, 30000, 2048),   # 313 workgroups
+])
+def test_ks_w8a8_tiles_and_slices(ql, orc, M, N, K):
+    _w8a8(ql, orc, M, N, K, seed=M + N)
+
+
+@pytest.mark.parametrize("M", list(range(3, 17)))
+def test_ks_w8a8_every_m(ql, orc, M):
+    _w8a8(ql, orc, M, 1500, 3072, seed=M, per_channel=M % 2 == 0, per_token=M % 3 != 0, w_pad=256)
