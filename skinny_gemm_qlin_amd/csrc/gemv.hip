@@ -219,14 +219,16 @@ struct KsPlan { int L, T; unsigned G; int64_t R; };
 
 // K = 1024 * L with L in [2, lmax]; G = one workgroup per compute unit, or
 // one per 16 rows when N is small, or more when a workgroup would get more
-// than kKsMaxTiles tiles; R = rows per workgroup, T = its tiles.
+// than kKsMaxTiles tiles; the ceil(N/4) runs of 4 rows are dealt out in turn,
+// R = rows per workgroup (a multiple of 4), T = its tiles.
 bool ks_plan(int64_t N, int64_t K, int lmax, KsPlan& p) {
     if (N < 1 || K % 1024 != 0 || K / 1024 < 2 || K / 1024 > lmax) return false;
+    const int64_t runs = (N + 3) / 4;
     int64_t G = std::min<int64_t>(cu_count(), (N + 15) / 16);
-    int64_t R = (N + G - 1) / G;
+    int64_t R = 4 * ((runs + G - 1) / G);
     if ((R + 15) / 16 > kKsMaxTiles) {
-        G = (N + 16 * kKsMaxTiles - 1) / (16 * kKsMaxTiles);
-        R = (N + G - 1) / G;
+        G = (runs + 4 * kKsMaxTiles - 1) / (4 * kKsMaxTiles);
+        R = 4 * ((runs + G - 1) / G);
     }
     p = {(int)(K / 1024), (int)((R + 15) / 16), (unsigned)G, R};
     return true;

@@ -131,3 +131,31 @@ def test_ks_w8a8_tiles_and_slices(ql, orc, M, N, K):
 @pytest.mark.parametrize("M", list(range(3, 17)))
 def test_ks_w8a8_every_m(ql, orc, M):
     _w8a8(ql, orc, M, 1500, 3072, seed=M, per_channel=M % 2 == 0, per_token=M % 3 != 0, w_pad=256)
+
+
+# ----------------------------------------------------------------------------- output rows
+
+def test_ks_unaligned_output_rows(ql, orc):
+    # output views with an odd row pitch and a 2- or 4-byte base offset: every
+    # output lands in place and nothing outside the [M, N] view is written
+    M, N, K = 5, 1001, 2048
+    d = gen_int8(M, N, K, seed=31)
+    xq, xs = orc.act_quant_i8(d["x"])
+    oacc, oy = orc.gemv_i8(xq, xs, d["w"], d["ws"])
+    buf = torch.full((M, N + 3), -1.0, dtype=torch.bfloat16, device="cuda")
+    y = ql.qlin_gemv_i8(dev(xq), dev(xs), dev(d["w"]), dev(d["ws"]), y=buf[:, 1:N + 1])
+    buf32 = torch.full((M, N + 2), 7, dtype=torch.int32, device="cuda")
+    acc = ql.qlin_gemv_i8(dev(xq), dev(xs), dev(d["w"]), dev(d["ws"]), y=buf32[:, 1:N + 1], out_kind=1)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(y), oy)
+    assert np.array_equal(host(acc), oacc)
+    assert torch.all(buf[:, 0] == -1.0) and torch.all(buf[:, N + 1:] == -1.0)
+    assert torch.all(buf32[:, 0] == 7) and torch.all(buf32[:, N + 1:] == 7)
+
+    f = gen_fp8(M, N, K, seed=32)
+    _, ye, S = orc.gemv_fp8(f["x"], f["w"], f["ws"])
+    buf = torch.full((M, N + 3), -1.0, dtype=torch.bfloat16, device="cuda")
+    y = ql.qlin_gemv_fp8(dev_bf16(f["x"]), dev(f["w"]), dev(f["ws"]), y=buf[:, 1:N + 1])
+    torch.cuda.synchronize()
+    check_float(host_bits(y), ye, S, K)
+    assert torch.all(buf[:, 0] == -1.0) and torch.all(buf[:, N + 1:] == -1.0)
