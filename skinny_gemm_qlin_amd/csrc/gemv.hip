@@ -10,7 +10,7 @@
 //     VALU with smaller lane groups (and, for INT8 / E4M3, several rows per
 //     group, so that each activation load feeds more weight rows);
 //   * K a multiple of 1024 (at most 8192 for INT8, 5120 for the E4M3 kinds),
-//     from M = 3 (E4M3 weight-only from M = 2; W8A8 for E4M3 x E4M3 only):
+//     from M = 3 (E4M3 weight-only from M = 2; W8A8 in all four format pairs):
 //     the K-slice matrix-core kernels of ks_kernels.hpp (INT8 at M = 4 / 8 /
 //     16: 16.5 / 17.0 / 18.4 us against 17.5 / 19.1 / 21.4 us for one
 //     workgroup per 16-row tile);
@@ -237,33 +237,33 @@ bool ks_plan(int64_t N, int64_t K, int lmax, KsPlan& p) {
 constexpr int kKsMaxLI8 = 8;     // INT8 holds 2L + 3 * 2L 16-byte registers per lane
 constexpr int kKsMaxLFloat = 5;  // the float kinds hold 4L + 2 * 2L
 
-template <int KIND, int L>
+template <int KIND, int L, int XF, int WF>
 hipError_t run_ks_t(const KsArgs& a, const KsPlan& p, hipStream_t st) {
     const dim3 grid(p.G), block(64 * kKsWaves);
     switch (p.T) {
-        case 1: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 1>), grid, block, 0, st, a); break;
-        case 2: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 2>), grid, block, 0, st, a); break;
-        case 3: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 3>), grid, block, 0, st, a); break;
-        case 4: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 4>), grid, block, 0, st, a); break;
-        case 5: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 5>), grid, block, 0, st, a); break;
-        default: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 6>), grid, block, 0, st, a); break;
+        case 1: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 1, XF, WF>), grid, block, 0, st, a); break;
+        case 2: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 2, XF, WF>), grid, block, 0, st, a); break;
+        case 3: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 3, XF, WF>), grid, block, 0, st, a); break;
+        case 4: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 4, XF, WF>), grid, block, 0, st, a); break;
+        case 5: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 5, XF, WF>), grid, block, 0, st, a); break;
+        default: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 6, XF, WF>), grid, block, 0, st, a); break;
     }
     return hipGetLastError();
 }
 
-template <int KIND>
+template <int KIND, int XF = kFmtE4M3, int WF = kFmtE4M3>
 hipError_t run_ks(const KsArgs& a, const KsPlan& p, hipStream_t st) {
     switch (p.L) {
-        case 2: return run_ks_t<KIND, 2>(a, p, st);
-        case 3: return run_ks_t<KIND, 3>(a, p, st);
-        case 4: return run_ks_t<KIND, 4>(a, p, st);
-        case 5: return run_ks_t<KIND, 5>(a, p, st);
+        case 2: return run_ks_t<KIND, 2, XF, WF>(a, p, st);
+        case 3: return run_ks_t<KIND, 3, XF, WF>(a, p, st);
+        case 4: return run_ks_t<KIND, 4, XF, WF>(a, p, st);
+        case 5: return run_ks_t<KIND, 5, XF, WF>(a, p, st);
         default:
             if constexpr (KIND == kKsI8) {
                 switch (p.L) {
-                    case 6: return run_ks_t<KIND, 6>(a, p, st);
-                    case 7: return run_ks_t<KIND, 7>(a, p, st);
-                    default: return run_ks_t<KIND, 8>(a, p, st);
+                    case 6: return run_ks_t<KIND, 6, XF, WF>(a, p, st);
+                    case 7: return run_ks_t<KIND, 7, XF, WF>(a, p, st);
+                    default: return run_ks_t<KIND, 8, XF, WF>(a, p, st);
                 }
             }
             return hipErrorInvalidValue;  // not reached: ks_plan caps L per kind
@@ -350,10 +350,14 @@ hipError_t launch_gemv_fp8_w8a8(const W8A8F8Args& a, hipStream_t st) {
     // from three tokens the K-slice kernels where they apply (E4M3 x E4M3,
     // 17408 x 5120: 16.8 against 18.3 us for the VALU kernel below at M = 3)
     KsPlan p;
-    if (a.x_fmt == kFmtE4M3 && a.w_fmt == kFmtE4M3 && ks_plan(a.N, a.K, kKsMaxLFloat, p)) {
+    if (ks_plan(a.N, a.K, kKsMaxLFloat, p)) {
         const KsArgs k{a.xq, a.ldxq, a.xs, a.xs_step, (int)a.M, a.w, a.ldw, a.N, p.R,
                        a.ws, a.ws_step, nullptr, a.y, a.ldy, 0};
-        return run_ks<kKsW8A8>(k, p, st);
+        if (a.x_fmt == kFmtE5M2)
+            return a.w_fmt == kFmtE5M2 ? run_ks<kKsW8A8, kFmtE5M2, kFmtE5M2>(k, p, st)
+                                       : run_ks<kKsW8A8, kFmtE5M2, kFmtE4M3>(k, p, st);
+        return a.w_fmt == kFmtE5M2 ? run_ks<kKsW8A8, kFmtE4M3, kFmtE5M2>(k, p, st)
+                                   : run_ks<kKsW8A8, kFmtE4M3, kFmtE4M3>(k, p, st);
     }
     // three rows per group at three tokens (17.8-17.9 us against 19.1-19.3 us
     // for the matrix-core kernel); from four tokens the matrix core wins

@@ -9,7 +9,7 @@ namespace qlin {
 
 // ------------------------------------------------------------------ K-slice kernels (decode shapes)
 // For K a multiple of 1024 the dense decode paths (INT8, E4M3 weight-only,
-// E4M3 x E4M3 W8A8) also have kernels laid out for the whole chip rather than
+// FP8 W8A8 in its four format pairs) also have kernels laid out for the whole chip rather than
 // for one row tile.  The grid holds one workgroup per compute unit (fewer when
 // N is small); workgroup b owns the runs of 4 rows b, b + G, b + 2G, ...
 // (row j of the workgroup is n = 4*((j/4)*G + b) + j%4, j < R, so that no
@@ -27,7 +27,7 @@ namespace qlin {
 // compiler's load counters stay exact and each wait covers one tile only.
 constexpr int kKsI8 = 0;      // INT8 codes x INT8 codes, int32 sums
 constexpr int kKsF8 = 1;      // E4M3 weights x bf16 activations, fp32 sums
-constexpr int kKsW8A8 = 2;    // E4M3 weights x E4M3 activation codes, fp32 sums
+constexpr int kKsW8A8 = 2;    // FP8 weights (WF) x FP8 activation codes (XF), fp32 sums
 constexpr int kKsWaves = 8;   // waves per workgroup = K slices
 constexpr int kKsMaxTiles = 6;
 constexpr int kKsPitch = 128 + 16;  // LDS row pitch of the transpose column (the pad spreads banks)
@@ -42,7 +42,7 @@ struct KsArgs {
     void* y; int64_t ldy; int out_kind;  // INT8: out_kind 1 stores the raw int32 sums
 };
 
-template <int KIND, int L, int T>
+template <int KIND, int L, int T, int XF = kFmtE4M3, int WF = kFmtE4M3>
 __global__ __launch_bounds__(64 * kKsWaves) void gemv_ks_kernel(const KsArgs a) {
     constexpr bool I8 = KIND == kKsI8;
     constexpr int NQ = 2 * L;                  // loads per tile = 64-K steps of the slice
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(64 * kKsWaves) void gemv_ks_kernel(const KsArgs a) 
                     xb[s] = c;
                 } else {
                     bf16x8_t lo, hi;
-                    fp8x16_to_bf16x8x2<kFmtE4M3>(c, lo, hi);
+                    fp8x16_to_bf16x8x2<XF>(c, lo, hi);
                     xb[2 * s] = __builtin_bit_cast(u32x4_t, lo);
                     xb[2 * s + 1] = __builtin_bit_cast(u32x4_t, hi);
                 }
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(64 * kKsWaves) void gemv_ks_kernel(const KsArgs a) 
                                                                __builtin_bit_cast(i32x4_t, xb[s]), acc, 0, 0, 0);
                 } else {
                     bf16x8_t a0, a1;
-                    e4m3x16_to_bf16x8x2(wa, a0, a1);
+                    fp8x16_to_bf16x8x2<WF>(wa, a0, a1);
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(bf16x8_t, xb[2 * s]), acc, 0, 0, 0);
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(bf16x8_t, xb[2 * s + 1]), acc, 0, 0, 0);
                 }

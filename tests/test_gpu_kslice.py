@@ -1,5 +1,5 @@
 """GPU parity of the K-slice decode kernels (K a multiple of 1024, M <= 16:
-INT8 from M = 3, E4M3 weight-only from M = 2, E4M3 x E4M3 W8A8 from M = 3)
+INT8 from M = 3, E4M3 weight-only from M = 2, FP8 W8A8 from M = 3)
 against the CPU oracle, over every slice length L = K/1024 and every tile
 count T per workgroup they are built for.  The (L, T) noted per case is what a 256-compute-unit device runs: one
 workgroup per compute unit, or one per 16 rows when N < 4096, or N/96 of them
@@ -104,13 +104,13 @@ def test_ks_fp8_every_m(ql, orc, M):
 
 # ----------------------------------------------------------------------------- W8A8 E4M3 x E4M3
 
-def _w8a8(ql, orc, M, N, K, seed, per_channel=True, per_token=True, w_pad=0):
-    d = gen_fp8_w8a8(M, N, K, w_fmt=0, per_channel=per_channel, seed=seed)
-    xq, xs = orc.act_quant_fp8(d["x"], 0, per_token)
+def _w8a8(ql, orc, M, N, K, seed, per_channel=True, per_token=True, w_pad=0, x_fmt=0, w_fmt=0):
+    d = gen_fp8_w8a8(M, N, K, w_fmt=w_fmt, per_channel=per_channel, seed=seed)
+    xq, xs = orc.act_quant_fp8(d["x"], x_fmt, per_token)
     wd = dev(d["w"]) if w_pad == 0 else padded(d["w"], w_pad)
-    y = ql.qlin_gemv_fp8_w8a8(dev(xq), dev(xs), wd, dev(d["ws"]), 0, 0)
+    y = ql.qlin_gemv_fp8_w8a8(dev(xq), dev(xs), wd, dev(d["ws"]), x_fmt, w_fmt)
     torch.cuda.synchronize()
-    _, ye, S = orc.gemv_fp8_w8a8(xq, xs, 0, d["w"], d["ws"], 0)
+    _, ye, S = orc.gemv_fp8_w8a8(xq, xs, x_fmt, d["w"], d["ws"], w_fmt)
     check_float(host_bits(y), ye, S, K)
 
 
@@ -159,3 +159,10 @@ def test_ks_unaligned_output_rows(ql, orc):
     torch.cuda.synchronize()
     check_float(host_bits(y), ye, S, K)
     assert torch.all(buf[:, 0] == -1.0) and torch.all(buf[:, N + 1:] == -1.0)
+
+
+@pytest.mark.parametrize("x_fmt,w_fmt", [(0, 1), (1, 0), (1, 1)])
+@pytest.mark.parametrize("M,N,K", [(3, 700, 2048), (16, 5000, 5120), (9, 17408, 4096)])
+def test_ks_w8a8_other_formats(ql, orc, M, N, K, x_fmt, w_fmt):
+    # E5M2 activations and / or weights: the same kernels with the other widening
+    _w8a8(ql, orc, M, N, K, seed=M + N + 10 * x_fmt + w_fmt, x_fmt=x_fmt, w_fmt=w_fmt)
