@@ -152,3 +152,40 @@ def test_int8_deterministic(ql):
         xq2, xs2 = ql.qlin_act_quant_i8(x)
         y = ql.qlin_gemv_i8(xq2, xs2, w, ws)
         assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
+
+
+def test_int8_quantiser_divides(ql, orc):
+    # bf16 inputs on which x/s and x*(1/s) give different codes: the kernel's
+    # codes must be those of the one correctly rounded division
+    from test_oracle_int8 import DIV_CASES
+    K = 16
+    rows = np.zeros((len(DIV_CASES), K), np.float32)
+    for i, (amax, xv, _) in enumerate(DIV_CASES):
+        rows[i, :3] = [amax, xv, -xv]
+    x = bf16_bits(rows)
+    xq, xs = ql.qlin_act_quant_i8(dev_bf16(x))
+    torch.cuda.synchronize()
+    oxq, oxs = orc.act_quant_i8(x)
+    assert np.array_equal(host(xq), oxq) and np.array_equal(host(xs).view(np.uint32), oxs.view(np.uint32))
+    for i, (_, _, code) in enumerate(DIV_CASES):
+        assert list(host(xq)[i, :3]) == [127, code, -code]
+
+
+# Each epilogue kernel applies (acc*xs)*ws itself: the vector kernels (1-2
+# tokens), the matrix-core kernel (K not a multiple of 1024), the K-slice
+# kernel (K a multiple of 1024) and the prefill GEMM (more than 16 tokens).
+@pytest.mark.parametrize("K,reps", [(16, 1), (1024, 1), (16, 3)])
+def test_int8_epilogue_order_constructed(ql, orc, K, reps):
+    from test_oracle_int8 import epilogue_case_arrays
+    xq4, w4, xs, ws = epilogue_case_arrays()
+    C = len(xs)
+    xq = np.zeros((C * reps, K), np.int8)
+    xq[:, :4] = np.tile(xq4, (reps, 1))
+    xsr = np.tile(xs, reps)
+    w = np.zeros((C, K), np.int8)
+    w[:, :4] = w4
+    _, oy = orc.gemv_i8(xq, xsr, w, ws)
+    for M in sorted({1, 2, C * reps}):
+        y = ql.qlin_gemv_i8(dev(xq[:M]), dev(xsr[:M]), dev(w), dev(ws))
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(y), oy[:M]), f"M={M}"

@@ -5,6 +5,7 @@ arithmetic (library routines the oracle does not use)."""
 from fractions import Fraction
 
 import numpy as np
+import pytest
 import torch
 
 from skinny_gemm_qlin_amd.inputs import bf16_bits, bf16_values, gen_int8
@@ -137,3 +138,106 @@ def test_gemv_i8_one_hot_closed_form(orc):
     assert np.array_equal(acc[0], 127 * w[:, k].astype(np.int32))
     t = (torch.from_numpy((127 * w[:, k].astype(np.int64))).float() * float(xs[0])) * torch.from_numpy(ws)
     assert np.array_equal(y[0], t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+
+
+# ----------------------------------------------------------------------------- division and epilogue order
+
+# bf16 pairs (amax, x) found by exhaustive search over x for random amax:
+# with s = fp32(amax / 127), the fp32 quotient x / s and the product
+# x * fp32(1 / s) land on opposite sides of (or on) a rounding boundary, so
+# the code depends on the quantiser using one correctly rounded division
+# (stated scale absmax/127, round half to even).
+DIV_CASES = [(1.6875, 0.84375, 64), (0.296875, 0.1484375, 64), (0.00162506103515625, 0.000812530517578125, 64),
+             (208.0, 104.0, 63), (298.0, 149.0, 63), (0.0003414154052734375, 0.00017070770263671875, 63)]
+
+
+def _torch_codes(xf32):
+    """Reference quantiser from torch fp32 primitives: s = amax / 127 (one
+    IEEE division), q = round_half_even(x / s) clamped to +-127."""
+    x = torch.from_numpy(xf32)
+    amax = x.abs().amax(dim=1, keepdim=True)
+    s = amax / 127.0
+    q = torch.where(amax > 0, torch.round(x / s), torch.zeros_like(x)).clamp(-127, 127)
+    return q.to(torch.int8).numpy(), s[:, 0].numpy()
+
+
+@pytest.mark.parametrize("amax,xv,code", DIV_CASES)
+def test_act_quant_i8_divides_rather_than_multiplies(orc, amax, xv, code):
+    x = _row([amax, xv, -xv])
+    assert np.array_equal(bf16_values(x)[0], np.float32([amax, xv, -xv]))
+    xq, xs = orc.act_quant_i8(x)
+    s = np.float32(np.float32(amax) / np.float32(127))
+    assert xs[0] == s
+    t_div = np.float32(np.float32(xv) / s)
+    t_mul = np.float32(np.float32(xv) * (np.float32(1) / s))
+    assert np.rint(t_div) != np.rint(t_mul)
+    assert int(np.rint(t_div)) == code
+    assert list(xq[0]) == [127, code, -code]
+
+
+def test_act_quant_i8_equals_torch_division_and_round(orc):
+    # 100,000 random rows with magnitudes spread over many binades, plus the
+    # rows of the 17408 x 5120 decode workload (16 tokens of 5120 values)
+    rng = np.random.default_rng(17)
+    R, K = 100_000, 16
+    mag = np.float32(2.0) ** rng.integers(-40, 40, size=(R, 1)).astype(np.float32)
+    x = bf16_bits(rng.standard_normal((R, K), dtype=np.float32) * mag)
+    xq, xs = orc.act_quant_i8(x)
+    q_ref, s_ref = _torch_codes(bf16_values(x))
+    assert np.array_equal(xs.view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(xq, q_ref)
+    d = gen_int8(16, 8, 5120, seed=0)
+    xq, xs = orc.act_quant_i8(d["x"])
+    q_ref, s_ref = _torch_codes(bf16_values(d["x"]))
+    assert np.array_equal(xs.view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(xq, q_ref)
+
+
+# Int8 dot products (4 terms) with fp32 scales found by a random search over
+# 2e6 triples: bf16((acc*xs)*ws) differs from bf16((acc*ws)*xs) ("swap"),
+# from bf16(acc*(xs*ws)) ("combined scale") or from the once-rounded exact
+# product ("fp64") on some of them.  The epilogue order is the page's:
+# (acc * x_s) * w_s in fp32, then the cast to bf16.
+EPI_CASES = [
+    ([93, -55, 26, -114], [4, -3, -1, -24], 0.016517382115125656, 0.001961976522579789),
+    ([125, 126, 92, 38], [-119, -98, 110, 76], 0.037236087024211884, 0.002826492767781019),
+    ([23, -127, 90, -121], [51, 68, -110, 72], 0.024325739592313766, 0.005899771116673946),
+    ([33, -98, 109, -89], [59, 117, -68, -87], 0.03755415230989456, 0.0015679452335461974),
+    ([-13, 107, -58, -83], [37, 8, -44, 9], 0.030231665819883347, 0.005378833040595055),
+    ([46, -107, -48, -112], [-123, 114, -125, -88], 0.03696686774492264, 0.005032483953982592),
+    ([99, -92, 111, -101], [-55, 82, 6, -49], 0.017969688400626183, 0.0024983659386634827),
+    ([-118, 45, -1, 90], [-96, 24, 98, -45], 0.020163405686616898, 0.005523406434804201),
+    ([-24, 68, -61, -99], [42, -93, 110, -56], 0.03669118881225586, 0.0062264129519462585),
+]
+
+
+def epilogue_case_arrays():
+    """(xq [C,4] int8, w [C,4] int8, xs [C] f32, ws [C] f32): case i is token i
+    against weight row i."""
+    xq = np.array([c[0] for c in EPI_CASES], np.int8)
+    w = np.array([c[1] for c in EPI_CASES], np.int8)
+    xs = np.array([c[2] for c in EPI_CASES], np.float32)
+    ws = np.array([c[3] for c in EPI_CASES], np.float32)
+    return xq, w, xs, ws
+
+
+def _bf16_bits_t(t):
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_gemv_i8_epilogue_order_constructed(orc):
+    xq, w, xs, ws = epilogue_case_arrays()
+    acc, y = orc.gemv_i8(xq, xs, w, ws)
+    acc_ref = xq.astype(np.int64) @ w.astype(np.int64).T
+    assert np.array_equal(acc.astype(np.int64), acc_ref)
+    a = torch.from_numpy(acc_ref).to(torch.float32)
+    txs, tws = torch.from_numpy(xs), torch.from_numpy(ws)
+    ref = _bf16_bits_t((a * txs[:, None]) * tws[None, :])
+    assert np.array_equal(y, ref)
+    # each alternative order is wrong on at least one diagonal case
+    diag = np.arange(len(EPI_CASES))
+    swap = _bf16_bits_t((a * tws[None, :]) * txs[:, None])
+    comb = _bf16_bits_t(a * (txs[:, None] * tws[None, :]))
+    f64 = _bf16_bits_t(torch.from_numpy(acc_ref).double() * txs.double()[:, None] * tws.double()[None, :])
+    for alt in (swap, comb, f64):
+        assert np.any(alt[diag, diag] != ref[diag, diag])

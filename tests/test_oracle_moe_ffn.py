@@ -155,3 +155,55 @@ def test_routed_ffn_end_to_end_is_the_composition(orc):
     assert np.array_equal(ids, np.argsort(-ref_lg, axis=1, kind="stable")[:, :3].astype(np.int32))
     assert np.allclose(g, scipy.special.softmax(np.take_along_axis(ref_lg, ids.astype(np.int64), 1), 1),
                        rtol=1e-12)
+
+
+# ----------------------------------------------------------------------------- activation rounding
+
+# (gate, up) bf16 pairs found by a random search: the fp64 SwiGLU value lies a
+# fraction of an fp32 ulp from a bf16 rounding midpoint, so rounding it once
+# to bf16 differs from rounding it to fp32 first and then to bf16 (ties to
+# even).  The activation is the input of the bf16 down projection and is
+# rounded once.
+ROUNDING_PAIRS = [(-0.1923828125, 4.03125), (-0.7578125, -1.5546875), (-0.1923828125, 8.0625),
+                  (-0.7578125, 6.21875)]
+
+
+def _bf16_nearest_exact(v: float) -> int:
+    """bf16 bits of the value nearest to v, by exact rational comparison of
+    the two bf16 neighbours (v is never a tie here)."""
+    from fractions import Fraction
+    f = np.float32(v)
+    hi = int(f.view(np.uint32)) >> 16
+    cands = [hi - 1, hi, hi + 1]
+    vals = [Fraction(float(np.uint32(c << 16).view(np.float32))) for c in cands]
+    d = [abs(c - Fraction(v)) for c in vals]
+    assert sorted(d)[0] != sorted(d)[1]
+    return cands[d.index(min(d))]
+
+
+def test_ffn_activation_is_rounded_once(orc):
+    import math
+    I, H = 32, 64
+    w13 = np.zeros((1, 2 * I, H // 2), np.uint8)
+    s13 = np.full((1, 2 * I, H // 32), 127, np.uint8)  # scale 2^0
+    x = np.zeros((1, H), np.float32)
+    expect = {}
+    for i, (a, b) in enumerate(ROUNDING_PAIRS):
+        # gate row i reads x[i], up row i reads x[I + i], each through code 1.0 (nibble 0b0010)
+        w13[0, i, i // 2] |= 0x2 << (4 * (i % 2))
+        w13[0, I + i, (I + i) // 2] |= 0x2 << (4 * ((I + i) % 2))
+        x[0, i], x[0, I + i] = a, b
+        v = a / (1.0 + math.exp(-a)) * b
+        single = _bf16_nearest_exact(v)
+        f = np.float32(v)
+        double = int(torch.tensor([float(f)], dtype=torch.float32).to(torch.bfloat16).view(torch.int16)[0]) & 0xFFFF
+        assert single != double
+        expect[i] = single
+    w2 = np.zeros((1, H, I // 2), np.uint8)
+    s2 = np.full((1, H, I // 32), 127, np.uint8)
+    xb = bf16_bits(x)
+    assert np.array_equal(bf16_values(xb), x)
+    act, _, _, _ = orc.moe_ffn_mxfp4(xb, w13, s13, w2, s2, np.zeros((1, 1), np.int32), np.ones((1, 1)))
+    for i, bits in expect.items():
+        assert int(act[0, i]) == bits, (i, hex(int(act[0, i])), hex(bits))
+    assert not act[0, len(ROUNDING_PAIRS):].any()
