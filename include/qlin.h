@@ -259,6 +259,31 @@ int qlin_moe_mxfp4(const void* x, int64_t ldx, int64_t M, int64_t K,
                    void* y, int64_t ldy,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* Largest workspace qlin_moe_mxfp4_noalloc can use (4 MiB): enough for
+ * M * topk * N <= 1,048,576 at M <= 16 (M = 16, topk = 8, N = 8192), less
+ * the pair-sort arrays above 16 tokens. */
+#define QLIN_NOALLOC_SCRATCH_BYTES (4u << 20)
+
+/* qlin_moe_mxfp4 for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the workspace taken from a
+ * library-owned device array of QLIN_NOALLOC_SCRATCH_BYTES per GPU, held until
+ * the process ends.  The caller still passes inputs and outputs.  The call
+ * allocates nothing (no hipMalloc/hipFree, no allocating library routine);
+ * the first call on a GPU looks up that GPU's copy of the array
+ * (hipGetSymbolAddress, the stream's device made current for the lookup).
+ * Arguments, layouts and errors as qlin_moe_mxfp4, and QLIN_ERR_WORKSPACE when
+ * qlin_moe_mxfp4_workspace_bytes(M, N, topk, E) exceeds
+ * QLIN_NOALLOC_SCRATCH_BYTES.  Every call on one GPU shares that GPU's
+ * array: two calls that can overlap on one GPU (different streams, or
+ * different host threads) race and may give wrong results; serialise them.
+ * Nothing in the array needs to start at zero (every value read was written
+ * earlier in the same call). */
+int qlin_moe_mxfp4_noalloc(const void* x, int64_t ldx, int64_t M, int64_t K,
+                           const uint8_t* w_fp4, const uint8_t* s_ue8m0, int64_t E, int64_t N,
+                           const int32_t* topk_ids, const float* topk_w, int64_t topk,
+                           void* y, int64_t ldy, void* stream);
+
 /* ------------------------------------------------------------------------
  * (e) Routed MXFP4 expert FFN with on-device routing -- [DSV4] 9.3 (MXFP4
  *     expert path), 6.6 (J09) and 9.4 (SwiGLU: alpha 1.0, limit 10.0),

@@ -20,7 +20,7 @@ from ._lib import QLIN_FMT_E4M3, QLIN_FMT_E5M2, QlinError, check, load, status_s
 __all__ = [
     "QlinError", "qlin_act_quant_i8", "qlin_gemv_i8", "qlin_gemv_fp8", "qlin_gemv_fp8_blk",
     "qlin_act_quant_fp8", "qlin_gemv_fp8_w8a8", "QLIN_FMT_E4M3", "QLIN_FMT_E5M2", "qlin_gemv_fp8_blk_ex",
-    "qlin_moe_mxfp4", "qlin_moe_mxfp4_workspace_bytes", "status_str",
+    "qlin_moe_mxfp4", "qlin_moe_mxfp4_workspace_bytes", "qlin_moe_mxfp4_noalloc", "status_str",
 ]
 
 
@@ -243,6 +243,34 @@ def qlin_moe_mxfp4(x, w, s, topk_ids, topk_w, y=None, workspace=None, stream=Non
                                 topk_ids.data_ptr(), topk_w.data_ptr(), topk, y.data_ptr(), y.stride(0),
                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                 _stream(x, stream)), "qlin_moe_mxfp4")
+    return y
+
+
+QLIN_NOALLOC_SCRATCH_BYTES = 4 << 20  # the library's per-GPU scratch array behind qlin_moe_mxfp4_noalloc
+
+
+def qlin_moe_mxfp4_noalloc(x, w, s, topk_ids, topk_w, y, stream=None):
+    """qlin_moe_mxfp4 with the library's own per-GPU scratch array as its
+    workspace: the call allocates nothing (y, the output, is the caller's).
+    Calls that can overlap on one GPU share that array and must be serialised."""
+    _need(x, "x", (torch.bfloat16,), 2)
+    _need(w, "w", (torch.uint8,), 3)
+    _need(s, "s", (torch.uint8,), 3)
+    _need(topk_ids, "topk_ids", (torch.int32,), 2)
+    _need(topk_w, "topk_w", (torch.float32,), 2)
+    _need(y, "y", (torch.bfloat16,), 2)
+    M, K = x.shape
+    E, N, Kh = w.shape
+    topk = topk_ids.shape[1]
+    if Kh * 2 != K or tuple(s.shape) != (E, N, K // 32):
+        raise ValueError(f"w {tuple(w.shape)} / s {tuple(s.shape)} do not match K={K}")
+    if not (w.is_contiguous() and s.is_contiguous() and topk_ids.is_contiguous() and topk_w.is_contiguous()):
+        raise ValueError("w, s, topk_ids, topk_w must be contiguous")
+    if tuple(topk_ids.shape) != (M, topk) or tuple(topk_w.shape) != (M, topk) or tuple(y.shape) != (M, N):
+        raise ValueError("topk_ids / topk_w must be [M, topk] and y [M, N]")
+    check(load().qlin_moe_mxfp4_noalloc(x.data_ptr(), x.stride(0), M, K, w.data_ptr(), s.data_ptr(), E, N,
+                                        topk_ids.data_ptr(), topk_w.data_ptr(), topk, y.data_ptr(), y.stride(0),
+                                        _stream(x, stream)), "qlin_moe_mxfp4_noalloc")
     return y
 
 

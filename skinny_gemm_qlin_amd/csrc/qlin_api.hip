@@ -3,8 +3,11 @@
 // Each entry point validates every host-visible argument (pointers, shapes,
 // pitches, alignment, flags) and returns a QLIN_ERR_* code before anything is
 // enqueued; only then does it launch the kernels on the caller's stream.
-// No allocation, no synchronisation, no state.
+// No allocation, no synchronisation.  The only state is the per-device
+// address of the scratch array behind qlin_moe_mxfp4_noalloc.
 #include <hip/hip_runtime.h>
+
+#include <mutex>
 
 #include "../../include/qlin.h"
 #include "qlin_launch.hpp"
@@ -172,10 +175,14 @@ size_t qlin_moe_mxfp4_workspace_bytes(int64_t M, int64_t N, int64_t topk, int64_
     return b + s;
 }
 
-int qlin_moe_mxfp4(const void* x, int64_t ldx, int64_t M, int64_t K,
-                   const uint8_t* w_fp4, const uint8_t* s_ue8m0, int64_t E, int64_t N,
-                   const int32_t* topk_ids, const float* topk_w, int64_t topk,
-                   void* y, int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of qlin_moe_mxfp4 other than the workspace.
+int moe_mxfp4_check(const void* x, int64_t ldx, int64_t M, int64_t K, const uint8_t* w_fp4,
+                    const uint8_t* s_ue8m0, int64_t E, int64_t N, const int32_t* topk_ids, const float* topk_w,
+                    int64_t topk, const void* y, int64_t ldy) {
     if (!x || !w_fp4 || !s_ue8m0 || !topk_ids || !topk_w || !y) return QLIN_ERR_NULL;
     if (M < 1 || M > QLIN_MAX_M_PREFILL || N < 1 || E < 1 || K < 32 || K % 32 != 0 || K > 30720 || topk < 1 ||
         topk > 16)
@@ -185,12 +192,81 @@ int qlin_moe_mxfp4(const void* x, int64_t ldx, int64_t M, int64_t K,
     if (misaligned(x, 16) || ldx % 8 != 0 || misaligned(w_fp4, 16) || misaligned(topk_ids, 4) ||
         misaligned(topk_w, 4) || misaligned(y, 2))
         return QLIN_ERR_ALIGN;
-    if (!workspace || workspace_bytes < qlin_moe_mxfp4_workspace_bytes(M, N, topk, E)) return QLIN_ERR_WORKSPACE;
-    if (misaligned(workspace, 16)) return QLIN_ERR_ALIGN;
+    return QLIN_OK;
+}
+
+int moe_mxfp4_launch(const void* x, int64_t ldx, int64_t M, int64_t K, const uint8_t* w_fp4,
+                     const uint8_t* s_ue8m0, int64_t E, int64_t N, const int32_t* topk_ids, const float* topk_w,
+                     int64_t topk, void* y, int64_t ldy, void* workspace, hipStream_t stream) {
     const size_t part_bytes = ((size_t)M * topk * N * sizeof(float) + 255) & ~(size_t)255;
     qlin::MoeArgs a{(const uint16_t*)x, ldx, M, K, w_fp4, s_ue8m0, E, N, topk_ids, topk_w, topk,
                     (uint16_t*)y, ldy, (float*)workspace, (int32_t*)((char*)workspace + part_bytes)};
-    return launch_status(qlin::launch_moe_mxfp4(a, (hipStream_t)stream));
+    return launch_status(qlin::launch_moe_mxfp4(a, stream));
+}
+
+// Workspace of qlin_moe_mxfp4_noalloc: one copy per GPU, alive until the
+// process ends.  Host code never passes `scratch` itself to a kernel (on the
+// host it names a stand-in, not device memory): it passes the device address
+// looked up once per device with hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[QLIN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device ordinal; null until looked up
+
+// Device address of `scratch` on the device that owns `stream` (the current
+// device for the null stream), looked up with that device current.
+hipError_t scratch_for_stream(hipStream_t stream, void** out) {
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess) return e;
+        if (back != hipSuccess) return back;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qlin_moe_mxfp4(const void* x, int64_t ldx, int64_t M, int64_t K,
+                   const uint8_t* w_fp4, const uint8_t* s_ue8m0, int64_t E, int64_t N,
+                   const int32_t* topk_ids, const float* topk_w, int64_t topk,
+                   void* y, int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
+    const int st = moe_mxfp4_check(x, ldx, M, K, w_fp4, s_ue8m0, E, N, topk_ids, topk_w, topk, y, ldy);
+    if (st != QLIN_OK) return st;
+    if (!workspace || workspace_bytes < qlin_moe_mxfp4_workspace_bytes(M, N, topk, E)) return QLIN_ERR_WORKSPACE;
+    if (misaligned(workspace, 16)) return QLIN_ERR_ALIGN;
+    return moe_mxfp4_launch(x, ldx, M, K, w_fp4, s_ue8m0, E, N, topk_ids, topk_w, topk, y, ldy, workspace,
+                            (hipStream_t)stream);
+}
+
+int qlin_moe_mxfp4_noalloc(const void* x, int64_t ldx, int64_t M, int64_t K,
+                           const uint8_t* w_fp4, const uint8_t* s_ue8m0, int64_t E, int64_t N,
+                           const int32_t* topk_ids, const float* topk_w, int64_t topk,
+                           void* y, int64_t ldy, void* stream) {
+    const int st = moe_mxfp4_check(x, ldx, M, K, w_fp4, s_ue8m0, E, N, topk_ids, topk_w, topk, y, ldy);
+    if (st != QLIN_OK) return st;
+    if (qlin_moe_mxfp4_workspace_bytes(M, N, topk, E) > (size_t)QLIN_NOALLOC_SCRATCH_BYTES)
+        return QLIN_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (scratch_for_stream((hipStream_t)stream, &ws) != hipSuccess) return QLIN_ERR_LAUNCH;
+    return moe_mxfp4_launch(x, ldx, M, K, w_fp4, s_ue8m0, E, N, topk_ids, topk_w, topk, y, ldy, ws,
+                            (hipStream_t)stream);
 }
 
 static size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
