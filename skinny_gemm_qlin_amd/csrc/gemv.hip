@@ -4,8 +4,10 @@
 // decode shapes (N=17408, K=5120 for INT8 / E4M3; N=4096, K=7168 for block
 // FP8):
 //   * M = 1: VALU, one whole wavefront per row (GS=64), all K steps of the
-//     row in flight (up to 8), 4 waves per workgroup; block FP8 uses its own
-//     M = 1 kernel that shares the scale bytes of a batch across the wave;
+//     row in flight (up to 8); INT8 with 4 waves per workgroup, the FP8
+//     kinds (weight-only and W8A8) with the token row staged once per
+//     8-wave workgroup in LDS as bf16; block FP8 uses its own M = 1 kernel
+//     that shares the scale bytes of a batch across the wave;
 //   * M = 2 (INT8, FP8 W8A8, and E4M3 where the next item does not apply):
 //     VALU with smaller lane groups (and, for INT8 / E4M3, several rows per
 //     group, so that each activation load feeds more weight rows);
@@ -94,6 +96,40 @@ inline int steps64(int64_t K) { return (int)(((K >> 4) + 63) / 64); }
         default: return RUN<1, 64, 1, 8, 4>(a, st);                   \
     }
 
+
+// One token, FP8 weights: the activation row staged once per workgroup in LDS
+// (gemv_fp8_m1_lds_kernel), K <= 8192 (at most 8 steps of 1 KB per row).
+// 8 waves per workgroup (17408 x 5120: 14.6-15.1 us against 15.3-16.1 us for
+// the register-only kernel it replaced).
+constexpr int kM1LdsWaves = 8;
+constexpr int64_t kM1LdsMaxK = 8192;
+
+template <int W8A8, int XF, int WF, int U>
+void launch_fp8_m1_lds_u(const void* x, const float* xs, int64_t K, const uint8_t* w, int64_t ldw, int64_t N,
+                         const float* ws, int ws_step, uint16_t* y, hipStream_t st) {
+    const size_t lds = (size_t)(((K >> 3) + 63) / 64) * 1024;  // whole 1 KB direct-load blocks of 2*K/16 halves
+    hipLaunchKernelGGL((gemv_fp8_m1_lds_kernel<W8A8, U, kM1LdsWaves, XF, WF>),
+                       dim3((unsigned)((N + kM1LdsWaves - 1) / kM1LdsWaves)), dim3(64 * kM1LdsWaves), lds, st,
+                       x, xs, K, w, ldw, N, ws, ws_step, y);
+}
+
+template <int W8A8, int XF = kFmtE4M3, int WF = kFmtE4M3>
+hipError_t run_fp8_m1_lds(const void* x, const float* xs, int64_t K, const uint8_t* w, int64_t ldw, int64_t N,
+                          const float* ws, int ws_step, uint16_t* y, hipStream_t st) {
+#define QLIN_M1_LDS(U_) launch_fp8_m1_lds_u<W8A8, XF, WF, U_>(x, xs, K, w, ldw, N, ws, ws_step, y, st); break;
+    switch (steps64(K)) {
+        case 1: QLIN_M1_LDS(1)
+        case 2: QLIN_M1_LDS(2)
+        case 3: QLIN_M1_LDS(3)
+        case 4: QLIN_M1_LDS(4)
+        case 5: QLIN_M1_LDS(5)
+        case 6: QLIN_M1_LDS(6)
+        case 7: QLIN_M1_LDS(7)
+        default: QLIN_M1_LDS(8)
+    }
+#undef QLIN_M1_LDS
+    return hipGetLastError();
+}
 
 // Matrix-core kernels: one workgroup of KS waves per 16-row tile, one chunk
 // of 256 K per wave per batch (few registers, so the whole grid is resident
@@ -314,7 +350,10 @@ hipError_t launch_gemv_i8(const I8Args& a, hipStream_t st) {
 hipError_t launch_gemv_fp8(const F8Args& a, hipStream_t st) {
     if (a.M > kDecodeMaxM) return launch_gemm_fp8(a, st);
     switch (a.M) {
-        case 1: return run_fp8<1, 32, 2, 1, 1>(a, st);
+        case 1:
+            if (a.K <= kM1LdsMaxK)
+                return run_fp8_m1_lds<0>(a.x, nullptr, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.y, st);
+            return run_fp8<1, 32, 2, 1, 1>(a, st);
         default: {
             // K-slice kernels from M = 2 (17408 x 5120: 17.4 against 18.2 us
             // for the VALU kernel at M = 2)
@@ -336,6 +375,15 @@ hipError_t launch_gemv_fp8(const F8Args& a, hipStream_t st) {
 // 5 steps); the matrix-core kernel from M = 3.
 hipError_t launch_gemv_fp8_w8a8(const W8A8F8Args& a, hipStream_t st) {
     if (a.M > kDecodeMaxM) return launch_gemm_fp8_w8a8(a, st);
+    if (a.M == 1 && a.K <= kM1LdsMaxK) {
+        if (a.x_fmt == kFmtE5M2)
+            return a.w_fmt == kFmtE5M2
+                       ? run_fp8_m1_lds<1, kFmtE5M2, kFmtE5M2>(a.xq, a.xs, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.y, st)
+                       : run_fp8_m1_lds<1, kFmtE5M2, kFmtE4M3>(a.xq, a.xs, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.y, st);
+        return a.w_fmt == kFmtE5M2
+                   ? run_fp8_m1_lds<1, kFmtE4M3, kFmtE5M2>(a.xq, a.xs, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.y, st)
+                   : run_fp8_m1_lds<1, kFmtE4M3, kFmtE4M3>(a.xq, a.xs, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.y, st);
+    }
     if (a.M == 1) {
         switch (std::min(steps64(a.K), 3)) {
             case 1: return run_w8a8<1, 64, 1, 1, 4>(a, st);

@@ -569,4 +569,109 @@ __global__ __launch_bounds__(64 * WPB) void gemv_fp8_blk_m1_fq_kernel(
     if (j == 0) y[n] = f32_to_bf16(acc);
 }
 
+// ------------------------------------------------------------------ one token, activations in LDS
+// M = 1 for FP8 weight-only and FP8 W8A8 [Z100 operator-family table, FP8
+// row; section 2.2].  A wave owns one weight row and keeps all U <= 8 of its
+// 1 KB steps in flight (lane j reads chunk j + 64u), like the INT8 M = 1
+// kernel; the workgroup's WPB waves share one copy of the token row in LDS
+// (as bf16), so the activations cost one read per workgroup instead of one
+// per row (re-reading them per row from the caches measured ~2 us slower at
+// 17408 x 5120).  LDS layout: the first 8 values of chunk c at slot c, the
+// last 8 at slot nchunk + c (16 bytes each), so lane j's reads of either half
+// are contiguous across the wave.  Staging: bf16 activations go global ->
+// LDS with direct loads issued before the weight loads, so the wait for them
+// leaves the weights in flight; FP8 activation codes (W8A8) go through
+// registers and are widened to bf16 once.  Per lane the chunks are summed in
+// order (8 v_dot2 each), then across the wave; epilogue bf16(acc * ws)
+// (weight-only) or bf16((acc * xs) * ws) (W8A8), as the other kernels.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <int W8A8, int U, int WPB, int XF = kFmtE4M3, int WF = kFmtE4M3>
+__global__ __launch_bounds__(64 * WPB) void gemv_fp8_m1_lds_kernel(
+    const void* __restrict__ x, const float* __restrict__ xs, int64_t K,
+    const uint8_t* __restrict__ w, int64_t ldw, int64_t N,
+    const float* __restrict__ ws, int ws_step, uint16_t* __restrict__ y) {
+    extern __shared__ __align__(16) u32x4_t xl[];  // [2 * nchunk] 16-byte halves
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t nchunk = K >> 4, nh = 2 * nchunk;
+    // 1. activations (issued first)
+    constexpr int NT = 64 * WPB;
+    if constexpr (!W8A8) {
+        // bf16: one direct load instruction fills 1 KB (64 halves) of LDS
+        const uint16_t* xb = (const uint16_t*)x;
+        const int ni = (int)((nh + 63) >> 6);
+        for (int inst = wv; inst < ni; inst += WPB) {  // wave-uniform
+            const int64_t q = (int64_t)inst * 64 + lane, qq = q < nh ? q : nh - 1;
+            const int64_t h = qq >= nchunk, c = qq - h * nchunk;
+            __builtin_amdgcn_global_load_lds((const void*)(xb + c * 16 + h * 8), (lds_void_t*)(xl + (int64_t)inst * 64),
+                                             16, 0, 0);
+        }
+    }
+    // W8A8: each thread widens at most kCodeChunks chunks of codes (K <= 8192)
+    constexpr int kCodeChunks = (512 + NT - 1) / NT;
+    u32x4_t xc[W8A8 ? kCodeChunks : 1];
+    if constexpr (W8A8) {
+#pragma unroll
+        for (int i = 0; i < kCodeChunks; ++i) {
+            const int64_t c = tid + (int64_t)i * NT, cc = c < nchunk ? c : nchunk - 1;
+            xc[i] = ld16((const uint8_t*)x + cc * 16);
+        }
+    }
+    // 2. this wave's row, every step in flight
+    const int64_t n = (int64_t)blockIdx.x * WPB + wv;
+    const int64_t nn = n < N ? n : N - 1;
+    const uint8_t* wr = w + nn * ldw;
+    u32x4_t wq[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t c = (int64_t)u * 64 + lane, cc = c < nchunk ? c : nchunk - 1;
+        wq[u] = ld_stream(wr + cc * 16);
+    }
+    const float wsv = ws[nn * ws_step];
+    // 3. publish the activations: every load issued before the U weight loads
+    //    has landed once at most U loads are outstanding
+    if constexpr (W8A8) {
+#pragma unroll
+        for (int i = 0; i < kCodeChunks; ++i) {
+            const int64_t c = tid + (int64_t)i * NT;
+            if (c < nchunk) {
+                bf16x2_t b[8];
+                fp8x16<XF>(xc[i], b);
+                xl[c] = u32x4_t{__builtin_bit_cast(uint32_t, b[0]), __builtin_bit_cast(uint32_t, b[1]),
+                                __builtin_bit_cast(uint32_t, b[2]), __builtin_bit_cast(uint32_t, b[3])};
+                xl[nchunk + c] = u32x4_t{__builtin_bit_cast(uint32_t, b[4]), __builtin_bit_cast(uint32_t, b[5]),
+                                         __builtin_bit_cast(uint32_t, b[6]), __builtin_bit_cast(uint32_t, b[7])};
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the LDS stores are done
+    } else {
+        __builtin_amdgcn_s_waitcnt((U & 15) | 0x70 | 0xF00);  // vmcnt(U)
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();  // not __syncthreads(): that would also wait for the weights
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    // 4. the row's dot product
+    float acc = 0.0f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t c = (int64_t)u * 64 + lane;
+        const bool ok = c < nchunk;
+        const int64_t cc = ok ? c : nchunk - 1;
+        bf16x2_t wb[8];
+        fp8x16<WF>(wq[u], wb);
+        u32x4_t a = xl[cc], b = xl[nchunk + cc];
+        if (!ok) a = b = u32x4_t{0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = dot2(wb[e], as_bf16x2(a[e]), acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = dot2(wb[4 + e], as_bf16x2(b[e]), acc);
+    }
+    acc = group_sum<64>(acc);
+    if (lane == 0 && n < N) {
+        const float t = W8A8 ? (acc * xs[0]) * wsv : acc * wsv;
+        y[n] = f32_to_bf16(t);
+    }
+}
+
 }  // namespace qlin
