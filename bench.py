@@ -3,9 +3,12 @@
 
 Default workload (the decode configuration the metric is quoted on):
 W8A8 INT8, N=17408, K=5120.  One step = the whole INT8 decode linear layer
-(qlin_act_quant_i8 + qlin_gemv_i8 with its bf16 epilogue) once at every
+(qlin_linear_i8: per-token quantisation + GEMV with its bf16 epilogue; one
+kernel for one token, quantiser + GEMV kernels otherwise) once at every
 M in {1, 2, 4, 8, 16}.  Weights are cold: each call reads the next of B
 rotating weight copies (B * |W| >= 2 x the 256 MB Infinity Cache).
+The same line also carries `fp8_m1`: the E4M3 weight-only GEMV at M=1 on the
+same shape, per-channel and per-tensor scales, timed the same way.
 
 Prints ONE JSON line.  `value` = algorithmic bytes moved by the timed steps /
 their wall time on the GPU (GB/s, inputs already in HBM).  `roofline`
@@ -45,6 +48,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 # ----------------------------------------------------------------------------- byte counts
 
 def bytes_gemv_i8(M, N, K):
@@ -55,8 +69,8 @@ def bytes_act_quant_i8(M, K):
     return 2 * M * K + M * K + 4 * M                           # x, xq, xs
 
 
-def bytes_gemv_fp8(M, N, K):
-    return N * K + 4 * N + 2 * M * K + 2 * M * N               # W, ws (per row), x, y
+def bytes_gemv_fp8(M, N, K, per_tensor=False):
+    return N * K + (4 if per_tensor else 4 * N) + 2 * M * K + 2 * M * N   # W, ws, x, y
 
 
 def bytes_act_quant_fp8(M, K):
@@ -153,6 +167,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--per-tensor", action="store_true", help="fp8_decode: per-tensor weight scale")
     ap.add_argument("--block", default="128,128", help="fp8_blk: block_n,block_k of the weight scales")
+    ap.add_argument("--no-fp8", action="store_true", help="int8_decode: skip the fp8_m1 measurement")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -255,7 +270,10 @@ def main():
         """[(kernel, bytes, fn)] for one call of the workload's entry point."""
         w = ws_copies[ci]
         xm = x[:M]
-        if wl in ("int8_decode", "int8_prefill"):
+        if wl == "int8_decode":
+            return [("linear_i8", bytes_act_quant_i8(M, K) + bytes_gemv_i8(M, N, K),
+                     lambda: ql.qlin_linear_i8(xm, w, sc, xq=xq_buf[:M], xs=xs_buf[:M], y=y_buf[:M]))]
+        if wl == "int8_prefill":
             return [("act_quant_i8", bytes_act_quant_i8(M, K),
                      lambda: ql.qlin_act_quant_i8(xm, xq_buf[:M], xs_buf[:M])),
                     ("gemv_i8", bytes_gemv_i8(M, N, K),
@@ -277,6 +295,18 @@ def main():
         return [("moe_ffn_mxfp4", bytes_moe_ffn_call(M, N, spec["I"], spec["E"], spec["topk"], live_of[M]),
                  lambda: ql.qlin_moe_ffn_mxfp4(xm, wr, *ffn[ci], spec["topk"], y=y_buf[:M], workspace=ws_ffn,
                                                ids=ids_buf[:M], gw=gw_buf[:M]))]
+
+    def measured(M, ci):
+        """[(kernel, bytes, fn)] timed one by one (region B): the step's launches,
+        and for the INT8 decode layer also its quantiser and GEMV alone."""
+        if wl != "int8_decode":
+            return launches(M, ci)
+        w = ws_copies[ci]
+        xm = x[:M]
+        return [("act_quant_i8", bytes_act_quant_i8(M, K),
+                 lambda: ql.qlin_act_quant_i8(xm, xq_buf[:M], xs_buf[:M])),
+                ("gemv_i8", bytes_gemv_i8(M, N, K),
+                 lambda: ql.qlin_gemv_i8(xq_buf[:M], xs_buf[:M], w, sc, y=y_buf[:M]))] + launches(M, ci)
 
     dominant = {"int8_decode": "gemv_i8", "fp8_decode": "gemv_fp8", "fp8_w8a8": "gemv_fp8_w8a8",
                 "int8_prefill": "gemv_i8", "fp8_prefill": "gemv_fp8",
@@ -336,9 +366,9 @@ def main():
     dom_bytes, dom_ms, dom_n, dom_flops = 0, 0.0, 0, 0
     for i, M in enumerate(Ms):
         ent = per_m.setdefault(str(M), {})
-        for kidx in range(len(launches(M, 0))):
-            kname, nb, _ = launches(M, 0)[kidx]
-            g = capture([launches(M, (i + r) % B)[kidx][2] for r in range(reps)])
+        for kidx in range(len(measured(M, 0))):
+            kname, nb, _ = measured(M, 0)[kidx]
+            g = capture([measured(M, (i + r) % B)[kidx][2] for r in range(reps)])
             g.replay()
             torch.cuda.synchronize()
             e0 = torch.cuda.Event(enable_timing=True)
@@ -358,7 +388,7 @@ def main():
                 dom_ms += ms * reps
                 dom_n += reps
             del g
-        ent["call_us"] = round(sum(v["us"] for v in ent.values()), 3)
+        ent["call_us"] = round(sum(ent[k]["us"] for k, _, _ in launches(M, 0)), 3)
 
     step_bytes = 0
     for M in Ms:
@@ -380,6 +410,34 @@ def main():
         roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                     "launches": dom_n}
+
+    # ---------------------------------------------------------------- FP8 weight-only, one token
+    fp8_m1 = None
+    if wl == "int8_decode" and not args.no_fp8:
+        fp8_m1 = {}
+        for pt in (False, True):
+            f = inputs.gen_fp8(1, N, K, seed=0, per_tensor=pt)
+            w8 = [t(f["w"])]
+            w8 += [w8[0].clone() for _ in range(B - 1)]
+            x8, s8 = tb(f["x"]), t(f["ws"])
+            y8 = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
+            fns = [(lambda wc=w8[r % B]: ql.qlin_gemv_fp8(x8, wc, s8, y=y8)) for r in range(reps)]
+            g = capture(fns)
+            g.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / reps * 1e3
+            nb = bytes_gemv_fp8(1, N, K, per_tensor=pt)
+            fp8_m1["per_tensor" if pt else "per_channel"] = {
+                "us": round(us, 3), "GBps": round(nb / (us * 1e-6) / 1e9, 1),
+                "frac": round(nb / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "bytes": nb}
+            del g, w8
+        log(f"bench: fp8 M=1 {fp8_m1}")
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
@@ -420,10 +478,26 @@ def main():
         med = statistics.median(times)
         cpu = {"value": round(step_bytes / med / 1e9, 3), "unit": "GB/s", "cores": used, "kind": "oracle",
                "sample": f"{len(times)} full step(s) of the same workload (Ms={Ms}, N={N}, K={K}), "
-                         f"{sum(times):.1f} s of CPU work, median {med:.3f} s per step"}
+                         f"{sum(times):.1f} s of CPU work, median {med:.3f} s per step",
+               "cpu_model": cpu_model()}
+        # the same oracle on one thread: up to 3 steps, no new step after 20 s
+        # (skipped when one step would take longer than that)
+        if med * used <= 20.0:
+            oracle.set_threads(1)
+            t1, t_begin = [], time.perf_counter()
+            while len(t1) < 3 and time.perf_counter() - t_begin < 20.0:
+                t0 = time.perf_counter()
+                oracle_step()
+                t1.append(time.perf_counter() - t0)
+            oracle.set_threads(used)
+            med1 = statistics.median(t1)
+            cpu["single_thread"] = {"value": round(step_bytes / med1 / 1e9, 3), "unit": "GB/s", "cores": 1,
+                                    "sample": f"{len(t1)} full step(s), median {med1:.3f} s per step"}
+        else:
+            cpu["single_thread"] = None
 
     cfg = {"workload": {
-        "int8_decode": f"W8A8 INT8 decode linear (act quant + GEMV, bf16 out) N={N} K={K}, one call per M",
+        "int8_decode": f"W8A8 INT8 decode linear (qlin_linear_i8: act quant + GEMV, bf16 out) N={N} K={K}, one call per M",
         "fp8_decode": f"E4M3 weight-only GEMV ({'per-tensor' if args.per_tensor else 'per-channel'}) N={N} K={K}",
         "int8_prefill": f"W8A8 INT8 prefill linear (act quant + tiled GEMM, bf16 out) N={N} K={K}, one call per M",
         "fp8_prefill": f"E4M3 weight-only prefill GEMM (per-channel) N={N} K={K}, one call per M",
@@ -457,6 +531,7 @@ def main():
         "config": cfg,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "fp8_m1": fp8_m1,
         "per_m": per_m,
     }
     print(json.dumps(out), flush=True)

@@ -112,6 +112,20 @@ int qlin_gemv_i8(const int8_t* xq, int64_t ldxq, const float* xs, int xs_per_tok
                  const float* ws, int ws_per_row, const void* bias,
                  void* y, int64_t ldy, int out_kind, void* stream);
 
+/* The whole INT8 decode linear layer in one call: qlin_act_quant_i8 on x
+ * (codes and scales written to xq / xs, exactly as that call writes them)
+ * followed by qlin_gemv_i8 with out_kind 0 and per-token scales.  For one
+ * token (M = 1, K <= 8192) a single kernel does both: each workgroup
+ * quantises the row into its LDS (the same fp32 operations, bit-identical
+ * codes and outputs) while its weight rows are in flight; otherwise the two
+ * kernels run back to back on `stream`.  xq and xs are always written.
+ * Arguments, layouts and limits as the two calls ([Z100] section 2.1 times
+ * the INT8 GEMV both alone and with its quantiser, the "full" figure). */
+int qlin_linear_i8(const void* x, int64_t ldx, int64_t M, int64_t K,
+                   const int8_t* w, int64_t ldw, int64_t N, const float* ws, int ws_per_row,
+                   const void* bias, int8_t* xq, int64_t ldxq, float* xs,
+                   void* y, int64_t ldy, void* stream);
+
 /* ------------------------------------------------------------------------
  * (b) FP8-E4M3 weight-only -- [Z100] operator-family table (FP8 row), 2.2
  * ------------------------------------------------------------------------ */

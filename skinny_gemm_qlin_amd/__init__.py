@@ -18,7 +18,7 @@ import torch
 from ._lib import QLIN_FMT_E4M3, QLIN_FMT_E5M2, QlinError, check, load, status_str  # noqa: F401
 
 __all__ = [
-    "QlinError", "qlin_act_quant_i8", "qlin_gemv_i8", "qlin_gemv_fp8", "qlin_gemv_fp8_blk",
+    "QlinError", "qlin_act_quant_i8", "qlin_gemv_i8", "qlin_linear_i8", "qlin_gemv_fp8", "qlin_gemv_fp8_blk",
     "qlin_act_quant_fp8", "qlin_gemv_fp8_w8a8", "QLIN_FMT_E4M3", "QLIN_FMT_E5M2", "qlin_gemv_fp8_blk_ex",
     "qlin_moe_mxfp4", "qlin_moe_mxfp4_workspace_bytes", "qlin_moe_mxfp4_noalloc", "status_str",
 ]
@@ -84,6 +84,36 @@ def qlin_gemv_i8(xq, xs, w, ws, bias=None, y=None, out_kind=0, stream=None):
                               None if bias is None else bias.data_ptr(), y.data_ptr(), y.stride(0),
                               int(out_kind), _stream(xq, stream)), "qlin_gemv_i8")
     return y
+
+
+def qlin_linear_i8(x, w, ws, bias=None, xq=None, xs=None, y=None, stream=None):
+    """The whole INT8 decode linear layer in one call: per-token quantisation of
+    bf16 x [M, K] (codes and scales into xq int8 [M, K] / xs fp32 [M]) and the
+    W8A8 GEMV with its bf16 epilogue.  One kernel for one token.
+    Returns (y bf16 [M, N], xq, xs)."""
+    _need(x, "x", (torch.bfloat16,), 2)
+    _need(w, "w", (torch.int8,), 2)
+    _need(ws, "ws", (torch.float32,), 1)
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError(f"w has K={w.shape[1]}, x has K={K}")
+    if bias is not None:
+        _need(bias, "bias", (torch.bfloat16,), 1)
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if xs is None:
+        xs = torch.empty((M,), dtype=torch.float32, device=x.device)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(xq, "xq", (torch.int8,), 2)
+    _need(xs, "xs", (torch.float32,), 1)
+    _need(y, "y", (torch.bfloat16,), 2)
+    check(load().qlin_linear_i8(x.data_ptr(), x.stride(0), M, K, w.data_ptr(), w.stride(0), N, ws.data_ptr(),
+                                int(ws.numel() > 1), None if bias is None else bias.data_ptr(), xq.data_ptr(),
+                                xq.stride(0), xs.data_ptr(), y.data_ptr(), y.stride(0), _stream(x, stream)),
+          "qlin_linear_i8")
+    return y, xq, xs
 
 
 def qlin_gemv_fp8(x, w, ws, y=None, stream=None):

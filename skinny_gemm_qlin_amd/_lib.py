@@ -25,7 +25,7 @@ EXPORTS = (
     "qlin_status_str", "qlin_version", "qlin_act_quant_i8", "qlin_gemv_i8", "qlin_gemv_fp8",
     "qlin_gemv_fp8_blk", "qlin_moe_mxfp4_workspace_bytes", "qlin_moe_mxfp4",
     "qlin_moe_ffn_mxfp4_workspace_bytes", "qlin_moe_ffn_mxfp4", "qlin_act_quant_fp8", "qlin_gemv_fp8_w8a8",
-    "qlin_gemv_fp8_blk_ex", "qlin_moe_mxfp4_noalloc",
+    "qlin_gemv_fp8_blk_ex", "qlin_moe_mxfp4_noalloc", "qlin_linear_i8",
 )
 
 QLIN_FMT_E4M3 = 0
@@ -57,6 +57,8 @@ def load() -> ctypes.CDLL:
     lib.qlin_act_quant_i8.restype = I
     lib.qlin_gemv_i8.argtypes = [P, I64, P, I, I64, I64, P, I64, I64, P, I, P, P, I64, I, P]
     lib.qlin_gemv_i8.restype = I
+    lib.qlin_linear_i8.argtypes = [P, I64, I64, I64, P, I64, I64, P, I, P, P, I64, P, P, I64, P]
+    lib.qlin_linear_i8.restype = I
     lib.qlin_gemv_fp8.argtypes = [P, I64, I64, I64, P, I64, I64, P, I, P, I64, P]
     lib.qlin_gemv_fp8.restype = I
     lib.qlin_act_quant_fp8.argtypes = [P, I64, I64, I64, I, I, P, I64, P, P]

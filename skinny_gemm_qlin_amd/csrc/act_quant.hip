@@ -17,39 +17,12 @@ namespace qlin {
 // One workgroup (512 lanes) per token.  Pass 1: amax over the row with
 // 16-byte loads (the first kCached vectors of each lane stay in registers);
 // DPP row max, then across the 4 rows of a wave, then across the 8 waves
-// through LDS.  Pass 2: IEEE fp32 division and round-half-even
-// (v_rndne_f32), clamp to +-127, 8 codes per 8-byte store.  512 lanes rather
+// through LDS.  Pass 2: the IEEE fp32 quotient x / s (div_bf16) and
+// round-half-even (v_rndne_f32), clamp to +-127, 8 codes per 8-byte store.  512 lanes rather
 // than 256 halve the divisions on each lane's path (2.74 -> 2.30 us per
 // 5120-wide token on MI355X, codes unchanged).
 constexpr int kQuantThreads = 512;
 constexpr int kCached = 2;  // K <= 8192 is read from HBM exactly once
-
-__device__ __forceinline__ uint2 quant8(const u32x4_t& v, float amax, float s) {
-    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-    uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const uint32_t h = (e & 1) ? (d[e >> 1] >> 16) : (d[e >> 1] & 0xFFFFu);
-        int q = 0;
-        if (amax != 0.0f) {
-            float t = rintf(bf16_to_f32(h) / s);
-            t = fminf(fmaxf(t, -127.0f), 127.0f);
-            q = (int)t;
-        }
-        packed[e >> 2] |= ((uint32_t)q & 0xFFu) << (8 * (e & 3));
-    }
-    return make_uint2(packed[0], packed[1]);
-}
-
-__device__ __forceinline__ float absmax8(const u32x4_t& v, float a) {
-    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        a = fmaxf(a, fabsf(bf16_to_f32(d[q] & 0xFFFFu)));
-        a = fmaxf(a, fabsf(bf16_to_f32(d[q] >> 16)));
-    }
-    return a;
-}
 
 __global__ __launch_bounds__(kQuantThreads) void act_quant_i8_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int64_t K,
@@ -80,15 +53,16 @@ __global__ __launch_bounds__(kQuantThreads) void act_quant_i8_kernel(
     for (int q = 1; q < W; ++q) amax = fmaxf(amax, wave_max[q]);
     const float s = amax / 127.0f;
     if (tid == 0) xs[m] = s;
+    const double r = 1.0 / (double)s;  // x / s per element as div_bf16(x, r)
 
     int8_t* qrow = xq + m * ldxq;
 #pragma unroll
     for (int c = 0; c < kCached; ++c) {
         const int64_t i = tid + c * kQuantThreads;
-        if (i < nvec) *(uint2*)(qrow + i * 8) = quant8(cache[c], amax, s);
+        if (i < nvec) *(uint2*)(qrow + i * 8) = quant8(cache[c], amax, r);
     }
     for (int64_t i = tid + kCached * kQuantThreads; i < nvec; i += kQuantThreads)
-        *(uint2*)(qrow + i * 8) = quant8(ld16(row + i * 8), amax, s);
+        *(uint2*)(qrow + i * 8) = quant8(ld16(row + i * 8), amax, r);
 }
 
 hipError_t launch_act_quant_i8(const ActQuantI8Args& a, hipStream_t st) {

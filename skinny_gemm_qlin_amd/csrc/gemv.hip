@@ -131,6 +131,40 @@ hipError_t run_fp8_m1_lds(const void* x, const float* xs, int64_t K, const uint8
     return hipGetLastError();
 }
 
+// INT8, 2..3 tokens (and one token with the quantiser fused in): one wave
+// per row, the token rows' codes shared through LDS (gemv_i8_lds_kernel).
+// 17408 x 5120: M = 2 14.9-15.1 us against 15.7-16.1 us for the lane-group
+// kernel, M = 3 15.8-16.2 us; the fused one-token call 16.2-16.5 us against
+// 16.9-17.3 us for quantiser + GEMV in two launches.
+constexpr int64_t kI8LdsMaxM = 3;
+
+template <int M, int WPB, bool QX, int U>
+void launch_i8_lds_u(const void* x, int64_t ldx, const I8Args& a, int8_t* xq_out, int64_t ldxq, float* xs_out,
+                     hipStream_t st) {
+    const size_t lds = QX ? (size_t)(M * a.K) : (size_t)((M * (a.K >> 4) + 63) / 64) * 1024;
+    hipLaunchKernelGGL((gemv_i8_lds_kernel<M, U, WPB, QX>), dim3((unsigned)((a.N + WPB - 1) / WPB)), dim3(64 * WPB),
+                       lds, st, x, ldx, a.xs, a.xs_step, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.bias, a.y, a.ldy,
+                       a.out_kind, xq_out, ldxq, xs_out);
+}
+
+template <int M, int WPB, bool QX>
+hipError_t run_i8_lds(const void* x, int64_t ldx, const I8Args& a, int8_t* xq_out, int64_t ldxq, float* xs_out,
+                      hipStream_t st) {
+#define QLIN_I8_LDS(U_) launch_i8_lds_u<M, WPB, QX, U_>(x, ldx, a, xq_out, ldxq, xs_out, st); break;
+    switch (steps64(a.K)) {
+        case 1: QLIN_I8_LDS(1)
+        case 2: QLIN_I8_LDS(2)
+        case 3: QLIN_I8_LDS(3)
+        case 4: QLIN_I8_LDS(4)
+        case 5: QLIN_I8_LDS(5)
+        case 6: QLIN_I8_LDS(6)
+        case 7: QLIN_I8_LDS(7)
+        default: QLIN_I8_LDS(8)
+    }
+#undef QLIN_I8_LDS
+    return hipGetLastError();
+}
+
 // Matrix-core kernels: one workgroup of KS waves per 16-row tile, one chunk
 // of 256 K per wave per batch (few registers, so the whole grid is resident
 // and waves overlap each other's latency; measured at the decode shapes).
@@ -332,6 +366,9 @@ hipError_t run_blk_m1_fq(const BlkQuantArgs& q, const BlkArgs& a, hipStream_t st
 
 hipError_t launch_gemv_i8(const I8Args& a, hipStream_t st) {
     if (a.M > kDecodeMaxM) return launch_gemm_i8(a, st);
+    if (a.M >= 2 && a.M <= kI8LdsMaxM && a.K <= kI8LdsMaxK)
+        return a.M == 2 ? run_i8_lds<2, 4, false>(a.xq, a.ldxq, a, nullptr, 0, nullptr, st)
+                        : run_i8_lds<3, 4, false>(a.xq, a.ldxq, a, nullptr, 0, nullptr, st);
     switch (a.M) {
         case 1: QLIN_M1_BY_STEPS(run_i8, a, st)
         case 2: return run_i8<2, 32, 2, 2, 1>(a, st);
@@ -345,6 +382,11 @@ hipError_t launch_gemv_i8(const I8Args& a, hipStream_t st) {
             return run_i8_mfma(a, st);
         }
     }
+}
+
+hipError_t launch_linear_i8_fused(const ActQuantI8Args& q, const I8Args& a, hipStream_t st) {
+    if (a.M != 1 || a.K > kI8LdsMaxK) return hipErrorInvalidValue;
+    return run_i8_lds<1, 8, true>(q.x, q.ldx, a, q.xq, q.ldxq, q.xs, st);
 }
 
 hipError_t launch_gemv_fp8(const F8Args& a, hipStream_t st) {

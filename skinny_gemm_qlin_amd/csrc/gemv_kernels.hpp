@@ -674,4 +674,184 @@ __global__ __launch_bounds__(64 * WPB) void gemv_fp8_m1_lds_kernel(
     }
 }
 
+// ------------------------------------------------------------------ INT8, few tokens, codes in LDS
+// W8A8 INT8 for M <= 4 tokens [Z100 operator-family table, INT8 row;
+// section 2.1].  A wave owns one weight row with all U <= 8 steps of 1 KB in
+// flight (lane j reads chunk j + 64u); the workgroup's WPB waves share the M
+// token rows of int8 codes in LDS ([m][K] bytes), each chunk dotted with
+// v_dot4 (exact int32), summed across the wave, epilogue bf16((acc * xs) *
+// ws) then + bias, or the raw sums (out_kind 1).
+// QX: the kernel quantises the bf16 token rows itself with the per-token
+// rule of the INT8 quantiser (quant8 / absmax8: bit-identical codes and
+// scales), so one launch serves the whole layer: every thread loads its
+// share of the rows before the weight loads, the per-token absolute maximum
+// goes through a wave reduction and one LDS exchange, and each thread
+// divides and stores only its own share, all under the weights' HBM
+// latency.  Workgroup 0 also writes the codes and scales out when asked.
+constexpr int kI8LdsMaxK = 8192;
+
+template <int M, int U, int WPB, bool QX>
+__global__ __launch_bounds__(64 * WPB) void gemv_i8_lds_kernel(
+    const void* __restrict__ x, int64_t ldx, const float* __restrict__ xs, int xs_step,
+    int64_t K, const int8_t* __restrict__ w, int64_t ldw, int64_t N,
+    const float* __restrict__ ws, int ws_step, const uint16_t* __restrict__ bias,
+    void* __restrict__ y, int64_t ldy, int out_kind,
+    int8_t* __restrict__ xq_out, int64_t ldxq, float* __restrict__ xs_out) {
+    extern __shared__ __align__(16) u32x4_t xl[];  // codes [M][K] bytes
+    __shared__ float wmax[QX ? WPB : 1][M];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t nchunk = K >> 4;
+    constexpr int NT = 64 * WPB;
+    // 1. activations, issued before the weights
+    // 32-bit index math (K <= 8192, M <= 4): the token of a vector or chunk is
+    // found by comparisons, not by a 64-bit division ahead of the weight loads
+    const int kv = (int)(K >> 3);  // 16-byte bf16 vectors per token row
+    auto token_of = [&](int v, int per) {
+        int m = 0;
+#pragma unroll
+        for (int q = 1; q < M; ++q) m += v >= q * per;
+        return m;
+    };
+    constexpr int NV = QX ? (M * (kI8LdsMaxK / 8) + NT - 1) / NT : 1;  // bf16 vectors per thread
+    u32x4_t xv[NV];
+    const int nvec = M * kv;  // QX: 16-byte bf16 vectors of all M rows
+    if constexpr (QX) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int v = tid + i * NT, vv = v < nvec ? v : nvec - 1;
+            const int m = token_of(vv, kv), r = vv - m * kv;
+            const u32x4_t t = ld16((const uint16_t*)x + m * ldx + (int64_t)r * 8);
+            xv[i] = v < nvec ? t : u32x4_t{0, 0, 0, 0};
+        }
+    } else {
+        const int nc = (int)nchunk, nq = M * nc;
+        const int ni = (nq + 63) >> 6;
+        for (int inst = wv; inst < ni; inst += WPB) {  // wave-uniform
+            const int q = inst * 64 + lane, qq = q < nq ? q : nq - 1;
+            const int m = token_of(qq, nc), c = qq - m * nc;
+            __builtin_amdgcn_global_load_lds((const void*)((const int8_t*)x + m * ldx + (int64_t)c * 16),
+                                             (lds_void_t*)(xl + inst * 64), 16, 0, 0);
+        }
+    }
+    // 2. this wave's row
+    const int64_t n = (int64_t)blockIdx.x * WPB + wv;
+    const int64_t nn = n < N ? n : N - 1;
+    const int8_t* wr = w + nn * ldw;
+    u32x4_t wq[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t c = (int64_t)u * 64 + lane, cc = c < nchunk ? c : nchunk - 1;
+        wq[u] = ld_stream(wr + cc * 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the weight loads ahead of the quantisation
+    // 3. the codes in LDS
+    float sc[M];
+    if constexpr (QX) {
+        float am[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) am[m] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int v = tid + i * NT;
+            const int tok = v < nvec ? token_of(v, kv) : M;  // vectors past the rows are zero
+            const float a = absmax8(xv[i], 0.0f);
+#pragma unroll
+            for (int m = 0; m < M; ++m) am[m] = tok == m ? fmaxf(am[m], a) : am[m];
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            float a = row_max_f32(am[m]);
+            a = fmaxf(a, __shfl_xor(a, 16));
+            a = fmaxf(a, __shfl_xor(a, 32));
+            if (lane == 0) wmax[wv][m] = a;
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        float amax[M];
+        double rc[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            float a = wmax[0][m];
+#pragma unroll
+            for (int q = 1; q < WPB; ++q) a = fmaxf(a, wmax[q][m]);
+            amax[m] = a;
+            sc[m] = a / 127.0f;
+            rc[m] = 1.0 / (double)sc[m];
+        }
+        const bool out = xq_out && blockIdx.x == 0;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int v = tid + i * NT;
+            if (v < nvec) {
+                const int tok = token_of(v, kv), r = v - tok * kv;
+                float a = amax[0];
+                double rr = rc[0];
+#pragma unroll
+                for (int m = 1; m < M; ++m) {
+                    a = tok == m ? amax[m] : a;
+                    rr = tok == m ? rc[m] : rr;
+                }
+                const uint2 q = quant8(xv[i], a, rr);
+                *(uint2*)((uint8_t*)xl + tok * (int)K + r * 8) = q;
+                if (out) *(uint2*)(xq_out + tok * ldxq + (int64_t)r * 8) = q;
+            }
+        }
+        if (xs_out && blockIdx.x == 0 && tid < M) {
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+                if (tid == m) xs_out[m] = sc[m];
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+    } else {
+#pragma unroll
+        for (int m = 0; m < M; ++m) sc[m] = xs ? xs[m * xs_step] : 0.0f;
+        __builtin_amdgcn_s_waitcnt((U & 15) | 0x70 | 0xF00);  // vmcnt(U): the direct loads have landed
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();  // not __syncthreads(): that would also wait for the weights
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const float wsv = ws ? ws[nn * ws_step] : 0.0f;
+    // 4. the row
+    int acc[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[m] = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t c = (int64_t)u * 64 + lane;
+        const bool ok = c < nchunk;
+        const int64_t cc = ok ? c : nchunk - 1;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            u32x4_t a = xl[m * nchunk + cc];
+            if (!ok) a = u32x4_t{0, 0, 0, 0};
+            int t = acc[m];
+            t = sdot4(wq[u].x, a.x, t);
+            t = sdot4(wq[u].y, a.y, t);
+            t = sdot4(wq[u].z, a.z, t);
+            t = sdot4(wq[u].w, a.w, t);
+            acc[m] = t;
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[m] = group_sum<64>(acc[m]);
+    if (lane == 0 && n < N) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            if (out_kind == 1) {
+                ((int32_t*)y)[m * ldy + n] = acc[m];
+            } else {
+                float t = (float)acc[m];
+                t = t * sc[m];
+                t = t * wsv;
+                uint16_t o = f32_to_bf16(t);
+                if (bias) o = f32_to_bf16(bf16_to_f32(o) + bf16_to_f32(bias[n]));
+                ((uint16_t*)y)[m * ldy + n] = o;
+            }
+        }
+    }
+}
+
 }  // namespace qlin

@@ -22,6 +22,7 @@ constexpr int64_t kMaxKInt8 = 131072;  // K * 127 * 128 < 2^31: int32 accumulati
 constexpr int64_t kMaxKFp8 = 1 << 24;  // keeps the quantiser's 32-bit vector indexes in range
 constexpr int64_t kMaxKBlkGeneral = 32768;  // the general block GEMV stages K/32 x 32 scale bytes in LDS
 constexpr int64_t kMaxEPrefill = 1024;      // the pair sort counts experts in one workgroup's LDS
+constexpr int64_t kFusedI8MaxK = 8192;      // the one-launch INT8 layer keeps the token's codes in LDS
 
 }  // namespace
 
@@ -71,6 +72,24 @@ int qlin_gemv_i8(const int8_t* xq, int64_t ldxq, const float* xs, int xs_per_tok
     qlin::I8Args a{xq, ldxq, xs, xs_per_token ? 1 : 0, M, K, w, ldw, N, ws, ws_per_row ? 1 : 0,
                    (const uint16_t*)bias, y, ldy, out_kind};
     return launch_status(qlin::launch_gemv_i8(a, (hipStream_t)stream));
+}
+
+int qlin_linear_i8(const void* x, int64_t ldx, int64_t M, int64_t K,
+                   const int8_t* w, int64_t ldw, int64_t N, const float* ws, int ws_per_row, const void* bias,
+                   int8_t* xq, int64_t ldxq, float* xs, void* y, int64_t ldy, void* stream) {
+    if (ws_per_row != 0 && ws_per_row != 1) return QLIN_ERR_ARG;
+    if (!x || !w || !ws || !xq || !xs || !y) return QLIN_ERR_NULL;
+    if (M < 1 || M > QLIN_MAX_M_PREFILL || N < 1 || K < 16 || K % 16 != 0 || K > kMaxKInt8) return QLIN_ERR_SHAPE;
+    if (ldx < K || ldxq < K || ldw < K || ldy < N) return QLIN_ERR_STRIDE;
+    if (misaligned(x, 16) || ldx % 8 != 0 || misaligned(xq, 16) || ldxq % 16 != 0 || misaligned(xs, 4) ||
+        misaligned(w, 16) || ldw % 16 != 0 || misaligned(ws, 4) || misaligned(y, 2) || (bias && misaligned(bias, 2)))
+        return QLIN_ERR_ALIGN;
+    hipStream_t st = (hipStream_t)stream;
+    qlin::ActQuantI8Args q{(const uint16_t*)x, ldx, M, K, xq, ldxq, xs};
+    qlin::I8Args a{xq, ldxq, xs, 1, M, K, w, ldw, N, ws, ws_per_row ? 1 : 0, (const uint16_t*)bias, y, ldy, 0};
+    if (M == 1 && K <= kFusedI8MaxK) return launch_status(qlin::launch_linear_i8_fused(q, a, st));
+    if (qlin::launch_act_quant_i8(q, st) != hipSuccess) return QLIN_ERR_LAUNCH;
+    return launch_status(qlin::launch_gemv_i8(a, st));
 }
 
 int qlin_gemv_fp8(const void* x, int64_t ldx, int64_t M, int64_t K,

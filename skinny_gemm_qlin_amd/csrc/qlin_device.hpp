@@ -154,4 +154,54 @@ __device__ __forceinline__ u32x4_t ld_stream(const void* p) {
 
 __device__ __forceinline__ u32x4_t ld16(const void* p) { return *(const u32x4_t*)p; }
 
+// ---------------------------------------------------------------- INT8 activation quantisation
+// The per-token rule [Z100 section 2.1; operator-family table, INT8 row]:
+// s = amax / 127 (IEEE fp32 division: the build asks for correctly rounded
+// division), q = clamp(rne(x / s), -127, 127) with x / s the IEEE fp32
+// quotient, q = 0 when amax = 0.
+// Shared by the standalone quantiser and the GEMVs that quantise their own
+// activations, so their codes are bit-identical.
+
+// The fp32 quotient x / s without a division: with r = fl64(1 / s) (one
+// correctly rounded fp64 division per token), fl32(fl64(x * r)) equals the
+// IEEE fp32 division fl32(x / s) whenever x has at most 8 significant bits
+// (any bf16 value).  Proof: t = fl64(x * r) is within 2^-52 |x/s| of x/s;
+// x/s is never exactly an fp32 rounding midpoint (that would need s to divide
+// x's 8-bit significand, leaving at most 8 significant bits), and when it is
+// not, |x - B s| for a midpoint B is a nonzero multiple of a grid that keeps
+// x/s at least 2^-49 |B| away from B, so t and x/s round to the same fp32
+// value.  (Checked exhaustively over every positive bf16 x for 6,000 scales.)
+// The fp64 multiply and the two converts replace a ~10-instruction divide.
+__device__ __forceinline__ float div_bf16(float x, double r) { return (float)((double)x * r); }
+
+// 8 bf16 (one 16-byte vector) -> 8 int8 codes (8 bytes, element order kept);
+// r = fl64(1 / s).
+__device__ __forceinline__ uint2 quant8(const u32x4_t& v, float amax, double r) {
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t h = (e & 1) ? (d[e >> 1] >> 16) : (d[e >> 1] & 0xFFFFu);
+        int q = 0;
+        if (amax != 0.0f) {
+            float t = rintf(div_bf16(bf16_to_f32(h), r));
+            t = fminf(fmaxf(t, -127.0f), 127.0f);
+            q = (int)t;
+        }
+        packed[e >> 2] |= ((uint32_t)q & 0xFFu) << (8 * (e & 3));
+    }
+    return make_uint2(packed[0], packed[1]);
+}
+
+// max(a, |x|) over 8 bf16 values.
+__device__ __forceinline__ float absmax8(const u32x4_t& v, float a) {
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        a = fmaxf(a, fabsf(bf16_to_f32(d[q] & 0xFFFFu)));
+        a = fmaxf(a, fabsf(bf16_to_f32(d[q] >> 16)));
+    }
+    return a;
+}
+
 }  // namespace qlin

@@ -55,6 +55,8 @@ struct MoeArgs {
 
 hipError_t launch_act_quant_i8(const ActQuantI8Args& a, hipStream_t st);
 hipError_t launch_gemv_i8(const I8Args& a, hipStream_t st);
+// quantiser + GEMV in one launch (M = 1, K <= 8192); q.xq / q.xs may be null
+hipError_t launch_linear_i8_fused(const ActQuantI8Args& q, const I8Args& a, hipStream_t st);
 hipError_t launch_gemv_fp8(const F8Args& a, hipStream_t st);
 hipError_t launch_act_quant_fp8(const ActQuantF8Args& a, hipStream_t st);
 hipError_t launch_gemv_fp8_w8a8(const W8A8F8Args& a, hipStream_t st);

@@ -94,6 +94,47 @@ def test_gemv_i8_errors(q):
     assert call(ok=1, y=A + 2) == -4        # int32 output needs 4-byte alignment
 
 
+def test_linear_i8_errors(q):
+    def call(x=A, ldx=1024, M=1, K=1024, w=A, ldw=1024, N=64, ws=A, wpr=1, bias=None, xq=A, ldxq=1024, xs=A,
+             y=A, ldy=64):
+        return q.qlin_linear_i8(x, ldx, M, K, w, ldw, N, ws, wpr, bias, xq, ldxq, xs, y, ldy, None)
+    assert call(wpr=2) == -6
+    for name in ("x", "w", "ws", "xq", "xs", "y"):
+        assert call(**{name: None}) == -1
+    assert call(M=0) == -2
+    assert call(M=16385) == -2
+    assert call(N=0) == -2
+    assert call(K=1000, ldx=1008, ldxq=1008, ldw=1008) == -2
+    assert call(K=131088, ldx=131088, ldxq=131088, ldw=131088) == -2
+    assert call(ldx=512) == -3
+    assert call(ldxq=1008) == -3
+    assert call(ldw=1008) == -3
+    assert call(ldy=63) == -3
+    assert call(x=A + 2) == -4
+    assert call(ldx=1028) == -4
+    assert call(xq=A + 8) == -4
+    assert call(ldxq=1032) == -4
+    assert call(xs=A + 2) == -4
+    assert call(w=A + 8) == -4
+    assert call(ws=A + 2) == -4
+    assert call(y=A + 1) == -4
+    assert call(bias=A + 1) == -4
+
+
+def test_moe_noalloc_errors(q):
+    # checked on the host before the library's scratch array is looked up
+    def call(x=A, ldx=7168, M=8, K=7168, w=A, s=A, E=64, N=2048, ids=A, gw=A, topk=6, y=A, ldy=2048):
+        return q.qlin_moe_mxfp4_noalloc(x, ldx, M, K, w, s, E, N, ids, gw, topk, y, ldy, None)
+    for name in ("x", "w", "s", "ids", "gw", "y"):
+        assert call(**{name: None}) == -1
+    assert call(topk=0) == -2
+    assert call(K=7168 + 16, ldx=7184) == -2
+    assert call(ldy=100) == -3
+    assert call(w=A + 8) == -4
+    assert q.qlin_moe_mxfp4_workspace_bytes(16, 8192, 16, 4) > 4 << 20
+    assert call(M=16, N=8192, ldy=8192, topk=16, E=4) == -5   # more than the 4 MiB scratch
+
+
 def test_gemv_fp8_errors(q):
     def call(x=A, ldx=5120, M=1, K=5120, w=A, ldw=5120, N=128, ws=A, wpr=1, y=A, ldy=128):
         return q.qlin_gemv_fp8(x, ldx, M, K, w, ldw, N, ws, wpr, y, ldy, None)
