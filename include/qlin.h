@@ -194,12 +194,21 @@ int qlin_gemv_fp8_w8a8(const uint8_t* xq, int64_t ldxq, const float* xs, int xs_
  *    xq / xs are written to the caller's buffers (they are also the exported
  *    quantised activations).  For M = 1 and K <= 32768 both steps run in one
  *    kernel (each workgroup quantises the row into its LDS, and each group is
- *    written to xq / xs by exactly one workgroup); otherwise the step-2
- *    kernel reads xq / xs back.  The results are the same either way.
+ *    written to xq / xs by exactly one workgroup); there xq and xs are
+ *    optional (NULL: not exported).  Otherwise the step-2 kernel reads xq /
+ *    xs back, so both are required (QLIN_ERR_NULL).  The results are the
+ *    same either way.  Overflow: an activation group is scaled by a power of
+ *    two chosen so that its codes never saturate, but a weight-scale product
+ *    (2^(xs-127) * 2^(ws-127) times a block sum) can exceed fp32; such an
+ *    output is +-inf or NaN, unspecified, like other non-finite results.
  * 2. out[m,n] = sum_kb ( sum_{k in kb} xq[m,k] * w[n,k] )
  *                     * 2^(xs[m,kb]-127) * 2^(ws[n/128, kb]-127)
  *    The block scales multiply each lane's partial sum of the current block
- *    before any reduction (scale folding); fp32 accumulation; y = bf16(out).
+ *    before any reduction (scale folding), the activation scale first:
+ *    (partial * 2^(xs-127)) * 2^(ws-127).  The activation scale follows the
+ *    data, so the intermediate stays near the output's own magnitude and an
+ *    extreme weight scale byte (0 or 254) cannot overflow or underflow it
+ *    first.  fp32 accumulation; y = bf16(out).
  *   x  bf16 [M, ldx]; w E4M3 [N, ldw]; ws UE8M0 [ceil(N/128), K/128]
  *   (row-major, byte 255 decodes to NaN); xq uint8 [M, K]; xs uint8
  *   [M, K/128]; y bf16 [M, ldy].

@@ -187,9 +187,19 @@ def qlin_gemv_fp8_w8a8(xq, xs, w, ws, x_fmt=QLIN_FMT_E4M3, w_fmt=QLIN_FMT_E4M3, 
     return y
 
 
-def qlin_gemv_fp8_blk(x, w, ws, xq=None, xs=None, y=None, stream=None):
+def qlin_gemv_fp8_blk(x, w, ws, xq=None, xs=None, y=None, stream=None, export=True):
     """Block-scaled FP8: x bf16 [M, K], w E4M3 [N, K], ws UE8M0 [ceil(N/128), K/128].
-    Returns (y bf16 [M, N], xq E4M3 [M, K], xs UE8M0 [M, K/128])."""
+    Returns (y bf16 [M, N], xq E4M3 [M, K], xs UE8M0 [M, K/128]).  export=False
+    passes NULL code / scale buffers (accepted for one token, K <= 32768) and
+    returns (y, None, None)."""
+    if not export:
+        _need(x, "x", (torch.bfloat16,), 2)
+        if y is None:
+            y = torch.empty((x.shape[0], w.shape[0]), dtype=torch.bfloat16, device=x.device)
+        check(load().qlin_gemv_fp8_blk(x.data_ptr(), x.stride(0), x.shape[0], x.shape[1], w.data_ptr(),
+                                       w.stride(0), w.shape[0], ws.data_ptr(), None, None, y.data_ptr(),
+                                       y.stride(0), _stream(x, stream)), "qlin_gemv_fp8_blk")
+        return y, None, None
     _need(x, "x", (torch.bfloat16,), 2)
     _need(w, "w", _U8, 2)
     _need(ws, "ws", (torch.uint8,), 2)

@@ -220,7 +220,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
                         const float sx = ue8m0_to_f32(p.xsb[(m < M ? m : M - 1) * nkb + kb]);
 #pragma unroll
                         for (int i = 0; i < TN; ++i) {
-                            acc[i][j] += (dblk[i][j] * sw) * sx;
+                            acc[i][j] += (dblk[i][j] * sx) * sw;
                             dblk[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
                         }
                     }
@@ -586,7 +586,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const GemmParams p) {
             for (int i = 0; i < TN; ++i)
 #pragma unroll
                 for (int j = 0; j < TM; ++j) {
-                    acc[i][j] += (dblk[i][j] * sw) * sx[j];
+                    acc[i][j] += (dblk[i][j] * sx[j]) * sw;
                     dblk[i][j] = acc_t{};
                 }
         }

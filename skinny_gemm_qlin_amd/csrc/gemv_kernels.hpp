@@ -453,9 +453,9 @@ __global__ __launch_bounds__(64 * WPB) void gemv_fp8_blk_m1_kernel(
 // blk_act_quant_kernel: bit-identical codes) with the decoded group scales
 // 2^(E-127), so the quantisation runs under the weights' HBM latency.  After
 // one barrier each wave runs the gemv_fp8_blk_m1_kernel loop on its row with
-// codes and scales read from LDS.  Group g is exported to xq / xs by
-// workgroup g % gridDim.x alone.  Dynamic LDS: K code bytes, then K/128
-// floats.
+// codes and scales read from LDS.  Group g is exported to xq / xs (each
+// optional) by workgroup g % gridDim.x alone.  Dynamic LDS: K code bytes,
+// then K/128 floats.
 template <int U, int WPB>
 __global__ __launch_bounds__(64 * WPB) void gemv_fp8_blk_m1_fq_kernel(
     const uint16_t* __restrict__ x, int64_t K,
@@ -510,9 +510,9 @@ __global__ __launch_bounds__(64 * WPB) void gemv_fp8_blk_m1_fq_kernel(
             const uint2 c = make_uint2((uint32_t)lo, (uint32_t)hi);
             *(uint2*)(xl + g * 128 + jj * 8) = c;
             if (jj == 0) sl[g] = ue8m0_to_f32((uint32_t)E);
-            if ((uint32_t)g % gridDim.x == blockIdx.x) {
-                *(uint2*)(xq + g * 128 + jj * 8) = c;
-                if (jj == 0) xs[g] = (uint8_t)E;
+            if ((uint32_t)g % gridDim.x == blockIdx.x) {  // exported only when asked for
+                if (xq) *(uint2*)(xq + g * 128 + jj * 8) = c;
+                if (xs && jj == 0) xs[g] = (uint8_t)E;
             }
         }
     };

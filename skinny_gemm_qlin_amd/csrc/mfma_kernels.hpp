@@ -476,7 +476,7 @@ __global__ __launch_bounds__(64 * KS) void gemv_fp8_blk_mfma_kernel(
                     d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, d, 0, 0, 0);
                     d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, d, 0, 0, 0);
                 }
-                acc += (d * sw[u][b]) * sx[u][b];
+                acc += (d * sx[u][b]) * sw[u][b];  // activation scale first, as every block kernel
             }
         }
     }
@@ -540,7 +540,7 @@ __global__ __launch_bounds__(64 * KS) void gemv_fp8_blkg_mfma_kernel(
         const uint32_t s4 = *(const uint32_t*)(swt + kb_cur * 16 + 4 * mg);
         const float sx = ue8m0_to_f32(sxt[kb_cur * 16 + mi]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] += (d[r] * ue8m0_to_f32((s4 >> (8 * r)) & 0xFFu)) * sx;
+        for (int r = 0; r < 4; ++r) acc[r] += (d[r] * sx) * ue8m0_to_f32((s4 >> (8 * r)) & 0xFFu);
         d = f32x4_t{0.f, 0.f, 0.f, 0.f};
     };
     constexpr int STEP = PAIR ? 64 : 32;

@@ -139,17 +139,18 @@ int qlin_gemv_fp8_w8a8(const uint8_t* xq, int64_t ldxq, const float* xs, int xs_
 int qlin_gemv_fp8_blk(const void* x, int64_t ldx, int64_t M, int64_t K,
                       const uint8_t* w, int64_t ldw, int64_t N, const uint8_t* ws,
                       uint8_t* xq, uint8_t* xs, void* y, int64_t ldy, void* stream) {
-    if (!x || !w || !ws || !xq || !xs || !y) return QLIN_ERR_NULL;
+    if (!x || !w || !ws || !y) return QLIN_ERR_NULL;
     if (M < 1 || M > QLIN_MAX_M_PREFILL || N < 1 || K < 128 || K % 128 != 0) return QLIN_ERR_SHAPE;
+    const bool fused = M == 1 && K <= qlin::kBlkFusedMaxK;  // one launch; xq / xs then optional
+    if (!fused && (!xq || !xs)) return QLIN_ERR_NULL;
     if (ldx < K || ldw < K || ldy < N) return QLIN_ERR_STRIDE;
-    if (misaligned(x, 16) || ldx % 8 != 0 || misaligned(w, 16) || ldw % 16 != 0 || misaligned(xq, 16) ||
+    if (misaligned(x, 16) || ldx % 8 != 0 || misaligned(w, 16) || ldw % 16 != 0 || (xq && misaligned(xq, 16)) ||
         misaligned(y, 2))
         return QLIN_ERR_ALIGN;
     hipStream_t st = (hipStream_t)stream;
     qlin::BlkQuantArgs qa{(const uint16_t*)x, ldx, M, K, xq, xs};
     qlin::BlkArgs a{xq, xs, M, K, w, ldw, N, ws, (uint16_t*)y, ldy};
-    if (M == 1 && K <= qlin::kBlkFusedMaxK)  // one launch
-        return launch_status(qlin::launch_gemv_fp8_blk_fq(qa, a, st));
+    if (fused) return launch_status(qlin::launch_gemv_fp8_blk_fq(qa, a, st));
     hipError_t e = qlin::launch_blk_act_quant(qa, st);
     if (e != hipSuccess) return QLIN_ERR_LAUNCH;
     return launch_status(qlin::launch_gemv_fp8_blk(a, st));

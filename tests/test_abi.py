@@ -202,9 +202,11 @@ def test_gemv_fp8_w8a8_errors(q):
 def test_gemv_fp8_blk_errors(q):
     def call(x=A, ldx=7168, M=1, K=7168, w=A, ldw=7168, N=256, ws=A, xq=A, xs=A, y=A, ldy=256):
         return q.qlin_gemv_fp8_blk(x, ldx, M, K, w, ldw, N, ws, xq, xs, y, ldy, None)
-    assert call(xq=None) == -1
-    assert call(xs=None) == -1
+    assert call(M=2, ldy=256, xq=None) == -1     # more than one token: the codes are needed
+    assert call(M=2, xs=None) == -1
+    assert call(K=32896, ldx=32896, ldw=32896, xq=None) == -1   # one token past the fused kernel's K
     assert call(ws=None) == -1
+    assert call(y=None) == -1
     assert call(K=7168 + 16, ldx=7184, ldw=7184) == -2   # K % 128
     assert call(M=16385) == -2
     assert call(ldw=7000) == -3

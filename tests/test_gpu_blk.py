@@ -123,3 +123,61 @@ def test_blk_padded_activation_stride(ql, orc, M):
     y, xq, xs = ql.qlin_gemv_fp8_blk(xp, dev(d["w"]), dev(d["ws"]))
     torch.cuda.synchronize()
     _check(orc, d, (host_bits(y), host(xq), host(xs)))
+
+
+def test_blk_act_quant_edge_values_one_token(ql, orc):
+    # the same edge rows one token at a time: the one-kernel path (quantiser
+    # fused into the M = 1 GEMV) sees midpoints, signed zeros, zero / tiny /
+    # huge groups
+    rng = np.random.default_rng(40)
+    K = 128 * 12
+    x = rng.standard_normal((3, K)).astype(np.float32)
+    e4 = orc.e4m3_decode(np.arange(0x7F)).astype(np.float64)
+    mids = ((e4[:-1] + e4[1:]) / 2).astype(np.float32)
+    x[0, :126] = mids
+    x[0, 126] = 448.0
+    x[0, 128:254] = -mids
+    x[0, 254] = -448.0
+    x[1, 256:384] = 0.0
+    x[1, 384:512] = -0.0
+    x[1, 512:640] *= 1e-35
+    x[1, 640:768] *= 3e25
+    x[2, 768:896] = np.where(np.arange(128) % 2 == 0, 1e-6, -1e-6)
+    x[2, 800] = 100.0
+    w = rng.integers(0, 0x7E, (130, K)).astype(np.uint8)
+    ws = rng.integers(110, 140, (2, K // 128)).astype(np.uint8)
+    for r in range(3):
+        print(f"blk edge row {r} as one token", flush=True)
+        d = {"x": bf16_bits(x[r:r + 1]), "w": w, "ws": ws}
+        _check(orc, d, _gpu(ql, d))
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_blk_extreme_weight_scale_bytes(ql, orc, M):
+    # weight scale bytes 0 (2^-127, an fp32 subnormal), 1, 253 and 254 (2^127);
+    # activation groups sized so every output stays finite: tiny groups where
+    # the weight scale is huge, large groups where it is tiny
+    rng = np.random.default_rng(45)
+    K, N = 128 * 4, 256
+    ws = np.array([[0, 1, 253, 254], [1, 0, 254, 253]], np.uint8)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x[:, 0:256] *= 1e10    # groups 0, 1: weight scales 2^-127 / 2^-126
+    x[:, 256:512] *= 1e-30  # groups 2, 3: weight scales 2^126 / 2^127
+    w = gen_fp8_blk(1, N, K, seed=46)["w"]
+    d = {"x": bf16_bits(x), "w": w, "ws": ws}
+    assert np.all(np.isfinite(bf16_values(orc.fp8_blk(d["x"], d["w"], d["ws"])[2])))
+    print(f"blk extreme scale bytes M={M}", flush=True)
+    _check(orc, d, _gpu(ql, d))
+
+
+def test_blk_one_token_without_exported_codes(ql, orc):
+    # one token: the codes / scales buffers are optional (NULL: not written)
+    d = gen_fp8_blk(1, 4096, 7168, seed=47)
+    y, xq, xs = ql.qlin_gemv_fp8_blk(dev_bf16(d["x"]), dev(d["w"]), dev(d["ws"]), export=False)
+    torch.cuda.synchronize()
+    assert xq is None and xs is None
+    y_ref = _gpu(ql, d)[0]
+    assert np.array_equal(host_bits(y), y_ref)
+    with pytest.raises(ql.QlinError):  # two tokens need the buffers
+        ql.qlin_gemv_fp8_blk(dev_bf16(gen_fp8_blk(2, 64, 256, seed=1)["x"]), dev(d["w"][:64, :256]),
+                             dev(d["ws"][:1, :2].copy()), export=False)

@@ -98,3 +98,25 @@ def test_moe_deterministic(ql):
     ref = ql.qlin_moe_mxfp4(*args)
     for _ in range(10):
         assert torch.equal(ql.qlin_moe_mxfp4(*args).view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("M", [1, 8, 16])
+def test_moe_extreme_scale_bytes(ql, orc, M):
+    # UE8M0 bytes 0 (2^-127, an fp32 subnormal), 1, 253 and 254 (2^127) on the
+    # decode path; 32-blocks with a huge scale see tiny activations, blocks with
+    # a tiny scale ordinary ones, so every output stays finite
+    from skinny_gemm_qlin_amd.inputs import bf16_bits
+    E, N, K, topk = 8, 96, 512, 3
+    d = gen_moe(M, E, N, K, topk, seed=60 + M)
+    rng = np.random.default_rng(61)
+    nkb = K // 32
+    huge = (np.arange(nkb) % 2 == 0)
+    s = np.where(huge[None, None, :], rng.choice([253, 254], (E, N, nkb)), rng.choice([0, 1], (E, N, nkb)))
+    d["s"] = s.astype(np.uint8)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x[:, np.repeat(huge, 32)] *= 1e-30
+    d["x"] = bf16_bits(x)
+    _, ye, _ = orc.moe_mxfp4(d["x"], d["w"], d["s"], d["ids"], d["gw"])
+    assert np.all(np.isfinite(ye))
+    print(f"moe extreme scale bytes M={M}", flush=True)
+    _check(orc, ql, d)
