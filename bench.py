@@ -107,6 +107,7 @@ def bytes_moe_ffn_call(M, H, I, E, topk, live):
 KERNEL_SOURCES = {
     "int8_decode": ("gemv.hip",),
     "int8_prefill": ("gemm.hip",),
+    "int8_prefill_smalln": ("gemv.hip",),
     "fp8_prefill": ("gemm.hip",),
     "fp8_decode": ("gemv.hip",),
     "fp8_w8a8": ("gemv.hip",),
@@ -161,7 +162,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="int8_decode",
                     choices=["int8_decode", "fp8_decode", "fp8_w8a8", "fp8_blk", "moe_mxfp4", "moe_ffn_mxfp4",
-                             "int8_prefill", "fp8_prefill", "moe_prefill"])
+                             "int8_prefill", "int8_prefill_smalln", "fp8_prefill", "moe_prefill"])
     ap.add_argument("--ms", default=None, help="comma list of M values (default: the workload's)")
     ap.add_argument("--rotate", type=int, default=0, help="weight copies (0 = enough to defeat the MALL)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
@@ -201,7 +202,7 @@ def main():
 
     # ---------------------------------------------------------------- inputs (seed 0)
     log(f"bench: generating {wl} inputs N={N} K={K} Ms={Ms}")
-    if wl in ("int8_decode", "int8_prefill"):
+    if wl in ("int8_decode", "int8_prefill", "int8_prefill_smalln"):
         d = inputs.gen_int8(Mmax, N, K, seed=0)
         wbytes = N * K
     elif wl in ("fp8_decode", "fp8_prefill"):
@@ -273,7 +274,7 @@ def main():
         if wl == "int8_decode":
             return [("linear_i8", bytes_act_quant_i8(M, K) + bytes_gemv_i8(M, N, K),
                      lambda: ql.qlin_linear_i8(xm, w, sc, xq=xq_buf[:M], xs=xs_buf[:M], y=y_buf[:M]))]
-        if wl == "int8_prefill":
+        if wl in ("int8_prefill", "int8_prefill_smalln"):
             return [("act_quant_i8", bytes_act_quant_i8(M, K),
                      lambda: ql.qlin_act_quant_i8(xm, xq_buf[:M], xs_buf[:M])),
                     ("gemv_i8", bytes_gemv_i8(M, N, K),
@@ -309,7 +310,7 @@ def main():
                  lambda: ql.qlin_gemv_i8(xq_buf[:M], xs_buf[:M], w, sc, y=y_buf[:M]))] + launches(M, ci)
 
     dominant = {"int8_decode": "gemv_i8", "fp8_decode": "gemv_fp8", "fp8_w8a8": "gemv_fp8_w8a8",
-                "int8_prefill": "gemv_i8", "fp8_prefill": "gemv_fp8",
+                "int8_prefill": "gemv_i8", "int8_prefill_smalln": "gemv_i8", "fp8_prefill": "gemv_fp8",
                 "fp8_blk": "act_quant_blk+gemv_fp8_blk", "moe_mxfp4": "moe_mxfp4", "moe_prefill": "moe_mxfp4",
                 "moe_ffn_mxfp4": "moe_ffn_mxfp4"}[wl]
 
@@ -397,7 +398,7 @@ def main():
 
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = load_traffic(wl)
-    if wl in ("int8_prefill", "fp8_prefill"):
+    if wl in ("int8_prefill", "int8_prefill_smalln", "fp8_prefill"):
         # compute-bound: algorithmic MACs x 2 per launch / launch duration, against
         # the dense matrix-core peak of the instruction's type (int8 5.0 POP/s,
         # bf16 2.5 PFLOP/s)
@@ -451,7 +452,7 @@ def main():
         def oracle_step():
             for M in Ms:
                 xm = d["x"][:M]
-                if wl in ("int8_decode", "int8_prefill"):
+                if wl in ("int8_decode", "int8_prefill", "int8_prefill_smalln"):
                     xq, xs = oracle.act_quant_i8(xm)
                     oracle.gemv_i8(xq, xs, d["w"], d["ws"])
                 elif wl in ("fp8_decode", "fp8_prefill"):
@@ -500,6 +501,8 @@ def main():
         "int8_decode": f"W8A8 INT8 decode linear (qlin_linear_i8: act quant + GEMV, bf16 out) N={N} K={K}, one call per M",
         "fp8_decode": f"E4M3 weight-only GEMV ({'per-tensor' if args.per_tensor else 'per-channel'}) N={N} K={K}",
         "int8_prefill": f"W8A8 INT8 prefill linear (act quant + tiled GEMM, bf16 out) N={N} K={K}, one call per M",
+        "int8_prefill_smalln": f"W8A8 INT8 prefill linear on a few-row matrix (act quant + split-K over "
+                               f"16-token blocks, bf16 out) N={N} K={K}, one call per M",
         "fp8_prefill": f"E4M3 weight-only prefill GEMM (per-channel) N={N} K={K}, one call per M",
         "fp8_w8a8": f"FP8 W8A8 E4M3 x E4M3 (per-token act quant + GEMV, per-channel ws) N={N} K={K}",
         "fp8_blk": f"{args.block.replace(',', 'x')} block-scaled FP8 (act quant + GEMV) N={N} K={K}",
@@ -524,7 +527,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"int8_decode": "int8", "fp8_decode": "fp8e4m3*bf16->f32", "fp8_w8a8": "fp8e4m3*fp8e4m3->f32",
-                  "int8_prefill": "int8", "fp8_prefill": "fp8e4m3*bf16->f32",
+                  "int8_prefill": "int8", "int8_prefill_smalln": "int8", "fp8_prefill": "fp8e4m3*bf16->f32",
                   "fp8_blk": "fp8e4m3->f32", "moe_mxfp4": "fp4e2m1*bf16->f32", "moe_prefill": "fp4e2m1*bf16->f32",
                   "moe_ffn_mxfp4": "fp4e2m1*bf16->f32"}[wl],
         "data": "synthetic",

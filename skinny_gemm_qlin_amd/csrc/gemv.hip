@@ -17,7 +17,10 @@
 //     16: 16.5 / 17.0 / 18.4 us against 17.5 / 19.1 / 21.4 us for one
 //     workgroup per 16-row tile);
 //   * otherwise: the matrix-core kernels of mfma_kernels.hpp;
-//   * M > 16 (prefill): the tiled matrix-core GEMM of gemm.hip.
+//   * M > 16 (prefill): the tiled matrix-core GEMM of gemm.hip; on a matrix
+//     too small to give the chip enough 64 x 64 tiles, the matrix-core
+//     kernels above over a grid of 16-token blocks (split-K inside each
+//     workgroup).
 #include <algorithm>
 #include <atomic>
 
@@ -271,6 +274,78 @@ hipError_t run_w8a8_mfma(const W8A8F8Args& a, hipStream_t st) {
                                : run_w8a8_mfma_fmt<kFmtE4M3, kFmtE4M3>(a, st);
 }
 
+// ---- prefill on a small weight matrix: split-K over the token-block grid
+// The tiled GEMM gives each workgroup a 64 x 64 (or larger) output tile and
+// walks all of K in it, so a matrix with few rows gets few workgroups (N = 48,
+// M = 64: one workgroup on a 256-unit chip).  Below a quarter of the compute
+// units' worth of 64 x 64 tiles the matrix-core decode kernels run instead,
+// over a grid of 16-row tiles x 16-token blocks, each workgroup splitting K
+// between its waves and summing their partial tiles in wave order.
+int cu_count();
+
+bool small_gemm(int64_t M, int64_t N) {
+    const int64_t tiles64 = ((N + 63) / 64) * ((M + 63) / 64);
+    return tiles64 * 4 < cu_count();
+}
+
+// waves per workgroup of the token-block grid: about 4096 waves in all
+inline int grid_ks(int64_t N, int64_t M, int64_t K) {
+    const int64_t wgs = ((N + 15) / 16) * ((M + 15) / 16), nch = (K + 255) >> 8;
+    int ks = wgs >= 1024 ? 4 : (wgs >= 512 ? 8 : 16);
+    while (ks > 4 && ks / 2 >= nch) ks /= 2;
+    return ks;
+}
+
+inline dim3 token_block_grid(int64_t N, int64_t M) {
+    return dim3((unsigned)((N + 15) / 16), (unsigned)((M + 15) / 16));
+}
+
+hipError_t run_i8_split(const I8Args& a, hipStream_t st) {
+    QLIN_BY_KS(gemv_i8_mfma_kernel, grid_ks(a.N, a.M, a.K), token_block_grid(a.N, a.M), 0, st, a.xq, a.ldxq,
+               a.xs, a.xs_step, (int)a.M, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.bias, a.y, a.ldy, a.out_kind)
+    return hipGetLastError();
+}
+
+hipError_t run_fp8_split(const F8Args& a, hipStream_t st) {
+    QLIN_BY_KS(gemv_fp8_mfma_kernel, grid_ks(a.N, a.M, a.K), token_block_grid(a.N, a.M), 0, st, a.x, a.ldx,
+               (int)a.M, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.y, a.ldy)
+    return hipGetLastError();
+}
+
+template <int XF, int WF>
+hipError_t run_w8a8_split_fmt(const W8A8F8Args& a, hipStream_t st) {
+    const dim3 grid = token_block_grid(a.N, a.M);
+    switch (grid_ks(a.N, a.M, a.K)) {
+        case 16:
+            hipLaunchKernelGGL((gemv_fp8_w8a8_mfma_kernel<1, 16, XF, WF, true>), grid, dim3(1024), 0, st, a.xq, a.ldxq,
+                               a.xs, a.xs_step, (int)a.M, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.y, a.ldy);
+            break;
+        case 8:
+            hipLaunchKernelGGL((gemv_fp8_w8a8_mfma_kernel<1, 8, XF, WF, true>), grid, dim3(512), 0, st, a.xq, a.ldxq,
+                               a.xs, a.xs_step, (int)a.M, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.y, a.ldy);
+            break;
+        default:
+            hipLaunchKernelGGL((gemv_fp8_w8a8_mfma_kernel<1, 4, XF, WF, true>), grid, dim3(256), 0, st, a.xq, a.ldxq,
+                               a.xs, a.xs_step, (int)a.M, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.y, a.ldy);
+            break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t run_w8a8_split(const W8A8F8Args& a, hipStream_t st) {
+    if (a.x_fmt == kFmtE5M2)
+        return a.w_fmt == kFmtE5M2 ? run_w8a8_split_fmt<kFmtE5M2, kFmtE5M2>(a, st)
+                                   : run_w8a8_split_fmt<kFmtE5M2, kFmtE4M3>(a, st);
+    return a.w_fmt == kFmtE5M2 ? run_w8a8_split_fmt<kFmtE4M3, kFmtE5M2>(a, st)
+                               : run_w8a8_split_fmt<kFmtE4M3, kFmtE4M3>(a, st);
+}
+
+hipError_t run_blk_split(const BlkArgs& a, hipStream_t st) {
+    QLIN_BY_KS(gemv_fp8_blk_mfma_kernel, grid_ks(a.N, a.M, a.K), token_block_grid(a.N, a.M), 0, st, a.xq, a.xs,
+               (int)a.M, a.K, a.w, a.ldw, a.N, a.ws, a.y, a.ldy)
+    return hipGetLastError();
+}
+
 // ---- K-slice kernels: the plan and the launch
 // Compute units of the current device (queried once per device).
 int cu_count() {
@@ -365,7 +440,7 @@ hipError_t run_blk_m1_fq(const BlkQuantArgs& q, const BlkArgs& a, hipStream_t st
 }  // namespace
 
 hipError_t launch_gemv_i8(const I8Args& a, hipStream_t st) {
-    if (a.M > kDecodeMaxM) return launch_gemm_i8(a, st);
+    if (a.M > kDecodeMaxM) return small_gemm(a.M, a.N) ? run_i8_split(a, st) : launch_gemm_i8(a, st);
     if (a.M >= 2 && a.M <= kI8LdsMaxM && a.K <= kI8LdsMaxK)
         return a.M == 2 ? run_i8_lds<2, 4, false>(a.xq, a.ldxq, a, nullptr, 0, nullptr, st)
                         : run_i8_lds<3, 4, false>(a.xq, a.ldxq, a, nullptr, 0, nullptr, st);
@@ -390,7 +465,7 @@ hipError_t launch_linear_i8_fused(const ActQuantI8Args& q, const I8Args& a, hipS
 }
 
 hipError_t launch_gemv_fp8(const F8Args& a, hipStream_t st) {
-    if (a.M > kDecodeMaxM) return launch_gemm_fp8(a, st);
+    if (a.M > kDecodeMaxM) return small_gemm(a.M, a.N) ? run_fp8_split(a, st) : launch_gemm_fp8(a, st);
     switch (a.M) {
         case 1:
             if (a.K <= kM1LdsMaxK)
@@ -416,7 +491,7 @@ hipError_t launch_gemv_fp8(const F8Args& a, hipStream_t st) {
 // M = 1 best with 3 steps of one row per wave, M = 2 with 32-lane groups and
 // 5 steps); the matrix-core kernel from M = 3.
 hipError_t launch_gemv_fp8_w8a8(const W8A8F8Args& a, hipStream_t st) {
-    if (a.M > kDecodeMaxM) return launch_gemm_fp8_w8a8(a, st);
+    if (a.M > kDecodeMaxM) return small_gemm(a.M, a.N) ? run_w8a8_split(a, st) : launch_gemm_fp8_w8a8(a, st);
     if (a.M == 1 && a.K <= kM1LdsMaxK) {
         if (a.x_fmt == kFmtE5M2)
             return a.w_fmt == kFmtE5M2
@@ -457,9 +532,9 @@ hipError_t launch_gemv_fp8_w8a8(const W8A8F8Args& a, hipStream_t st) {
 
 template <bool PAIR>
 hipError_t run_blkg(const BlkArgs& a, int64_t bn, int64_t bk, hipStream_t st) {
-    dim3 grid((unsigned)((a.N + 15) / 16));
+    const dim3 grid = token_block_grid(a.N, a.M);  // blockIdx.y: 16-token block
     const size_t lds = (size_t)(a.K / bk) * 32;  // transposed weight and token scale tables
-    switch (mfma_ks(a.N, a.K)) {
+    switch (grid_ks(a.N, a.M, a.K)) {
         case 16:
             hipLaunchKernelGGL((gemv_fp8_blkg_mfma_kernel<16, PAIR>), grid, dim3(1024), lds, st, a.xq, a.xs, (int)a.M,
                                a.K, a.w, a.ldw, a.N, a.ws, bn, bk, a.y, a.ldy);
@@ -481,7 +556,7 @@ hipError_t launch_gemv_fp8_blkg(const BlkArgs& a, int64_t bn, int64_t bk, hipStr
 }
 
 hipError_t launch_gemv_fp8_blk(const BlkArgs& a, hipStream_t st) {
-    if (a.M > kDecodeMaxM) return launch_gemm_fp8_blk(a, st);
+    if (a.M > kDecodeMaxM) return small_gemm(a.M, a.N) ? run_blk_split(a, st) : launch_gemm_fp8_blk(a, st);
     if (a.M > 1) return run_blk_mfma(a, st);
     switch (std::min(steps64(a.K), 8)) {
         case 1: return run_blk_m1<1>(a, st);

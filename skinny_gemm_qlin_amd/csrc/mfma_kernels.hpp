@@ -99,6 +99,17 @@ __device__ __forceinline__ void e4m3x16_to_bf16x8x2(const u32x4_t& c, bf16x8_t& 
     hi = bf16x8_t{b[4][0], b[4][1], b[5][0], b[5][1], b[6][0], b[6][1], b[7][0], b[7][1]};
 }
 
+// Token block of a workgroup: blockIdx.y selects 16 tokens.  At decode the
+// grid has one block row (blockIdx.y = 0, M <= 16); a prefill-sized call on
+// a matrix too small to fill the chip runs these kernels over a grid of
+// token blocks, so that each 16-row tile's K is still split between KS waves
+// (split-K inside the workgroup, reduced in wave order: deterministic).
+__device__ __forceinline__ int token_block_start() { return (int)blockIdx.y * 16; }
+__device__ __forceinline__ int token_block_size(int M) {
+    const int r = M - token_block_start();
+    return r < 16 ? r : 16;
+}
+
 // ------------------------------------------------------------------ INT8 W8A8 (v_mfma_i32_16x16x64_i8)
 // acc exact in int32; epilogue bf16((acc*xs)*ws) (+ bias) as the VALU kernel
 // [Z100 operator-family table, INT8 row; section 2.1].
@@ -108,6 +119,13 @@ __global__ __launch_bounds__(64 * KS) void gemv_i8_mfma_kernel(
     int64_t K, const int8_t* __restrict__ w, int64_t ldw, int64_t N,
     const float* __restrict__ ws, int ws_step, const uint16_t* __restrict__ bias,
     void* __restrict__ y, int64_t ldy, int out_kind) {
+    {
+        const int mb = token_block_start();
+        xq += mb * ldxq;
+        if (xs) xs += mb * xs_step;  // out_kind 1 may pass no scales
+        y = (uint8_t*)y + mb * ldy * (out_kind == 1 ? 4 : 2);
+        M = token_block_size(M);
+    }
     __shared__ __align__(16) uint8_t tile[KS][16 * kTilePitch];
     __shared__ i32x4_t red[KS][64];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -200,6 +218,13 @@ __global__ __launch_bounds__(64 * KS) void gemv_i8_mfma_xl_kernel(
     int64_t K, const int8_t* __restrict__ w, int64_t ldw, int64_t N,
     const float* __restrict__ ws, int ws_step, const uint16_t* __restrict__ bias,
     void* __restrict__ y, int64_t ldy, int out_kind) {
+    {
+        const int mb = token_block_start();
+        xq += mb * ldxq;
+        if (xs) xs += mb * xs_step;  // out_kind 1 may pass no scales
+        y = (uint8_t*)y + mb * ldy * (out_kind == 1 ? 4 : 2);
+        M = token_block_size(M);
+    }
     __shared__ __align__(16) uint8_t tile[KS][RT][16 * kTilePitch];
     __shared__ __align__(16) uint8_t xtile[KS][16 * kTilePitch];
     __shared__ i32x4_t red[KS][64];
@@ -274,6 +299,12 @@ __global__ __launch_bounds__(64 * KS) void gemv_fp8_mfma_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int M, int64_t K,
     const uint8_t* __restrict__ w, int64_t ldw, int64_t N,
     const float* __restrict__ ws, int ws_step, uint16_t* __restrict__ y, int64_t ldy) {
+    {
+        const int mb = token_block_start();
+        x += mb * ldx;
+        y += mb * ldy;
+        M = token_block_size(M);
+    }
     __shared__ __align__(16) uint8_t tile[KS][16 * kTilePitch];
     __shared__ f32x4_t red[KS][64];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -345,6 +376,13 @@ __global__ __launch_bounds__(64 * KS) void gemv_fp8_w8a8_mfma_kernel(
     const uint8_t* __restrict__ xq, int64_t ldxq, const float* __restrict__ xs, int xs_step, int M,
     int64_t K, const uint8_t* __restrict__ w, int64_t ldw, int64_t N,
     const float* __restrict__ ws, int ws_step, uint16_t* __restrict__ y, int64_t ldy) {
+    {
+        const int mb = token_block_start();
+        xq += mb * ldxq;
+        xs += mb * xs_step;
+        y += mb * ldy;
+        M = token_block_size(M);
+    }
     __shared__ __align__(16) uint8_t tile[KS][16 * kTilePitch];
     __shared__ __align__(16) uint8_t xtile[XL ? KS : 1][16 * kTilePitch];
     __shared__ f32x4_t red[KS][64];
@@ -421,6 +459,13 @@ __global__ __launch_bounds__(64 * KS) void gemv_fp8_blk_mfma_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, int M, int64_t K,
     const uint8_t* __restrict__ w, int64_t ldw, int64_t N,
     const uint8_t* __restrict__ ws, uint16_t* __restrict__ y, int64_t ldy) {
+    {
+        const int mb = token_block_start();
+        xq += mb * K;
+        xs += mb * (K >> 7);
+        y += mb * ldy;
+        M = token_block_size(M);
+    }
     __shared__ __align__(16) uint8_t tile[KS][16 * kTilePitch];
     __shared__ f32x4_t red[KS][64];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -510,6 +555,13 @@ __global__ __launch_bounds__(64 * KS) void gemv_fp8_blkg_mfma_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, int M, int64_t K,
     const uint8_t* __restrict__ w, int64_t ldw, int64_t N,
     const uint8_t* __restrict__ ws, int64_t bn, int64_t bk, uint16_t* __restrict__ y, int64_t ldy) {
+    {
+        const int mb = token_block_start();
+        xq += mb * K;
+        xs += mb * (K / bk);
+        y += mb * ldy;
+        M = token_block_size(M);
+    }
     __shared__ __align__(16) uint8_t tile[KS][16 * kTilePitch];
     __shared__ f32x4_t red[KS][64];
     extern __shared__ __align__(16) uint8_t sct[];  // [nkb][16] weight scales, then [nkb][16] token scales

@@ -173,17 +173,11 @@ int qlin_gemv_fp8_blk_ex(const void* x, int64_t ldx, int64_t M, int64_t K,
     hipStream_t st = (hipStream_t)stream;
     qlin::BlkQuantArgs qa{(const uint16_t*)x, ldx, M, K, xq, xs};
     if (qlin::launch_blkg_act_quant(qa, block_k, st) != hipSuccess) return QLIN_ERR_LAUNCH;
-    const int64_t nkb = K / block_k;
-    if (M > QLIN_MAX_M && K % 128 == 0) {  // prefill: one GEMM over all tokens
-        qlin::BlkArgs a{xq, xs, M, K, w, ldw, N, ws, (uint16_t*)y, ldy};
+    qlin::BlkArgs a{xq, xs, M, K, w, ldw, N, ws, (uint16_t*)y, ldy};
+    if (M > QLIN_MAX_M && K % 128 == 0)  // prefill: one GEMM over all tokens
         return launch_status(qlin::launch_gemm_fp8_blkg(a, block_n, block_k, st));
-    }
-    for (int64_t m0 = 0; m0 < M; m0 += QLIN_MAX_M) {  // 16 tokens per launch
-        const int64_t mc = M - m0 < QLIN_MAX_M ? M - m0 : QLIN_MAX_M;
-        qlin::BlkArgs a{xq + m0 * K, xs + m0 * nkb, mc, K, w, ldw, N, ws, (uint16_t*)y + m0 * ldy, ldy};
-        if (qlin::launch_gemv_fp8_blkg(a, block_n, block_k, st) != hipSuccess) return QLIN_ERR_LAUNCH;
-    }
-    return QLIN_OK;
+    // the matrix-core kernel over a grid of 16-token blocks
+    return launch_status(qlin::launch_gemv_fp8_blkg(a, block_n, block_k, st));
 }
 
 size_t qlin_moe_mxfp4_workspace_bytes(int64_t M, int64_t N, int64_t topk, int64_t E) {

@@ -138,6 +138,7 @@ WORKLOADS = {
     "fp8_w8a8": {"kind": "fp8_w8a8", "N": 17408, "K": 5120, "Ms": [1, 2, 4, 8, 16]},
     "int8_prefill": {"kind": "int8", "N": 17408, "K": 5120, "Ms": [128, 512, 2048]},
     "fp8_prefill": {"kind": "fp8", "N": 17408, "K": 5120, "Ms": [128, 512, 2048]},
+    "int8_prefill_smalln": {"kind": "int8", "N": 48, "K": 5120, "Ms": [64, 512]},
     "fp8_blk": {"kind": "fp8_blk", "N": 4096, "K": 7168, "Ms": [1, 8, 16]},
     "moe_mxfp4": {"kind": "moe", "E": 64, "N": 2048, "K": 7168, "Ms": [8], "topk": 6},
     "moe_prefill": {"kind": "moe", "E": 64, "N": 2048, "K": 7168, "Ms": [64, 512], "topk": 6},

@@ -224,3 +224,117 @@ def test_prefill_deterministic(ql):
     ref = ql.qlin_gemv_fp8(x, w, ws)
     for _ in range(10):
         assert torch.equal(ql.qlin_gemv_fp8(x, w, ws).view(torch.int16), ref.view(torch.int16))
+
+
+# ----------------------------------------------------------------------------- few rows: split-K
+
+# Fewer than a quarter of the compute units' worth of 64 x 64 output tiles:
+# the matrix-core kernels over 16-row x 16-token workgroups, K split between
+# the waves of each and summed in wave order.  The shapes the Z100 record
+# lists for its small-N gap (N = 48 at M = 64) and its neighbours, plus
+# ragged ones.
+SPLIT_SHAPES = [(64, 48, 5120), (512, 48, 5120), (64, 96, 5120), (512, 96, 5120), (64, 200, 5120),
+                (512, 200, 5120), (17, 47, 1040), (100, 1, 272), (513, 33, 2064)]
+
+
+@pytest.mark.parametrize("M,N,K", SPLIT_SHAPES)
+def test_prefill_split_int8(ql, orc, M, N, K):
+    d = gen_int8(M, N, K, seed=M + 2 * N + K)
+    oxq, oxs = orc.act_quant_i8(d["x"])
+    rng = np.random.default_rng(N)
+    bias = bf16_bits(rng.standard_normal(N).astype(np.float32))
+    acc = ql.qlin_gemv_i8(dev(oxq), dev(oxs), dev(d["w"]), dev(d["ws"]), out_kind=1)
+    y = ql.qlin_gemv_i8(dev(oxq), dev(oxs), dev(d["w"]), dev(d["ws"]), bias=dev_bf16(bias))
+    torch.cuda.synchronize()
+    oacc, oy = orc.gemv_i8(oxq, oxs, d["w"], d["ws"], bias=bias)
+    assert np.array_equal(host(acc), oacc)
+    assert np.array_equal(host_bits(y), oy)
+
+
+@pytest.mark.parametrize("M,N,K", SPLIT_SHAPES)
+def test_prefill_split_fp8(ql, orc, M, N, K):
+    d = gen_fp8(M, N, K, seed=M + 3 * N + K)
+    y = ql.qlin_gemv_fp8(padded(d["x"].view(np.int16), 64).view(torch.bfloat16), dev(d["w"]), dev(d["ws"]))
+    torch.cuda.synchronize()
+    _, ye, S = orc.gemv_fp8(d["x"], d["w"], d["ws"])
+    check_float(host_bits(y), ye, S, K)
+
+
+@pytest.mark.parametrize("M,N,K", SPLIT_SHAPES)
+def test_prefill_split_fp8_w8a8(ql, orc, M, N, K):
+    d = gen_fp8_w8a8(M, N, K, w_fmt=0, seed=M + 5 * N + K)
+    oxq, oxs = orc.act_quant_fp8(d["x"], 0, True)
+    y = ql.qlin_gemv_fp8_w8a8(dev(oxq), dev(oxs), dev(d["w"]), dev(d["ws"]), 0, 0)
+    torch.cuda.synchronize()
+    _, ye, S = orc.gemv_fp8_w8a8(oxq, oxs, 0, d["w"], d["ws"], 0)
+    check_float(host_bits(y), ye, S, K)
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 48, 5120), (512, 48, 5120), (512, 200, 5120), (17, 47, 1024),
+                                   (100, 130, 384)])
+def test_prefill_split_fp8_blk(ql, orc, M, N, K):
+    d = gen_fp8_blk(M, N, K, seed=M + 7 * N)
+    y, xq, xs = ql.qlin_gemv_fp8_blk(dev_bf16(d["x"]), dev(d["w"]), dev(d["ws"]))
+    torch.cuda.synchronize()
+    oxq, oxs, _, ye, S = orc.fp8_blk(d["x"], d["w"], d["ws"])
+    assert np.array_equal(host(xq), oxq) and np.array_equal(host(xs), oxs)
+    check_float(host_bits(y), ye, S, K)
+
+
+def test_prefill_split_deterministic(ql):
+    d = gen_fp8(512, 48, 5120, seed=8)
+    x, w, ws = dev_bf16(d["x"]), dev(d["w"]), dev(d["ws"])
+    ref = ql.qlin_gemv_fp8(x, w, ws)
+    for _ in range(10):
+        assert torch.equal(ql.qlin_gemv_fp8(x, w, ws).view(torch.int16), ref.view(torch.int16))
+
+
+# ----------------------------------------------------------------------------- enough rows for the tiled GEMM
+
+# at least a quarter of the compute units' worth of 64 x 64 tiles, ragged M and
+# N at every tile size; K % 128 != 0 (register-staged kernel) and K % 128 == 0
+# (direct-to-LDS kernel)
+GEMM_SHAPES = [(17, 4100, 272), (129, 2050, 528), (300, 1100, 2064), (17, 4100, 128), (100, 2050, 1024),
+               (256, 1030, 384), (600, 530, 640), (1030, 520, 384)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_prefill_gemm_int8(ql, orc, M, N, K):
+    d = gen_int8(M, N, K, seed=M + 11 * N + K)
+    oxq, oxs = orc.act_quant_i8(d["x"])
+    acc = ql.qlin_gemv_i8(dev(oxq), dev(oxs), dev(d["w"]), dev(d["ws"]), out_kind=1)
+    y = ql.qlin_gemv_i8(dev(oxq), dev(oxs), padded(d["w"], 64), dev(d["ws"]))
+    torch.cuda.synchronize()
+    oacc, oy = orc.gemv_i8(oxq, oxs, d["w"], d["ws"])
+    assert np.array_equal(host(acc), oacc)
+    assert np.array_equal(host_bits(y), oy)
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_prefill_gemm_fp8(ql, orc, M, N, K):
+    d = gen_fp8(M, N, K, seed=M + 13 * N + K)
+    y = ql.qlin_gemv_fp8(dev_bf16(d["x"]), dev(d["w"]), dev(d["ws"]))
+    torch.cuda.synchronize()
+    _, ye, S = orc.gemv_fp8(d["x"], d["w"], d["ws"])
+    check_float(host_bits(y), ye, S, K)
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+@pytest.mark.parametrize("x_fmt,w_fmt", [(0, 0), (1, 0)])
+def test_prefill_gemm_fp8_w8a8(ql, orc, M, N, K, x_fmt, w_fmt):
+    d = gen_fp8_w8a8(M, N, K, w_fmt=w_fmt, seed=M + 17 * N + K)
+    oxq, oxs = orc.act_quant_fp8(d["x"], x_fmt, True)
+    y = ql.qlin_gemv_fp8_w8a8(dev(oxq), dev(oxs), dev(d["w"]), dev(d["ws"]), x_fmt, w_fmt)
+    torch.cuda.synchronize()
+    _, ye, S = orc.gemv_fp8_w8a8(oxq, oxs, x_fmt, d["w"], d["ws"], w_fmt)
+    check_float(host_bits(y), ye, S, K)
+
+
+@pytest.mark.parametrize("M,N,K", [(17, 4100, 128), (100, 2050, 1024), (600, 530, 640), (1030, 520, 384)])
+def test_prefill_gemm_fp8_blk(ql, orc, M, N, K):
+    d = gen_fp8_blk(M, N, K, seed=M + 19 * N)
+    y, xq, xs = ql.qlin_gemv_fp8_blk(dev_bf16(d["x"]), dev(d["w"]), dev(d["ws"]))
+    torch.cuda.synchronize()
+    oxq, oxs, _, ye, S = orc.fp8_blk(d["x"], d["w"], d["ws"])
+    assert np.array_equal(host(xq), oxq) and np.array_equal(host(xs), oxs)
+    check_float(host_bits(y), ye, S, K)
