@@ -117,12 +117,12 @@ __global__ __launch_bounds__(64) void blk_act_quant_kernel(
 // ---------------------------------------------------------------- FP8 W8A8
 // The INT8 rule with the format's largest finite value fmax (448 for E4M3,
 // 57344 for E5M2) in place of 127: s = amax / fmax and q = rne(x / s), both
-// IEEE fp32 divisions.  |x / s| can exceed fmax by a rounding error (and by
+// IEEE fp32 quotients (x / s formed by div_bf16, the same bits).  |x / s| can exceed fmax by a rounding error (and by
 // more when s is an fp32 subnormal); such values saturate to +-fmax before
 // the convert, so every code is finite.  The comparisons keep a NaN (which
 // then converts to a NaN code).  amax == 0 gives s = 0 and zero codes.
 template <int F>
-__device__ __forceinline__ uint2 quant_fp8x8(const u32x4_t& v, float amax, float s) {
+__device__ __forceinline__ uint2 quant_fp8x8(const u32x4_t& v, float amax, double r) {
     constexpr float fmax = F == kFmtE5M2 ? 57344.0f : 448.0f;
     const uint32_t d[4] = {v.x, v.y, v.z, v.w};
     float t[8];
@@ -131,7 +131,7 @@ __device__ __forceinline__ uint2 quant_fp8x8(const u32x4_t& v, float amax, float
         const uint32_t h = (e & 1) ? (d[e >> 1] >> 16) : (d[e >> 1] & 0xFFFFu);
         float q = 0.0f;
         if (amax != 0.0f) {
-            q = bf16_to_f32(h) / s;
+            q = div_bf16(bf16_to_f32(h), r);  // the IEEE fp32 quotient x / s, r = fl64(1 / s)
             q = q > fmax ? fmax : (q < -fmax ? -fmax : q);
         }
         t[e] = q;
@@ -191,19 +191,20 @@ __global__ __launch_bounds__(T) void act_quant_fp8_kernel(
     for (int q = 1; q < W; ++q) amax = fmaxf(amax, wave_max[q]);
     const float s = amax / fmax;
     if (tid == 0) xs[blockIdx.x] = s;
+    const double rs = 1.0 / (double)s;
 
 #pragma unroll
     for (int c = 0; c < C; ++c) {
         const int i = tid + c * T;
         if (i < total) {
             const int r = ONE_ROW ? 0 : i / nvec, v = i - r * nvec;
-            *(uint2*)(xq + (m0 + r) * ldxq + (int64_t)v * 8) = quant_fp8x8<F>(cache[c], amax, s);
+            *(uint2*)(xq + (m0 + r) * ldxq + (int64_t)v * 8) = quant_fp8x8<F>(cache[c], amax, rs);
         }
     }
     for (int i = tid + C * T; i < total; i += T) {
         const int r = ONE_ROW ? 0 : i / nvec, v = i - r * nvec;
         *(uint2*)(xq + (m0 + r) * ldxq + (int64_t)v * 8) =
-            quant_fp8x8<F>(ld16(x + (m0 + r) * ldx + (int64_t)v * 8), amax, s);
+            quant_fp8x8<F>(ld16(x + (m0 + r) * ldx + (int64_t)v * 8), amax, rs);
     }
 }
 
