@@ -854,4 +854,125 @@ __global__ __launch_bounds__(64 * WPB) void gemv_i8_lds_kernel(
     }
 }
 
+// ------------------------------------------------------------------ block FP8, one token, activations in LDS
+// M = 1 block-scaled FP8 with the activation quantisation fused in [Z100
+// section 2.4: block formula, per-block fold; DSV4 section 3.3: per-token
+// per-128 E4M3 activations with UE8M0 scales].  The workgroup loads the
+// bf16 row first, then every wave issues all U steps of its weight row and
+// the row's weight scale bytes; the row is quantised with the rule of
+// blk_act_quant_kernel (a 16-lane DPP row per 128-group, exponent from the
+// bits of amax, exact power-of-two scaling, RNE convert: bit-identical
+// codes), and the decoded code values (exact in bf16) go to LDS in the
+// two-half layout of gemv_fp8_m1_lds_kernel, the group scales 2^(E-127) next
+// to them.  The barrier after the LDS stores does not wait for the weights,
+// so each step's products start as soon as that step's bytes arrive.  Per
+// chunk of 16 (inside one 128-block): 8 v_dot2 of widened weights against
+// the staged values, then acc += (dot * 2^(xs-127)) * 2^(ws-127), the fold
+// order of every block kernel.  Group g goes to xq / xs (each optional) from
+// workgroup g % gridDim.x.  Dynamic LDS: 2K bytes of bf16, then K/128 floats.
+constexpr int64_t kBlkM1LdsMaxK = 8192;  // U <= 8 steps: a lane holds one K block's weight scale
+
+template <int U, int WPB>
+__global__ __launch_bounds__(64 * WPB) void gemv_fp8_blk_m1_lds_kernel(
+    const uint16_t* __restrict__ x, int64_t K,
+    const uint8_t* __restrict__ w, int64_t ldw, int64_t N, const uint8_t* __restrict__ ws,
+    uint8_t* __restrict__ xq, uint8_t* __restrict__ xs, uint16_t* __restrict__ y) {
+    static_assert(U >= 1 && U <= 8, "one scale byte per lane covers at most 8 steps");
+    extern __shared__ __align__(16) u32x4_t xl[];  // [2 * nchunk] 16-byte halves of bf16
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nchunk = (int)(K >> 4), nkb = (int)(K >> 7);
+    float* sl = (float*)(xl + 2 * nchunk);
+    constexpr int NT = 64 * WPB;
+    // 1. the bf16 row: vector i = 8 values, group i / 16; one per thread and pass
+    const int nvec = (int)(K >> 3);
+    constexpr int kMaxPass = (kBlkM1LdsMaxK / 8 + NT - 1) / NT;
+    const int npass = (nvec + NT - 1) / NT;
+    u32x4_t xv[kMaxPass];
+#pragma unroll
+    for (int p = 0; p < kMaxPass; ++p) {
+        const int i = tid + p * NT;
+        xv[p] = p < npass ? ld16(x + (int64_t)(i < nvec ? i : nvec - 1) * 8) : u32x4_t{0, 0, 0, 0};
+    }
+    // 2. this wave's row: every step and the row's scale bytes
+    const int64_t n = (int64_t)blockIdx.x * WPB + wv;
+    const int64_t nn = n < N ? n : N - 1;
+    const uint8_t* wr = w + nn * ldw;
+    u32x4_t wq[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = u * 64 + lane;
+        wq[u] = ld_stream(wr + (int64_t)(c < nchunk ? c : nchunk - 1) * 16);
+    }
+    const uint8_t* wsr = ws + (nn >> 7) * nkb;
+    const uint8_t swb = wsr[lane < nkb ? lane : nkb - 1];  // lane l: weight scale byte of K block l
+    __builtin_amdgcn_sched_barrier(0);  // keep the weight loads ahead of the quantisation
+    // 3. quantise: the 16 lanes of a DPP row hold the 16 vectors of one group
+#pragma unroll
+    for (int p = 0; p < kMaxPass; ++p) {
+        if (p < npass) {  // workgroup-uniform
+            const int i = tid + p * NT;
+            const bool ok = i < nvec;
+            const int g = ok ? (i >> 4) : nkb - 1, jj = i & 15;
+            const uint32_t d[4] = {xv[p].x, xv[p].y, xv[p].z, xv[p].w};
+            float f[8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                f[2 * q] = bf16_to_f32(d[q] & 0xFFFFu);
+                f[2 * q + 1] = bf16_to_f32(d[q] >> 16);
+            }
+            float a = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(f[e]));
+            a = row_max_f32(a);
+            const int E = blk_group_exp(a);
+            const float sc = blk_group_inv_scale(E);
+            int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0] * sc, f[1] * sc, 0, false);
+            lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2] * sc, f[3] * sc, lo, true);
+            int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4] * sc, f[5] * sc, 0, false);
+            hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6] * sc, f[7] * sc, hi, true);
+            if (ok) {
+                bf16x2_t b[4];
+                e4m3x4_to_bf16((uint32_t)lo, b[0], b[1]);
+                e4m3x4_to_bf16((uint32_t)hi, b[2], b[3]);
+                // vector i is half (i & 1) of chunk i >> 1
+                xl[(i & 1) * nchunk + (i >> 1)] =
+                    u32x4_t{__builtin_bit_cast(uint32_t, b[0]), __builtin_bit_cast(uint32_t, b[1]),
+                            __builtin_bit_cast(uint32_t, b[2]), __builtin_bit_cast(uint32_t, b[3])};
+                if (jj == 0) sl[g] = ue8m0_to_f32((uint32_t)E);
+                if ((uint32_t)g % gridDim.x == blockIdx.x) {  // exported only when asked for
+                    if (xq) *(uint2*)(xq + (int64_t)i * 8) = make_uint2((uint32_t)lo, (uint32_t)hi);
+                    if (xs && jj == 0) xs[g] = (uint8_t)E;
+                }
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the LDS stores are done
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();  // not __syncthreads(): that would also wait for the weights
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    // 4. the row: chunk c = u*64 + lane lies in K block c / 8
+    const float swl = ue8m0_to_f32(swb);
+    float acc = 0.0f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = u * 64 + lane;
+        const bool ok = c < nchunk;
+        const int cc = ok ? c : nchunk - 1;
+        const float sw = __shfl(swl, cc >> 3);
+        const float sx = sl[cc >> 3];
+        bf16x2_t wb[8];
+        e4m3x16(wq[u], wb);
+        const u32x4_t a0 = xl[cc], a1 = xl[nchunk + cc];
+        float loc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) loc = dot2(wb[e], as_bf16x2(a0[e]), loc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) loc = dot2(wb[4 + e], as_bf16x2(a1[e]), loc);
+        acc += ok ? (loc * sx) * sw : 0.0f;  // a lane past the row end adds 0
+    }
+    acc = group_sum<64>(acc);
+    if (lane == 0 && n < N) y[n] = f32_to_bf16(acc);
+}
+
 }  // namespace qlin
