@@ -16,22 +16,23 @@ hipError_t run_gemm(const GemmParams& p, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int WF, int ACT, int EPI, int BN, int BM, int NW = 4>
+template <int WF, int ACT, int EPI, int BN, int BM, int NW = 4, int NS = 2>
 hipError_t run_gemm_dma(const GemmParams& p, hipStream_t st) {
     const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
     const int64_t grid = (tiles + 7) / 8 * 8;
-    hipLaunchKernelGGL((gemm_dma_kernel<WF, ACT, EPI, BN, BM, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, st, p);
+    hipLaunchKernelGGL((gemm_dma_kernel<WF, ACT, EPI, BN, BM, NW, NS>), dim3((unsigned)grid), dim3(64 * NW), 0, st,
+                       p);
     return hipGetLastError();
 }
 
 // Direct-to-LDS kernel, one-byte operands, K % 128 == 0.  Tiles (weight rows
 // x tokens, measured with INT8 at N = 17408, K = 5120): 64 x 64 up to 256
-// tokens, 64 x 128 up to 1024, 128 x 128 above.
+// tokens, 64 x 128 up to 1024, 128 x 128 with 8 waves above.
 template <int WF, int ACT, int EPI>
 hipError_t run_dma(const GemmParams& p, hipStream_t st) {
     if (p.M <= 256) return run_gemm_dma<WF, ACT, EPI, 64, 64>(p, st);
     if (p.M <= 1024) return run_gemm_dma<WF, ACT, EPI, 64, 128>(p, st);
-    return run_gemm_dma<WF, ACT, EPI, 128, 128>(p, st);
+    return run_gemm_dma<WF, ACT, EPI, 128, 128, 8>(p, st);
 }
 
 }  // namespace

@@ -286,7 +286,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
 // as fragments are read (exact) for v_mfma_f32_32x32x16_bf16.  The block-FP8
 // epilogue folds both scales per K tile (= one 128-wide K block).
 // Measured at N = 17408, K = 5120 (INT8): M = 128 / 512 / 2048 / 4096 about
-// 8 / 20 / 11 / 10% faster than gemm_kernel.
+// 8 / 20 / 11 / 10% faster than gemm_kernel.  The kernel is bound by the
+// tile loads (with the matrix-core work taken out it runs within 3% of the
+// full kernel at M = 2048), so the choices below are about feeding it:
+// 8 waves on a 128 x 128 tile (two workgroups, 16 waves per compute unit)
+// beat 4 (355 -> 310 us at M = 2048), and a banded tile order (below)
+// trims L2 misses (310 -> 302 us); deeper LDS rings (3-5 stages, one
+// workgroup per unit), 256 x 256 / 256 x 128 tiles (4, 8 or 16 waves) and
+// a per-workgroup rotation of the K order were all slower (340-460 us).
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef int i32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -322,7 +329,9 @@ __device__ __forceinline__ bf16x8_t e4m3x8_scaled(uint2 c, float sc) {
 template <int XB>
 __device__ __forceinline__ int dma_xswz(int row) { return XB == 2 ? (row & 15) : dma_swz(row); }
 
-template <int WF, int ACT, int EPI, int BN, int BM, int NW = 4>
+constexpr int64_t kBandM = 8;  // token tiles per raster band (measured at 2048 x 17408 x 5120: 8 > 4 > 2 > none)
+
+template <int WF, int ACT, int EPI, int BN, int BM, int NW = 4, int NS = 2>
 __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const GemmParams p) {
     constexpr bool kI8 = ACT == kActI8;
     static_assert(NW == 4 || NW == 8, "waves");
@@ -335,7 +344,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const GemmParams p) {
     constexpr int WI = BN / 8 / NW, XI = BM / XRPI / NW;   // load instructions per wave and stage
     static_assert(WI >= 1 && XI >= 1, "load split");
     constexpr int TN = BN / WGN / 32, TM = BM / WGM / 32;  // 32 x 32 tiles per wave
-    __shared__ __align__(16) uint8_t lds[2 * ST];
+    static_assert(NS == 2 || (EPI != kEpiBlk && EPI < kEpiBlkG), "deeper rings: no scale loads in the loop");
+    __shared__ __align__(16) uint8_t lds[NS * ST];
 
     const int64_t M = p.M, N = p.N, K = p.K;
     const int64_t tiles_m = (M + BM - 1) / BM;
@@ -343,7 +353,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const GemmParams p) {
     const int64_t per_xcd = (int64_t)gridDim.x / 8;  // the grid is a multiple of 8
     const int64_t t = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     if (t >= tiles) return;  // workgroup-uniform
-    const int64_t n0 = (t / tiles_m) * BN, m0 = (t % tiles_m) * BM;
+    // bands of kBandM token tiles: the tile order runs over all weight-row
+    // tiles of one band before the next band, so the workgroups that run at
+    // once on an XCD share about as many activation tiles as weight tiles
+    const int64_t tiles_n = (N + BN - 1) / BN, bsz = kBandM * tiles_n, band = t / bsz, rr = t - band * bsz;
+    const int64_t gm = tiles_m - band * kBandM < kBandM ? tiles_m - band * kBandM : kBandM;
+    const int64_t n0 = (rr / gm) * BN, m0 = (band * kBandM + rr % gm) * BM;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
 
     // this lane's load sources: row (wv*WI + i)*8 + lane/8, the chunk that
@@ -474,9 +489,15 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const GemmParams p) {
     };
     load_scales(0);
     load_gscales(0);
-    issue(0, 0);
+    // NS - 1 tiles in flight: tiles 0 .. NS-2 into slots 0 .. NS-2 (past the
+    // last tile, the last tile again: same count of loads on every path)
+#pragma unroll
+    for (int s2 = 0; s2 < NS - 1; ++s2) issue(s2 < ktiles ? s2 : ktiles - 1, s2);
+    int slot = 0;  // slot of tile kt
     for (int64_t kt = 0; kt < ktiles; ++kt) {
-        wait_vmcnt<0>();  // this wave's loads of tile kt (and its scales), the only ones outstanding
+        // this wave's loads of tile kt (and, NS = 2, its scales) have landed:
+        // at most the NS - 2 younger tiles' loads remain
+        wait_vmcnt<(NS - 2) * (WI + XI)>();
         stage_barrier();  // tile kt complete for everyone; everyone is done with tile kt-1
         float sw = 1.0f, sx[TM];
         if constexpr (EPI == kEpiBlk) {
@@ -518,8 +539,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const GemmParams p) {
         // unconditional, so the scale loads above complete before it on every
         // path (a conditional issue makes the compiler wait for everything);
         // the last tile reloads itself into the idle slot
-        issue(kt + 1 < ktiles ? kt + 1 : kt, (int)((kt + 1) & 1));
-        const uint8_t* Wt = lds + (kt & 1) * ST;
+        // tile kt + NS - 1 into the slot of tile kt - 1
+        const int nslot = slot == 0 ? NS - 1 : slot - 1;
+        issue(kt + NS - 1 < ktiles ? kt + NS - 1 : ktiles - 1, nslot);
+        const uint8_t* Wt = lds + slot * ST;
+        slot = slot + 1 == NS ? 0 : slot + 1;
         const uint8_t* Xt = Wt + WT;
 #pragma unroll
         for (int ks = 0; ks < BK / 32; ++ks) {
