@@ -155,3 +155,53 @@ def test_graph_moe_ffn(ql):
                               ids=ids, gw=gw)
         return [y, ids, gw]
     _check_replays(step, inp, _xfeeds(lambda s: gen_moe_ffn(M, E, H, I, topk, seed=s)))
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_graph_linear_i8(ql, M):
+    # the one-call INT8 layer: one fused kernel at M = 1, quantiser + GEMV above
+    N, K = 512, 1024
+    d = gen_int8(M, N, K, seed=7)
+    inp = {"x": dev_bf16(d["x"])}
+    w, ws = dev(d["w"]), dev(d["ws"])
+    xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    xs = torch.empty((M,), dtype=torch.float32, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        ql.qlin_linear_i8(inp["x"], w, ws, xq=xq, xs=xs, y=y)
+        return [xq, xs, y]
+    _check_replays(step, inp, _xfeeds(lambda s: gen_int8(M, N, K, seed=s)))
+
+
+def test_graph_fp8_blk_one_token_without_export(ql):
+    # one token, no code / scale buffers (NULL): the fused kernel alone
+    N, K = 512, 2048
+    d = gen_fp8_blk(1, N, K, seed=8)
+    inp = {"x": dev_bf16(d["x"])}
+    w, ws = dev(d["w"]), dev(d["ws"])
+    y = torch.empty((1, N), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        ql.qlin_gemv_fp8_blk(inp["x"], w, ws, y=y, export=False)
+        return [y]
+    _check_replays(step, inp, _xfeeds(lambda s: gen_fp8_blk(1, N, K, seed=s)))
+
+
+def test_graph_moe_noalloc(ql):
+    # the entry point that allocates nothing (its workspace is the library's
+    # static per-GPU array): captured like the others
+    M, E, N, K, topk = 8, 16, 256, 512, 4
+    d = gen_moe(M, E, N, K, topk, seed=9)
+    inp = {"x": dev_bf16(d["x"]), "ids": dev(d["ids"]), "gw": dev(d["gw"])}
+    w, s = dev(d["w"]), dev(d["s"])
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        ql.qlin_moe_mxfp4_noalloc(inp["x"], w, s, inp["ids"], inp["gw"], y)
+        return [y]
+    feeds = []
+    for seed in (210, 211, 212):
+        e = gen_moe(M, E, N, K, topk, seed=seed)
+        feeds.append({"x": dev_bf16(e["x"]), "ids": dev(e["ids"]), "gw": dev(e["gw"])})
+    _check_replays(step, inp, feeds)
