@@ -27,11 +27,11 @@ hipError_t run_gemm_dma(const GemmParams& p, hipStream_t st) {
 
 // Direct-to-LDS kernel, one-byte operands, K % 128 == 0.  Tiles (weight rows
 // x tokens, measured with INT8 at N = 17408, K = 5120): 64 x 64 up to 256
-// tokens, 64 x 128 up to 1024, 128 x 128 with 8 waves above.
+// tokens, 64 x 128 up to 1024 and 128 x 128 above, both with 8 waves.
 template <int WF, int ACT, int EPI>
 hipError_t run_dma(const GemmParams& p, hipStream_t st) {
     if (p.M <= 256) return run_gemm_dma<WF, ACT, EPI, 64, 64>(p, st);
-    if (p.M <= 1024) return run_gemm_dma<WF, ACT, EPI, 64, 128>(p, st);
+    if (p.M <= 1024) return run_gemm_dma<WF, ACT, EPI, 64, 128, 8>(p, st);
     return run_gemm_dma<WF, ACT, EPI, 128, 128, 8>(p, st);
 }
 

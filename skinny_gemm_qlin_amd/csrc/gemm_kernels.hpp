@@ -290,7 +290,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
 // tile loads (with the matrix-core work taken out it runs within 3% of the
 // full kernel at M = 2048), so the choices below are about feeding it:
 // 8 waves on a 128 x 128 tile (two workgroups, 16 waves per compute unit)
-// beat 4 (355 -> 310 us at M = 2048), and a banded tile order (below)
+// beat 4 (355 -> 310 us at M = 2048; on the 64 x 128 tile at M = 512,
+// 112.6 -> 109.0 us), and a banded tile order (below)
 // trims L2 misses (310 -> 302 us); deeper LDS rings (3-5 stages, one
 // workgroup per unit), 256 x 256 / 256 x 128 tiles (4, 8 or 16 waves) and
 // a per-workgroup rotation of the K order were all slower (340-460 us).
@@ -335,8 +336,10 @@ template <int WF, int ACT, int EPI, int BN, int BM, int NW = 4, int NS = 2>
 __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const GemmParams p) {
     constexpr bool kI8 = ACT == kActI8;
     static_assert(NW == 4 || NW == 8, "waves");
-    constexpr int WGN = NW / 2, WGM = 2;                   // wave grid (weight rows x tokens)
-    static_assert(BN % (32 * WGN) == 0 && BM % 64 == 0 && BN <= 32 * WGN * 2 && BM <= 128, "tile");
+    // wave grid (weight rows x tokens): two token columns, or four when 8
+    // waves share a 64-row tile
+    constexpr int WGM = (NW == 8 && BN < 128) ? 4 : 2, WGN = NW / WGM;
+    static_assert(BN % (32 * WGN) == 0 && BM % (32 * WGM) == 0 && BN <= 32 * WGN * 2 && BM <= 128, "tile");
     constexpr int BK = 128;                                // K elements per stage (= weight bytes per row)
     constexpr int XB = ACT == kActBf16 ? 2 : 1;            // bytes per activation element
     constexpr int XRB = BK * XB, XRPI = 1024 / XRB;        // activation row bytes, rows per load instruction
