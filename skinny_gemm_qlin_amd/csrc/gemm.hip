@@ -16,12 +16,11 @@ hipError_t run_gemm(const GemmParams& p, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int WF, int ACT, int EPI, int BN, int BM, int NW = 4, int NS = 2>
+template <int WF, int ACT, int EPI, int BN, int BM, int NW = 4>
 hipError_t run_gemm_dma(const GemmParams& p, hipStream_t st) {
     const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
     const int64_t grid = (tiles + 7) / 8 * 8;
-    hipLaunchKernelGGL((gemm_dma_kernel<WF, ACT, EPI, BN, BM, NW, NS>), dim3((unsigned)grid), dim3(64 * NW), 0, st,
-                       p);
+    hipLaunchKernelGGL((gemm_dma_kernel<WF, ACT, EPI, BN, BM, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, st, p);
     return hipGetLastError();
 }
 

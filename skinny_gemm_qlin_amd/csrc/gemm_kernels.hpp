@@ -332,7 +332,7 @@ __device__ __forceinline__ int dma_xswz(int row) { return XB == 2 ? (row & 15) :
 
 constexpr int64_t kBandM = 8;  // token tiles per raster band (measured at 2048 x 17408 x 5120: 8 > 4 > 2 > none)
 
-template <int WF, int ACT, int EPI, int BN, int BM, int NW = 4, int NS = 2>
+template <int WF, int ACT, int EPI, int BN, int BM, int NW = 4>
 __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const GemmParams p) {
     constexpr bool kI8 = ACT == kActI8;
     static_assert(NW == 4 || NW == 8, "waves");
@@ -347,8 +347,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const GemmParams p) {
     constexpr int WI = BN / 8 / NW, XI = BM / XRPI / NW;   // load instructions per wave and stage
     static_assert(WI >= 1 && XI >= 1, "load split");
     constexpr int TN = BN / WGN / 32, TM = BM / WGM / 32;  // 32 x 32 tiles per wave
-    static_assert(NS == 2 || (EPI != kEpiBlk && EPI < kEpiBlkG), "deeper rings: no scale loads in the loop");
-    __shared__ __align__(16) uint8_t lds[NS * ST];
+    __shared__ __align__(16) uint8_t lds[2 * ST];
 
     const int64_t M = p.M, N = p.N, K = p.K;
     const int64_t tiles_m = (M + BM - 1) / BM;
@@ -492,15 +491,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const GemmParams p) {
     };
     load_scales(0);
     load_gscales(0);
-    // NS - 1 tiles in flight: tiles 0 .. NS-2 into slots 0 .. NS-2 (past the
-    // last tile, the last tile again: same count of loads on every path)
-#pragma unroll
-    for (int s2 = 0; s2 < NS - 1; ++s2) issue(s2 < ktiles ? s2 : ktiles - 1, s2);
-    int slot = 0;  // slot of tile kt
+    issue(0, 0);
     for (int64_t kt = 0; kt < ktiles; ++kt) {
-        // this wave's loads of tile kt (and, NS = 2, its scales) have landed:
-        // at most the NS - 2 younger tiles' loads remain
-        wait_vmcnt<(NS - 2) * (WI + XI)>();
+        wait_vmcnt<0>();  // this wave's loads of tile kt (and its scales), the only ones outstanding
         stage_barrier();  // tile kt complete for everyone; everyone is done with tile kt-1
         float sw = 1.0f, sx[TM];
         if constexpr (EPI == kEpiBlk) {
@@ -542,11 +535,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const GemmParams p) {
         // unconditional, so the scale loads above complete before it on every
         // path (a conditional issue makes the compiler wait for everything);
         // the last tile reloads itself into the idle slot
-        // tile kt + NS - 1 into the slot of tile kt - 1
-        const int nslot = slot == 0 ? NS - 1 : slot - 1;
-        issue(kt + NS - 1 < ktiles ? kt + NS - 1 : ktiles - 1, nslot);
-        const uint8_t* Wt = lds + slot * ST;
-        slot = slot + 1 == NS ? 0 : slot + 1;
+        issue(kt + 1 < ktiles ? kt + 1 : kt, (int)((kt + 1) & 1));
+        const uint8_t* Wt = lds + (kt & 1) * ST;
         const uint8_t* Xt = Wt + WT;
 #pragma unroll
         for (int ks = 0; ks < BK / 32; ++ks) {
