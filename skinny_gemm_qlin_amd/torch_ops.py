@@ -22,7 +22,7 @@ from typing import Optional, Tuple
 import torch
 
 from . import (qlin_act_quant_fp8, qlin_act_quant_i8, qlin_gemv_fp8, qlin_gemv_fp8_blk, qlin_gemv_fp8_blk_ex,
-               qlin_gemv_fp8_w8a8, qlin_gemv_i8, qlin_moe_ffn_mxfp4, qlin_moe_mxfp4)
+               qlin_gemv_fp8_w8a8, qlin_gemv_i8, qlin_linear_i8, qlin_moe_ffn_mxfp4, qlin_moe_mxfp4)
 
 hits = collections.Counter()
 
@@ -60,10 +60,10 @@ def _(xq, xs, w, ws, bias=None):
 @torch.library.custom_op("qlin::linear_i8", mutates_args=())
 def linear_i8(x: torch.Tensor, w: torch.Tensor, ws: torch.Tensor,
               bias: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Dynamic per-token quantisation followed by the INT8 GEMV (two kernels)."""
+    """Dynamic per-token quantisation and the INT8 GEMV through qlin_linear_i8
+    (one kernel for one token, quantiser + GEMV otherwise)."""
     hits["linear_i8"] += 1
-    xq, xs = qlin_act_quant_i8(x)
-    return qlin_gemv_i8(xq, xs, w, ws, bias=bias)
+    return qlin_linear_i8(x, w, ws, bias=bias)[0]
 
 
 @linear_i8.register_fake
@@ -127,7 +127,8 @@ def _(x, w, ws, x_fmt=0, w_fmt=0, per_token=True):
 @torch.library.custom_op("qlin::gemv_fp8_blk", mutates_args=())
 def gemv_fp8_blk(x: torch.Tensor, w: torch.Tensor, ws: torch.Tensor) -> torch.Tensor:
     hits["gemv_fp8_blk"] += 1
-    return qlin_gemv_fp8_blk(x, w, ws)[0]
+    # one token: the fused kernel needs no code / scale buffers
+    return qlin_gemv_fp8_blk(x, w, ws, export=not (x.shape[0] == 1 and x.shape[1] <= 32768))[0]
 
 
 @gemv_fp8_blk.register_fake
