@@ -382,22 +382,42 @@ bool ks_plan(int64_t N, int64_t K, int lmax, KsPlan& p) {
 constexpr int kKsMaxLI8 = 8;     // INT8 holds 2L + 3 * 2L 16-byte registers per lane
 constexpr int kKsMaxLFloat = 5;  // the float kinds hold 4L + 2 * 2L
 
-template <int KIND, int L, int XF, int WF>
+template <int KIND, int L, int XF, int WF, bool XS = false>
 hipError_t run_ks_t(const KsArgs& a, const KsPlan& p, hipStream_t st) {
     const dim3 grid(p.G), block(64 * kKsWaves);
     switch (p.T) {
-        case 1: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 1, XF, WF>), grid, block, 0, st, a); break;
-        case 2: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 2, XF, WF>), grid, block, 0, st, a); break;
-        case 3: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 3, XF, WF>), grid, block, 0, st, a); break;
-        case 4: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 4, XF, WF>), grid, block, 0, st, a); break;
-        case 5: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 5, XF, WF>), grid, block, 0, st, a); break;
-        default: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 6, XF, WF>), grid, block, 0, st, a); break;
+        case 1: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 1, XF, WF, XS>), grid, block, 0, st, a); break;
+        case 2: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 2, XF, WF, XS>), grid, block, 0, st, a); break;
+        case 3: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 3, XF, WF, XS>), grid, block, 0, st, a); break;
+        case 4: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 4, XF, WF, XS>), grid, block, 0, st, a); break;
+        case 5: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 5, XF, WF, XS>), grid, block, 0, st, a); break;
+        default: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 6, XF, WF, XS>), grid, block, 0, st, a); break;
     }
     return hipGetLastError();
 }
 
+// One-byte activation codes (INT8, FP8 W8A8) from kKsStageXMinM tokens,
+// with at most 5 lines per slice (LDS: the staged slices take 16 KB x L
+// next to the transpose columns and the partial tiles) and the activation
+// block addressable with 32-bit offsets: the slice is staged through LDS
+// (XS; INT8 M = 4 / 8 / 16: 16.5 / 17.0 / 18.6 -> 16.4 / 16.8 / 17.7 us).
+constexpr int64_t kKsStageXMinM = 4;
+bool ks_stage_x(const KsArgs& a, const KsPlan& p) {
+    return a.M >= kKsStageXMinM && p.L <= 5 && (int64_t)(a.M - 1) * a.ldx + 1024 * p.L <= INT32_MAX;
+}
+
 template <int KIND, int XF = kFmtE4M3, int WF = kFmtE4M3>
 hipError_t run_ks(const KsArgs& a, const KsPlan& p, hipStream_t st) {
+    if constexpr (KIND != kKsF8) {
+        if (ks_stage_x(a, p)) {
+            switch (p.L) {
+                case 2: return run_ks_t<KIND, 2, XF, WF, true>(a, p, st);
+                case 3: return run_ks_t<KIND, 3, XF, WF, true>(a, p, st);
+                case 4: return run_ks_t<KIND, 4, XF, WF, true>(a, p, st);
+                default: return run_ks_t<KIND, 5, XF, WF, true>(a, p, st);
+            }
+        }
+    }
     switch (p.L) {
         case 2: return run_ks_t<KIND, 2, XF, WF>(a, p, st);
         case 3: return run_ks_t<KIND, 3, XF, WF>(a, p, st);
