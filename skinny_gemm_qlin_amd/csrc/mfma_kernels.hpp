@@ -501,9 +501,16 @@ __global__ __launch_bounds__(64 * KS) void gemv_fp8_blk_mfma_kernel(
                 const int64_t kb = (c + u) * 2 + b;
                 const bool okb = (c + u < c1) && kb < nkb;
                 const int64_t kbc = okb ? kb : 0;
-                // an idle block folds in exactly 0 (its partial is 0 as well)
-                sw[u][b] = okb ? ue8m0_to_f32(wsr[kbc]) : 0.0f;
-                sx[u][b] = okb ? ue8m0_to_f32(xsr[kbc]) : 0.0f;
+                // An idle block (past the wave's range or past K) has zero
+                // activation codes, so its partial D is a zero and folds in
+                // as one whatever finite scales it meets: it reads block 0's
+                // (a NaN weight scale there makes the tile's outputs NaN in
+                // any case).  Selecting 0 for it instead (`okb ? scale : 0`)
+                // had the compiler branch over each pair of byte loads and
+                // wait for it on its own, a round trip per block (0.7 us of
+                // a 10 us call at 4096 x 7168).
+                sw[u][b] = ue8m0_to_f32(wsr[kbc]);
+                sx[u][b] = ue8m0_to_f32(xsr[kbc]);
             }
         }
 #pragma unroll
