@@ -169,6 +169,7 @@ def main():
     ap.add_argument("--per-tensor", action="store_true", help="fp8_decode: per-tensor weight scale")
     ap.add_argument("--block", default="128,128", help="fp8_blk: block_n,block_k of the weight scales")
     ap.add_argument("--no-fp8", action="store_true", help="int8_decode: skip the fp8_m1 measurement")
+    ap.add_argument("--bias", action="store_true", help="INT8 workloads: add a bf16 bias (seeded N(0, 1))")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -243,6 +244,12 @@ def main():
         w0 = t(d["w"])
         ws_copies = [w0] + [w0.clone() for _ in range(B - 1)]
     sc = t(d["ws"]) if "ws" in d else None
+    bias = None
+    if args.bias:
+        if not wl.startswith("int8"):
+            raise SystemExit("--bias applies to the INT8 workloads only")
+        bias = tb(inputs.bf16_bits(np.random.default_rng(1).standard_normal(N, dtype=np.float32)))
+    bias_bytes = 2 * N if args.bias else 0
 
     # ---------------------------------------------------------------- per-call launch lists
     xq_buf = torch.empty((Mmax, K), dtype=torch.int8 if wl.startswith("int8") else torch.uint8, device=dev)
@@ -272,13 +279,13 @@ def main():
         w = ws_copies[ci]
         xm = x[:M]
         if wl == "int8_decode":
-            return [("linear_i8", bytes_act_quant_i8(M, K) + bytes_gemv_i8(M, N, K),
-                     lambda: ql.qlin_linear_i8(xm, w, sc, xq=xq_buf[:M], xs=xs_buf[:M], y=y_buf[:M]))]
+            return [("linear_i8", bytes_act_quant_i8(M, K) + bytes_gemv_i8(M, N, K) + bias_bytes,
+                     lambda: ql.qlin_linear_i8(xm, w, sc, bias=bias, xq=xq_buf[:M], xs=xs_buf[:M], y=y_buf[:M]))]
         if wl in ("int8_prefill", "int8_prefill_smalln"):
             return [("act_quant_i8", bytes_act_quant_i8(M, K),
                      lambda: ql.qlin_act_quant_i8(xm, xq_buf[:M], xs_buf[:M])),
-                    ("gemv_i8", bytes_gemv_i8(M, N, K),
-                     lambda: ql.qlin_gemv_i8(xq_buf[:M], xs_buf[:M], w, sc, y=y_buf[:M]))]
+                    ("gemv_i8", bytes_gemv_i8(M, N, K) + bias_bytes,
+                     lambda: ql.qlin_gemv_i8(xq_buf[:M], xs_buf[:M], w, sc, bias=bias, y=y_buf[:M]))]
         if wl in ("fp8_decode", "fp8_prefill"):
             return [("gemv_fp8", bytes_gemv_fp8(M, N, K), lambda: ql.qlin_gemv_fp8(xm, w, sc, y=y_buf[:M]))]
         if wl == "fp8_w8a8":
@@ -306,8 +313,8 @@ def main():
         xm = x[:M]
         return [("act_quant_i8", bytes_act_quant_i8(M, K),
                  lambda: ql.qlin_act_quant_i8(xm, xq_buf[:M], xs_buf[:M])),
-                ("gemv_i8", bytes_gemv_i8(M, N, K),
-                 lambda: ql.qlin_gemv_i8(xq_buf[:M], xs_buf[:M], w, sc, y=y_buf[:M]))] + launches(M, ci)
+                ("gemv_i8", bytes_gemv_i8(M, N, K) + bias_bytes,
+                 lambda: ql.qlin_gemv_i8(xq_buf[:M], xs_buf[:M], w, sc, bias=bias, y=y_buf[:M]))] + launches(M, ci)
 
     dominant = {"int8_decode": "gemv_i8", "fp8_decode": "gemv_fp8", "fp8_w8a8": "gemv_fp8_w8a8",
                 "int8_prefill": "gemv_i8", "int8_prefill_smalln": "gemv_i8", "fp8_prefill": "gemv_fp8",
@@ -514,6 +521,8 @@ def main():
     }[wl], "N": N, "K": K, "Ms": Ms, "weight_copies": B, "cold_weights": B * wbytes >= 2 * MALL_BYTES}
     if wl in ("moe_mxfp4", "moe_ffn_mxfp4", "moe_prefill"):
         cfg["live_experts"] = int(live)
+    if args.bias:
+        cfg["bias"] = "bf16 [N]"
 
     out = {
         "metric": "us/call + achieved HBM GB/s (% of peak) for quantized decode GEMV, M=1..16",
