@@ -382,16 +382,16 @@ bool ks_plan(int64_t N, int64_t K, int lmax, KsPlan& p) {
 constexpr int kKsMaxLI8 = 8;     // INT8 holds 2L + 3 * 2L 16-byte registers per lane
 constexpr int kKsMaxLFloat = 5;  // the float kinds hold 4L + 2 * 2L
 
-template <int KIND, int L, int XF, int WF, bool XS = false>
+template <int KIND, int L, int XF, int WF, bool XS = false, bool CB = false>
 hipError_t run_ks_t(const KsArgs& a, const KsPlan& p, hipStream_t st) {
     const dim3 grid(p.G), block(64 * kKsWaves);
     switch (p.T) {
-        case 1: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 1, XF, WF, XS>), grid, block, 0, st, a); break;
-        case 2: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 2, XF, WF, XS>), grid, block, 0, st, a); break;
-        case 3: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 3, XF, WF, XS>), grid, block, 0, st, a); break;
-        case 4: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 4, XF, WF, XS>), grid, block, 0, st, a); break;
-        case 5: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 5, XF, WF, XS>), grid, block, 0, st, a); break;
-        default: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 6, XF, WF, XS>), grid, block, 0, st, a); break;
+        case 1: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 1, XF, WF, XS, CB>), grid, block, 0, st, a); break;
+        case 2: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 2, XF, WF, XS, CB>), grid, block, 0, st, a); break;
+        case 3: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 3, XF, WF, XS, CB>), grid, block, 0, st, a); break;
+        case 4: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 4, XF, WF, XS, CB>), grid, block, 0, st, a); break;
+        case 5: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 5, XF, WF, XS, CB>), grid, block, 0, st, a); break;
+        default: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 6, XF, WF, XS, CB>), grid, block, 0, st, a); break;
     }
     return hipGetLastError();
 }
@@ -406,16 +406,36 @@ bool ks_stage_x(const KsArgs& a, const KsPlan& p) {
     return a.M >= kKsStageXMinM && p.L <= 5 && (int64_t)(a.M - 1) * a.ldx + 1024 * p.L <= INT32_MAX;
 }
 
+// Contiguous row blocks (CB) for the staged kernels from kKsContigMinM
+// tokens (17408 x 5120, GEMV alone, against the runs dealt out in turn: INT8
+// M = 4 / 8 / 12 / 16 +0.5 / +0.15 / -0.3 / -0.5 us, FP8 W8A8 ~0 / -0.3..0 /
+// -0.4 / -0.55..-0.7 us; the unstaged weight-only kernel was 0.5-0.7 us
+// slower at every M with them, and does not use them).
+constexpr int64_t kKsContigMinM = 12;
+bool ks_contig(int kind, int64_t M) { return kind != kKsF8 && M >= kKsContigMinM; }
+
+template <int KIND, int XF, int WF, bool CB>
+hipError_t run_ks_staged(const KsArgs& a, const KsPlan& p, hipStream_t st) {
+    switch (p.L) {
+        case 2: return run_ks_t<KIND, 2, XF, WF, true, CB>(a, p, st);
+        case 3: return run_ks_t<KIND, 3, XF, WF, true, CB>(a, p, st);
+        case 4: return run_ks_t<KIND, 4, XF, WF, true, CB>(a, p, st);
+        default: return run_ks_t<KIND, 5, XF, WF, true, CB>(a, p, st);
+    }
+}
+
 template <int KIND, int XF = kFmtE4M3, int WF = kFmtE4M3>
 hipError_t run_ks(const KsArgs& a, const KsPlan& p, hipStream_t st) {
     if constexpr (KIND != kKsF8) {
         if (ks_stage_x(a, p)) {
-            switch (p.L) {
-                case 2: return run_ks_t<KIND, 2, XF, WF, true>(a, p, st);
-                case 3: return run_ks_t<KIND, 3, XF, WF, true>(a, p, st);
-                case 4: return run_ks_t<KIND, 4, XF, WF, true>(a, p, st);
-                default: return run_ks_t<KIND, 5, XF, WF, true>(a, p, st);
+            if (ks_contig(KIND, a.M)) {
+                KsArgs b = a;
+                const int64_t runs = (a.N + 3) / 4;
+                b.rbase = runs / p.G;
+                b.rrem = runs - b.rbase * p.G;
+                return run_ks_staged<KIND, XF, WF, true>(b, p, st);
             }
+            return run_ks_staged<KIND, XF, WF, false>(a, p, st);
         }
     }
     switch (p.L) {

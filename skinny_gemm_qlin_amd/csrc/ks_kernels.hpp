@@ -14,7 +14,8 @@ namespace qlin {
 // N is small); workgroup b owns the runs of 4 rows b, b + G, b + 2G, ...
 // (row j of the workgroup is n = 4*((j/4)*G + b) + j%4, j < R, so that no
 // workgroup has more than one run above another and a lane's 4 output rows
-// are adjacent), taken as T tiles of 16.  Each of its 8 waves owns one eighth of K (L lines of 128
+// are adjacent), or with CB a contiguous block of them (see CB below), taken
+// as T tiles of 16.  Each of its 8 waves owns one eighth of K (L lines of 128
 // bytes) for the whole kernel: it loads its slice of the M token rows once,
 // into registers in the MFMA B layout (one-byte codes from 4 tokens on
 // through an LDS stage, see XS below), then streams its slice of the T weight
@@ -41,6 +42,7 @@ struct KsArgs {
     const float* ws; int ws_step;
     const uint16_t* bias;            // INT8: optional bf16 bias
     void* y; int64_t ldy; int out_kind;  // INT8: out_kind 1 stores the raw int32 sums
+    int64_t rbase, rrem;                 // CB: ceil(N/4) runs = rbase * gridDim.x + rrem
 };
 
 // XS (one-byte activation codes: INT8, FP8 W8A8): the wave's activation
@@ -48,10 +50,15 @@ struct KsArgs {
 // one 128-byte line of 8 token rows (instead of 16 rows x 64 bytes per
 // register load), the weight tiles' loads queue behind it, and the B
 // operands are read back from LDS (M = 16, INT8: 18.6 -> 17.7 us).
-template <int KIND, int L, int T, int XF = kFmtE4M3, int WF = kFmtE4M3, bool XS = false>
+// CB (with XS): the runs are split into G contiguous blocks whose sizes differ
+// by at most one run (the first rrem workgroups take one more), so workgroup
+// b's rows are 4*P_b, 4*P_b + 1, ... with P_b = b*rbase + min(b, rrem), and a
+// tile's outputs are 16 adjacent rows.
+template <int KIND, int L, int T, int XF = kFmtE4M3, int WF = kFmtE4M3, bool XS = false, bool CB = false>
 __global__ __launch_bounds__(64 * kKsWaves) void gemv_ks_kernel(const KsArgs a) {
     constexpr bool I8 = KIND == kKsI8;
     static_assert(!XS || KIND != kKsF8, "activation staging: one-byte codes");
+    static_assert(!CB || XS, "contiguous blocks: staged activations");
     constexpr int NQ = 2 * L;                  // loads per tile = 64-K steps of the slice
     constexpr int NX = I8 ? NQ : 2 * NQ;       // B operand registers (16 bytes each) of the slice
     constexpr int DMAX = (I8 && L <= 6) ? 3 : 2;
@@ -63,10 +70,19 @@ __global__ __launch_bounds__(64 * kKsWaves) void gemv_ks_kernel(const KsArgs a) 
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int mi = lane & 15, mg = lane >> 4, lr = lane >> 3, lp = lane & 7;
     const int64_t G = gridDim.x, wg = blockIdx.x;
+    // CB: the block's first row and its rows (at least one run: G never
+    // exceeds the runs)
+    const int64_t cb_first = 4 * (wg * a.rbase + (wg < a.rrem ? wg : a.rrem));
+    const int64_t cb_rows = 4 * (a.rbase + (wg < a.rrem ? 1 : 0));
     // row of the workgroup's j-th row, or -1 past its range
     auto row = [&](int64_t j) -> int64_t {
-        const int64_t n = 4 * ((j >> 2) * G + wg) + (j & 3);
-        return (j < a.R && n < a.N) ? n : -1;
+        if constexpr (CB) {
+            const int64_t n = cb_first + j;
+            return (j < cb_rows && n < a.N) ? n : -1;
+        } else {
+            const int64_t n = 4 * ((j >> 2) * G + wg) + (j & 3);
+            return (j < a.R && n < a.N) ? n : -1;
+        }
     };
     const int64_t k0 = (int64_t)wv * (L * 128);
     const uint8_t* wb = a.w + k0 + 16 * lp;
@@ -74,10 +90,10 @@ __global__ __launch_bounds__(64 * kKsWaves) void gemv_ks_kernel(const KsArgs a) 
     // load j of a tile: line j/2 of rows 8*(j%2) + lane/8.  Rows past the
     // range read the tile's first row instead (the same lines as a lane of
     // the same or the previous load, so no extra HBM traffic), or the
-    // workgroup's first row 4*wg when the whole tile is past the range; they
-    // are never stored.
+    // workgroup's first row when the whole tile is past the range; they are
+    // never stored.
     auto load_tile = [&](u32x4_t (&buf)[NQ], int t) {
-        const int64_t r0 = row(16 * t), fb = r0 >= 0 ? r0 : 4 * wg;
+        const int64_t r0 = row(16 * t), fb = r0 >= 0 ? r0 : (CB ? cb_first : 4 * wg);
         const int64_t ra = row(16 * t + lr), rb = row(16 * t + 8 + lr);
         const uint8_t* p0 = wb + (ra >= 0 ? ra : fb) * a.ldw;
         const uint8_t* p1 = wb + (rb >= 0 ? rb : fb) * a.ldw;
@@ -195,7 +211,7 @@ __global__ __launch_bounds__(64 * kKsWaves) void gemv_ks_kernel(const KsArgs a) 
 #pragma unroll
         for (int q = 1; q < kKsWaves; ++q) acc += part[t][q][lane];
         if (mi >= a.M) continue;
-        // rows n0 .. n0+3 (one run; R is a multiple of 4, so only N can cut it)
+        // rows n0 .. n0+3 (one run; blocks are whole runs, so only N can cut it)
         const int64_t n0 = row(16 * t + 4 * mg);
         if (n0 < 0) continue;
         const int nv = a.N - n0 < 4 ? (int)(a.N - n0) : 4;

@@ -49,6 +49,10 @@ def _i8(ql, orc, M, N, K, seed, w_pad=0, bias=False):
     (7, 30000, 2048),   # more than six tiles per unit: 313 workgroups of 96 rows
     (16, 1, 2048),      # one row
     (3, 17, 2048),      # two workgroups, 9 and 8 rows
+    # from 12 tokens the rows are split into contiguous blocks
+    (16, 30000, 2048),  # 313 blocks of 23 runs, the first 301 with one more
+    (12, 17, 2048),     # two blocks, 3 runs and 2 runs (the last one row)
+    (13, 17412, 5120),  # 4353 runs: one block of 18, the rest 17
 ])
 def test_ks_int8_tiles_and_slices(ql, orc, M, N, K):
     _i8(ql, orc, M, N, K, seed=M * 7 + N)
@@ -123,6 +127,10 @@ def _w8a8(ql, orc, M, N, K, seed, per_channel=True, per_token=True, w_pad=0, x_f
     (16, 16500, 2048),  # L=2, T=5
     (4, 21000, 2048),   # L=2, T=6
     (7, 30000, 2048),   # 313 workgroups
+    # from 8 tokens the rows are split into contiguous blocks
+    (8, 30000, 2048),   # 313 blocks
+    (9, 17, 2048),      # two blocks
+    (16, 17412, 5120),  # one block of 18 runs, the rest 17
 ])
 def test_ks_w8a8_tiles_and_slices(ql, orc, M, N, K):
     _w8a8(ql, orc, M, N, K, seed=M + N)
