@@ -382,16 +382,16 @@ bool ks_plan(int64_t N, int64_t K, int lmax, KsPlan& p) {
 constexpr int kKsMaxLI8 = 8;     // INT8 holds 2L + 3 * 2L 16-byte registers per lane
 constexpr int kKsMaxLFloat = 5;  // the float kinds hold 4L + 2 * 2L
 
-template <int KIND, int L, int XF, int WF, bool XS = false, bool CB = false>
+template <int KIND, int L, int XF, int WF, bool XS = false, int LAYOUT = kKsTurn>
 hipError_t run_ks_t(const KsArgs& a, const KsPlan& p, hipStream_t st) {
     const dim3 grid(p.G), block(64 * kKsWaves);
     switch (p.T) {
-        case 1: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 1, XF, WF, XS, CB>), grid, block, 0, st, a); break;
-        case 2: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 2, XF, WF, XS, CB>), grid, block, 0, st, a); break;
-        case 3: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 3, XF, WF, XS, CB>), grid, block, 0, st, a); break;
-        case 4: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 4, XF, WF, XS, CB>), grid, block, 0, st, a); break;
-        case 5: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 5, XF, WF, XS, CB>), grid, block, 0, st, a); break;
-        default: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 6, XF, WF, XS, CB>), grid, block, 0, st, a); break;
+        case 1: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 1, XF, WF, XS, LAYOUT>), grid, block, 0, st, a); break;
+        case 2: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 2, XF, WF, XS, LAYOUT>), grid, block, 0, st, a); break;
+        case 3: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 3, XF, WF, XS, LAYOUT>), grid, block, 0, st, a); break;
+        case 4: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 4, XF, WF, XS, LAYOUT>), grid, block, 0, st, a); break;
+        case 5: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 5, XF, WF, XS, LAYOUT>), grid, block, 0, st, a); break;
+        default: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 6, XF, WF, XS, LAYOUT>), grid, block, 0, st, a); break;
     }
     return hipGetLastError();
 }
@@ -406,37 +406,51 @@ bool ks_stage_x(const KsArgs& a, const KsPlan& p) {
     return a.M >= kKsStageXMinM && p.L <= 5 && (int64_t)(a.M - 1) * a.ldx + 1024 * p.L <= INT32_MAX;
 }
 
-// Contiguous row blocks (CB) for the staged kernels from kKsContigMinM
-// tokens (17408 x 5120, GEMV alone, against the runs dealt out in turn: INT8
-// M = 4 / 8 / 12 / 16 +0.5 / +0.15 / -0.3 / -0.5 us, FP8 W8A8 ~0 / -0.3..0 /
-// -0.4 / -0.55..-0.7 us; the unstaged weight-only kernel was 0.5-0.7 us
-// slower at every M with them, and does not use them).
-constexpr int64_t kKsContigMinM = 12;
-bool ks_contig(int kind, int64_t M) { return kind != kKsF8 && M >= kKsContigMinM; }
+// Row layout per kind and token count (17408 x 5120, GEMV alone, against
+// the runs dealt out in turn): INT8 with contiguous blocks +0.5 / +0.15 /
+// -0.3 / -0.5 us at M = 4 / 8 / 12 / 16 (with bands -0.0..-0.3 from 12 but
+// +0.5 at 4); FP8 W8A8 with bands ~0 / -0.4 / -0.4 / -0.7 us; E4M3
+// weight-only with bands ~0 / ~0 / -0.4 / -0.7 us (with blocks +0.5 to +0.7
+// at every M).
+int ks_layout(int kind, int64_t M) {
+    if (kind == kKsI8) return M >= 12 ? kKsBlocks : kKsTurn;
+    if (kind == kKsW8A8) return M >= 8 ? kKsBands : kKsTurn;
+    return M >= 12 ? kKsBands : kKsTurn;
+}
 
-template <int KIND, int XF, int WF, bool CB>
-hipError_t run_ks_staged(const KsArgs& a, const KsPlan& p, hipStream_t st) {
+template <int KIND, int XF, int WF, bool XS, int LAYOUT>
+hipError_t run_ks_l(const KsArgs& a, const KsPlan& p, hipStream_t st) {
     switch (p.L) {
-        case 2: return run_ks_t<KIND, 2, XF, WF, true, CB>(a, p, st);
-        case 3: return run_ks_t<KIND, 3, XF, WF, true, CB>(a, p, st);
-        case 4: return run_ks_t<KIND, 4, XF, WF, true, CB>(a, p, st);
-        default: return run_ks_t<KIND, 5, XF, WF, true, CB>(a, p, st);
+        case 2: return run_ks_t<KIND, 2, XF, WF, XS, LAYOUT>(a, p, st);
+        case 3: return run_ks_t<KIND, 3, XF, WF, XS, LAYOUT>(a, p, st);
+        case 4: return run_ks_t<KIND, 4, XF, WF, XS, LAYOUT>(a, p, st);
+        default: return run_ks_t<KIND, 5, XF, WF, XS, LAYOUT>(a, p, st);  // L <= 5 on these paths
     }
 }
 
 template <int KIND, int XF = kFmtE4M3, int WF = kFmtE4M3>
 hipError_t run_ks(const KsArgs& a, const KsPlan& p, hipStream_t st) {
+    const int layout = ks_layout(KIND, a.M);
+    KsArgs b = a;
+    const int64_t runs = (a.N + 3) / 4;
+    if (layout == kKsBlocks) {
+        b.rbase = runs / p.G;
+        b.rrem = runs - b.rbase * p.G;
+    } else if (layout == kKsBands) {
+        b.rbase = runs / (4 * (int64_t)p.G);
+        b.rrem = 0;
+    }
     if constexpr (KIND != kKsF8) {
         if (ks_stage_x(a, p)) {
-            if (ks_contig(KIND, a.M)) {
-                KsArgs b = a;
-                const int64_t runs = (a.N + 3) / 4;
-                b.rbase = runs / p.G;
-                b.rrem = runs - b.rbase * p.G;
-                return run_ks_staged<KIND, XF, WF, true>(b, p, st);
+            if constexpr (KIND == kKsI8) {
+                if (layout == kKsBlocks) return run_ks_l<KIND, XF, WF, true, kKsBlocks>(b, p, st);
+            } else {
+                if (layout == kKsBands) return run_ks_l<KIND, XF, WF, true, kKsBands>(b, p, st);
             }
-            return run_ks_staged<KIND, XF, WF, false>(a, p, st);
+            return run_ks_l<KIND, XF, WF, true, kKsTurn>(a, p, st);
         }
+    } else {
+        if (layout == kKsBands && p.L <= 5) return run_ks_l<KIND, XF, WF, false, kKsBands>(b, p, st);
     }
     switch (p.L) {
         case 2: return run_ks_t<KIND, 2, XF, WF>(a, p, st);

@@ -14,8 +14,8 @@ namespace qlin {
 // N is small); workgroup b owns the runs of 4 rows b, b + G, b + 2G, ...
 // (row j of the workgroup is n = 4*((j/4)*G + b) + j%4, j < R, so that no
 // workgroup has more than one run above another and a lane's 4 output rows
-// are adjacent), or with CB a contiguous block of them (see CB below), taken
-// as T tiles of 16.  Each of its 8 waves owns one eighth of K (L lines of 128
+// are adjacent), or in one of two other layouts (LAYOUT below), taken as T
+// tiles of 16.  Each of its 8 waves owns one eighth of K (L lines of 128
 // bytes) for the whole kernel: it loads its slice of the M token rows once,
 // into registers in the MFMA B layout (one-byte codes from 4 tokens on
 // through an LDS stage, see XS below), then streams its slice of the T weight
@@ -31,6 +31,11 @@ constexpr int kKsI8 = 0;      // INT8 codes x INT8 codes, int32 sums
 constexpr int kKsF8 = 1;      // E4M3 weights x bf16 activations, fp32 sums
 constexpr int kKsW8A8 = 2;    // FP8 weights (WF) x FP8 activation codes (XF), fp32 sums
 constexpr int kKsWaves = 8;   // waves per workgroup = K slices
+// Row layouts (runs = ceil(N/4) runs of 4 rows; G workgroups)
+constexpr int kKsTurn = 0;    // the runs dealt out in turn: workgroup b takes runs b, b + G, ...
+constexpr int kKsBlocks = 1;  // G contiguous blocks of floor(runs/G) runs or one more (the first runs mod G)
+constexpr int kKsBands = 2;   // whole 16-row tiles dealt out in turn (floor(runs/4G) each), then the
+                              // remaining runs in turn
 constexpr int kKsMaxTiles = 6;
 constexpr int kKsPitch = 128 + 16;  // LDS row pitch of the transpose column (the pad spreads banks)
 
@@ -42,7 +47,7 @@ struct KsArgs {
     const float* ws; int ws_step;
     const uint16_t* bias;            // INT8: optional bf16 bias
     void* y; int64_t ldy; int out_kind;  // INT8: out_kind 1 stores the raw int32 sums
-    int64_t rbase, rrem;                 // CB: ceil(N/4) runs = rbase * gridDim.x + rrem
+    int64_t rbase, rrem;                 // blocks: runs = rbase * G + rrem; bands: rbase = full tiles each
 };
 
 // XS (one-byte activation codes: INT8, FP8 W8A8): the wave's activation
@@ -50,15 +55,15 @@ struct KsArgs {
 // one 128-byte line of 8 token rows (instead of 16 rows x 64 bytes per
 // register load), the weight tiles' loads queue behind it, and the B
 // operands are read back from LDS (M = 16, INT8: 18.6 -> 17.7 us).
-// CB (with XS): the runs are split into G contiguous blocks whose sizes differ
-// by at most one run (the first rrem workgroups take one more), so workgroup
-// b's rows are 4*P_b, 4*P_b + 1, ... with P_b = b*rbase + min(b, rrem), and a
-// tile's outputs are 16 adjacent rows.
-template <int KIND, int L, int T, int XF = kFmtE4M3, int WF = kFmtE4M3, bool XS = false, bool CB = false>
+// LAYOUT: kKsTurn keeps no workgroup more than one run above another and
+// streams one band of rows per tile step; kKsBlocks (workgroup b's rows are
+// 4*P_b, 4*P_b + 1, ... with P_b = b*rbase + min(b, rrem)) and kKsBands
+// (tile t < rbase of workgroup b is rows 16*(t*G + b) .. +15) make a tile's
+// outputs 16 adjacent rows, with the same balance.
+template <int KIND, int L, int T, int XF = kFmtE4M3, int WF = kFmtE4M3, bool XS = false, int LAYOUT = kKsTurn>
 __global__ __launch_bounds__(64 * kKsWaves) void gemv_ks_kernel(const KsArgs a) {
     constexpr bool I8 = KIND == kKsI8;
     static_assert(!XS || KIND != kKsF8, "activation staging: one-byte codes");
-    static_assert(!CB || XS, "contiguous blocks: staged activations");
     constexpr int NQ = 2 * L;                  // loads per tile = 64-K steps of the slice
     constexpr int NX = I8 ? NQ : 2 * NQ;       // B operand registers (16 bytes each) of the slice
     constexpr int DMAX = (I8 && L <= 6) ? 3 : 2;
@@ -70,15 +75,25 @@ __global__ __launch_bounds__(64 * kKsWaves) void gemv_ks_kernel(const KsArgs a) 
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int mi = lane & 15, mg = lane >> 4, lr = lane >> 3, lp = lane & 7;
     const int64_t G = gridDim.x, wg = blockIdx.x;
-    // CB: the block's first row and its rows (at least one run: G never
+    // blocks: the block's first row and its rows (at least one run: G never
     // exceeds the runs)
     const int64_t cb_first = 4 * (wg * a.rbase + (wg < a.rrem ? wg : a.rrem));
     const int64_t cb_rows = 4 * (a.rbase + (wg < a.rrem ? 1 : 0));
-    // row of the workgroup's j-th row, or -1 past its range
+    // row of the workgroup's j-th row, or -1 past its range (a run past the
+    // last one starts at or beyond N)
     auto row = [&](int64_t j) -> int64_t {
-        if constexpr (CB) {
+        if constexpr (LAYOUT == kKsBlocks) {
             const int64_t n = cb_first + j;
             return (j < cb_rows && n < a.N) ? n : -1;
+        } else if constexpr (LAYOUT == kKsBands) {
+            const int64_t t = j >> 4;
+            if (t < a.rbase) {
+                const int64_t n = 16 * (t * G + wg) + (j & 15);
+                return n < a.N ? n : -1;
+            }
+            const int64_t jj = j - 16 * a.rbase;
+            const int64_t n = 4 * (4 * G * a.rbase + (jj >> 2) * G + wg) + (jj & 3);
+            return n < a.N ? n : -1;
         } else {
             const int64_t n = 4 * ((j >> 2) * G + wg) + (j & 3);
             return (j < a.R && n < a.N) ? n : -1;
@@ -93,7 +108,7 @@ __global__ __launch_bounds__(64 * kKsWaves) void gemv_ks_kernel(const KsArgs a) 
     // workgroup's first row when the whole tile is past the range; they are
     // never stored.
     auto load_tile = [&](u32x4_t (&buf)[NQ], int t) {
-        const int64_t r0 = row(16 * t), fb = r0 >= 0 ? r0 : (CB ? cb_first : 4 * wg);
+        const int64_t r0 = row(16 * t), fb = r0 >= 0 ? r0 : (LAYOUT == kKsBlocks ? cb_first : 4 * wg);
         const int64_t ra = row(16 * t + lr), rb = row(16 * t + 8 + lr);
         const uint8_t* p0 = wb + (ra >= 0 ? ra : fb) * a.ldw;
         const uint8_t* p1 = wb + (rb >= 0 ? rb : fb) * a.ldw;

@@ -88,6 +88,10 @@ def test_ks_int8_decode_shape_is_deterministic(ql):
     (4, 21000, 2048),   # L=2, T=6
     (7, 30000, 2048),   # 313 workgroups
     (9, 1, 5120),
+    # from 12 tokens whole 16-row tiles are dealt out in turn, then the runs left
+    (12, 30000, 2048),  # 313 workgroups: 5 whole tiles each, then 3 or 4 of the 1240 runs left
+    (16, 17, 2048),     # two workgroups, no whole tiles
+    (13, 17412, 5120),  # 4 whole tiles each, then 257 runs
 ])
 def test_ks_fp8_tiles_and_slices(ql, orc, M, N, K):
     d = gen_fp8(M, N, K, seed=M + N)
@@ -127,10 +131,10 @@ def _w8a8(ql, orc, M, N, K, seed, per_channel=True, per_token=True, w_pad=0, x_f
     (16, 16500, 2048),  # L=2, T=5
     (4, 21000, 2048),   # L=2, T=6
     (7, 30000, 2048),   # 313 workgroups
-    # from 8 tokens the rows are split into contiguous blocks
-    (8, 30000, 2048),   # 313 blocks
-    (9, 17, 2048),      # two blocks
-    (16, 17412, 5120),  # one block of 18 runs, the rest 17
+    # from 8 tokens whole 16-row tiles are dealt out in turn, then the runs left
+    (8, 30000, 2048),   # 313 workgroups: 5 whole tiles each, then 3 or 4 of the 1240 runs left
+    (9, 17, 2048),      # two workgroups, no whole tiles
+    (16, 17412, 5120),  # 4 whole tiles each, then 257 runs (one workgroup takes two)
 ])
 def test_ks_w8a8_tiles_and_slices(ql, orc, M, N, K):
     _w8a8(ql, orc, M, N, K, seed=M + N)
