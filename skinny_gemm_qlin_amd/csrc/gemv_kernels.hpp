@@ -651,6 +651,12 @@ __global__ __launch_bounds__(64 * WPB) void gemv_fp8_m1_lds_kernel(
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_barrier();  // not __syncthreads(): that would also wait for the weights
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    // The scales are waited for here, under the weight loads: left to
+    // itself the compiler sinks their scalar loads into the store's branch,
+    // a round trip after the dot product (E4M3 weight-only 17408 x 5120:
+    // 14.6 -> 14.5 us per-channel, 14.85 -> 14.6-14.75 us per-tensor).
+    const float xsv = W8A8 ? xs[0] : 1.0f;
+    asm volatile("" ::"s"(wsv), "s"(xsv));
     // 4. the row's dot product
     float acc = 0.0f;
 #pragma unroll
@@ -669,7 +675,7 @@ __global__ __launch_bounds__(64 * WPB) void gemv_fp8_m1_lds_kernel(
     }
     acc = group_sum<64>(acc);
     if (lane == 0 && n < N) {
-        const float t = W8A8 ? (acc * xs[0]) * wsv : acc * wsv;
+        const float t = W8A8 ? (acc * xsv) * wsv : acc * wsv;
         y[n] = f32_to_bf16(t);
     }
 }
