@@ -16,8 +16,12 @@ describes the dominant kernel (the GEMV): algorithmic bytes per launch /
 mean launch duration, from HIP events recorded on the stream the kernel runs
 on around a batch of back-to-back launches (rotating weight copies) per M.
 All timed launches are replayed from HIP graphs, so the host's per-call
-overhead is not in the measurement.  `cpu_baseline` times the CPU oracle (oracle/, plain C,
-OpenMP over rows) on the host on the same workload.
+overhead is not in the measurement.  The whole-step region replays graphs of
+--graph-steps consecutive steps (default 10, as a decode step's graph holds
+many layers); each replay of a graph adds a fixed cost of several
+microseconds, which --graph-steps 1 charges to every step.
+`cpu_baseline` times the CPU oracle (oracle/, plain C, OpenMP over rows) on
+the host on the same workload.
 
 Other workloads (--workload fp8_decode | fp8_w8a8 | fp8_blk | moe_mxfp4 |
 moe_ffn_mxfp4) time the other
@@ -160,6 +164,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--graph-steps", type=int, default=10,
+                    help="steps captured in one HIP graph for the timed region (one replay per graph)")
     ap.add_argument("--workload", default="int8_decode",
                     choices=["int8_decode", "fp8_decode", "fp8_w8a8", "fp8_blk", "moe_mxfp4", "moe_ffn_mxfp4",
                              "int8_prefill", "int8_prefill_smalln", "fp8_prefill", "moe_prefill"])
@@ -342,25 +348,42 @@ def main():
         run_step(s)
     torch.cuda.synchronize()
 
-    # one graph per step offset: step s uses weight copies (s*len(Ms)+i) % B
-    step_graphs = []
-    for s in range(B):
+    # step s uses weight copies (s*len(Ms)+i) % B.  The timed steps are replayed
+    # from graphs of `graph_steps` consecutive steps each (the last graph holds
+    # the remainder), one graph per distinct starting copy offset.
+    S = max(1, min(args.graph_steps, args.steps))
+
+    def step_fns(s):
         fns = []
         for i, M in enumerate(Ms):
             fns += [fn for _, _, fn in launches(M, (s * len(Ms) + i) % B)]
-        step_graphs.append(capture(fns))
-    for s in range(args.warmup):
-        step_graphs[s % B].replay()
+        return fns
+
+    graphs = {}
+
+    def chunk_graph(s0, n):
+        key = ((s0 * len(Ms)) % B, n)
+        if key not in graphs:
+            fns = []
+            for s in range(s0, s0 + n):
+                fns += step_fns(s)
+            graphs[key] = capture(fns)
+        return graphs[key]
+
+    chunks = [(s0, min(S, args.steps - s0)) for s0 in range(0, args.steps, S)]
+    plan = [chunk_graph(s0, n) for s0, n in chunks]
+    for g in plan[:max(1, -(-args.warmup // S))]:
+        g.replay()
     torch.cuda.synchronize()
 
     # timed region A: the whole job, args.steps steps
-    log(f"bench: timing {args.steps} steps")
+    log(f"bench: timing {args.steps} steps ({len(plan)} graph replays of up to {S} steps)")
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for s in range(args.steps):
-        step_graphs[s % B].replay()
+    for g in plan:
+        g.replay()
     end.record(stream)
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(end)
@@ -518,7 +541,8 @@ def main():
                        f"E={spec.get('E')} N={N} K={K}",
         "moe_ffn_mxfp4": f"MXFP4 top-{spec.get('topk')} expert FFN with routing E={spec.get('E')} "
                          f"H={N} I={spec.get('I')} (router, gate/up+SwiGLU, down, combine)",
-    }[wl], "N": N, "K": K, "Ms": Ms, "weight_copies": B, "cold_weights": B * wbytes >= 2 * MALL_BYTES}
+    }[wl], "N": N, "K": K, "Ms": Ms, "weight_copies": B, "cold_weights": B * wbytes >= 2 * MALL_BYTES,
+           "graph_steps": S}
     if wl in ("moe_mxfp4", "moe_ffn_mxfp4", "moe_prefill"):
         cfg["live_experts"] = int(live)
     if args.bias:
