@@ -50,6 +50,60 @@ struct KsArgs {
     int64_t rbase, rrem;                 // blocks: runs = rbase * G + rrem; bands: rbase = full tiles each
 };
 
+// The workgroup's rows in the chosen LAYOUT: rows(j) is the row of its j-th
+// row, or -1 past its range (a run past the last one starts at or beyond N).
+template <int LAYOUT>
+struct KsRows {
+    int64_t G, wg, N, R, rbase, first, count;
+    __device__ explicit KsRows(const KsArgs& a)
+        : G(gridDim.x), wg(blockIdx.x), N(a.N), R(a.R), rbase(a.rbase) {
+        // blocks: the block's first row and its rows (at least one run: G
+        // never exceeds the runs)
+        first = 4 * (wg * a.rbase + (wg < a.rrem ? wg : a.rrem));
+        count = 4 * (a.rbase + (wg < a.rrem ? 1 : 0));
+    }
+    __device__ int64_t operator()(int64_t j) const {
+        if constexpr (LAYOUT == kKsBlocks) {
+            const int64_t n = first + j;
+            return (j < count && n < N) ? n : -1;
+        } else if constexpr (LAYOUT == kKsBands) {
+            const int64_t t = j >> 4;
+            if (t < rbase) {
+                const int64_t n = 16 * (t * G + wg) + (j & 15);
+                return n < N ? n : -1;
+            }
+            const int64_t jj = j - 16 * rbase;
+            const int64_t n = 4 * (4 * G * rbase + (jj >> 2) * G + wg) + (jj & 3);
+            return n < N ? n : -1;
+        } else {
+            const int64_t n = 4 * ((j >> 2) * G + wg) + (j & 3);
+            return (j < R && n < N) ? n : -1;
+        }
+    }
+    // the row read in place of rows past the range when a whole tile is past it
+    __device__ int64_t spare() const { return LAYOUT == kKsBlocks ? first : 4 * wg; }
+};
+
+// Load j of tile t (8 rows x 128 bytes per instruction): line j/2 of rows
+// 8*(j%2) + lane/8 of the wave's K slice (wb = the slice's first byte plus
+// the lane's 16-byte chunk).  Rows past the range read the tile's first row
+// instead (the same lines as a lane of the same or the previous load, so no
+// extra HBM traffic), or spare() when the whole tile is past the range; they
+// are never stored.
+template <int L, int LAYOUT>
+__device__ __forceinline__ void ks_load_tile(u32x4_t (&buf)[2 * L], const KsRows<LAYOUT>& row, const uint8_t* wb,
+                                             int64_t ldw, int t, int lr) {
+    const int64_t r0 = row(16 * t), fb = r0 >= 0 ? r0 : row.spare();
+    const int64_t ra = row(16 * t + lr), rb = row(16 * t + 8 + lr);
+    const uint8_t* p0 = wb + (ra >= 0 ? ra : fb) * ldw;
+    const uint8_t* p1 = wb + (rb >= 0 ? rb : fb) * ldw;
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+        buf[2 * j] = ld_stream(p0 + 128 * j);
+        buf[2 * j + 1] = ld_stream(p1 + 128 * j);
+    }
+}
+
 // XS (one-byte activation codes: INT8, FP8 W8A8): the wave's activation
 // slice goes to LDS first, by buffer loads with the LDS bit that each cover
 // one 128-byte line of 8 token rows (instead of 16 rows x 64 bytes per
@@ -74,50 +128,11 @@ __global__ __launch_bounds__(64 * kKsWaves) void gemv_ks_kernel(const KsArgs a) 
     __shared__ __align__(16) uint8_t xst[XS ? kKsWaves : 1][XS ? NQ * 1024 : 16];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int mi = lane & 15, mg = lane >> 4, lr = lane >> 3, lp = lane & 7;
-    const int64_t G = gridDim.x, wg = blockIdx.x;
-    // blocks: the block's first row and its rows (at least one run: G never
-    // exceeds the runs)
-    const int64_t cb_first = 4 * (wg * a.rbase + (wg < a.rrem ? wg : a.rrem));
-    const int64_t cb_rows = 4 * (a.rbase + (wg < a.rrem ? 1 : 0));
-    // row of the workgroup's j-th row, or -1 past its range (a run past the
-    // last one starts at or beyond N)
-    auto row = [&](int64_t j) -> int64_t {
-        if constexpr (LAYOUT == kKsBlocks) {
-            const int64_t n = cb_first + j;
-            return (j < cb_rows && n < a.N) ? n : -1;
-        } else if constexpr (LAYOUT == kKsBands) {
-            const int64_t t = j >> 4;
-            if (t < a.rbase) {
-                const int64_t n = 16 * (t * G + wg) + (j & 15);
-                return n < a.N ? n : -1;
-            }
-            const int64_t jj = j - 16 * a.rbase;
-            const int64_t n = 4 * (4 * G * a.rbase + (jj >> 2) * G + wg) + (jj & 3);
-            return n < a.N ? n : -1;
-        } else {
-            const int64_t n = 4 * ((j >> 2) * G + wg) + (j & 3);
-            return (j < a.R && n < a.N) ? n : -1;
-        }
-    };
+    const KsRows<LAYOUT> row(a);
     const int64_t k0 = (int64_t)wv * (L * 128);
     const uint8_t* wb = a.w + k0 + 16 * lp;
     uint8_t* cp = col[wv];
-    // load j of a tile: line j/2 of rows 8*(j%2) + lane/8.  Rows past the
-    // range read the tile's first row instead (the same lines as a lane of
-    // the same or the previous load, so no extra HBM traffic), or the
-    // workgroup's first row when the whole tile is past the range; they are
-    // never stored.
-    auto load_tile = [&](u32x4_t (&buf)[NQ], int t) {
-        const int64_t r0 = row(16 * t), fb = r0 >= 0 ? r0 : (LAYOUT == kKsBlocks ? cb_first : 4 * wg);
-        const int64_t ra = row(16 * t + lr), rb = row(16 * t + 8 + lr);
-        const uint8_t* p0 = wb + (ra >= 0 ? ra : fb) * a.ldw;
-        const uint8_t* p1 = wb + (rb >= 0 ? rb : fb) * a.ldw;
-#pragma unroll
-        for (int j = 0; j < L; ++j) {
-            buf[2 * j] = ld_stream(p0 + 128 * j);
-            buf[2 * j + 1] = ld_stream(p1 + 128 * j);
-        }
-    };
+    auto load_tile = [&](u32x4_t (&buf)[NQ], int t) { ks_load_tile<L, LAYOUT>(buf, row, wb, a.ldw, t, lr); };
 
     if constexpr (XS) {
         // load 2j + hh: line j of token rows 8hh + lane/8 (token 0 past M),
