@@ -75,6 +75,8 @@ def test_blk_act_quant_edge_values(ql, orc):
     x[1, 640:768] *= 3e25  # E ~ 202; the result stays inside the fp32/bf16 range
     x[2, 768:896] = np.where(np.arange(128) % 2 == 0, 1e-6, -1e-6)
     x[2, 800] = 100.0
+    x[2, 1024:1152] *= 1e-38  # below every exponent byte above 0: E clamped at 1
+    x[2, 1152:1280] *= 1e-40  # bf16 subnormals
     d = {"x": bf16_bits(x), "w": rng.integers(0, 0x7E, (130, K)).astype(np.uint8),
          "ws": rng.integers(110, 140, (2, K // 128)).astype(np.uint8)}
     assert np.all(np.isfinite(bf16_values(orc.fp8_blk(d["x"], d["w"], d["ws"])[2])))
@@ -144,6 +146,8 @@ def test_blk_act_quant_edge_values_one_token(ql, orc):
     x[1, 640:768] *= 3e25
     x[2, 768:896] = np.where(np.arange(128) % 2 == 0, 1e-6, -1e-6)
     x[2, 800] = 100.0
+    x[2, 1024:1152] *= 1e-38  # below every exponent byte above 0: E clamped at 1
+    x[2, 1152:1280] *= 1e-40  # bf16 subnormals
     w = rng.integers(0, 0x7E, (130, K)).astype(np.uint8)
     ws = rng.integers(110, 140, (2, K // 128)).astype(np.uint8)
     for r in range(3):

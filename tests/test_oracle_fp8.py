@@ -105,6 +105,32 @@ def test_blk_act_quant_zero_group(orc):
     assert np.all(xq[1, 128:] == 0x7C)
 
 
+def test_blk_act_quant_exponent_clamp(orc):
+    # groups too small for any exponent byte above 0: the exponent stays at
+    # its lower clamp E = 1 (scale 2^-126) and the codes are x * 2^126;
+    # bf16 subnormals included
+    rng = np.random.default_rng(24)
+    g = rng.standard_normal((3, 128)).astype(np.float32)
+    g[0] *= np.float32(1e-38)
+    g[1] *= np.float32(1e-40)
+    g[2, :] = 0.0
+    g[2, 5] = np.float32(2.0 ** -133)  # one subnormal value, the rest zero
+    x = bf16_bits(g)
+    xq, xs = orc.blk_act_quant(x)
+    xf = bf16_values(x).astype(np.float64)
+    for m in range(3):
+        amax = np.abs(xf[m]).max()
+        assert 0.0 < amax <= 448.0 * 2.0 ** -126
+        assert xs[m, 0] == 1
+        v = (xf[m] * 2.0 ** 126).astype(np.float32)
+        ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(xq[m], ref)
+    # just above the clamp the rule applies again: amax in (448 * 2^-126, 448 * 2^-125] gives E = 2
+    x2 = bf16_bits(np.full((1, 128), 448.0 * 2.0 ** -125, np.float32))
+    _, xs2 = orc.blk_act_quant(x2)
+    assert xs2[0, 0] == 2
+
+
 # ----------------------------------------------------------------------------- block GEMV
 
 def test_blk_unit_scales_reduce_to_plain_gemv(orc):
