@@ -6,7 +6,7 @@ import pytest
 import torch
 
 from gpu_util import dev, dev_bf16, host, host_bits, lib, need_gpu, padded
-from parity import check_float
+from oracle.compare import check_float
 from skinny_gemm_qlin_amd.inputs import bf16_bits, bf16_values, gen_fp8_blk
 
 pytestmark = pytest.mark.gpu

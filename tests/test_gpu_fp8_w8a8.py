@@ -7,7 +7,7 @@ import pytest
 import torch
 
 from gpu_util import dev, dev_bf16, host, host_bits, lib, need_gpu, padded
-from parity import bf16_to_f64, check_float
+from oracle.compare import bf16_to_f64, check_float
 from skinny_gemm_qlin_amd.inputs import bf16_bits, gen_fp8_w8a8
 
 pytestmark = pytest.mark.gpu

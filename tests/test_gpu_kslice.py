@@ -11,7 +11,7 @@ import pytest
 import torch
 
 from gpu_util import dev, dev_bf16, host, host_bits, lib, need_gpu, padded
-from parity import check_float
+from oracle.compare import check_float
 from skinny_gemm_qlin_amd.inputs import bf16_bits, gen_fp8, gen_fp8_w8a8, gen_int8
 
 pytestmark = pytest.mark.gpu

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 from gpu_util import dev, dev_bf16, host_bits, lib, need_gpu
-from parity import bf16_to_f64, check_float
+from oracle.compare import bf16_to_f64, check_float
 from skinny_gemm_qlin_amd.inputs import gen_moe
 
 pytestmark = pytest.mark.gpu

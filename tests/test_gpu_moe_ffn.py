@@ -21,7 +21,7 @@ import pytest
 import torch
 
 from gpu_util import dev, dev_bf16, host, host_bits, lib, need_gpu
-from parity import bf16_to_f64, bf16_ulp, check_float
+from oracle.compare import bf16_to_f64, bf16_ulp, check_float
 from skinny_gemm_qlin_amd.inputs import bf16_values, gen_moe_ffn
 
 pytestmark = pytest.mark.gpu
