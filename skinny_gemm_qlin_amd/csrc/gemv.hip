@@ -134,6 +134,28 @@ hipError_t run_fp8_m1_lds(const void* x, const float* xs, int64_t K, const uint8
     return hipGetLastError();
 }
 
+// E4M3 weight-only, one token, 9 to 16 steps of 1 KB per row (8192 < K <=
+// 16384): the same kernel with every step in flight (4096 x 14336: 21.5 us
+// on the lane-group kernel before).
+constexpr int64_t kM1LdsWideMaxK = 16384;
+
+hipError_t run_fp8_m1_lds_wide(const void* x, int64_t K, const uint8_t* w, int64_t ldw, int64_t N, const float* ws,
+                               int ws_step, uint16_t* y, hipStream_t st) {
+#define QLIN_M1_LDS(U_) launch_fp8_m1_lds_u<0, kFmtE4M3, kFmtE4M3, U_>(x, nullptr, K, w, ldw, N, ws, ws_step, y, st); break;
+    switch (steps64(K)) {
+        case 9: QLIN_M1_LDS(9)
+        case 10: QLIN_M1_LDS(10)
+        case 11: QLIN_M1_LDS(11)
+        case 12: QLIN_M1_LDS(12)
+        case 13: QLIN_M1_LDS(13)
+        case 14: QLIN_M1_LDS(14)
+        case 15: QLIN_M1_LDS(15)
+        default: QLIN_M1_LDS(16)
+    }
+#undef QLIN_M1_LDS
+    return hipGetLastError();
+}
+
 // INT8, 2..3 tokens (and one token with the quantiser fused in): one wave
 // per row, the token rows' codes shared through LDS (gemv_i8_lds_kernel).
 // 17408 x 5120: M = 2 14.9-15.1 us against 15.7-16.1 us for the lane-group
@@ -360,22 +382,23 @@ int cu_count() {
     return n;
 }
 
-struct KsPlan { int L, T; unsigned G; int64_t R; };
+struct KsPlan { int L, T; unsigned G; int64_t R; int npass; };
 
 // K = 1024 * L with L in [2, lmax]; G = one workgroup per compute unit, or
-// one per 16 rows when N is small, or more when a workgroup would get more
-// than kKsMaxTiles tiles; the ceil(N/4) runs of 4 rows are dealt out in turn,
-// R = rows per workgroup (a multiple of 4), T = its tiles.
+// one per 16 rows when N is small; the ceil(N/4) runs of 4 rows are dealt
+// out in turn, R = rows per workgroup (a multiple of 4).  A workgroup with
+// more than kKsMaxTiles tiles runs them in npass passes of T tiles (then
+// 4 <= T <= kKsMaxTiles), so the grid never exceeds one workgroup per
+// compute unit (a second round of workgroups: 28672 x 4096, M = 4..16,
+// 27.9-29.2 us against 22.5-26.3 us in two passes).
 bool ks_plan(int64_t N, int64_t K, int lmax, KsPlan& p) {
     if (N < 1 || K % 1024 != 0 || K / 1024 < 2 || K / 1024 > lmax) return false;
     const int64_t runs = (N + 3) / 4;
-    int64_t G = std::min<int64_t>(cu_count(), (N + 15) / 16);
-    int64_t R = 4 * ((runs + G - 1) / G);
-    if ((R + 15) / 16 > kKsMaxTiles) {
-        G = (runs + 4 * kKsMaxTiles - 1) / (4 * kKsMaxTiles);
-        R = 4 * ((runs + G - 1) / G);
-    }
-    p = {(int)(K / 1024), (int)((R + 15) / 16), (unsigned)G, R};
+    const int64_t G = std::min<int64_t>(cu_count(), (N + 15) / 16);
+    const int64_t R = 4 * ((runs + G - 1) / G);
+    const int64_t tiles = (R + 15) / 16;
+    const int64_t npass = (tiles + kKsMaxTiles - 1) / kKsMaxTiles;
+    p = {(int)(K / 1024), (int)((tiles + npass - 1) / npass), (unsigned)G, R, (int)npass};
     return true;
 }
 
@@ -385,6 +408,14 @@ constexpr int kKsMaxLFloat = 5;  // the float kinds hold 4L + 2 * 2L
 template <int KIND, int L, int XF, int WF, bool XS = false, int LAYOUT = kKsTurn>
 hipError_t run_ks_t(const KsArgs& a, const KsPlan& p, hipStream_t st) {
     const dim3 grid(p.G), block(64 * kKsWaves);
+    if (p.npass > 1) {  // then 4 <= T <= kKsMaxTiles
+        switch (p.T) {
+            case 4: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 4, XF, WF, XS, LAYOUT, true>), grid, block, 0, st, a); break;
+            case 5: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 5, XF, WF, XS, LAYOUT, true>), grid, block, 0, st, a); break;
+            default: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 6, XF, WF, XS, LAYOUT, true>), grid, block, 0, st, a); break;
+        }
+        return hipGetLastError();
+    }
     switch (p.T) {
         case 1: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 1, XF, WF, XS, LAYOUT>), grid, block, 0, st, a); break;
         case 2: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 2, XF, WF, XS, LAYOUT>), grid, block, 0, st, a); break;
@@ -432,6 +463,7 @@ template <int KIND, int XF = kFmtE4M3, int WF = kFmtE4M3>
 hipError_t run_ks(const KsArgs& a, const KsPlan& p, hipStream_t st) {
     const int layout = ks_layout(KIND, a.M);
     KsArgs b = a;
+    b.npass = p.npass;
     const int64_t runs = (a.N + 3) / 4;
     if (layout == kKsBlocks) {
         b.rbase = runs / p.G;
@@ -447,22 +479,22 @@ hipError_t run_ks(const KsArgs& a, const KsPlan& p, hipStream_t st) {
             } else {
                 if (layout == kKsBands) return run_ks_l<KIND, XF, WF, true, kKsBands>(b, p, st);
             }
-            return run_ks_l<KIND, XF, WF, true, kKsTurn>(a, p, st);
+            return run_ks_l<KIND, XF, WF, true, kKsTurn>(b, p, st);
         }
     } else {
         if (layout == kKsBands && p.L <= 5) return run_ks_l<KIND, XF, WF, false, kKsBands>(b, p, st);
     }
     switch (p.L) {
-        case 2: return run_ks_t<KIND, 2, XF, WF>(a, p, st);
-        case 3: return run_ks_t<KIND, 3, XF, WF>(a, p, st);
-        case 4: return run_ks_t<KIND, 4, XF, WF>(a, p, st);
-        case 5: return run_ks_t<KIND, 5, XF, WF>(a, p, st);
+        case 2: return run_ks_t<KIND, 2, XF, WF>(b, p, st);
+        case 3: return run_ks_t<KIND, 3, XF, WF>(b, p, st);
+        case 4: return run_ks_t<KIND, 4, XF, WF>(b, p, st);
+        case 5: return run_ks_t<KIND, 5, XF, WF>(b, p, st);
         default:
             if constexpr (KIND == kKsI8) {
                 switch (p.L) {
-                    case 6: return run_ks_t<KIND, 6, XF, WF>(a, p, st);
-                    case 7: return run_ks_t<KIND, 7, XF, WF>(a, p, st);
-                    default: return run_ks_t<KIND, 8, XF, WF>(a, p, st);
+                    case 6: return run_ks_t<KIND, 6, XF, WF>(b, p, st);
+                    case 7: return run_ks_t<KIND, 7, XF, WF>(b, p, st);
+                    default: return run_ks_t<KIND, 8, XF, WF>(b, p, st);
                 }
             }
             return hipErrorInvalidValue;  // not reached: ks_plan caps L per kind
@@ -524,6 +556,8 @@ hipError_t launch_gemv_fp8(const F8Args& a, hipStream_t st) {
         case 1:
             if (a.K <= kM1LdsMaxK)
                 return run_fp8_m1_lds<0>(a.x, nullptr, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.y, st);
+            if (a.K <= kM1LdsWideMaxK)
+                return run_fp8_m1_lds_wide(a.x, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.y, st);
             return run_fp8<1, 32, 2, 1, 1>(a, st);
         default: {
             // K-slice kernels from M = 2 (17408 x 5120: 17.4 against 18.2 us

@@ -571,8 +571,9 @@ __global__ __launch_bounds__(64 * WPB) void gemv_fp8_blk_m1_fq_kernel(
 
 // ------------------------------------------------------------------ one token, activations in LDS
 // M = 1 for FP8 weight-only and FP8 W8A8 [Z100 operator-family table, FP8
-// row; section 2.2].  A wave owns one weight row and keeps all U <= 8 of its
-// 1 KB steps in flight (lane j reads chunk j + 64u), like the INT8 M = 1
+// row; section 2.2].  A wave owns one weight row and keeps all U of its 1 KB
+// steps in flight (lane j reads chunk j + 64u; U <= 8 for W8A8, whose codes
+// are widened through registers, U <= 16 for bf16 activations), like the INT8 M = 1
 // kernel; the workgroup's WPB waves share one copy of the token row in LDS
 // (as bf16), so the activations cost one read per workgroup instead of one
 // per row (re-reading them per row from the caches measured ~2 us slower at
@@ -646,7 +647,7 @@ __global__ __launch_bounds__(64 * WPB) void gemv_fp8_m1_lds_kernel(
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the LDS stores are done
     } else {
-        __builtin_amdgcn_s_waitcnt((U & 15) | 0x70 | 0xF00);  // vmcnt(U)
+        __builtin_amdgcn_s_waitcnt((U & 15) | ((U >> 4) << 14) | 0x70 | 0xF00);  // vmcnt(U)
     }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_barrier();  // not __syncthreads(): that would also wait for the weights

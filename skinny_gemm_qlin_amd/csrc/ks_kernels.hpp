@@ -15,7 +15,7 @@ namespace qlin {
 // (row j of the workgroup is n = 4*((j/4)*G + b) + j%4, j < R, so that no
 // workgroup has more than one run above another and a lane's 4 output rows
 // are adjacent), or in one of two other layouts (LAYOUT below), taken as T
-// tiles of 16.  Each of its 8 waves owns one eighth of K (L lines of 128
+// tiles of 16 (in npass passes of T tiles when a workgroup has more rows).  Each of its 8 waves owns one eighth of K (L lines of 128
 // bytes) for the whole kernel: it loads its slice of the M token rows once,
 // into registers in the MFMA B layout (one-byte codes from 4 tokens on
 // through an LDS stage, see XS below), then streams its slice of the T weight
@@ -48,6 +48,7 @@ struct KsArgs {
     const uint16_t* bias;            // INT8: optional bf16 bias
     void* y; int64_t ldy; int out_kind;  // INT8: out_kind 1 stores the raw int32 sums
     int64_t rbase, rrem;                 // blocks: runs = rbase * G + rrem; bands: rbase = full tiles each
+    int npass = 1;                       // passes of T tiles over the workgroup's rows
 };
 
 // The workgroup's rows in the chosen LAYOUT: rows(j) is the row of its j-th
@@ -114,7 +115,10 @@ __device__ __forceinline__ void ks_load_tile(u32x4_t (&buf)[2 * L], const KsRows
 // 4*P_b, 4*P_b + 1, ... with P_b = b*rbase + min(b, rrem)) and kKsBands
 // (tile t < rbase of workgroup b is rows 16*(t*G + b) .. +15) make a tile's
 // outputs 16 adjacent rows, with the same balance.
-template <int KIND, int L, int T, int XF = kFmtE4M3, int WF = kFmtE4M3, bool XS = false, int LAYOUT = kKsTurn>
+// MP: the workgroup's rows may take more than one pass (a.npass); without it
+// the pass loop folds away and the kernel runs exactly one.
+template <int KIND, int L, int T, int XF = kFmtE4M3, int WF = kFmtE4M3, bool XS = false, int LAYOUT = kKsTurn,
+          bool MP = false>
 __global__ __launch_bounds__(64 * kKsWaves) void gemv_ks_kernel(const KsArgs a) {
     constexpr bool I8 = KIND == kKsI8;
     static_assert(!XS || KIND != kKsF8, "activation staging: one-byte codes");
@@ -208,72 +212,80 @@ __global__ __launch_bounds__(64 * kKsWaves) void gemv_ks_kernel(const KsArgs a) 
         for (int d = 1; d < D; ++d) load_tile(bufs[d], d);
     }
 
+    // pass p covers the workgroup's tiles p*T .. p*T + T - 1 (one pass unless
+    // a workgroup has more rows than T tiles hold)
+    for (int tb = 0;; tb += T) {
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-        u32x4_t (&buf)[NQ] = bufs[t % D];
-        acc_t acc = {};
+        for (int t = 0; t < T; ++t) {
+            u32x4_t (&buf)[NQ] = bufs[t % D];
+            acc_t acc = {};
 #pragma unroll
-        for (int j = 0; j < L; ++j) {
-            *(u32x4_t*)(cp + lr * kKsPitch + 16 * lp) = buf[2 * j];
-            *(u32x4_t*)(cp + (8 + lr) * kKsPitch + 16 * lp) = buf[2 * j + 1];
+            for (int j = 0; j < L; ++j) {
+                *(u32x4_t*)(cp + lr * kKsPitch + 16 * lp) = buf[2 * j];
+                *(u32x4_t*)(cp + (8 + lr) * kKsPitch + 16 * lp) = buf[2 * j + 1];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int s = 2 * j + h;
-                const u32x4_t wa = *(const u32x4_t*)(cp + mi * kKsPitch + 64 * h + 16 * mg);
-                if constexpr (I8) {
-                    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, wa),
-                                                               __builtin_bit_cast(i32x4_t, xb[s]), acc, 0, 0, 0);
-                } else {
-                    bf16x8_t a0, a1;
-                    fp8x16_to_bf16x8x2<WF>(wa, a0, a1);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(bf16x8_t, xb[2 * s]), acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(bf16x8_t, xb[2 * s + 1]), acc, 0, 0, 0);
+                for (int h = 0; h < 2; ++h) {
+                    const int s = 2 * j + h;
+                    const u32x4_t wa = *(const u32x4_t*)(cp + mi * kKsPitch + 64 * h + 16 * mg);
+                    if constexpr (I8) {
+                        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, wa),
+                                                                   __builtin_bit_cast(i32x4_t, xb[s]), acc, 0, 0, 0);
+                    } else {
+                        bf16x8_t a0, a1;
+                        fp8x16_to_bf16x8x2<WF>(wa, a0, a1);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(bf16x8_t, xb[2 * s]), acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(bf16x8_t, xb[2 * s + 1]), acc, 0, 0, 0);
+                    }
                 }
             }
+            part[t][wv][lane] = acc;
+            if (t + D < T) load_tile(buf, tb + t + D);
         }
-        part[t][wv][lane] = acc;
-        if (t + D < T) load_tile(buf, t + D);
-    }
-    __syncthreads();
+        __syncthreads();
 
-    for (int t = wv; t < T; t += kKsWaves) {
-        acc_t acc = part[t][0][lane];
+        for (int t = wv; t < T; t += kKsWaves) {
+            acc_t acc = part[t][0][lane];
 #pragma unroll
-        for (int q = 1; q < kKsWaves; ++q) acc += part[t][q][lane];
-        if (mi >= a.M) continue;
-        // rows n0 .. n0+3 (one run; blocks are whole runs, so only N can cut it)
-        const int64_t n0 = row(16 * t + 4 * mg);
-        if (n0 < 0) continue;
-        const int nv = a.N - n0 < 4 ? (int)(a.N - n0) : 4;
-        if constexpr (I8) {
-            if (a.out_kind == 1) {
-                int32_t* yp = (int32_t*)a.y + mi * a.ldy + n0;
-                for (int r = 0; r < nv; ++r) yp[r] = acc[r];
-                continue;
-            }
-        }
-        uint16_t o[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t n = n0 + (r < nv ? r : 0);
+            for (int q = 1; q < kKsWaves; ++q) acc += part[t][q][lane];
+            if (mi >= a.M) continue;
+            // rows n0 .. n0+3 (one run; blocks are whole runs, so only N can cut it)
+            const int64_t n0 = row(16 * (tb + t) + 4 * mg);
+            if (n0 < 0) continue;
+            const int nv = a.N - n0 < 4 ? (int)(a.N - n0) : 4;
             if constexpr (I8) {
-                float v = (float)acc[r];
-                v = v * a.xs[mi * a.xs_step];
-                v = v * a.ws[n * a.ws_step];
-                o[r] = f32_to_bf16(v);
-                if (a.bias) o[r] = f32_to_bf16(bf16_to_f32(o[r]) + bf16_to_f32(a.bias[n]));
-            } else if constexpr (KIND == kKsW8A8) {
-                float v = acc[r] * a.xs[mi * a.xs_step];
-                v = v * a.ws[n * a.ws_step];
-                o[r] = f32_to_bf16(v);
-            } else {
-                o[r] = f32_to_bf16(acc[r] * a.ws[n * a.ws_step]);
+                if (a.out_kind == 1) {
+                    int32_t* yp = (int32_t*)a.y + mi * a.ldy + n0;
+                    for (int r = 0; r < nv; ++r) yp[r] = acc[r];
+                    continue;
+                }
             }
+            uint16_t o[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t n = n0 + (r < nv ? r : 0);
+                if constexpr (I8) {
+                    float v = (float)acc[r];
+                    v = v * a.xs[mi * a.xs_step];
+                    v = v * a.ws[n * a.ws_step];
+                    o[r] = f32_to_bf16(v);
+                    if (a.bias) o[r] = f32_to_bf16(bf16_to_f32(o[r]) + bf16_to_f32(a.bias[n]));
+                } else if constexpr (KIND == kKsW8A8) {
+                    float v = acc[r] * a.xs[mi * a.xs_step];
+                    v = v * a.ws[n * a.ws_step];
+                    o[r] = f32_to_bf16(v);
+                } else {
+                    o[r] = f32_to_bf16(acc[r] * a.ws[n * a.ws_step]);
+                }
+            }
+            // element-wise stores: one 8-byte store behind a run-time alignment
+            // test measured 28-34 us against 16.4-18.4 us for the whole kernel
+            uint16_t* yp = (uint16_t*)a.y + mi * a.ldy + n0;
+            for (int r = 0; r < nv; ++r) yp[r] = o[r];
         }
-        // element-wise stores: one 8-byte store behind a run-time alignment
-        // test measured 28-34 us against 16.4-18.4 us for the whole kernel
-        uint16_t* yp = (uint16_t*)a.y + mi * a.ldy + n0;
-        for (int r = 0; r < nv; ++r) yp[r] = o[r];
+        if (!MP || tb + T >= a.npass * T) break;
+        __syncthreads();  // every wave has read part[] before the next pass writes it
+#pragma unroll
+        for (int d = 0; d < D; ++d) load_tile(bufs[d], tb + T + d);
     }
 }
 

@@ -2,7 +2,7 @@
 pitch (ldx > K) on every decode kernel family (one-token, two-token, K-slice
 and matrix-core kernels), and of the one-token FP8 kernels (activations staged
 once per workgroup in LDS) at ragged shapes.  INT8 is compared bit-exactly,
-the float kinds under the comparison rules of tests/parity.py."""
+the float kinds under the comparison rules of oracle/compare.py."""
 import numpy as np
 import pytest
 import torch

@@ -1,6 +1,6 @@
 """GPU parity of the 128x128 block-scaled FP8 path (qlin_gemv_fp8_blk): the
 exported activation codes and UE8M0 exponents are compared bit-exactly, the
-output under the float rules of tests/parity.py."""
+output under the float rules of oracle/compare.py."""
 import numpy as np
 import pytest
 import torch

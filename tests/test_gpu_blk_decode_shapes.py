@@ -4,7 +4,7 @@ row to 4096 with partial row runs and 128-row blocks, padded pitches, edge
 values, extreme weight scale bytes, a scale buffer at an odd address, and
 repeat determinism.  Exported E4M3 codes and UE8M0 exponents are compared
 bit-exactly with the CPU oracle, outputs under the float rules of
-tests/parity.py."""
+oracle/compare.py."""
 import numpy as np
 import pytest
 import torch

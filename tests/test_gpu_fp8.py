@@ -1,5 +1,5 @@
 """GPU parity of the FP8-E4M3 weight-only GEMV (qlin_gemv_fp8) against the CPU
-oracle, under the float comparison rules of tests/parity.py, plus an exhaustive
+oracle, under the float comparison rules of oracle/compare.py, plus an exhaustive
 check of the hardware E4M3 decode through the product path."""
 import numpy as np
 import pytest
@@ -54,6 +54,21 @@ def test_fp8_ragged(ql, orc, M, N, K):
     d = gen_fp8(M, N, K, seed=N + K)
     y, ye, S = orc.gemv_fp8(d["x"], d["w"], d["ws"])
     check_float(_gpu(ql, d), ye, S, K)
+
+
+# one token with 9 to 16 steps of 1 KB per row (8192 < K <= 16384): the
+# LDS-staged kernel with every step in flight; a partial last step, N not a
+# multiple of the 8 rows of a workgroup, a padded row stride
+@pytest.mark.parametrize("N,K,per_tensor,pad", [(777, 8208, False, 0), (4099, 12288, True, 0),
+                                                (300, 14336, False, 256), (1001, 16384, False, 0),
+                                                (65, 16368, True, 48)])
+def test_fp8_one_token_long_rows(ql, orc, N, K, per_tensor, pad):
+    d = gen_fp8(1, N, K, seed=N + K, per_tensor=per_tensor)
+    wd = dev(d["w"]) if pad == 0 else padded(d["w"], pad)
+    y = ql.qlin_gemv_fp8(dev_bf16(d["x"]), wd, dev(d["ws"]))
+    torch.cuda.synchronize()
+    _, ye, S = orc.gemv_fp8(d["x"], d["w"], d["ws"])
+    check_float(host_bits(y), ye, S, K)
 
 
 @pytest.mark.parametrize("M", [1, 4, 8])

@@ -1,6 +1,6 @@
 """GPU parity of the FP8 W8A8 path (qlin_act_quant_fp8, qlin_gemv_fp8_w8a8)
 against the CPU oracle: codes and scales bit-exact, GEMV outputs under the
-float comparison rules of tests/parity.py; every E4M3 / E5M2 code decoded
+float comparison rules of oracle/compare.py; every E4M3 / E5M2 code decoded
 through the product path on both operands."""
 import numpy as np
 import pytest

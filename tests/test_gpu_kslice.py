@@ -1,11 +1,12 @@
 """GPU parity of the K-slice decode kernels (K a multiple of 1024, M <= 16:
 INT8 from M = 3, E4M3 weight-only from M = 2, FP8 W8A8 from M = 3)
 against the CPU oracle, over every slice length L = K/1024 and every tile
-count T per workgroup they are built for.  The (L, T) noted per case is what a 256-compute-unit device runs: one
-workgroup per compute unit, or one per 16 rows when N < 4096, or N/96 of them
-when a workgroup would get more than six tiles; parity does not depend on it.
-INT8 is compared bit-exactly (codes, int32 sums, bf16 outputs), the float
-kinds under the comparison rules of tests/parity.py."""
+count T per workgroup they are built for.  The (L, T) noted per case is what
+a 256-compute-unit device runs: one workgroup per compute unit, or one per 16
+rows when N < 4096; a workgroup with more than six tiles runs them in passes
+of T tiles; parity does not depend on it.  INT8 is compared bit-exactly
+(codes, int32 sums, bf16 outputs), the float kinds under the comparison rules
+of oracle/compare.py."""
 import numpy as np
 import pytest
 import torch
@@ -46,13 +47,17 @@ def _i8(ql, orc, M, N, K, seed, w_pad=0, bias=False):
     (12, 13000, 6144),  # L=6, T=4
     (16, 17000, 7168),  # L=7, T=5
     (4, 21000, 8192),   # L=8, T=6
-    (7, 30000, 2048),   # more than six tiles per unit: 313 workgroups of 96 rows
+    (7, 30000, 2048),   # eight tiles per unit: two passes of four
+    (4, 28672, 4096),   # L=4, seven tiles: two passes of four, the last tile empty
+    (9, 50001, 2048),   # 13 tiles: three passes of five
     (16, 1, 2048),      # one row
     (3, 17, 2048),      # two workgroups, 9 and 8 rows
     # from 12 tokens the rows are split into contiguous blocks
-    (16, 30000, 2048),  # 313 blocks of 23 runs, the first 301 with one more
+    (16, 30000, 2048),  # 256 blocks of 29 runs, the first 76 with one more: two passes
     (12, 17, 2048),     # two blocks, 3 runs and 2 runs (the last one row)
     (13, 17412, 5120),  # 4353 runs: one block of 18, the rest 17
+    (16, 28675, 4096),  # 7169 runs: blocks of 28 or 29 runs, two passes of four tiles
+    (12, 50001, 3072),  # three passes of five tiles
 ])
 def test_ks_int8_tiles_and_slices(ql, orc, M, N, K):
     _i8(ql, orc, M, N, K, seed=M * 7 + N)
@@ -86,12 +91,14 @@ def test_ks_int8_decode_shape_is_deterministic(ql):
     (11, 13000, 2048),  # L=2, T=4
     (16, 16500, 2048),  # L=2, T=5
     (4, 21000, 2048),   # L=2, T=6
-    (7, 30000, 2048),   # 313 workgroups
+    (7, 30000, 2048),   # eight tiles per unit: two passes of four
+    (2, 28672, 4096),   # two passes of four, the last tile empty
     (9, 1, 5120),
     # from 12 tokens whole 16-row tiles are dealt out in turn, then the runs left
-    (12, 30000, 2048),  # 313 workgroups: 5 whole tiles each, then 3 or 4 of the 1240 runs left
+    (12, 30000, 2048),  # 7 whole tiles each, then 1 or 2 of the 332 runs left: two passes
     (16, 17, 2048),     # two workgroups, no whole tiles
     (13, 17412, 5120),  # 4 whole tiles each, then 257 runs
+    (16, 50001, 2048),  # 12 whole tiles each, then 0 or 1 of the 213 runs left: three passes of five
 ])
 def test_ks_fp8_tiles_and_slices(ql, orc, M, N, K):
     d = gen_fp8(M, N, K, seed=M + N)
@@ -130,11 +137,13 @@ def _w8a8(ql, orc, M, N, K, seed, per_channel=True, per_token=True, w_pad=0, x_f
     (11, 13000, 2048),  # L=2, T=4
     (16, 16500, 2048),  # L=2, T=5
     (4, 21000, 2048),   # L=2, T=6
-    (7, 30000, 2048),   # 313 workgroups
+    (7, 30000, 2048),   # eight tiles per unit: two passes of four
+    (3, 28672, 4096),   # two passes of four, the last tile empty
     # from 8 tokens whole 16-row tiles are dealt out in turn, then the runs left
-    (8, 30000, 2048),   # 313 workgroups: 5 whole tiles each, then 3 or 4 of the 1240 runs left
+    (8, 30000, 2048),   # 7 whole tiles each, then 1 or 2 of the 332 runs left: two passes
     (9, 17, 2048),      # two workgroups, no whole tiles
     (16, 17412, 5120),  # 4 whole tiles each, then 257 runs (one workgroup takes two)
+    (12, 50001, 3072),  # three passes of five
 ])
 def test_ks_w8a8_tiles_and_slices(ql, orc, M, N, K):
     _w8a8(ql, orc, M, N, K, seed=M + N)

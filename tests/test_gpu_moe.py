@@ -1,5 +1,5 @@
 """GPU parity of the top-k MXFP4 expert GEMV (qlin_moe_mxfp4) against the CPU
-oracle, under the float rules of tests/parity.py; includes an exhaustive
+oracle, under the float rules of oracle/compare.py; includes an exhaustive
 E2M1 decode / nibble-order check through the product path."""
 import numpy as np
 import pytest

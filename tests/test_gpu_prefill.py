@@ -1,7 +1,7 @@
 """GPU parity of the prefill path (M > 16: the tiled matrix-core GEMM behind
 the dense entry points) against the CPU oracle.  INT8 codes, scales, int32
 accumulators and bf16 outputs are bit-exact; FP8 outputs follow the float
-comparison rules of tests/parity.py.  Small shapes are compared in full
+comparison rules of oracle/compare.py.  Small shapes are compared in full
 (several 128 x 128 tiles, ragged M, N and K); the 17408 x 5120 decode matrix
 at M = 512 is compared on sampled tokens and rows, each computed by the
 oracle one by one."""
