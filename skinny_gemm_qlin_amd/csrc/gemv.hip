@@ -190,6 +190,28 @@ hipError_t run_i8_lds(const void* x, int64_t ldx, const I8Args& a, int8_t* xq_ou
     return hipGetLastError();
 }
 
+// One to three tokens with 9 to 16 steps of 1 KB per row (8192 < K <=
+// 16384): the same kernel, every step of the row in flight (4096 x 14336,
+// M = 2: 13.7 -> 11.4 us against the lane-group kernel).
+constexpr int64_t kI8LdsWideMaxK = 16384;
+
+template <int M>
+hipError_t run_i8_lds_wide(const I8Args& a, hipStream_t st) {
+#define QLIN_I8_LDS(U_) launch_i8_lds_u<M, 4, false, U_>(a.xq, a.ldxq, a, nullptr, 0, nullptr, st); break;
+    switch (steps64(a.K)) {
+        case 9: QLIN_I8_LDS(9)
+        case 10: QLIN_I8_LDS(10)
+        case 11: QLIN_I8_LDS(11)
+        case 12: QLIN_I8_LDS(12)
+        case 13: QLIN_I8_LDS(13)
+        case 14: QLIN_I8_LDS(14)
+        case 15: QLIN_I8_LDS(15)
+        default: QLIN_I8_LDS(16)
+    }
+#undef QLIN_I8_LDS
+    return hipGetLastError();
+}
+
 // Matrix-core kernels: one workgroup of KS waves per 16-row tile, one chunk
 // of 256 K per wave per batch (few registers, so the whole grid is resident
 // and waves overlap each other's latency; measured at the decode shapes).
@@ -402,7 +424,8 @@ bool ks_plan(int64_t N, int64_t K, int lmax, KsPlan& p) {
     return true;
 }
 
-constexpr int kKsMaxLI8 = 8;     // INT8 holds 2L + 3 * 2L 16-byte registers per lane
+constexpr int kKsMaxLI8 = 14;    // INT8 holds 2L + D * 2L 16-byte registers per lane (D = 3 / 2 / 1 tiles in
+                                 // flight up to 6 / 8 / 14 lines)
 constexpr int kKsMaxLFloat = 5;  // the float kinds hold 4L + 2 * 2L
 
 template <int KIND, int L, int XF, int WF, bool XS = false, int LAYOUT = kKsTurn>
@@ -494,7 +517,13 @@ hipError_t run_ks(const KsArgs& a, const KsPlan& p, hipStream_t st) {
                 switch (p.L) {
                     case 6: return run_ks_t<KIND, 6, XF, WF>(b, p, st);
                     case 7: return run_ks_t<KIND, 7, XF, WF>(b, p, st);
-                    default: return run_ks_t<KIND, 8, XF, WF>(b, p, st);
+                    case 8: return run_ks_t<KIND, 8, XF, WF>(b, p, st);
+                    case 9: return run_ks_t<KIND, 9, XF, WF>(b, p, st);
+                    case 10: return run_ks_t<KIND, 10, XF, WF>(b, p, st);
+                    case 11: return run_ks_t<KIND, 11, XF, WF>(b, p, st);
+                    case 12: return run_ks_t<KIND, 12, XF, WF>(b, p, st);
+                    case 13: return run_ks_t<KIND, 13, XF, WF>(b, p, st);
+                    default: return run_ks_t<KIND, 14, XF, WF>(b, p, st);
                 }
             }
             return hipErrorInvalidValue;  // not reached: ks_plan caps L per kind
@@ -530,12 +559,21 @@ hipError_t launch_gemv_i8(const I8Args& a, hipStream_t st) {
     if (a.M >= 2 && a.M <= kI8LdsMaxM && a.K <= kI8LdsMaxK)
         return a.M == 2 ? run_i8_lds<2, 4, false>(a.xq, a.ldxq, a, nullptr, 0, nullptr, st)
                         : run_i8_lds<3, 4, false>(a.xq, a.ldxq, a, nullptr, 0, nullptr, st);
+    if (a.M >= 2 && a.M <= kI8LdsMaxM && a.K <= kI8LdsWideMaxK)
+        return a.M == 2 ? run_i8_lds_wide<2>(a, st) : run_i8_lds_wide<3>(a, st);
     switch (a.M) {
-        case 1: QLIN_M1_BY_STEPS(run_i8, a, st)
+        case 1:
+            // above 8 steps the codes-in-LDS kernel keeps every step in flight
+            // (4096 x 10240: the lane-group kernel loops over 8 at a time)
+            if (a.K > kI8LdsMaxK && a.K <= kI8LdsWideMaxK) return run_i8_lds_wide<1>(a, st);
+            QLIN_M1_BY_STEPS(run_i8, a, st)
         case 2: return run_i8<2, 32, 2, 2, 1>(a, st);
         default: {
+            // above 8 lines (one tile in flight) the K-slice kernels serve up
+            // to 8 tokens (4096 x 14336: 12.7 against 13.4 us at M = 8, but
+            // 15.2 against 14.6 us at M = 16 for the per-tile kernel)
             KsPlan p;
-            if (ks_plan(a.N, a.K, kKsMaxLI8, p)) {
+            if (ks_plan(a.N, a.K, a.M <= 8 ? kKsMaxLI8 : 8, p)) {
                 const KsArgs k{a.xq, a.ldxq, a.xs, a.xs_step, (int)a.M, (const uint8_t*)a.w, a.ldw, a.N, p.R,
                                a.ws, a.ws_step, a.bias, a.y, a.ldy, a.out_kind};
                 return run_ks<kKsI8>(k, p, st);

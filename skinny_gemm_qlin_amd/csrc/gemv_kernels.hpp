@@ -683,8 +683,9 @@ __global__ __launch_bounds__(64 * WPB) void gemv_fp8_m1_lds_kernel(
 
 // ------------------------------------------------------------------ INT8, few tokens, codes in LDS
 // W8A8 INT8 for M <= 4 tokens [Z100 operator-family table, INT8 row;
-// section 2.1].  A wave owns one weight row with all U <= 8 steps of 1 KB in
-// flight (lane j reads chunk j + 64u); the workgroup's WPB waves share the M
+// section 2.1].  A wave owns one weight row with all U steps of 1 KB in
+// flight (lane j reads chunk j + 64u; U <= 8 with QX, else U <= 16); the
+// workgroup's WPB waves share the M
 // token rows of int8 codes in LDS ([m][K] bytes), each chunk dotted with
 // v_dot4 (exact int32), summed across the wave, epilogue bf16((acc * xs) *
 // ws) then + bias, or the raw sums (out_kind 1).
@@ -815,7 +816,8 @@ __global__ __launch_bounds__(64 * WPB) void gemv_i8_lds_kernel(
     } else {
 #pragma unroll
         for (int m = 0; m < M; ++m) sc[m] = xs ? xs[m * xs_step] : 0.0f;
-        __builtin_amdgcn_s_waitcnt((U & 15) | 0x70 | 0xF00);  // vmcnt(U): the direct loads have landed
+        __builtin_amdgcn_s_waitcnt((U & 15) | ((U >> 4) << 14) | 0x70 | 0xF00);  // vmcnt(U): the direct loads
+                                                                                  // have landed
     }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_barrier();  // not __syncthreads(): that would also wait for the weights

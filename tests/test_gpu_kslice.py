@@ -47,6 +47,13 @@ def _i8(ql, orc, M, N, K, seed, w_pad=0, bias=False):
     (12, 13000, 6144),  # L=6, T=4
     (16, 17000, 7168),  # L=7, T=5
     (4, 21000, 8192),   # L=8, T=6
+    (7, 3000, 9216),    # L=9 (one tile in flight from here, up to 8 tokens), T=1
+    (8, 1001, 12288),   # L=12
+    (4, 4096, 14336),   # L=14, T=1
+    (5, 28672, 10240),  # L=10, seven tiles: two passes of four
+    (12, 1001, 12288),  # above 8 lines and 8 tokens: the per-tile matrix-core kernel
+    (16, 9000, 14336),
+    (6, 700, 15360),    # L=15: past the K-slice kernels, the per-tile matrix-core kernel
     (7, 30000, 2048),   # eight tiles per unit: two passes of four
     (4, 28672, 4096),   # L=4, seven tiles: two passes of four, the last tile empty
     (9, 50001, 2048),   # 13 tiles: three passes of five

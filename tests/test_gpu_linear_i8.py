@@ -95,10 +95,15 @@ def test_linear_i8_repeats_are_identical(ql):
         assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
 
 
-# the two- and three-token GEMV kernels (codes in LDS, K <= 8192) and the
-# lane-group kernel past that K
+# the two- and three-token GEMV kernels (codes in LDS, K <= 16384; for one
+# token from K = 8208) and the lane-group kernel past that K
 @pytest.mark.parametrize("M,N,K", [(2, 17408, 5120), (3, 17408, 5120), (2, 1, 16), (3, 9, 8192), (2, 100, 8208),
-                                   (3, 1001, 1040)])
+                                   (3, 1001, 1040),
+                                   # 9 to 16 steps of 1 KB per row, also for one token
+                                   (2, 4096, 14336), (3, 1001, 8208), (2, 77, 16384), (3, 513, 12304),
+                                   (1, 4096, 14336), (1, 77, 8208), (1, 1001, 16384),
+                                   # past them: the lane-group kernel
+                                   (2, 300, 16400)])
 def test_gemv_i8_two_three_tokens(ql, orc, M, N, K):
     d = gen_int8(M, N, K, seed=M * 100 + N)
     oxq, oxs = orc.act_quant_i8(d["x"])
