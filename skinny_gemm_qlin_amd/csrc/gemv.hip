@@ -426,7 +426,7 @@ bool ks_plan(int64_t N, int64_t K, int lmax, KsPlan& p) {
 
 constexpr int kKsMaxLI8 = 14;    // INT8 holds 2L + D * 2L 16-byte registers per lane (D = 3 / 2 / 1 tiles in
                                  // flight up to 6 / 8 / 14 lines)
-constexpr int kKsMaxLFloat = 5;  // the float kinds hold 4L + 2 * 2L
+constexpr int kKsMaxLFloat = 8;  // the float kinds hold 4L + D * 2L (D = 2 / 1 up to 6 / 8 lines)
 
 template <int KIND, int L, int XF, int WF, bool XS = false, int LAYOUT = kKsTurn>
 hipError_t run_ks_t(const KsArgs& a, const KsPlan& p, hipStream_t st) {
@@ -512,12 +512,12 @@ hipError_t run_ks(const KsArgs& a, const KsPlan& p, hipStream_t st) {
         case 3: return run_ks_t<KIND, 3, XF, WF>(b, p, st);
         case 4: return run_ks_t<KIND, 4, XF, WF>(b, p, st);
         case 5: return run_ks_t<KIND, 5, XF, WF>(b, p, st);
+        case 6: return run_ks_t<KIND, 6, XF, WF>(b, p, st);
+        case 7: return run_ks_t<KIND, 7, XF, WF>(b, p, st);
+        case 8: return run_ks_t<KIND, 8, XF, WF>(b, p, st);
         default:
             if constexpr (KIND == kKsI8) {
                 switch (p.L) {
-                    case 6: return run_ks_t<KIND, 6, XF, WF>(b, p, st);
-                    case 7: return run_ks_t<KIND, 7, XF, WF>(b, p, st);
-                    case 8: return run_ks_t<KIND, 8, XF, WF>(b, p, st);
                     case 9: return run_ks_t<KIND, 9, XF, WF>(b, p, st);
                     case 10: return run_ks_t<KIND, 10, XF, WF>(b, p, st);
                     case 11: return run_ks_t<KIND, 11, XF, WF>(b, p, st);
@@ -599,7 +599,8 @@ hipError_t launch_gemv_fp8(const F8Args& a, hipStream_t st) {
             return run_fp8<1, 32, 2, 1, 1>(a, st);
         default: {
             // K-slice kernels from M = 2 (17408 x 5120: 17.4 against 18.2 us
-            // for the VALU kernel at M = 2)
+            // for the VALU kernel at M = 2), up to 8 lines (14336 x 7168:
+            // 19.4-22.8 against 21.5-37.2 us for the per-tile kernel)
             KsPlan p;
             if (ks_plan(a.N, a.K, kKsMaxLFloat, p)) {
                 const KsArgs k{a.x, a.ldx, nullptr, 0, (int)a.M, a.w, a.ldw, a.N, p.R,
@@ -639,9 +640,14 @@ hipError_t launch_gemv_fp8_w8a8(const W8A8F8Args& a, hipStream_t st) {
     // with 2-5 steps in flight)
     if (a.M == 2) return run_w8a8<2, 32, 2, 1, 1>(a, st);
     // from three tokens the K-slice kernels where they apply (E4M3 x E4M3,
-    // 17408 x 5120: 16.8 against 18.3 us for the VALU kernel below at M = 3)
+    // 17408 x 5120: 16.8 against 18.3 us for the VALU kernel below at M = 3);
+    // above 5 lines (codes widened in registers, one tile in flight from 7)
+    // only where a workgroup has at least 3 tiles of rows, or at M = 3: with
+    // two tiles the per-tile matrix-core kernel is faster from M = 4
+    // (8192 x 8192: 14.2-15.6 against 17.4-18.2 us; 14336 x 7168, four tiles:
+    // 19.3-20.8 against 22.6-26.6 us)
     KsPlan p;
-    if (ks_plan(a.N, a.K, kKsMaxLFloat, p)) {
+    if (ks_plan(a.N, a.K, kKsMaxLFloat, p) && (p.L <= 5 || a.M == 3 || (int64_t)p.T * p.npass >= 3)) {
         const KsArgs k{a.xq, a.ldxq, a.xs, a.xs_step, (int)a.M, a.w, a.ldw, a.N, p.R,
                        a.ws, a.ws_step, nullptr, a.y, a.ldy, 0};
         if (a.x_fmt == kFmtE5M2)

@@ -125,8 +125,8 @@ __global__ __launch_bounds__(64 * kKsWaves) void gemv_ks_kernel(const KsArgs a) 
     constexpr int NQ = 2 * L;                  // loads per tile = 64-K steps of the slice
     constexpr int NX = I8 ? NQ : 2 * NQ;       // B operand registers (16 bytes each) of the slice
     // tiles in flight per wave: as many as the registers hold next to the
-    // slice (INT8 above 8 lines: one)
-    constexpr int DMAX = I8 ? (L <= 6 ? 3 : (L <= 8 ? 2 : 1)) : 2;
+    // slice (INT8 above 8 lines, the float kinds above 6: one)
+    constexpr int DMAX = I8 ? (L <= 6 ? 3 : (L <= 8 ? 2 : 1)) : (L <= 6 ? 2 : 1);
     constexpr int D = T < DMAX ? T : DMAX;
     typedef typename std::conditional<I8, i32x4_t, f32x4_t>::type acc_t;
     __shared__ __align__(16) uint8_t col[kKsWaves][16 * kKsPitch];

@@ -106,6 +106,10 @@ def test_ks_int8_decode_shape_is_deterministic(ql):
     (16, 17, 2048),     # two workgroups, no whole tiles
     (13, 17412, 5120),  # 4 whole tiles each, then 257 runs
     (16, 50001, 2048),  # 12 whole tiles each, then 0 or 1 of the 213 runs left: three passes of five
+    (2, 3000, 6144),    # L=6, two tiles in flight
+    (5, 14336, 7168),   # L=7, one tile in flight, T=4
+    (16, 6001, 8192),   # L=8, T=2
+    (4, 28672, 8192),   # L=8, two passes of four
 ])
 def test_ks_fp8_tiles_and_slices(ql, orc, M, N, K):
     d = gen_fp8(M, N, K, seed=M + N)
@@ -151,6 +155,10 @@ def _w8a8(ql, orc, M, N, K, seed, per_channel=True, per_token=True, w_pad=0, x_f
     (9, 17, 2048),      # two workgroups, no whole tiles
     (16, 17412, 5120),  # 4 whole tiles each, then 257 runs (one workgroup takes two)
     (12, 50001, 3072),  # three passes of five
+    (3, 5000, 6144),    # L=6 at three tokens
+    (8, 14336, 7168),   # L=7, T=4
+    (16, 20000, 8192),  # L=8, T=5
+    (6, 6144, 8192),    # two tiles per unit: the per-tile matrix-core kernel
 ])
 def test_ks_w8a8_tiles_and_slices(ql, orc, M, N, K):
     _w8a8(ql, orc, M, N, K, seed=M + N)
