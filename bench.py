@@ -109,12 +109,12 @@ def bytes_moe_ffn_call(M, H, I, E, topk, live):
 # dominant kernel of each workload; the whole call for block FP8, the MoE
 # and the expert FFN)
 KERNEL_SOURCES = {
-    "int8_decode": ("gemv.hip",),
+    "int8_decode": ("gemv.hip", "ks_i8.hip"),
     "int8_prefill": ("gemm.hip",),
     "int8_prefill_smalln": ("gemv.hip",),
     "fp8_prefill": ("gemm.hip",),
-    "fp8_decode": ("gemv.hip",),
-    "fp8_w8a8": ("gemv.hip",),
+    "fp8_decode": ("gemv.hip", "ks_f8.hip"),
+    "fp8_w8a8": ("gemv.hip", "ks_w8a8_e4m3.hip"),
     "fp8_blk": ("act_quant.hip", "gemv.hip"),
     "moe_mxfp4": ("moe.hip",),
     "moe_prefill": ("moe.hip", "moe_prefill.hip"),

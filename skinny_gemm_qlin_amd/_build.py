@@ -22,8 +22,10 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqlin.so")
 
-SOURCES = ["qlin_api.hip", "act_quant.hip", "gemv.hip", "gemm.hip", "moe.hip", "moe_prefill.hip", "routing.hip"]
-HEADERS = ["qlin_device.hpp", "qlin_launch.hpp", "gemv_kernels.hpp", "mfma_kernels.hpp", "ks_kernels.hpp", "gemm_kernels.hpp"]
+SOURCES = ["gemv.hip", "ks_i8.hip", "ks_f8.hip", "ks_w8a8_e4m3.hip", "ks_w8a8_e5m2.hip", "qlin_api.hip",
+           "act_quant.hip", "gemm.hip", "moe.hip", "moe_prefill.hip", "routing.hip"]
+HEADERS = ["qlin_device.hpp", "qlin_launch.hpp", "gemv_kernels.hpp", "mfma_kernels.hpp", "ks_kernels.hpp",
+           "ks_launch.hpp", "gemm_kernels.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -47,7 +49,7 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     """Compile every HIP source and link libqlin.so next to this file."""
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]

@@ -295,7 +295,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
 // trims L2 misses (310 -> 302 us); deeper LDS rings (3-5 stages, one
 // workgroup per unit), 256 x 256 / 256 x 128 tiles (4, 8 or 16 waves) and
 // a per-workgroup rotation of the K order were all slower (340-460 us).
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef int i32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 

@@ -4,16 +4,19 @@
 // decode shapes (N=17408, K=5120 for INT8 / E4M3; N=4096, K=7168 for block
 // FP8):
 //   * M = 1: VALU, one whole wavefront per row (GS=64), all K steps of the
-//     row in flight (up to 8); INT8 with 4 waves per workgroup, the FP8
+//     row in flight (up to 8, or 16 with the token row in LDS); INT8 with 4
+//     waves per workgroup (the codes-in-LDS kernel above 8 steps), the FP8
 //     kinds (weight-only and W8A8) with the token row staged once per
 //     8-wave workgroup in LDS as bf16; block FP8 uses its own M = 1 kernel
 //     that shares the scale bytes of a batch across the wave;
 //   * M = 2 (INT8, FP8 W8A8, and E4M3 where the next item does not apply):
 //     VALU with smaller lane groups (and, for INT8 / E4M3, several rows per
 //     group, so that each activation load feeds more weight rows);
-//   * K a multiple of 1024 (at most 8192 for INT8, 5120 for the E4M3 kinds),
-//     from M = 3 (E4M3 weight-only from M = 2; W8A8 in all four format pairs):
-//     the K-slice matrix-core kernels of ks_kernels.hpp (INT8 at M = 4 / 8 /
+//   * K a multiple of 1024 (at most 14336 for INT8, 8192 for the E4M3
+//     kinds; see each launcher for the token counts), from M = 3 (E4M3
+//     weight-only from M = 2; W8A8 in all four format pairs): the K-slice
+//     matrix-core kernels of ks_kernels.hpp, planned here (ks_plan) and
+//     launched from ks_i8.hip / ks_f8.hip / ks_w8a8_*.hip (INT8 at M = 4 / 8 /
 //     16: 16.5 / 17.0 / 18.4 us against 17.5 / 19.1 / 21.4 us for one
 //     workgroup per 16-row tile);
 //   * otherwise: the matrix-core kernels of mfma_kernels.hpp;
@@ -25,7 +28,7 @@
 #include <atomic>
 
 #include "gemv_kernels.hpp"
-#include "ks_kernels.hpp"
+#include "ks_launch.hpp"
 #include "mfma_kernels.hpp"
 #include "qlin_launch.hpp"
 
@@ -404,8 +407,6 @@ int cu_count() {
     return n;
 }
 
-struct KsPlan { int L, T; unsigned G; int64_t R; int npass; };
-
 // K = 1024 * L with L in [2, lmax]; G = one workgroup per compute unit, or
 // one per 16 rows when N is small; the ceil(N/4) runs of 4 rows are dealt
 // out in turn, R = rows per workgroup (a multiple of 4).  A workgroup with
@@ -427,108 +428,6 @@ bool ks_plan(int64_t N, int64_t K, int lmax, KsPlan& p) {
 constexpr int kKsMaxLI8 = 14;    // INT8 holds 2L + D * 2L 16-byte registers per lane (D = 3 / 2 / 1 tiles in
                                  // flight up to 6 / 8 / 14 lines)
 constexpr int kKsMaxLFloat = 8;  // the float kinds hold 4L + D * 2L (D = 2 / 1 up to 6 / 8 lines)
-
-template <int KIND, int L, int XF, int WF, bool XS = false, int LAYOUT = kKsTurn>
-hipError_t run_ks_t(const KsArgs& a, const KsPlan& p, hipStream_t st) {
-    const dim3 grid(p.G), block(64 * kKsWaves);
-    if (p.npass > 1) {  // then 4 <= T <= kKsMaxTiles
-        switch (p.T) {
-            case 4: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 4, XF, WF, XS, LAYOUT, true>), grid, block, 0, st, a); break;
-            case 5: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 5, XF, WF, XS, LAYOUT, true>), grid, block, 0, st, a); break;
-            default: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 6, XF, WF, XS, LAYOUT, true>), grid, block, 0, st, a); break;
-        }
-        return hipGetLastError();
-    }
-    switch (p.T) {
-        case 1: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 1, XF, WF, XS, LAYOUT>), grid, block, 0, st, a); break;
-        case 2: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 2, XF, WF, XS, LAYOUT>), grid, block, 0, st, a); break;
-        case 3: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 3, XF, WF, XS, LAYOUT>), grid, block, 0, st, a); break;
-        case 4: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 4, XF, WF, XS, LAYOUT>), grid, block, 0, st, a); break;
-        case 5: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 5, XF, WF, XS, LAYOUT>), grid, block, 0, st, a); break;
-        default: hipLaunchKernelGGL((gemv_ks_kernel<KIND, L, 6, XF, WF, XS, LAYOUT>), grid, block, 0, st, a); break;
-    }
-    return hipGetLastError();
-}
-
-// One-byte activation codes (INT8, FP8 W8A8) from kKsStageXMinM tokens,
-// with at most 5 lines per slice (LDS: the staged slices take 16 KB x L
-// next to the transpose columns and the partial tiles) and the activation
-// block addressable with 32-bit offsets: the slice is staged through LDS
-// (XS; INT8 M = 4 / 8 / 16: 16.5 / 17.0 / 18.6 -> 16.4 / 16.8 / 17.7 us).
-constexpr int64_t kKsStageXMinM = 4;
-bool ks_stage_x(const KsArgs& a, const KsPlan& p) {
-    return a.M >= kKsStageXMinM && p.L <= 5 && (int64_t)(a.M - 1) * a.ldx + 1024 * p.L <= INT32_MAX;
-}
-
-// Row layout per kind and token count (17408 x 5120, GEMV alone, against
-// the runs dealt out in turn): INT8 with contiguous blocks +0.5 / +0.15 /
-// -0.3 / -0.5 us at M = 4 / 8 / 12 / 16 (with bands -0.0..-0.3 from 12 but
-// +0.5 at 4); FP8 W8A8 with bands ~0 / -0.4 / -0.4 / -0.7 us; E4M3
-// weight-only with bands ~0 / ~0 / -0.4 / -0.7 us (with blocks +0.5 to +0.7
-// at every M).
-int ks_layout(int kind, int64_t M) {
-    if (kind == kKsI8) return M >= 12 ? kKsBlocks : kKsTurn;
-    if (kind == kKsW8A8) return M >= 8 ? kKsBands : kKsTurn;
-    return M >= 12 ? kKsBands : kKsTurn;
-}
-
-template <int KIND, int XF, int WF, bool XS, int LAYOUT>
-hipError_t run_ks_l(const KsArgs& a, const KsPlan& p, hipStream_t st) {
-    switch (p.L) {
-        case 2: return run_ks_t<KIND, 2, XF, WF, XS, LAYOUT>(a, p, st);
-        case 3: return run_ks_t<KIND, 3, XF, WF, XS, LAYOUT>(a, p, st);
-        case 4: return run_ks_t<KIND, 4, XF, WF, XS, LAYOUT>(a, p, st);
-        default: return run_ks_t<KIND, 5, XF, WF, XS, LAYOUT>(a, p, st);  // L <= 5 on these paths
-    }
-}
-
-template <int KIND, int XF = kFmtE4M3, int WF = kFmtE4M3>
-hipError_t run_ks(const KsArgs& a, const KsPlan& p, hipStream_t st) {
-    const int layout = ks_layout(KIND, a.M);
-    KsArgs b = a;
-    b.npass = p.npass;
-    const int64_t runs = (a.N + 3) / 4;
-    if (layout == kKsBlocks) {
-        b.rbase = runs / p.G;
-        b.rrem = runs - b.rbase * p.G;
-    } else if (layout == kKsBands) {
-        b.rbase = runs / (4 * (int64_t)p.G);
-        b.rrem = 0;
-    }
-    if constexpr (KIND != kKsF8) {
-        if (ks_stage_x(a, p)) {
-            if constexpr (KIND == kKsI8) {
-                if (layout == kKsBlocks) return run_ks_l<KIND, XF, WF, true, kKsBlocks>(b, p, st);
-            } else {
-                if (layout == kKsBands) return run_ks_l<KIND, XF, WF, true, kKsBands>(b, p, st);
-            }
-            return run_ks_l<KIND, XF, WF, true, kKsTurn>(b, p, st);
-        }
-    } else {
-        if (layout == kKsBands && p.L <= 5) return run_ks_l<KIND, XF, WF, false, kKsBands>(b, p, st);
-    }
-    switch (p.L) {
-        case 2: return run_ks_t<KIND, 2, XF, WF>(b, p, st);
-        case 3: return run_ks_t<KIND, 3, XF, WF>(b, p, st);
-        case 4: return run_ks_t<KIND, 4, XF, WF>(b, p, st);
-        case 5: return run_ks_t<KIND, 5, XF, WF>(b, p, st);
-        case 6: return run_ks_t<KIND, 6, XF, WF>(b, p, st);
-        case 7: return run_ks_t<KIND, 7, XF, WF>(b, p, st);
-        case 8: return run_ks_t<KIND, 8, XF, WF>(b, p, st);
-        default:
-            if constexpr (KIND == kKsI8) {
-                switch (p.L) {
-                    case 9: return run_ks_t<KIND, 9, XF, WF>(b, p, st);
-                    case 10: return run_ks_t<KIND, 10, XF, WF>(b, p, st);
-                    case 11: return run_ks_t<KIND, 11, XF, WF>(b, p, st);
-                    case 12: return run_ks_t<KIND, 12, XF, WF>(b, p, st);
-                    case 13: return run_ks_t<KIND, 13, XF, WF>(b, p, st);
-                    default: return run_ks_t<KIND, 14, XF, WF>(b, p, st);
-                }
-            }
-            return hipErrorInvalidValue;  // not reached: ks_plan caps L per kind
-    }
-}
 
 template <int U>
 hipError_t run_blk_m1(const BlkArgs& a, hipStream_t st) {
@@ -576,7 +475,7 @@ hipError_t launch_gemv_i8(const I8Args& a, hipStream_t st) {
             if (ks_plan(a.N, a.K, a.M <= 8 ? kKsMaxLI8 : 8, p)) {
                 const KsArgs k{a.xq, a.ldxq, a.xs, a.xs_step, (int)a.M, (const uint8_t*)a.w, a.ldw, a.N, p.R,
                                a.ws, a.ws_step, a.bias, a.y, a.ldy, a.out_kind};
-                return run_ks<kKsI8>(k, p, st);
+                return launch_ks_i8(k, p, st);
             }
             return run_i8_mfma(a, st);
         }
@@ -605,7 +504,7 @@ hipError_t launch_gemv_fp8(const F8Args& a, hipStream_t st) {
             if (ks_plan(a.N, a.K, kKsMaxLFloat, p)) {
                 const KsArgs k{a.x, a.ldx, nullptr, 0, (int)a.M, a.w, a.ldw, a.N, p.R,
                                a.ws, a.ws_step, nullptr, a.y, a.ldy, 0};
-                return run_ks<kKsF8>(k, p, st);
+                return launch_ks_f8(k, p, st);
             }
             if (a.M == 2) return run_fp8<2, 64, 4, 1, 1>(a, st);
             return run_fp8_mfma(a, st);
@@ -650,11 +549,7 @@ hipError_t launch_gemv_fp8_w8a8(const W8A8F8Args& a, hipStream_t st) {
     if (ks_plan(a.N, a.K, kKsMaxLFloat, p) && (p.L <= 5 || a.M == 3 || (int64_t)p.T * p.npass >= 3)) {
         const KsArgs k{a.xq, a.ldxq, a.xs, a.xs_step, (int)a.M, a.w, a.ldw, a.N, p.R,
                        a.ws, a.ws_step, nullptr, a.y, a.ldy, 0};
-        if (a.x_fmt == kFmtE5M2)
-            return a.w_fmt == kFmtE5M2 ? run_ks<kKsW8A8, kFmtE5M2, kFmtE5M2>(k, p, st)
-                                       : run_ks<kKsW8A8, kFmtE5M2, kFmtE4M3>(k, p, st);
-        return a.w_fmt == kFmtE5M2 ? run_ks<kKsW8A8, kFmtE4M3, kFmtE5M2>(k, p, st)
-                                   : run_ks<kKsW8A8, kFmtE4M3, kFmtE4M3>(k, p, st);
+        return a.x_fmt == kFmtE5M2 ? launch_ks_w8a8_e5m2(k, p, a.w_fmt, st) : launch_ks_w8a8_e4m3(k, p, a.w_fmt, st);
     }
     // three rows per group at three tokens (17.8-17.9 us against 19.1-19.3 us
     // for the matrix-core kernel); from four tokens the matrix core wins

@@ -585,7 +585,6 @@ __global__ __launch_bounds__(64 * WPB) void gemv_fp8_blk_m1_fq_kernel(
 // registers and are widened to bf16 once.  Per lane the chunks are summed in
 // order (8 v_dot2 each), then across the wave; epilogue bf16(acc * ws)
 // (weight-only) or bf16((acc * xs) * ws) (W8A8), as the other kernels.
-typedef __attribute__((address_space(3))) void lds_void_t;
 
 template <int W8A8, int U, int WPB, int XF = kFmtE4M3, int WF = kFmtE4M3>
 __global__ __launch_bounds__(64 * WPB) void gemv_fp8_m1_lds_kernel(

@@ -16,6 +16,9 @@
 
 namespace qlin {
 
+// LDS destination of the buffer / global loads that write LDS directly
+typedef __attribute__((address_space(3))) void lds_void_t;
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short short2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
