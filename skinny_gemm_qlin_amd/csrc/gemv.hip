@@ -9,15 +9,15 @@
 //     kinds (weight-only and W8A8) with the token row staged once per
 //     8-wave workgroup in LDS as bf16; block FP8 uses its own M = 1 kernel
 //     that shares the scale bytes of a batch across the wave;
-//   * M = 2 (INT8, FP8 W8A8, and E4M3 where the next item does not apply):
-//     VALU with smaller lane groups (and, for INT8 / E4M3, several rows per
-//     group, so that each activation load feeds more weight rows);
+//   * M = 2: E4M3 weight-only (K <= 16384) one wave per row with both
+//     token rows in LDS; INT8 (K <= 16384) one wave per row with the codes
+//     in LDS; FP8 W8A8 VALU with 32-lane groups of two rows;
 //   * K a multiple of 1024 (at most 14336 for INT8, 8192 for the E4M3
 //     kinds; see each launcher for the token counts), from M = 3 (E4M3
-//     weight-only from M = 2; W8A8 in all four format pairs): the K-slice
+//     weight-only at M = 2 above K = 16384; W8A8 in all four format pairs): the K-slice
 //     matrix-core kernels of ks_kernels.hpp, planned here (ks_plan) and
 //     launched from ks_i8.hip / ks_f8.hip / ks_w8a8_*.hip (INT8 at M = 4 / 8 /
-//     16: 16.5 / 17.0 / 18.4 us against 17.5 / 19.1 / 21.4 us for one
+//     16: 16.4 / 16.8 / 17.3 us against 17.5 / 19.1 / 21.4 us for one
 //     workgroup per 16-row tile);
 //   * otherwise: the matrix-core kernels of mfma_kernels.hpp;
 //   * M > 16 (prefill): the tiled matrix-core GEMM of gemm.hip; on a matrix
@@ -156,6 +156,48 @@ hipError_t run_fp8_m1_lds_wide(const void* x, int64_t K, const uint8_t* w, int64
         default: QLIN_M1_LDS(16)
     }
 #undef QLIN_M1_LDS
+    return hipGetLastError();
+}
+
+// E4M3 weight-only, two tokens: one wave per row with every 1 KB step in
+// flight, the token rows staged once per 8-wave workgroup in LDS as bf16
+// (gemv_fp8_lds_kernel), K <= 16384.  Against the K-slice / lane-group
+// kernels it replaced at M = 2: 4096 x 14336 15.0 vs 18.5 us, 8192 x 8192
+// 14.1 vs 15.9 us, 4096 x 10240 10.8 vs 14.2 us, equal within 0.2 us at
+// 17408 x 5120, 14336 x 4096, 28672 x 4096 and 4096 x 4096.  With three or
+// four tokens its dot products outweigh the stream (17408 x 5120: 21.6 /
+// 25.5 us against 17.2 / 17.3 us for the K-slice kernels), so it stops at two.
+constexpr int64_t kF8LdsMaxK = 16384;
+
+template <int M, int U>
+void launch_fp8_lds_u(const F8Args& a, hipStream_t st) {
+    const size_t lds = (size_t)((M * (a.K >> 3) + 63) / 64) * 1024;
+    hipLaunchKernelGGL((gemv_fp8_lds_kernel<M, U, kM1LdsWaves>), dim3((unsigned)((a.N + kM1LdsWaves - 1) / kM1LdsWaves)),
+                       dim3(64 * kM1LdsWaves), lds, st, a.x, a.ldx, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.y, a.ldy);
+}
+
+template <int M>
+hipError_t run_fp8_lds(const F8Args& a, hipStream_t st) {
+#define QLIN_F8_LDS(U_) launch_fp8_lds_u<M, U_>(a, st); break;
+    switch (steps64(a.K)) {
+        case 1: QLIN_F8_LDS(1)
+        case 2: QLIN_F8_LDS(2)
+        case 3: QLIN_F8_LDS(3)
+        case 4: QLIN_F8_LDS(4)
+        case 5: QLIN_F8_LDS(5)
+        case 6: QLIN_F8_LDS(6)
+        case 7: QLIN_F8_LDS(7)
+        case 8: QLIN_F8_LDS(8)
+        case 9: QLIN_F8_LDS(9)
+        case 10: QLIN_F8_LDS(10)
+        case 11: QLIN_F8_LDS(11)
+        case 12: QLIN_F8_LDS(12)
+        case 13: QLIN_F8_LDS(13)
+        case 14: QLIN_F8_LDS(14)
+        case 15: QLIN_F8_LDS(15)
+        default: QLIN_F8_LDS(16)
+    }
+#undef QLIN_F8_LDS
     return hipGetLastError();
 }
 
@@ -497,9 +539,10 @@ hipError_t launch_gemv_fp8(const F8Args& a, hipStream_t st) {
                 return run_fp8_m1_lds_wide(a.x, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.y, st);
             return run_fp8<1, 32, 2, 1, 1>(a, st);
         default: {
-            // K-slice kernels from M = 2 (17408 x 5120: 17.4 against 18.2 us
-            // for the VALU kernel at M = 2), up to 8 lines (14336 x 7168:
-            // 19.4-22.8 against 21.5-37.2 us for the per-tile kernel)
+            if (a.M == 2 && a.K <= kF8LdsMaxK) return run_fp8_lds<2>(a, st);
+            // K-slice kernels from M = 3 (and at M = 2 above K = 16384), up
+            // to 8 lines (14336 x 7168: 19.4-22.8 against 21.5-37.2 us for
+            // the per-tile kernel)
             KsPlan p;
             if (ks_plan(a.N, a.K, kKsMaxLFloat, p)) {
                 const KsArgs k{a.x, a.ldx, nullptr, 0, (int)a.M, a.w, a.ldw, a.N, p.R,

@@ -680,6 +680,81 @@ __global__ __launch_bounds__(64 * WPB) void gemv_fp8_m1_lds_kernel(
     }
 }
 
+// ------------------------------------------------------------------ E4M3 weight-only, two tokens, rows in LDS
+// The one-token kernel above for M tokens (used at M = 2) [Z100 operator-family table, FP8
+// row; section 2.2]: the workgroup stages the M bf16 token rows once in LDS
+// (row m in halves [m * 2 * nchunk, (m + 1) * 2 * nchunk), in the same
+// two-half layout), a wave owns one weight row with all U of its 1 KB steps
+// in flight, widens each chunk of codes once and dots it with every token
+// row; lane m writes token m's output, bf16(acc * ws).  LDS: 2 * M * K
+// bytes (whole 1 KB direct-load blocks).
+template <int M, int U, int WPB>
+__global__ __launch_bounds__(64 * WPB) void gemv_fp8_lds_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, int64_t K,
+    const uint8_t* __restrict__ w, int64_t ldw, int64_t N,
+    const float* __restrict__ ws, int ws_step, uint16_t* __restrict__ y, int64_t ldy) {
+    extern __shared__ __align__(16) u32x4_t xl[];  // [M][2 * nchunk] 16-byte halves
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nchunk = (int)(K >> 4), nh = 2 * nchunk, nt = M * nh;
+    // 1. the token rows (issued first): one direct load instruction fills 1 KB
+    //    (64 halves) of LDS; slots past the last half repeat it
+    const int ni = (nt + 63) >> 6;
+    for (int inst = wv; inst < ni; inst += WPB) {  // wave-uniform
+        const int q = inst * 64 + lane, qq = q < nt ? q : nt - 1;
+        const int m = qq / nh, r = qq - m * nh;
+        const int h = r >= nchunk, c = r - h * nchunk;
+        __builtin_amdgcn_global_load_lds((const void*)(x + m * ldx + c * 16 + h * 8),
+                                         (lds_void_t*)(xl + (int64_t)inst * 64), 16, 0, 0);
+    }
+    // 2. this wave's row, every step in flight
+    const int64_t n = (int64_t)blockIdx.x * WPB + wv;
+    const int64_t nn = n < N ? n : N - 1;
+    const uint8_t* wr = w + nn * ldw;
+    u32x4_t wq[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = u * 64 + lane, cc = c < nchunk ? c : nchunk - 1;
+        wq[u] = ld_stream(wr + (int64_t)cc * 16);
+    }
+    const float wsv = ws[nn * ws_step];
+    // 3. publish the rows: every load issued before the U weight loads has
+    //    landed once at most U loads are outstanding
+    __builtin_amdgcn_s_waitcnt((U & 15) | ((U >> 4) << 14) | 0x70 | 0xF00);  // vmcnt(U)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();  // not __syncthreads(): that would also wait for the weights
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    asm volatile("" ::"s"(wsv));  // the scale waited for under the weight loads, as in the one-token kernel
+    // 4. the row's dot products
+    float acc[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = u * 64 + lane;
+        const bool ok = c < nchunk;
+        const int cc = ok ? c : nchunk - 1;
+        bf16x2_t wb[8];
+        fp8x16<kFmtE4M3>(wq[u], wb);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            u32x4_t a = xl[m * nh + cc], b = xl[m * nh + nchunk + cc];
+            if (!ok) a = b = u32x4_t{0, 0, 0, 0};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[m] = dot2(wb[e], as_bf16x2(a[e]), acc[m]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[m] = dot2(wb[4 + e], as_bf16x2(b[e]), acc[m]);
+        }
+    }
+    float out = 0.0f;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const float t = group_sum<64>(acc[m]);  // the total in every lane
+        out = lane == m ? t : out;
+    }
+    if (lane < M && n < N) y[lane * ldy + n] = f32_to_bf16(out * wsv);
+}
+
 // ------------------------------------------------------------------ INT8, few tokens, codes in LDS
 // W8A8 INT8 for M <= 4 tokens [Z100 operator-family table, INT8 row;
 // section 2.1].  A wave owns one weight row with all U steps of 1 KB in

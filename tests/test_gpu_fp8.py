@@ -92,3 +92,19 @@ def test_fp8_deterministic(ql):
     ref = ql.qlin_gemv_fp8(x, w, ws)
     for _ in range(20):
         assert torch.equal(ql.qlin_gemv_fp8(x, w, ws).view(torch.int16), ref.view(torch.int16))
+
+
+# two tokens with both rows staged in LDS (K <= 16384): K from one chunk to
+# the largest, ragged N, padded weight and activation pitches; past 16384 the
+# lane-group kernel
+@pytest.mark.parametrize("M,N,K", [(2, 1001, 16), (2, 77, 1040), (2, 1001, 5120), (2, 300, 16384), (2, 2000, 10912),
+                                   (2, 9, 8192), (2, 4097, 7168), (2, 1, 4096), (2, 130, 16400)])
+def test_fp8_two_tokens_rows_in_lds(ql, orc, M, N, K):
+    d = gen_fp8(M, N, K, seed=M * 11 + N + K, per_tensor=N % 2 == 0)
+    xp = np.zeros((M, K + 24), np.uint16)
+    xp[:, :K] = d["x"]
+    x = dev_bf16(xp)[:, :K]
+    y = ql.qlin_gemv_fp8(x, padded(d["w"], 48), dev(d["ws"]))
+    torch.cuda.synchronize()
+    _, ye, S = orc.gemv_fp8(d["x"], d["w"], d["ws"])
+    check_float(host_bits(y), ye, S, K)
