@@ -48,15 +48,6 @@ hipError_t run_i8(const I8Args& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int M, int GS, int R, int U, int WPB>
-hipError_t run_fp8(const F8Args& a, hipStream_t st) {
-    constexpr int rows_per_block = (64 / GS) * R * WPB;
-    dim3 grid((unsigned)((a.N + rows_per_block - 1) / rows_per_block));
-    hipLaunchKernelGGL((gemv_fp8_kernel<M, GS, R, U, WPB>), grid, dim3(64 * WPB), 0, st,
-                       a.x, a.ldx, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.y, a.ldy);
-    return hipGetLastError();
-}
-
 template <int M, int GS, int R, int U, int WPB, int XF, int WF>
 hipError_t run_w8a8_fmt(const W8A8F8Args& a, hipStream_t st) {
     constexpr int rows_per_block = (64 / GS) * R * WPB;
@@ -169,10 +160,10 @@ hipError_t run_fp8_m1_lds_wide(const void* x, int64_t K, const uint8_t* w, int64
 // 25.5 us against 17.2 / 17.3 us for the K-slice kernels), so it stops at two.
 constexpr int64_t kF8LdsMaxK = 16384;
 
-template <int M, int U>
+template <int M, int U, bool LOOP = false>
 void launch_fp8_lds_u(const F8Args& a, hipStream_t st) {
     const size_t lds = (size_t)((M * (a.K >> 3) + 63) / 64) * 1024;
-    hipLaunchKernelGGL((gemv_fp8_lds_kernel<M, U, kM1LdsWaves>), dim3((unsigned)((a.N + kM1LdsWaves - 1) / kM1LdsWaves)),
+    hipLaunchKernelGGL((gemv_fp8_lds_kernel<M, U, kM1LdsWaves, LOOP>), dim3((unsigned)((a.N + kM1LdsWaves - 1) / kM1LdsWaves)),
                        dim3(64 * kM1LdsWaves), lds, st, a.x, a.ldx, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.y, a.ldy);
 }
 
@@ -201,6 +192,18 @@ hipError_t run_fp8_lds(const F8Args& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// One token with rows of more than 16 steps on a matrix with fewer than 4096
+// rows: the same kernel taking 16 steps of the row at a time, the bf16 row in
+// LDS up to 64 KB (K <= 32768); 2048 x 32768: 17.0 against 22.7 us for the
+// per-tile matrix-core kernel, which is faster from 4096 rows (4096 x 20480:
+// 17.4 against 25.6 us).
+constexpr int64_t kF8LdsLoopMaxK = 32768;
+
+hipError_t run_fp8_lds_loop(const F8Args& a, hipStream_t st) {
+    launch_fp8_lds_u<1, 16, true>(a, st);
+    return hipGetLastError();
+}
+
 // INT8, 2..3 tokens (and one token with the quantiser fused in): one wave
 // per row, the token rows' codes shared through LDS (gemv_i8_lds_kernel).
 // 17408 x 5120: M = 2 14.9-15.1 us against 15.7-16.1 us for the lane-group
@@ -208,11 +211,11 @@ hipError_t run_fp8_lds(const F8Args& a, hipStream_t st) {
 // 16.9-17.3 us for quantiser + GEMV in two launches.
 constexpr int64_t kI8LdsMaxM = 3;
 
-template <int M, int WPB, bool QX, int U>
+template <int M, int WPB, bool QX, int U, bool LOOP = false>
 void launch_i8_lds_u(const void* x, int64_t ldx, const I8Args& a, int8_t* xq_out, int64_t ldxq, float* xs_out,
                      hipStream_t st) {
     const size_t lds = QX ? (size_t)(M * a.K) : (size_t)((M * (a.K >> 4) + 63) / 64) * 1024;
-    hipLaunchKernelGGL((gemv_i8_lds_kernel<M, U, WPB, QX>), dim3((unsigned)((a.N + WPB - 1) / WPB)), dim3(64 * WPB),
+    hipLaunchKernelGGL((gemv_i8_lds_kernel<M, U, WPB, QX, LOOP>), dim3((unsigned)((a.N + WPB - 1) / WPB)), dim3(64 * WPB),
                        lds, st, x, ldx, a.xs, a.xs_step, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.bias, a.y, a.ldy,
                        a.out_kind, xq_out, ldxq, xs_out);
 }
@@ -254,6 +257,21 @@ hipError_t run_i8_lds_wide(const I8Args& a, hipStream_t st) {
         default: QLIN_I8_LDS(16)
     }
 #undef QLIN_I8_LDS
+    return hipGetLastError();
+}
+
+// Two or three tokens with rows of more than 16 steps (K > 16384) on a matrix
+// with fewer than 4096 rows: the same kernel taking 16 steps of the row at a
+// time, while the codes fit in 64 KB of LDS.  There the per-tile matrix-core
+// kernel has fewer tiles than the chip has compute units (2048 x 32768, M =
+// 2: 16.4 against 21.5 us); from 4096 rows it is the faster one (4096 x
+// 20480: 16.9 against 24.3 us, 8192 x 28672: 38.6 against 52.0 us).
+constexpr int64_t kI8LdsLoopMaxBytes = 64 << 10;
+constexpr int64_t kLdsLoopMaxN = 4095;
+
+template <int M>
+hipError_t run_i8_lds_loop(const I8Args& a, hipStream_t st) {
+    launch_i8_lds_u<M, 4, false, 16, true>(a.xq, a.ldxq, a, nullptr, 0, nullptr, st);
     return hipGetLastError();
 }
 
@@ -502,13 +520,20 @@ hipError_t launch_gemv_i8(const I8Args& a, hipStream_t st) {
                         : run_i8_lds<3, 4, false>(a.xq, a.ldxq, a, nullptr, 0, nullptr, st);
     if (a.M >= 2 && a.M <= kI8LdsMaxM && a.K <= kI8LdsWideMaxK)
         return a.M == 2 ? run_i8_lds_wide<2>(a, st) : run_i8_lds_wide<3>(a, st);
+    if (a.M >= 2 && a.M <= kI8LdsMaxM && a.M * a.K <= kI8LdsLoopMaxBytes && a.N <= kLdsLoopMaxN)
+        return a.M == 2 ? run_i8_lds_loop<2>(a, st) : run_i8_lds_loop<3>(a, st);
     switch (a.M) {
         case 1:
             // above 8 steps the codes-in-LDS kernel keeps every step in flight
             // (4096 x 10240: the lane-group kernel loops over 8 at a time)
             if (a.K > kI8LdsMaxK && a.K <= kI8LdsWideMaxK) return run_i8_lds_wide<1>(a, st);
             QLIN_M1_BY_STEPS(run_i8, a, st)
-        case 2: return run_i8<2, 32, 2, 2, 1>(a, st);
+        case 2:
+            // above K = 16384 the per-tile matrix-core kernel (4096 x 20480:
+            // 17.2 against 20.4 us for the lane-group kernel; 2048 x 32768:
+            // 20.2 against 22.0 us)
+            if (a.K > kI8LdsWideMaxK) return run_i8_mfma(a, st);
+            return run_i8<2, 32, 2, 2, 1>(a, st);
         default: {
             // above 8 lines (one tile in flight) the K-slice kernels serve up
             // to 8 tokens (4096 x 14336: 12.7 against 13.4 us at M = 8, but
@@ -537,19 +562,21 @@ hipError_t launch_gemv_fp8(const F8Args& a, hipStream_t st) {
                 return run_fp8_m1_lds<0>(a.x, nullptr, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.y, st);
             if (a.K <= kM1LdsWideMaxK)
                 return run_fp8_m1_lds_wide(a.x, a.K, a.w, a.ldw, a.N, a.ws, a.ws_step, a.y, st);
-            return run_fp8<1, 32, 2, 1, 1>(a, st);
+            if (a.K <= kF8LdsLoopMaxK && a.N <= kLdsLoopMaxN) return run_fp8_lds_loop(a, st);
+            // else the per-tile matrix-core kernel
+            return run_fp8_mfma(a, st);
         default: {
             if (a.M == 2 && a.K <= kF8LdsMaxK) return run_fp8_lds<2>(a, st);
-            // K-slice kernels from M = 3 (and at M = 2 above K = 16384), up
-            // to 8 lines (14336 x 7168: 19.4-22.8 against 21.5-37.2 us for
-            // the per-tile kernel)
+            // K-slice kernels from M = 3, up to 8 lines (14336 x 7168:
+            // 19.4-22.8 against 21.5-37.2 us for the per-tile kernel), else
+            // the per-tile matrix-core kernel (two tokens above K = 16384 too:
+            // 4096 x 20480 18.1 against 25.6 us for the lane-group kernel)
             KsPlan p;
             if (ks_plan(a.N, a.K, kKsMaxLFloat, p)) {
                 const KsArgs k{a.x, a.ldx, nullptr, 0, (int)a.M, a.w, a.ldw, a.N, p.R,
                                a.ws, a.ws_step, nullptr, a.y, a.ldy, 0};
                 return launch_ks_f8(k, p, st);
             }
-            if (a.M == 2) return run_fp8<2, 64, 4, 1, 1>(a, st);
             return run_fp8_mfma(a, st);
         }
     }
@@ -579,7 +606,11 @@ hipError_t launch_gemv_fp8_w8a8(const W8A8F8Args& a, hipStream_t st) {
     }
     // two rows per lane group share each activation chunk's convert (measured
     // at N=17408, K=5120: 16.4 us against 17.7-18.5 us for one row per group
-    // with 2-5 steps in flight)
+    // with 2-5 steps in flight); with one step in flight per group that kernel
+    // falls behind on longer rows, where two and three tokens take the
+    // per-tile matrix-core kernel (4096 x 14336: 22.6 / 27.8 us on the VALU
+    // kernels against 12.8 us at M = 4; 7168 x 9216: 17.5 / 20.8 against 16.3)
+    if (a.M <= 3 && a.K > kM1LdsMaxK) return run_w8a8_mfma(a, st);
     if (a.M == 2) return run_w8a8<2, 32, 2, 1, 1>(a, st);
     // from three tokens the K-slice kernels where they apply (E4M3 x E4M3,
     // 17408 x 5120: 16.8 against 18.3 us for the VALU kernel below at M = 3);
@@ -594,8 +625,9 @@ hipError_t launch_gemv_fp8_w8a8(const W8A8F8Args& a, hipStream_t st) {
                        a.ws, a.ws_step, nullptr, a.y, a.ldy, 0};
         return a.x_fmt == kFmtE5M2 ? launch_ks_w8a8_e5m2(k, p, a.w_fmt, st) : launch_ks_w8a8_e4m3(k, p, a.w_fmt, st);
     }
-    // three rows per group at three tokens (17.8-17.9 us against 19.1-19.3 us
-    // for the matrix-core kernel); from four tokens the matrix core wins
+    // three rows per group at three tokens, K <= 8192 (17.8-17.9 us against
+    // 19.1-19.3 us for the matrix-core kernel); from four tokens the matrix
+    // core wins
     if (a.M == 3) return run_w8a8<3, 32, 3, 1, 1>(a, st);
     return run_w8a8_mfma(a, st);
 }

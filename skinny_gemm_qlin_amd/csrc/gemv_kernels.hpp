@@ -135,87 +135,6 @@ __global__ __launch_bounds__(64 * WPB) void gemv_i8_kernel(
         }
 }
 
-// ------------------------------------------------------------------ FP8-E4M3 weight-only
-// y = bf16(ws[n] * sum_k e4m3(w)*x): hardware E4M3 -> bf16 convert, v_dot2
-// bf16 with fp32 accumulation, the scale applied once after the reduction
-// [Z100 operator-family table, FP8 row; section 2.2].
-template <int M, int GS, int R, int U, int WPB>
-__global__ __launch_bounds__(64 * WPB) void gemv_fp8_kernel(
-    const uint16_t* __restrict__ x, int64_t ldx, int64_t K,
-    const uint8_t* __restrict__ w, int64_t ldw, int64_t N,
-    const float* __restrict__ ws, int ws_step, uint16_t* __restrict__ y, int64_t ldy) {
-    const int j = (threadIdx.x & 63) % GS;
-    const int64_t n0 = first_row<GS, R, WPB>();
-    const uint8_t* wr[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) wr[r] = w + (n0 + r < N ? n0 + r : N - 1) * ldw;
-
-    float acc[R][M];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
-
-    const int64_t nchunk = K >> 4;  // 16 codes per chunk
-    const int64_t nsteps = (nchunk + GS - 1) / GS;
-    for (int64_t s = 0; s < nsteps; s += U) {
-        u32x4_t wv[U][R], xa[U][M], xb[U][M];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t c = (s + u) * GS + j;
-            const int64_t cc = c < nchunk ? c : nchunk - 1;
-#pragma unroll
-            for (int r = 0; r < R; ++r) wv[u][r] = ld_stream(wr[r] + cc * 16);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t c = (s + u) * GS + j;
-            const int64_t cc = c < nchunk ? c : nchunk - 1;
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                const uint16_t* xp = x + m * ldx + cc * 16;
-                const u32x4_t a = ld16(xp), b = ld16(xp + 8);
-                xa[u][m] = c < nchunk ? a : u32x4_t{0, 0, 0, 0};
-                xb[u][m] = c < nchunk ? b : u32x4_t{0, 0, 0, 0};
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                bf16x2_t wb[8];
-                e4m3x16(wv[u][r], wb);
-#pragma unroll
-                for (int m = 0; m < M; ++m) {
-                    float a = acc[r][m];
-                    a = dot2(wb[0], as_bf16x2(xa[u][m].x), a);
-                    a = dot2(wb[1], as_bf16x2(xa[u][m].y), a);
-                    a = dot2(wb[2], as_bf16x2(xa[u][m].z), a);
-                    a = dot2(wb[3], as_bf16x2(xa[u][m].w), a);
-                    a = dot2(wb[4], as_bf16x2(xb[u][m].x), a);
-                    a = dot2(wb[5], as_bf16x2(xb[u][m].y), a);
-                    a = dot2(wb[6], as_bf16x2(xb[u][m].z), a);
-                    a = dot2(wb[7], as_bf16x2(xb[u][m].w), a);
-                    acc[r][m] = a;
-                }
-            }
-    }
-
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int m = 0; m < M; ++m) acc[r][m] = group_sum<GS>(acc[r][m]);
-
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const int v = r * M + m;
-            const int64_t n = n0 + r;
-            if ((v % GS) == j && n < N) y[m * ldy + n] = f32_to_bf16(acc[r][m] * ws[n * ws_step]);
-        }
-}
-
 // ------------------------------------------------------------------ FP8 W8A8
 // Both operands are FP8 codes (activations XF, weights WF: E4M3 or E5M2),
 // each widened to bf16 exactly by the hardware convert; a product of two
@@ -687,8 +606,9 @@ __global__ __launch_bounds__(64 * WPB) void gemv_fp8_m1_lds_kernel(
 // two-half layout), a wave owns one weight row with all U of its 1 KB steps
 // in flight, widens each chunk of codes once and dots it with every token
 // row; lane m writes token m's output, bf16(acc * ws).  LDS: 2 * M * K
-// bytes (whole 1 KB direct-load blocks).
-template <int M, int U, int WPB>
+// bytes (whole 1 KB direct-load blocks).  LOOP: rows of more than U steps,
+// taken U steps at a time (the next batch loaded after each one).
+template <int M, int U, int WPB, bool LOOP = false>
 __global__ __launch_bounds__(64 * WPB) void gemv_fp8_lds_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int64_t K,
     const uint8_t* __restrict__ w, int64_t ldw, int64_t N,
@@ -707,16 +627,19 @@ __global__ __launch_bounds__(64 * WPB) void gemv_fp8_lds_kernel(
         __builtin_amdgcn_global_load_lds((const void*)(x + m * ldx + c * 16 + h * 8),
                                          (lds_void_t*)(xl + (int64_t)inst * 64), 16, 0, 0);
     }
-    // 2. this wave's row, every step in flight
+    // 2. this wave's row, every step in flight (LOOP: its first U steps)
     const int64_t n = (int64_t)blockIdx.x * WPB + wv;
     const int64_t nn = n < N ? n : N - 1;
     const uint8_t* wr = w + nn * ldw;
     u32x4_t wq[U];
+    auto load_steps = [&](int s) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int c = u * 64 + lane, cc = c < nchunk ? c : nchunk - 1;
-        wq[u] = ld_stream(wr + (int64_t)cc * 16);
-    }
+        for (int u = 0; u < U; ++u) {
+            const int c = (s + u) * 64 + lane, cc = c < nchunk ? c : nchunk - 1;
+            wq[u] = ld_stream(wr + (int64_t)cc * 16);
+        }
+    };
+    load_steps(0);
     const float wsv = ws[nn * ws_step];
     // 3. publish the rows: every load issued before the U weight loads has
     //    landed once at most U loads are outstanding
@@ -725,26 +648,32 @@ __global__ __launch_bounds__(64 * WPB) void gemv_fp8_lds_kernel(
     __builtin_amdgcn_s_barrier();  // not __syncthreads(): that would also wait for the weights
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     asm volatile("" ::"s"(wsv));  // the scale waited for under the weight loads, as in the one-token kernel
-    // 4. the row's dot products
+    // 4. the row's dot products (LOOP: U steps at a time, the next U loaded
+    //    after each batch)
+    const int nsteps = LOOP ? (nchunk + 63) >> 6 : U;
     float acc[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+    for (int s = 0;; s += U) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int c = u * 64 + lane;
-        const bool ok = c < nchunk;
-        const int cc = ok ? c : nchunk - 1;
-        bf16x2_t wb[8];
-        fp8x16<kFmtE4M3>(wq[u], wb);
+        for (int u = 0; u < U; ++u) {
+            const int c = (s + u) * 64 + lane;
+            const bool ok = c < nchunk;
+            const int cc = ok ? c : nchunk - 1;
+            bf16x2_t wb[8];
+            fp8x16<kFmtE4M3>(wq[u], wb);
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-            u32x4_t a = xl[m * nh + cc], b = xl[m * nh + nchunk + cc];
-            if (!ok) a = b = u32x4_t{0, 0, 0, 0};
+            for (int m = 0; m < M; ++m) {
+                u32x4_t a = xl[m * nh + cc], b = xl[m * nh + nchunk + cc];
+                if (!ok) a = b = u32x4_t{0, 0, 0, 0};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[m] = dot2(wb[e], as_bf16x2(a[e]), acc[m]);
+                for (int e = 0; e < 4; ++e) acc[m] = dot2(wb[e], as_bf16x2(a[e]), acc[m]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[m] = dot2(wb[4 + e], as_bf16x2(b[e]), acc[m]);
+                for (int e = 0; e < 4; ++e) acc[m] = dot2(wb[4 + e], as_bf16x2(b[e]), acc[m]);
+            }
         }
+        if (!LOOP || s + U >= nsteps) break;
+        load_steps(s + U);
     }
     float out = 0.0f;
 #pragma unroll
@@ -758,8 +687,8 @@ __global__ __launch_bounds__(64 * WPB) void gemv_fp8_lds_kernel(
 // ------------------------------------------------------------------ INT8, few tokens, codes in LDS
 // W8A8 INT8 for M <= 4 tokens [Z100 operator-family table, INT8 row;
 // section 2.1].  A wave owns one weight row with all U steps of 1 KB in
-// flight (lane j reads chunk j + 64u; U <= 8 with QX, else U <= 16); the
-// workgroup's WPB waves share the M
+// flight (lane j reads chunk j + 64u; U <= 8 with QX, else U <= 16; LOOP:
+// longer rows U steps at a time); the workgroup's WPB waves share the M
 // token rows of int8 codes in LDS ([m][K] bytes), each chunk dotted with
 // v_dot4 (exact int32), summed across the wave, epilogue bf16((acc * xs) *
 // ws) then + bias, or the raw sums (out_kind 1).
@@ -772,7 +701,7 @@ __global__ __launch_bounds__(64 * WPB) void gemv_fp8_lds_kernel(
 // latency.  Workgroup 0 also writes the codes and scales out when asked.
 constexpr int kI8LdsMaxK = 8192;
 
-template <int M, int U, int WPB, bool QX>
+template <int M, int U, int WPB, bool QX, bool LOOP = false>
 __global__ __launch_bounds__(64 * WPB) void gemv_i8_lds_kernel(
     const void* __restrict__ x, int64_t ldx, const float* __restrict__ xs, int xs_step,
     int64_t K, const int8_t* __restrict__ w, int64_t ldw, int64_t N,
@@ -816,16 +745,20 @@ __global__ __launch_bounds__(64 * WPB) void gemv_i8_lds_kernel(
                                              (lds_void_t*)(xl + inst * 64), 16, 0, 0);
         }
     }
-    // 2. this wave's row
+    // 2. this wave's row (LOOP: its first U steps)
+    static_assert(!(LOOP && QX), "the fused quantiser serves rows of at most U steps");
     const int64_t n = (int64_t)blockIdx.x * WPB + wv;
     const int64_t nn = n < N ? n : N - 1;
     const int8_t* wr = w + nn * ldw;
     u32x4_t wq[U];
+    auto load_steps = [&](int s) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t c = (int64_t)u * 64 + lane, cc = c < nchunk ? c : nchunk - 1;
-        wq[u] = ld_stream(wr + cc * 16);
-    }
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = (int64_t)(s + u) * 64 + lane, cc = c < nchunk ? c : nchunk - 1;
+            wq[u] = ld_stream(wr + cc * 16);
+        }
+    };
+    load_steps(0);
     __builtin_amdgcn_sched_barrier(0);  // keep the weight loads ahead of the quantisation
     // 3. the codes in LDS
     float sc[M];
@@ -897,26 +830,31 @@ __global__ __launch_bounds__(64 * WPB) void gemv_i8_lds_kernel(
     __builtin_amdgcn_s_barrier();  // not __syncthreads(): that would also wait for the weights
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     const float wsv = ws ? ws[nn * ws_step] : 0.0f;
-    // 4. the row
+    // 4. the row (LOOP: U steps at a time, the next U loaded after each batch)
+    const int nsteps = LOOP ? (int)((nchunk + 63) >> 6) : U;
     int acc[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[m] = 0;
+    for (int s = 0;; s += U) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t c = (int64_t)u * 64 + lane;
-        const bool ok = c < nchunk;
-        const int64_t cc = ok ? c : nchunk - 1;
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = (int64_t)(s + u) * 64 + lane;
+            const bool ok = c < nchunk;
+            const int64_t cc = ok ? c : nchunk - 1;
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-            u32x4_t a = xl[m * nchunk + cc];
-            if (!ok) a = u32x4_t{0, 0, 0, 0};
-            int t = acc[m];
-            t = sdot4(wq[u].x, a.x, t);
-            t = sdot4(wq[u].y, a.y, t);
-            t = sdot4(wq[u].z, a.z, t);
-            t = sdot4(wq[u].w, a.w, t);
-            acc[m] = t;
+            for (int m = 0; m < M; ++m) {
+                u32x4_t a = xl[m * nchunk + cc];
+                if (!ok) a = u32x4_t{0, 0, 0, 0};
+                int t = acc[m];
+                t = sdot4(wq[u].x, a.x, t);
+                t = sdot4(wq[u].y, a.y, t);
+                t = sdot4(wq[u].z, a.z, t);
+                t = sdot4(wq[u].w, a.w, t);
+                acc[m] = t;
+            }
         }
+        if (!LOOP || s + U >= nsteps) break;
+        load_steps(s + U);
     }
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[m] = group_sum<64>(acc[m]);

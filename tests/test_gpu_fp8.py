@@ -58,10 +58,14 @@ def test_fp8_ragged(ql, orc, M, N, K):
 
 # one token with 9 to 16 steps of 1 KB per row (8192 < K <= 16384): the
 # LDS-staged kernel with every step in flight; a partial last step, N not a
-# multiple of the 8 rows of a workgroup, a padded row stride
+# multiple of the 8 rows of a workgroup, a padded row stride; longer rows up
+# to K = 32768 on fewer than 4096 rows: the row in LDS taken 16 steps at a
+# time; the rest on the per-tile matrix-core kernel
 @pytest.mark.parametrize("N,K,per_tensor,pad", [(777, 8208, False, 0), (4099, 12288, True, 0),
                                                 (300, 14336, False, 256), (1001, 16384, False, 0),
-                                                (65, 16368, True, 48)])
+                                                (65, 16368, True, 48), (130, 16400, False, 0),
+                                                (1000, 20480, True, 48), (2049, 32768, False, 16),
+                                                (33, 32784, False, 0), (4100, 20480, False, 0)])
 def test_fp8_one_token_long_rows(ql, orc, N, K, per_tensor, pad):
     d = gen_fp8(1, N, K, seed=N + K, per_tensor=per_tensor)
     wd = dev(d["w"]) if pad == 0 else padded(d["w"], pad)
@@ -96,9 +100,9 @@ def test_fp8_deterministic(ql):
 
 # two tokens with both rows staged in LDS (K <= 16384): K from one chunk to
 # the largest, ragged N, padded weight and activation pitches; past 16384 the
-# lane-group kernel
+# per-tile matrix-core kernel
 @pytest.mark.parametrize("M,N,K", [(2, 1001, 16), (2, 77, 1040), (2, 1001, 5120), (2, 300, 16384), (2, 2000, 10912),
-                                   (2, 9, 8192), (2, 4097, 7168), (2, 1, 4096), (2, 130, 16400)])
+                                   (2, 9, 8192), (2, 4097, 7168), (2, 1, 4096), (2, 130, 16400), (2, 1001, 24576)])
 def test_fp8_two_tokens_rows_in_lds(ql, orc, M, N, K):
     d = gen_fp8(M, N, K, seed=M * 11 + N + K, per_tensor=N % 2 == 0)
     xp = np.zeros((M, K + 24), np.uint16)

@@ -156,7 +156,9 @@ def test_w8a8_per_tensor_scales(ql, orc, M, per_channel, per_token):
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 16), (2, 3, 48), (3, 37, 272), (4, 129, 1040), (1, 77, 16400),
                                    (8, 255, 4112), (11, 17, 2064), (16, 1001, 784),
-                                   (3, 9000, 2048), (16, 9001, 2320)])
+                                   (3, 9000, 2048), (16, 9001, 2320),
+                                   # two and three tokens above K = 8192: the per-tile matrix-core kernel
+                                   (2, 1001, 8208), (3, 300, 14336), (2, 64, 20480), (3, 5, 9216)])
 @pytest.mark.parametrize("x_fmt,w_fmt", [(0, 0), (1, 1)])
 def test_w8a8_ragged(ql, orc, M, N, K, x_fmt, w_fmt):
     d, xq, xs, ye, S = _case(orc, M, N, K, x_fmt, w_fmt, seed=N + K)

@@ -96,14 +96,17 @@ def test_linear_i8_repeats_are_identical(ql):
 
 
 # the two- and three-token GEMV kernels (codes in LDS, K <= 16384; for one
-# token from K = 8208) and the lane-group kernel past that K
+# token from K = 8208; longer rows 16 steps at a time while the codes fit in
+# 64 KB and N < 4096) and the per-tile matrix-core kernel past that
 @pytest.mark.parametrize("M,N,K", [(2, 17408, 5120), (3, 17408, 5120), (2, 1, 16), (3, 9, 8192), (2, 100, 8208),
                                    (3, 1001, 1040),
                                    # 9 to 16 steps of 1 KB per row, also for one token
                                    (2, 4096, 14336), (3, 1001, 8208), (2, 77, 16384), (3, 513, 12304),
                                    (1, 4096, 14336), (1, 77, 8208), (1, 1001, 16384),
-                                   # past them: the lane-group kernel
-                                   (2, 300, 16400)])
+                                   # 16 steps at a time
+                                   (2, 300, 16400), (2, 1001, 20480), (2, 100, 32768), (3, 777, 21840),
+                                   # past them: the per-tile matrix-core kernel
+                                   (3, 64, 32768), (2, 50, 32784), (2, 4096, 20480)])
 def test_gemv_i8_two_three_tokens(ql, orc, M, N, K):
     d = gen_int8(M, N, K, seed=M * 100 + N)
     oxq, oxs = orc.act_quant_i8(d["x"])
