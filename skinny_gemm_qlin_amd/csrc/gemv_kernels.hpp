@@ -599,8 +599,9 @@ __global__ __launch_bounds__(64 * WPB) void gemv_fp8_m1_lds_kernel(
     }
 }
 
-// ------------------------------------------------------------------ E4M3 weight-only, two tokens, rows in LDS
-// The one-token kernel above for M tokens (used at M = 2) [Z100 operator-family table, FP8
+// ------------------------------------------------------------------ E4M3 weight-only, M tokens, rows in LDS
+// The one-token kernel above for M tokens (used at M = 2, and with LOOP at
+// M = 1 for rows of more than 16 steps) [Z100 operator-family table, FP8
 // row; section 2.2]: the workgroup stages the M bf16 token rows once in LDS
 // (row m in halves [m * 2 * nchunk, (m + 1) * 2 * nchunk), in the same
 // two-half layout), a wave owns one weight row with all U of its 1 KB steps
