@@ -9,12 +9,13 @@
 //     kinds (weight-only and W8A8) with the token row staged once per
 //     8-wave workgroup in LDS as bf16; block FP8 uses its own M = 1 kernel
 //     that shares the scale bytes of a batch across the wave;
-//   * M = 2: E4M3 weight-only (K <= 16384) one wave per row with both
-//     token rows in LDS; INT8 (K <= 16384) one wave per row with the codes
-//     in LDS; FP8 W8A8 VALU with 32-lane groups of two rows;
+//   * M = 2 (INT8 also M = 3): E4M3 weight-only (K <= 16384) one wave per
+//     row with both token rows in LDS; INT8 (K <= 16384) one wave per row
+//     with the codes in LDS; FP8 W8A8 (K <= 8192) VALU with 32-lane groups
+//     of two rows; longer rows as described at each launcher;
 //   * K a multiple of 1024 (at most 14336 for INT8, 8192 for the E4M3
-//     kinds; see each launcher for the token counts), from M = 3 (E4M3
-//     weight-only at M = 2 above K = 16384; W8A8 in all four format pairs): the K-slice
+//     kinds; see each launcher for the token counts), from M = 4 for INT8
+//     and M = 3 for the E4M3 kinds (W8A8 in all four format pairs): the K-slice
 //     matrix-core kernels of ks_kernels.hpp, planned here (ks_plan) and
 //     launched from ks_i8.hip / ks_f8.hip / ks_w8a8_*.hip (INT8 at M = 4 / 8 /
 //     16: 16.4 / 16.8 / 17.3 us against 17.5 / 19.1 / 21.4 us for one
@@ -529,11 +530,10 @@ hipError_t launch_gemv_i8(const I8Args& a, hipStream_t st) {
             if (a.K > kI8LdsMaxK && a.K <= kI8LdsWideMaxK) return run_i8_lds_wide<1>(a, st);
             QLIN_M1_BY_STEPS(run_i8, a, st)
         case 2:
-            // above K = 16384 the per-tile matrix-core kernel (4096 x 20480:
-            // 17.2 against 20.4 us for the lane-group kernel; 2048 x 32768:
-            // 20.2 against 22.0 us)
-            if (a.K > kI8LdsWideMaxK) return run_i8_mfma(a, st);
-            return run_i8<2, 32, 2, 2, 1>(a, st);
+            // rows the LDS kernels above do not take (K > 16384 from 4096
+            // rows, or codes past 64 KB): the per-tile matrix-core kernel
+            // (4096 x 20480: 17.2 against 20.4 us for the lane-group kernel)
+            return run_i8_mfma(a, st);
         default: {
             // above 8 lines (one tile in flight) the K-slice kernels serve up
             // to 8 tokens (4096 x 14336: 12.7 against 13.4 us at M = 8, but
