@@ -538,8 +538,15 @@ hipError_t launch_gemv_i8(const I8Args& a, hipStream_t st) {
             // above 8 lines (one tile in flight) the K-slice kernels serve up
             // to 8 tokens (4096 x 14336: 12.7 against 13.4 us at M = 8, but
             // 15.2 against 14.6 us at M = 16 for the per-tile kernel)
+            // except 12 and 13 lines with two or more tiles per workgroup,
+            // which run slower than the per-tile kernel (M = 4: 8192 x 12288
+            // 26.3 against 19.1 us, 8192 x 13312 22.1 against 19.9 us,
+            // 12288 x 12288 29.0 against 26.2 us; the compiler keeps far fewer
+            // loads in flight there: 126 VGPRs at 12 lines and two tiles
+            // against 164 at 11)
             KsPlan p;
-            if (ks_plan(a.N, a.K, a.M <= 8 ? kKsMaxLI8 : 8, p)) {
+            if (ks_plan(a.N, a.K, a.M <= 8 ? kKsMaxLI8 : 8, p) &&
+                !((p.L == 12 || p.L == 13) && (int64_t)p.T * p.npass >= 2)) {
                 const KsArgs k{a.xq, a.ldxq, a.xs, a.xs_step, (int)a.M, (const uint8_t*)a.w, a.ldw, a.N, p.R,
                                a.ws, a.ws_step, a.bias, a.y, a.ldy, a.out_kind};
                 return launch_ks_i8(k, p, st);

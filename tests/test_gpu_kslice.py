@@ -49,6 +49,8 @@ def _i8(ql, orc, M, N, K, seed, w_pad=0, bias=False):
     (4, 21000, 8192),   # L=8, T=6
     (7, 3000, 9216),    # L=9 (one tile in flight from here, up to 8 tokens), T=1
     (8, 1001, 12288),   # L=12
+    (4, 8192, 12288),   # L=12 with two tiles per unit: the per-tile matrix-core kernel
+    (6, 6000, 13312),   # L=13, two tiles: the same
     (4, 4096, 14336),   # L=14, T=1
     (5, 28672, 10240),  # L=10, seven tiles: two passes of four
     (12, 1001, 12288),  # above 8 lines and 8 tokens: the per-tile matrix-core kernel
